@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the triangle-attention forward on one MI355X.
+
+A step is one tri_attn_fwd call (the whole forward: one kernel launch) over
+the headline workload: bf16, B=1, N=768, H=4, Q=K=768, D=64, fp32 bias,
+kv_lengths drawn uniformly from {384, 392, ..., 768}; inputs resident in HBM
+before timing starts.  Prints one JSON line.
+
+  value      nominal TFLOP/s, 4*B*N*H*Q*K*D per step (the metric's formula)
+  roofline   the kernel against the bf16 dense MFMA peak, on ALGORITHMIC
+             flops (4*H*Q*D*sum_n len_n: only the keys the mask leaves)
+  cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
+             sample of the same workload (n rows), in the same unit
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBPS = 8000.0
+METRIC = "fwd TFLOP/s + % bf16 MFMA peak, triangle attn N=Q=K=768 H=4 D=64"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_config4.json")
+KERNEL_SRC = os.path.join(ROOT, "masked_attention_tri_amd", "csrc", "kernel_mfma.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4, help="named workload (4 = headline)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for counter scaling)")
+    return ap.parse_args()
+
+
+def work_counts(case):
+    """Nominal and algorithmic flops, algorithmic HBM bytes of one step."""
+    import torch
+
+    B, N, H, Q, K, D = case.shape
+    esz = case.q.element_size()
+    nominal = 4 * B * N * H * Q * K * D
+    if case.kv_lengths is not None:
+        keys = case.kv_lengths.view(B, N).clamp(0, K).to(torch.int64)  # visited keys per (b,n)
+        key_rows = int(keys.sum()) * H  # sum over (b,n,h) of visited keys
+        alg = 4 * Q * D * key_rows
+    elif case.block is not None:
+        # whole visited blocks (union of both lists, duplicates once)
+        blk = case.block
+        nkb = -(-K // blk.kv_block)
+        visited = 0
+        pairs = [(blk.kv_num_blocks, blk.kv_indices)]
+        if blk.full_kv_num_blocks is not None:
+            pairs.append((blk.full_kv_num_blocks, blk.full_kv_indices))
+        seen = torch.zeros(*blk.kv_num_blocks.shape, nkb + 1, dtype=torch.bool)
+        for num, idx in pairs:
+            j = torch.arange(idx.shape[-1])
+            ids = idx.long()
+            ok = (j < num.unsqueeze(-1)) & (ids >= 0) & (ids < nkb)
+            seen.scatter_(-1, torch.where(ok, ids, nkb), True)
+        lead = blk.kv_num_blocks.shape[:3]
+        reps = (B * N * H) // max(1, math.prod(lead))
+        visited = int(seen[..., :nkb].sum()) * reps
+        key_rows = visited * blk.kv_block * blk.q_block // Q  # key visits per query row
+        alg = 4 * D * visited * blk.kv_block * blk.q_block
+    else:
+        key_rows = B * N * H * K
+        alg = nominal
+    qo = 2 * B * N * H * Q * D * esz
+    kv = 2 * key_rows * D * esz
+    bias = B * H * Q * K * 4 if case.bias is not None else 0
+    aux = 2 * B * N * H * Q * 4
+    mask = (B * N * 4) if case.kv_lengths is not None else (B * N * K if case.mask is not None else 0)
+    return nominal, alg, qo + kv + bias + aux + mask
+
+
+def traffic_entry():
+    """Measured HBM bytes per launch, if the counters were taken on this
+    exact kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    if t.get("kernel_source_sha256") != src:
+        return None
+    return t
+
+
+def cpu_baseline(case, target_s):
+    """Time the fp64 oracle on the first n rows of the workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    B, N, H, Q, K, D = case.shape
+    threads = oracle.default_threads()
+
+    def run(ns):
+        sub_q, sub_k, sub_v = case.q[:, :ns], case.k[:, :ns], case.v[:, :ns]
+        lens = case.kv_lengths[:, :ns] if case.kv_lengths is not None else None
+        mask = case.mask[:, :ns] if case.mask is not None else None
+        t0 = time.perf_counter()
+        out = oracle.oracle_fwd(sub_q, sub_k, sub_v, case.bias, kv_lengths=lens, mask=mask,
+                                scale=case.scale, threads=threads)
+        return time.perf_counter() - t0, out
+
+    dt1, _ = run(1)
+    ns = max(1, min(N, int(target_s / max(dt1, 1e-3))))
+    dt, out = run(ns)
+    flops = 4 * B * ns * H * Q * K * D  # nominal formula, as for `value`
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {ns} of {N} n rows (all b, h, q), fp64, {dt:.1f} s",
+        "seconds": round(dt, 3),
+    }, ns, out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build "
+              "has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import masked_attention_tri_amd as mat
+    from masked_attention_tri_amd import _native as nat
+    from masked_attention_tri_amd import workloads as wl
+
+    mat.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case = wl.make_config(args.config)
+    g = case.to(dev)
+    B, N, H, Q, K, D = case.shape
+    out = torch.empty_like(g.q)
+    lse = torch.empty(B, N, H, Q, device=dev)
+    mx = torch.empty(B, N, H, Q, device=dev)
+    keep = []
+    desc = None
+    if g.mask is not None:
+        m = g.mask.contiguous().view(torch.uint8)
+        keep.append(m)
+        desc = nat.TriAttnMask()
+        desc.kind = nat.TRIATTN_MASK_DENSE
+        desc.dense = m.data_ptr()
+    elif g.kv_lengths is not None:
+        desc = nat.TriAttnMask()
+        desc.kind = nat.TRIATTN_MASK_KV_LENGTHS
+        desc.kv_lengths = g.kv_lengths.data_ptr()
+    elif g.block is not None:
+        b = g.block
+        bm = mat.BlockMask.from_kv_blocks(b.kv_num_blocks, b.kv_indices, b.full_kv_num_blocks,
+                                          b.full_kv_indices, BLOCK_SIZE=(b.kv_block, b.q_block),
+                                          mask_mod=b.mask_mod)
+        desc, conv = bm._descriptor(B, N, H, Q, K, dev)
+        keep.extend(conv)
+    shape = nat.TriAttnShape(B, N, H, Q, K, D)
+    dtype = nat.DTYPE_CODES[g.q.dtype]
+    scale = math.nan if g.scale is None else g.scale
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        st = mat.tri_attn_fwd(shape, dtype, g.q, g.k, g.v, g.bias, desc, scale, out, lse, mx,
+                              stream)
+        if st != nat.TRIATTN_OK:
+            raise RuntimeError(mat.tri_attn_status_str(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    # HIP events on the stream the kernel is launched on.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)",
+          file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        # plain copy of known size, so byte counters can be scaled
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    nominal, alg, alg_bytes = work_counts(case)
+    sec = ms * 1e-3
+    value = nominal / sec / 1e12
+    alg_tflops = alg / sec / 1e12
+    tr = traffic_entry()
+    traffic = None if tr is None else tr["bytes_per_launch"]
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[
+            case.dtype],
+        "data": "synthetic",
+        "pct_bf16_peak_nominal": round(100.0 * value / PEAK_BF16_TFLOPS, 3),
+        "tflops_algorithmic": round(alg_tflops, 3),
+        "pct_bf16_peak_algorithmic": round(100.0 * alg_tflops / PEAK_BF16_TFLOPS, 3),
+        "hbm_GBps_algorithmic": round(alg_bytes / sec / 1e9, 1),
+        "config": {
+            "workload": case.name,
+            "config_index": args.config,
+            "B": B, "N": N, "H": H, "Q": Q, "K": K, "D": D,
+            "nominal_flop": nominal,
+            "algorithmic_flop": alg,
+            "algorithmic_bytes": alg_bytes,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(alg_tflops, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(alg_tflops / PEAK_BF16_TFLOPS, 5),
+            "traffic": traffic,
+            "hbm_frac_algorithmic": round(alg_bytes / sec / 1e9 / PEAK_HBM_GBPS, 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        cb, ns, oracle_out = cpu_baseline(case, args.cpu_seconds)
+        # the same rows of the GPU result, for reference
+        import numpy as np
+
+        go = out[:, :ns].double().cpu().numpy()
+        cb["max_abs_err_O_vs_gpu"] = float(np.abs(go - oracle_out[0]).max())
+        res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

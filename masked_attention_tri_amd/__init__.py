@@ -1,0 +1,288 @@
+"""masked_attention_tri_amd: MI355X (gfx950) forward pass of masked, biased
+triangle attention.
+
+Python face of libtriattn (include/triattn.h).  ``triangle_attention``
+follows the signature of cuEquivariance's ``triangle_attention`` API page
+(q, k, v, bias, mask=None, scale=None, return_aux=False, *, kv_lengths=None)
+and adds ``block_mask`` for the BlockMask list format of the
+tensorplay.nn.attention page.  PyTorch only supplies device memory and
+streams; the computation runs in the library's HIP kernels, and there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple, Union
+
+import torch
+
+from . import _native
+from ._native import (  # noqa: F401
+    TRIATTN_BF16,
+    TRIATTN_ERR_HIP,
+    TRIATTN_ERR_INVALID_ARG,
+    TRIATTN_ERR_UNSUPPORTED,
+    TRIATTN_F16,
+    TRIATTN_F32,
+    TRIATTN_MASK_BLOCK,
+    TRIATTN_MASK_DENSE,
+    TRIATTN_MASK_KV_LENGTHS,
+    TRIATTN_MASK_NONE,
+    TRIATTN_MOD_CAUSAL,
+    TRIATTN_MOD_NONE,
+    TRIATTN_OK,
+    LibraryNotBuilt,
+    TriAttnMask,
+    TriAttnShape,
+    load_library,
+    tri_attn_check,
+    tri_attn_fwd,
+    tri_attn_mask_to_kv_lengths,
+    tri_attn_status_str,
+)
+
+__all__ = ["triangle_attention", "mask_to_kv_lengths", "BlockMask", "causal_mask",
+           "tri_attn_fwd", "tri_attn_check", "tri_attn_status_str",
+           "tri_attn_mask_to_kv_lengths", "load_library"]
+
+
+def causal_mask(b, h, q_idx, kv_idx):
+    """The causal mask_mod (q_idx >= kv_idx), in the (b, h, q_idx, kv_idx)
+    callable form of the BlockMask page.  Passing this function (or the
+    string "causal") as ``mask_mod`` selects the library's causal predicate;
+    other callables cannot cross the C ABI and are rejected."""
+    return q_idx >= kv_idx
+
+
+class BlockMask:
+    """Block-sparse key mask in the list format of the tensorplay.nn.attention
+    page: (kv_num_blocks, kv_indices) plus the optional (full_kv_num_blocks,
+    full_kv_indices) pair whose blocks skip mask_mod.
+
+    Tensors have shape (..., ROWS) and (..., ROWS, MAX_BLOCKS); up to three
+    leading dims broadcast against (B, N, H) like numpy (size 1 or the full
+    size).  BLOCK_SIZE is an int or, as the page writes it, the tuple
+    (KV_BLOCK_SIZE, Q_BLOCK_SIZE).  mask_mod is None, "causal" or
+    ``causal_mask``.
+    """
+
+    def __init__(self, kv_num_blocks, kv_indices, full_kv_num_blocks=None,
+                 full_kv_indices=None, BLOCK_SIZE: Union[int, Tuple[int, int]] = 128,
+                 mask_mod=None, seq_lengths: Optional[Tuple[int, int]] = None):
+        if kv_indices.dim() < 2:
+            raise RuntimeError("BlockMask kv_indices must have at least 2 dimensions")
+        if (full_kv_num_blocks is None) != (full_kv_indices is None):
+            raise AssertionError("full_kv_num_blocks and full_kv_indices must be given together")
+        if isinstance(BLOCK_SIZE, int):
+            kvb = qb = int(BLOCK_SIZE)
+        else:
+            kvb, qb = (int(x) for x in BLOCK_SIZE)
+        if mask_mod is None or mask_mod == "none":
+            mod = TRIATTN_MOD_NONE
+        elif mask_mod == "causal" or mask_mod is causal_mask:
+            mod = TRIATTN_MOD_CAUSAL
+        else:
+            raise ValueError("mask_mod must be None, 'causal' or masked_attention_tri_amd."
+                             "causal_mask; arbitrary callables cannot cross the C ABI")
+        self.kv_num_blocks = kv_num_blocks
+        self.kv_indices = kv_indices
+        self.full_kv_num_blocks = full_kv_num_blocks
+        self.full_kv_indices = full_kv_indices
+        self.kv_block = kvb
+        self.q_block = qb
+        self.mask_mod = mod
+        self.seq_lengths = seq_lengths
+
+    @classmethod
+    def from_kv_blocks(cls, kv_num_blocks, kv_indices, full_kv_num_blocks=None,
+                       full_kv_indices=None, BLOCK_SIZE: Union[int, Tuple[int, int]] = 128,
+                       mask_mod=None, seq_lengths: Optional[Tuple[int, int]] = None):
+        return cls(kv_num_blocks, kv_indices, full_kv_num_blocks, full_kv_indices, BLOCK_SIZE,
+                   mask_mod, seq_lengths)
+
+    @property
+    def shape(self):
+        """(*leading, Q_LEN, KV_LEN) of the dense mask this describes."""
+        rows = self.kv_num_blocks.shape[-1]
+        q_len, kv_len = self.seq_lengths or (rows * self.q_block,
+                                              self.kv_indices.shape[-1] * self.kv_block)
+        return (*self.kv_num_blocks.shape[:-1], q_len, kv_len)
+
+    def numel(self) -> int:
+        """Elements of the dense mask, not accounting for sparsity."""
+        return math.prod(self.shape)
+
+    def sparsity(self) -> float:
+        """Percentage of blocks not computed (visited = union of both lists,
+        duplicates and out-of-range ids ignored).  Metadata helper; reads the
+        lists on their device with torch ops."""
+        q_len, kv_len = self.shape[-2:]
+        nkb = -(-kv_len // self.kv_block)
+        rows = self.kv_num_blocks.shape[-1]
+        visited = torch.zeros(*self.kv_num_blocks.shape, nkb + 1, dtype=torch.bool,
+                              device=self.kv_num_blocks.device)
+        pairs = [(self.kv_num_blocks, self.kv_indices)]
+        if self.full_kv_num_blocks is not None:
+            pairs.append((self.full_kv_num_blocks, self.full_kv_indices))
+        for num, idx in pairs:
+            j = torch.arange(idx.shape[-1], device=idx.device)
+            live = j < num.unsqueeze(-1).clamp(min=0)
+            ids = idx.long()
+            ok = live & (ids >= 0) & (ids < nkb)
+            tgt = torch.where(ok, ids, torch.full_like(ids, nkb))
+            visited.scatter_(-1, tgt, torch.ones_like(tgt, dtype=torch.bool))
+        total = visited[..., :nkb].numel()
+        if total == 0:
+            return 0.0
+        return 100.0 * (1.0 - visited[..., :nkb].sum().item() / total)
+
+    def _descriptor(self, B, N, H, Q, K, device):
+        rows = -(-Q // self.q_block)
+        tensors = [self.kv_num_blocks, self.kv_indices, self.full_kv_num_blocks,
+                   self.full_kv_indices]
+        if self.kv_num_blocks.shape[-1] != rows:
+            raise ValueError(f"kv_num_blocks has {self.kv_num_blocks.shape[-1]} rows; "
+                             f"Q={Q} with q block {self.q_block} needs {rows}")
+        lead = tuple(self.kv_num_blocks.shape[:-1])
+        if len(lead) > 3:
+            raise ValueError("at most three leading (B, N, H) dims")
+        lead = (1,) * (3 - len(lead)) + lead
+        for size, full in zip(lead, (B, N, H)):
+            if size not in (1, full):
+                raise ValueError(f"leading dims {lead} do not broadcast against {(B, N, H)}")
+        conv = []
+        for t in tensors:
+            if t is None:
+                conv.append(None)
+                continue
+            if t.device != device:
+                raise ValueError("block lists must be on the same device as q")
+            t = t.to(torch.int32).contiguous()
+            conv.append(t)
+        for idx_t in (conv[1], conv[3]):
+            if idx_t is not None and tuple(idx_t.shape[:-1]) != tuple(self.kv_num_blocks.shape):
+                raise ValueError("index tensors must be (..., ROWS, MAX_BLOCKS)")
+        lb, ln, lh = lead
+        d = TriAttnMask()
+        d.kind = TRIATTN_MASK_BLOCK
+        d.mask_mod = self.mask_mod
+        d.kv_num_blocks = conv[0].data_ptr()
+        d.kv_indices = conv[1].data_ptr()
+        d.full_kv_num_blocks = conv[2].data_ptr() if conv[2] is not None else None
+        d.full_kv_indices = conv[3].data_ptr() if conv[3] is not None else None
+        d.q_block = self.q_block
+        d.kv_block = self.kv_block
+        d.max_blocks = conv[1].shape[-1]
+        d.full_max_blocks = conv[3].shape[-1] if conv[3] is not None else 1
+        d.stride_h = 1 if lh == H and H > 1 else 0
+        d.stride_n = lh if ln == N and N > 1 else 0
+        d.stride_b = ln * lh if lb == B and B > 1 else 0
+        return d, conv  # keep the converted tensors alive for the call
+
+
+def _as5(x, name):
+    if x is None:
+        return None
+    if x.dim() == 4:
+        return x.unsqueeze(0)
+    if x.dim() != 5:
+        raise ValueError(f"{name} must be 4-D (B=1) or 5-D, got {tuple(x.shape)}")
+    return x
+
+
+def triangle_attention(q, k, v, bias=None, mask=None, scale: Optional[float] = None,
+                       return_aux: bool = False, *, kv_lengths=None,
+                       block_mask: Optional[BlockMask] = None, stream=None):
+    """Attention_q = sum_k softmax_k(s Q_q.K_k + B_qk if key k is valid else
+    -1e9) V_k over (B, N, H, Q, D) tensors.
+
+    q (B,N,H,Q,D); k, v (B,N,H,K,D); bias (B,1,H,Q,K) (cast to fp32) or None;
+    mask (B,N,1,1,K) (cast to bool) | kv_lengths (B,N,1,1,1) int32 |
+    block_mask: at most one.  4-D inputs are accepted when B = 1.  scale None
+    means 1/sqrt(D).  Returns O (q's dtype), or (O, lse, max) with fp32 lse
+    and max of shape (B,N,H,Q,1) when return_aux.  Runs on `stream` (torch's
+    current stream by default) and does not synchronise.
+    """
+    if mask is not None and kv_lengths is not None:
+        raise ValueError("pass either mask or kv_lengths, not both")
+    if block_mask is not None and (mask is not None or kv_lengths is not None):
+        raise ValueError("block_mask cannot be combined with mask or kv_lengths")
+    four_d = q.dim() == 4
+    q5, k5, v5 = _as5(q, "q"), _as5(k, "k"), _as5(v, "v")
+    bias5, mask5, len5 = _as5(bias, "bias"), _as5(mask, "mask"), _as5(kv_lengths, "kv_lengths")
+    if q5.dtype not in _native.DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q5.dtype}")
+    if k5.dtype != q5.dtype or v5.dtype != q5.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    if not q5.is_cuda:
+        raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    B, N, H, Q, D = q5.shape
+    K = k5.shape[3]
+    if tuple(k5.shape) != (B, N, H, K, D) or tuple(v5.shape) != (B, N, H, K, D):
+        raise ValueError(f"k and v must be (B,N,H,K,D) = {(B, N, H, K, D)}")
+    dev = q5.device
+    q5, k5, v5 = q5.contiguous(), k5.contiguous(), v5.contiguous()
+    if bias5 is not None:
+        if tuple(bias5.shape) != (B, 1, H, Q, K):
+            raise ValueError(f"bias must be (B,1,H,Q,K) = {(B, 1, H, Q, K)}")
+        bias5 = bias5.to(device=dev, dtype=torch.float32).contiguous()
+
+    desc = None
+    keep = []
+    if mask5 is not None:
+        if tuple(mask5.shape) != (B, N, 1, 1, K):
+            raise ValueError(f"mask must be (B,N,1,1,K) = {(B, N, 1, 1, K)}")
+        m = mask5.to(device=dev, dtype=torch.bool).contiguous().view(torch.uint8)
+        keep.append(m)
+        desc = TriAttnMask()
+        desc.kind = TRIATTN_MASK_DENSE
+        desc.dense = m.data_ptr()
+    elif len5 is not None:
+        if tuple(len5.shape) != (B, N, 1, 1, 1):
+            raise ValueError(f"kv_lengths must be (B,N,1,1,1) = {(B, N, 1, 1, 1)}")
+        ln = len5.to(device=dev, dtype=torch.int32).contiguous()
+        keep.append(ln)
+        desc = TriAttnMask()
+        desc.kind = TRIATTN_MASK_KV_LENGTHS
+        desc.kv_lengths = ln.data_ptr()
+    elif block_mask is not None:
+        desc, conv = block_mask._descriptor(B, N, H, Q, K, dev)
+        keep.extend(conv)
+
+    out = torch.empty_like(q5)
+    lse = torch.empty(B, N, H, Q, 1, device=dev, dtype=torch.float32)
+    mx = torch.empty(B, N, H, Q, 1, device=dev, dtype=torch.float32)
+    shape = TriAttnShape(B, N, H, Q, K, D)
+    s = math.nan if scale is None else float(scale)
+    st = tri_attn_fwd(shape, _native.DTYPE_CODES[q5.dtype], q5, k5, v5, bias5, desc, s, out,
+                      lse, mx, stream)
+    if st != TRIATTN_OK:
+        raise RuntimeError(f"tri_attn_fwd: {tri_attn_status_str(st)}")
+    if four_d:
+        out, lse, mx = out.squeeze(0), lse.squeeze(0), mx.squeeze(0)
+    return (out, lse, mx) if return_aux else out
+
+
+def mask_to_kv_lengths(mask):
+    """Right-padded (B,N,1,1,K) bool mask -> (B,N,1,1,1) int32 lengths
+    (4-D (N,1,1,K) -> (N,1,1,1)).  Raises ValueError if a row is not a
+    prefix (a masked key followed by a valid one).  Synchronises once to read
+    that check."""
+    four_d = mask.dim() == 4
+    m5 = _as5(mask, "mask")
+    if not m5.is_cuda:
+        raise ValueError("mask must be on a GPU device")
+    B, N = m5.shape[:2]
+    K = m5.shape[-1]
+    if tuple(m5.shape) != (B, N, 1, 1, K):
+        raise ValueError("mask must be (B,N,1,1,K)")
+    m = m5.to(torch.bool).contiguous().view(torch.uint8)
+    lens = torch.empty(B, N, 1, 1, 1, device=m.device, dtype=torch.int32)
+    bad = torch.empty(1, device=m.device, dtype=torch.int32)
+    st = tri_attn_mask_to_kv_lengths(m, B * N, K, lens, bad)
+    if st != TRIATTN_OK:
+        raise RuntimeError(f"tri_attn_mask_to_kv_lengths: {tri_attn_status_str(st)}")
+    if int(bad.item()) != 0:
+        raise ValueError(f"{int(bad.item())} mask rows are not right-padded prefixes; "
+                         "pass the dense mask instead")
+    return lens.squeeze(0) if four_d else lens

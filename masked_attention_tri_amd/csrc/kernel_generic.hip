@@ -1,0 +1,203 @@
+// Generic forward kernel: one wavefront per query row, fp32 arithmetic.
+//
+// Serves every (dtype, D) in the envelope of the triangle_attention page
+// (Notes item 3) and every mask form; it is the path for fp32 inputs and
+// for shapes the MFMA kernel is not instantiated for.  Lanes split the keys
+// for the logits and the d coordinates for P.V; the softmax runs online over
+// chunks of 64 keys with a running max and sum (the max-shifted evaluation of
+// the page's softmax), so a row of any length needs O(D) state.
+#include <math.h>
+
+#include "triattn_internal.h"
+
+namespace triattn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) {
+    return static_cast<float>(x);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+__device__ __forceinline__ bool test_bit(const uint32_t* bits, int64_t i) {
+    return (bits[i >> 5] >> (i & 31)) & 1u;
+}
+
+// Sets the bit of every in-range block id among the first `count` entries
+// of one BlockMask list row (the tensorplay.nn.attention page, Basics: the
+// to-dense loop marks each listed block; later entries are undefined).
+__device__ void mark_list(uint32_t* bits, const int32_t* counts, const int32_t* ids,
+                          int64_t list_row, int64_t width, int64_t n_blocks, int lane) {
+    int64_t count = counts[list_row];
+    count = count < 0 ? 0 : (count > width ? width : count);
+    const int32_t* row = ids + list_row * width;
+    for (int64_t j = lane; j < count; j += 64) {
+        const int64_t id = row[j];
+        if (id >= 0 && id < n_blocks) atomicOr(&bits[id >> 5], 1u << (id & 31));
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
+    __shared__ uint32_t listed_bits[kWaves][kWords];
+    __shared__ uint32_t full_bits[kWaves][kWords];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t total = p.B * p.N * p.H * p.Q;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    const bool active = row < total;
+    const int64_t r = active ? row : 0;
+    const int64_t qi = r % p.Q;
+    const int64_t h = (r / p.Q) % p.H;
+    const int64_t n = (r / (p.Q * p.H)) % p.N;
+    const int64_t b = r / (p.Q * p.H * p.N);
+    const int64_t D = p.D, K = p.K;
+    const int64_t bnh = (b * p.N + n) * p.H + h;
+    const T* qrow = static_cast<const T*>(p.q) + r * D;
+    const T* kbase = static_cast<const T*>(p.k) + bnh * K * D;
+    const T* vbase = static_cast<const T*>(p.v) + bnh * K * D;
+    const float* brow = p.bias ? p.bias + ((b * p.H + h) * p.Q + qi) * K : nullptr;
+
+    // Visited and full kv blocks of this row's BlockMask row.
+    const bool block_kind = p.mask_kind == TRIATTN_MASK_BLOCK;
+    if (block_kind) {  // uniform over the workgroup
+        const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
+        for (int w = lane; w < words; w += 64) {
+            listed_bits[wave][w] = 0u;
+            full_bits[wave][w] = 0u;
+        }
+        __syncthreads();
+        if (active) {
+            const int64_t inst = b * p.stride_b + n * p.stride_n + h * p.stride_h;
+            const int64_t list_row = inst * p.n_q_rows + qi / p.q_block;
+            mark_list(listed_bits[wave], p.kv_num_blocks, p.kv_indices, list_row, p.max_blocks,
+                      p.n_kv_blocks, lane);
+            if (p.full_kv_num_blocks) {
+                mark_list(full_bits[wave], p.full_kv_num_blocks, p.full_kv_indices, list_row,
+                          p.full_max_blocks, p.n_kv_blocks, lane);
+                mark_list(listed_bits[wave], p.full_kv_num_blocks, p.full_kv_indices, list_row,
+                          p.full_max_blocks, p.n_kv_blocks, lane);
+            }
+        }
+        __syncthreads();
+    }
+    if (!active) return;
+
+    // Keys at or past `limit` are never valid.
+    int64_t limit = K;
+    if (p.mask_kind == TRIATTN_MASK_KV_LENGTHS) {
+        const int64_t len = p.kv_lengths[b * p.N + n];
+        limit = len < 0 ? 0 : (len > K ? K : len);
+    }
+    const uint8_t* mrow = p.mask_kind == TRIATTN_MASK_DENSE ? p.dense + (b * p.N + n) * K : nullptr;
+
+    float m = -INFINITY;  // running max of the valid logits
+    float l = 0.f;        // running sum of exp(z - m)
+    float o0 = 0.f, o1 = 0.f;  // O[lane], O[lane + 64]
+    const bool has0 = lane < D, has1 = lane + 64 < D;
+
+    for (int64_t c0 = 0; c0 < limit; c0 += 64) {
+        const int64_t kk = c0 + lane;
+        bool valid = kk < limit;
+        if (valid && mrow) valid = mrow[kk] != 0;
+        if (valid && block_kind) {
+            const int64_t blk = kk / p.kv_block;
+            if (!test_bit(listed_bits[wave], blk)) {
+                valid = false;
+            } else if (!test_bit(full_bits[wave], blk) && p.mask_mod == TRIATTN_MOD_CAUSAL) {
+                valid = qi >= kk;
+            }
+        }
+        float z = -INFINITY;
+        if (valid) {
+            const T* krow = kbase + kk * D;
+            float dot = 0.f;
+            for (int64_t d = 0; d < D; ++d) dot = fmaf(to_f32(qrow[d]), to_f32(krow[d]), dot);
+            z = fmaf(dot, p.scale, brow ? brow[kk] : 0.f);
+        }
+        const float m_new = fmaxf(m, wave_max(z));
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = expf(m - m_use);
+        const float pz = valid ? expf(z - m_use) : 0.f;
+        l = l * alpha + wave_sum(pz);
+        o0 *= alpha;
+        o1 *= alpha;
+        const int64_t jmax = (limit - c0) < 64 ? (limit - c0) : 64;
+        for (int j = 0; j < jmax; ++j) {
+            const float pj = __shfl(pz, j);
+            if (pj == 0.f) continue;  // uniform: pj is the same in every lane
+            const T* vrow = vbase + (c0 + j) * D;
+            if (has0) o0 = fmaf(pj, to_f32(vrow[lane]), o0);
+            if (has1) o1 = fmaf(pj, to_f32(vrow[lane + 64]), o1);
+        }
+        m = m_new;
+    }
+
+    float lse, mx;
+    if (m == -INFINITY) {
+        // No valid key: every logit is the -1e9 replacement, so the softmax
+        // is uniform over all K keys.
+        o0 = o1 = 0.f;
+        for (int64_t kk = 0; kk < K; ++kk) {
+            const T* vrow = vbase + kk * D;
+            if (has0) o0 += to_f32(vrow[lane]);
+            if (has1) o1 += to_f32(vrow[lane + 64]);
+        }
+        const float inv = 1.0f / static_cast<float>(K);
+        o0 *= inv;
+        o1 *= inv;
+        mx = kMaskedLogit;
+        lse = kMaskedLogit + logf(static_cast<float>(K));
+    } else {
+        const float inv = 1.0f / l;
+        o0 *= inv;
+        o1 *= inv;
+        mx = m;
+        lse = m + logf(l);
+    }
+    T* orow = static_cast<T*>(p.out) + r * D;
+    if (has0) orow[lane] = static_cast<T>(o0);
+    if (has1) orow[lane + 64] = static_cast<T>(o1);
+    if (lane == 0) {
+        if (p.lse) p.lse[r] = lse;
+        if (p.mx) p.mx[r] = mx;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_generic(const Params& p, int32_t dtype, hipStream_t stream) {
+    const int64_t rows = p.B * p.N * p.H * p.Q;
+    const int64_t blocks = (rows + kWaves - 1) / kWaves;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kWaves);
+    switch (dtype) {
+    case TRIATTN_F32:
+        hipLaunchKernelGGL(generic_fwd_kernel<float>, grid, block, 0, stream, p);
+        break;
+    case TRIATTN_F16:
+        hipLaunchKernelGGL(generic_fwd_kernel<_Float16>, grid, block, 0, stream, p);
+        break;
+    case TRIATTN_BF16:
+        hipLaunchKernelGGL(generic_fwd_kernel<__bf16>, grid, block, 0, stream, p);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace triattn

@@ -1,0 +1,196 @@
+// Host entry points of libtriattn: argument validation, instantiation
+// choice and launch.  The arguments follow the triangle_attention API page
+// (q, k, v, bias, mask | kv_lengths, scale; outputs O, lse, max) and the
+// BlockMask list format of the tensorplay.nn.attention page; the calling
+// convention (caller-owned buffers, scalar scale, stream last) follows the
+// fused-attention C functions of Transformer Engine's fused_attn.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "triattn_internal.h"
+
+namespace {
+
+using triattn::Params;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// a*b without signed overflow, or -1.
+int64_t mul_or_neg(int64_t a, int64_t b) {
+    if (a < 0 || b < 0) return -1;
+    if (a == 0 || b == 0) return 0;
+    if (a > INT64_MAX / b) return -1;
+    return a * b;
+}
+
+triattn_status check_impl(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                          const void* k, const void* v, const float* bias,
+                          const tri_attn_mask* mask, float scale, const void* out,
+                          const float* lse, const float* mx) {
+    if (!shape || !q || !k || !v || !out) return TRIATTN_ERR_INVALID_ARG;
+    const int64_t B = shape->B, N = shape->N, H = shape->H, Q = shape->Q, K = shape->K,
+                  D = shape->D;
+    if (B < 0 || N < 0 || H < 0 || Q < 0 || K < 1 || D < 1) return TRIATTN_ERR_INVALID_ARG;
+    if (dtype != TRIATTN_F32 && dtype != TRIATTN_F16 && dtype != TRIATTN_BF16)
+        return TRIATTN_ERR_INVALID_ARG;
+    if (isinf(scale)) return TRIATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return TRIATTN_ERR_INVALID_ARG;
+    if (!aligned(bias, 4) || !aligned(lse, 4) || !aligned(mx, 4)) return TRIATTN_ERR_INVALID_ARG;
+
+    if (mask) {
+        switch (mask->kind) {
+        case TRIATTN_MASK_NONE:
+            break;
+        case TRIATTN_MASK_DENSE:
+            // a dense mask and kv_lengths are mutually exclusive
+            if (!mask->dense || mask->kv_lengths) return TRIATTN_ERR_INVALID_ARG;
+            break;
+        case TRIATTN_MASK_KV_LENGTHS:
+            if (!mask->kv_lengths || mask->dense) return TRIATTN_ERR_INVALID_ARG;
+            break;
+        case TRIATTN_MASK_BLOCK:
+            if (!mask->kv_num_blocks || !mask->kv_indices) return TRIATTN_ERR_INVALID_ARG;
+            if (mask->dense || mask->kv_lengths) return TRIATTN_ERR_INVALID_ARG;
+            if ((mask->full_kv_num_blocks == nullptr) != (mask->full_kv_indices == nullptr))
+                return TRIATTN_ERR_INVALID_ARG;
+            if (mask->q_block < 1 || mask->kv_block < 1 || mask->max_blocks < 1)
+                return TRIATTN_ERR_INVALID_ARG;
+            if (mask->full_kv_num_blocks && mask->full_max_blocks < 1)
+                return TRIATTN_ERR_INVALID_ARG;
+            if (mask->mask_mod != TRIATTN_MOD_NONE && mask->mask_mod != TRIATTN_MOD_CAUSAL)
+                return TRIATTN_ERR_INVALID_ARG;
+            if (mask->stride_b < 0 || mask->stride_n < 0 || mask->stride_h < 0)
+                return TRIATTN_ERR_INVALID_ARG;
+            if (!aligned(mask->kv_num_blocks, 4) || !aligned(mask->kv_indices, 4) ||
+                !aligned(mask->full_kv_num_blocks, 4) || !aligned(mask->full_kv_indices, 4))
+                return TRIATTN_ERR_INVALID_ARG;
+            if ((K + mask->kv_block - 1) / mask->kv_block > triattn::kMaxKvBlocks)
+                return TRIATTN_ERR_UNSUPPORTED;
+            break;
+        default:
+            return TRIATTN_ERR_INVALID_ARG;
+        }
+        if (mask->kind == TRIATTN_MASK_KV_LENGTHS && !aligned(mask->kv_lengths, 4))
+            return TRIATTN_ERR_INVALID_ARG;
+    }
+
+    // Envelope of the triangle_attention page (Notes item 3).
+    if (dtype == TRIATTN_F32) {
+        if (D > 32 || D % 4 != 0) return TRIATTN_ERR_UNSUPPORTED;
+    } else {
+        if (D > 128 || D % 8 != 0) return TRIATTN_ERR_UNSUPPORTED;
+    }
+
+    // Index range: element counts must fit comfortably in int64, and the
+    // row count in the launch grid.
+    const int64_t rows = mul_or_neg(mul_or_neg(mul_or_neg(B, N), H), Q);
+    const int64_t kv = mul_or_neg(mul_or_neg(mul_or_neg(B, N), H), K);
+    const int64_t bias_elems = mul_or_neg(mul_or_neg(mul_or_neg(B, H), Q), K);
+    if (rows < 0 || kv < 0 || bias_elems < 0) return TRIATTN_ERR_UNSUPPORTED;
+    if (mul_or_neg(rows, D) < 0 || mul_or_neg(kv, D) < 0) return TRIATTN_ERR_UNSUPPORTED;
+    if (rows > (int64_t(1) << 40) || kv > (int64_t(1) << 40)) return TRIATTN_ERR_UNSUPPORTED;
+    if (mul_or_neg(mul_or_neg(B, N), K) < 0) return TRIATTN_ERR_UNSUPPORTED;
+    return TRIATTN_OK;
+}
+
+Params make_params(const tri_attn_shape* s, const void* q, const void* k, const void* v,
+                   const float* bias, const tri_attn_mask* mask, float scale, void* out,
+                   float* lse, float* mx) {
+    Params p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.bias = bias;
+    p.out = out;
+    p.lse = lse;
+    p.mx = mx;
+    p.B = s->B;
+    p.N = s->N;
+    p.H = s->H;
+    p.Q = s->Q;
+    p.K = s->K;
+    p.D = s->D;
+    // Default scale 1/sqrt(D), evaluated in double and rounded once.
+    p.scale = isnan(scale) ? static_cast<float>(1.0 / sqrt(static_cast<double>(s->D))) : scale;
+    p.mask_kind = mask ? mask->kind : TRIATTN_MASK_NONE;
+    p.mask_mod = TRIATTN_MOD_NONE;
+    p.q_block = p.kv_block = p.max_blocks = p.full_max_blocks = 1;
+    p.n_q_rows = p.n_kv_blocks = 1;
+    if (mask) {
+        p.dense = mask->dense;
+        p.kv_lengths = mask->kv_lengths;
+        if (mask->kind == TRIATTN_MASK_BLOCK) {
+            p.mask_mod = mask->mask_mod;
+            p.kv_num_blocks = mask->kv_num_blocks;
+            p.kv_indices = mask->kv_indices;
+            p.full_kv_num_blocks = mask->full_kv_num_blocks;
+            p.full_kv_indices = mask->full_kv_indices;
+            p.q_block = mask->q_block;
+            p.kv_block = mask->kv_block;
+            p.max_blocks = mask->max_blocks;
+            p.full_max_blocks = mask->full_kv_num_blocks ? mask->full_max_blocks : 1;
+            p.stride_b = mask->stride_b;
+            p.stride_n = mask->stride_n;
+            p.stride_h = mask->stride_h;
+            p.n_q_rows = (s->Q + mask->q_block - 1) / mask->q_block;
+            p.n_kv_blocks = (s->K + mask->kv_block - 1) / mask->kv_block;
+        }
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+triattn_status tri_attn_check(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                              const void* k, const void* v, const float* bias,
+                              const tri_attn_mask* mask, float scale, const void* out,
+                              const float* lse, const float* max) {
+    return check_impl(shape, dtype, q, k, v, bias, mask, scale, out, lse, max);
+}
+
+triattn_status tri_attn_fwd(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                            const void* k, const void* v, const float* bias,
+                            const tri_attn_mask* mask, float scale, void* out, float* lse,
+                            float* max, hipStream_t stream) {
+    const triattn_status st = check_impl(shape, dtype, q, k, v, bias, mask, scale, out, lse, max);
+    if (st != TRIATTN_OK) return st;
+    if (shape->B == 0 || shape->N == 0 || shape->H == 0 || shape->Q == 0) return TRIATTN_OK;
+    const Params p = make_params(shape, q, k, v, bias, mask, scale, out, lse, max);
+    const hipError_t err = triattn::mfma_supports(p, dtype)
+                               ? triattn::launch_mfma(p, dtype, stream)
+                               : triattn::launch_generic(p, dtype, stream);
+    return err == hipSuccess ? TRIATTN_OK : TRIATTN_ERR_HIP;
+}
+
+triattn_status tri_attn_mask_to_kv_lengths(const uint8_t* mask, int64_t rows, int64_t K,
+                                           int32_t* kv_lengths, int32_t* nonprefix_rows,
+                                           hipStream_t stream) {
+    if (rows < 0 || K < 1 || !nonprefix_rows) return TRIATTN_ERR_INVALID_ARG;
+    if (rows > 0 && (!mask || !kv_lengths)) return TRIATTN_ERR_INVALID_ARG;
+    if (!aligned(kv_lengths, 4) || !aligned(nonprefix_rows, 4)) return TRIATTN_ERR_INVALID_ARG;
+    if (K > INT32_MAX || rows > (int64_t(1) << 40) || mul_or_neg(rows, K) < 0)
+        return TRIATTN_ERR_UNSUPPORTED;
+    const hipError_t err =
+        triattn::launch_mask_to_kv_lengths(mask, rows, K, kv_lengths, nonprefix_rows, stream);
+    return err == hipSuccess ? TRIATTN_OK : TRIATTN_ERR_HIP;
+}
+
+const char* tri_attn_status_str(triattn_status status) {
+    switch (status) {
+    case TRIATTN_OK:
+        return "TRIATTN_OK";
+    case TRIATTN_ERR_INVALID_ARG:
+        return "TRIATTN_ERR_INVALID_ARG: invalid argument";
+    case TRIATTN_ERR_UNSUPPORTED:
+        return "TRIATTN_ERR_UNSUPPORTED: dtype, head dimension or size outside the supported "
+               "envelope";
+    case TRIATTN_ERR_HIP:
+        return "TRIATTN_ERR_HIP: a HIP launch failed";
+    }
+    return "unknown triattn_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+"""C-ABI tests that need no GPU: the library loads, exports every entry point
+declared in include/*.h, and tri_attn_check (a pure host function) returns
+the documented status for each invalid-argument case.  No compute call is
+made here."""
+import glob
+import math
+import os
+import re
+
+import pytest
+
+import masked_attention_tri_amd as mat
+from masked_attention_tri_amd import _native as nat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(tri_attn_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    assert set(declared_functions()) == set(nat.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mat.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libtriattn.so does not export {name}"
+
+
+def test_status_strings():
+    for code in (0, 1, 2, 3):
+        s = mat.tri_attn_status_str(code)
+        assert s.startswith("TRIATTN_")
+    assert "unknown" in mat.tri_attn_status_str(42)
+
+
+A = 0x10000  # aligned fake addresses: tri_attn_check never dereferences them
+
+
+def shape(B=1, N=2, H=2, Q=8, K=8, D=32):
+    return nat.TriAttnShape(B, N, H, Q, K, D)
+
+
+def check(shp=None, dtype=nat.TRIATTN_BF16, q=A, k=A, v=A, bias=A, mask=None, scale=math.nan,
+          out=A, lse=A, mx=A):
+    return nat.tri_attn_check(shp or shape(), dtype, q, k, v, bias, mask, scale, out, lse, mx)
+
+
+def block_desc(**kw):
+    d = nat.TriAttnMask()
+    d.kind = nat.TRIATTN_MASK_BLOCK
+    d.kv_num_blocks = A
+    d.kv_indices = A
+    d.q_block = d.kv_block = 128
+    d.max_blocks = 4
+    d.full_max_blocks = 4
+    for key, val in kw.items():
+        setattr(d, key, val)
+    return d
+
+
+def test_check_accepts_valid_arguments():
+    assert check() == nat.TRIATTN_OK
+    assert check(bias=0, lse=0, mx=0) == nat.TRIATTN_OK  # optional pointers
+    assert check(shape(D=32), dtype=nat.TRIATTN_F32) == nat.TRIATTN_OK
+    assert check(shape(D=128), dtype=nat.TRIATTN_F16) == nat.TRIATTN_OK
+    assert check(shape(B=0, Q=0)) == nat.TRIATTN_OK  # empty work is fine
+    assert check(mask=block_desc()) == nat.TRIATTN_OK
+    assert check(mask=block_desc(full_kv_num_blocks=A, full_kv_indices=A)) == nat.TRIATTN_OK
+    d = nat.TriAttnMask()
+    d.kind = nat.TRIATTN_MASK_DENSE
+    d.dense = A + 1  # byte mask: any alignment
+    assert check(mask=d) == nat.TRIATTN_OK
+    d = nat.TriAttnMask()
+    d.kind = nat.TRIATTN_MASK_KV_LENGTHS
+    d.kv_lengths = A
+    assert check(mask=d) == nat.TRIATTN_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=0), dict(k=0), dict(v=0), dict(out=0),
+    dict(q=A + 8), dict(out=A + 2), dict(bias=A + 2), dict(lse=A + 1), dict(mx=A + 3),
+    dict(dtype=7), dict(dtype=-1),
+    dict(shp=shape(K=0)), dict(shp=shape(D=0)), dict(shp=shape(B=-1)), dict(shp=shape(Q=-2)),
+    dict(scale=math.inf), dict(scale=-math.inf),
+])
+def test_check_invalid_args(kw):
+    assert check(**kw) == nat.TRIATTN_ERR_INVALID_ARG
+
+
+def test_check_rejects_shape_null():
+    lib = mat.load_library()
+    assert lib.tri_attn_check(None, 2, A, A, A, A, None, 1.0, A, A, A) == \
+        nat.TRIATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("dtype,D", [
+    (nat.TRIATTN_F32, 36), (nat.TRIATTN_F32, 30), (nat.TRIATTN_F32, 64),
+    (nat.TRIATTN_BF16, 136), (nat.TRIATTN_F16, 60), (nat.TRIATTN_BF16, 4),
+])
+def test_check_envelope(dtype, D):
+    # triangle_attention page, Notes item 3: fp32 D<=32, D%4==0; half D<=128, D%8==0
+    assert check(shape(D=D), dtype=dtype) == nat.TRIATTN_ERR_UNSUPPORTED
+
+
+def test_check_mask_descriptors():
+    both = nat.TriAttnMask()
+    both.kind = nat.TRIATTN_MASK_DENSE
+    both.dense = A
+    both.kv_lengths = A  # a dense mask and kv_lengths together
+    assert check(mask=both) == nat.TRIATTN_ERR_INVALID_ARG
+    both.kind = nat.TRIATTN_MASK_KV_LENGTHS
+    assert check(mask=both) == nat.TRIATTN_ERR_INVALID_ARG
+    missing = nat.TriAttnMask()
+    missing.kind = nat.TRIATTN_MASK_DENSE
+    assert check(mask=missing) == nat.TRIATTN_ERR_INVALID_ARG
+    missing.kind = nat.TRIATTN_MASK_KV_LENGTHS
+    assert check(mask=missing) == nat.TRIATTN_ERR_INVALID_ARG
+    bad_kind = nat.TriAttnMask()
+    bad_kind.kind = 9
+    assert check(mask=bad_kind) == nat.TRIATTN_ERR_INVALID_ARG
+    lens = nat.TriAttnMask()
+    lens.kind = nat.TRIATTN_MASK_KV_LENGTHS
+    lens.kv_lengths = A + 2
+    assert check(mask=lens) == nat.TRIATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(kv_num_blocks=None), dict(kv_indices=None),
+    dict(full_kv_num_blocks=A),        # only one of the full pair
+    dict(full_kv_indices=A),
+    dict(max_blocks=0), dict(q_block=0), dict(kv_block=0),
+    dict(full_kv_num_blocks=A, full_kv_indices=A, full_max_blocks=0),
+    dict(mask_mod=5), dict(stride_b=-1), dict(stride_h=-3),
+    dict(kv_indices=A + 2), dict(dense=A),
+])
+def test_check_block_descriptor(kw):
+    assert check(mask=block_desc(**kw)) == nat.TRIATTN_ERR_INVALID_ARG
+
+
+def test_check_block_count_limit():
+    d = block_desc(kv_block=1)
+    assert check(shape(K=8192), mask=d) == nat.TRIATTN_OK
+    assert check(shape(K=8193), mask=d) == nat.TRIATTN_ERR_UNSUPPORTED
+
+
+def test_check_index_range():
+    assert check(shape(B=1 << 20, N=1 << 20, H=1 << 20, Q=2)) == nat.TRIATTN_ERR_UNSUPPORTED
+    assert check(shape(B=1 << 62, N=4)) == nat.TRIATTN_ERR_UNSUPPORTED
+
+
+def test_blockmask_constructor_errors():
+    import torch
+
+    with pytest.raises(RuntimeError):
+        mat.BlockMask.from_kv_blocks(torch.zeros(4, dtype=torch.int32),
+                                     torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(AssertionError):
+        mat.BlockMask.from_kv_blocks(torch.zeros(4, dtype=torch.int32),
+                                     torch.zeros(4, 2, dtype=torch.int32),
+                                     full_kv_num_blocks=torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        mat.BlockMask.from_kv_blocks(torch.zeros(4, dtype=torch.int32),
+                                     torch.zeros(4, 2, dtype=torch.int32),
+                                     mask_mod=lambda b, h, q, k: q >= k)
+
+
+def test_blockmask_numel_and_sparsity():
+    import torch
+
+    rows = 4
+    num = torch.arange(1, rows + 1, dtype=torch.int32)
+    idx = torch.zeros(rows, rows, dtype=torch.int32)
+    for i in range(rows):
+        idx[i, : i + 1] = torch.arange(i + 1)
+    bm = mat.BlockMask.from_kv_blocks(num, idx, BLOCK_SIZE=16, mask_mod="causal")
+    assert bm.numel() == 64 * 64
+    # causal lists visit 10 of 16 blocks
+    assert abs(bm.sparsity() - 100.0 * 6 / 16) < 1e-9
+
+
+def test_triangle_attention_argument_errors():
+    import torch
+
+    q = torch.zeros(1, 2, 2, 4, 8)
+    with pytest.raises(ValueError):
+        mat.triangle_attention(q, q, q, None, mask=torch.ones(1, 2, 1, 1, 4, dtype=torch.bool),
+                               kv_lengths=torch.ones(1, 2, 1, 1, 1, dtype=torch.int32))
+    with pytest.raises(ValueError):  # there is no CPU path
+        mat.triangle_attention(q, q, q, None)

@@ -1,0 +1,155 @@
+"""GPU invariants of the library that hold at any size (mostly bitwise)."""
+import math
+
+import pytest
+import torch
+
+import masked_attention_tri_amd as mat
+from masked_attention_tri_amd import _native as nat
+from masked_attention_tri_amd import workloads as wl
+from tests.gpu_common import TOL, assert_parity, block_mask_of, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _eq(a, b):
+    return all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("D,dt", [(64, "bf16"), (32, "f16"), (24, "bf16"), (32, "f32")])
+def test_default_scale_is_inv_sqrt_d(D, dt):
+    say(f"default scale D={D} {dt}")
+    c = wl.make_case(1, 2, 2, 70, 90, D, dt, "dense", seed=3)
+    assert _eq(run_gpu(c, scale=None), run_gpu(c, scale=1.0 / math.sqrt(D)))
+
+
+@pytest.mark.parametrize("D", [64, 40])
+def test_kv_length_clamps(D):
+    say(f"kv_lengths clamps D={D}")
+    c = wl.make_case(1, 4, 2, 100, 90, D, "bf16", "kv_lengths", seed=4)
+    c.kv_lengths = torch.tensor([90, 0, 17, 64], dtype=torch.int32).view(1, 4, 1, 1, 1)
+    base = run_gpu(c)
+    c2 = wl.Case(c.name, c.dtype, c.q, c.k, c.v, c.bias, scale=c.scale,
+                 kv_lengths=torch.tensor([95, -3, 17, 64], dtype=torch.int32).view(1, 4, 1, 1, 1))
+    assert _eq(base, run_gpu(c2))
+    # a prefix dense mask gives the same answer
+    dense = torch.arange(90).view(1, 1, 1, 1, 90) < c.kv_lengths
+    c3 = wl.Case(c.name, c.dtype, c.q, c.k, c.v, c.bias, scale=c.scale, mask=dense)
+    d = run_gpu(c3)
+    tol = TOL[c.dtype]
+    assert (d[0].float() - base[0].float()).abs().max() <= tol["o"]
+    assert (d[1] - base[1]).abs().max() <= tol["lse"]
+
+
+def test_full_lists_are_only_an_optimisation():
+    say("full_kv lists on/off")
+    g = torch.Generator().manual_seed(8)
+    c = wl.make_case(2, 1, 2, 512, 512, 64, "bf16", "none", seed=8, bias=True)
+    c.block = wl.causal_block_lists(g, 4, 128, 128)
+    with_full = run_gpu(c)
+    c.block = wl.BlockLists(c.block.kv_num_blocks, c.block.kv_indices, None, None, 128, 128,
+                            "causal")
+    without = run_gpu(c)
+    assert _eq(with_full, without)
+    assert_parity(c, gpu=without)
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_run_to_run_determinism(cfg):
+    say(f"determinism config {cfg}")
+    c = wl.make_config(cfg)
+    assert _eq(run_gpu(c), run_gpu(c))
+
+
+@pytest.mark.parametrize("dt,D,kind", [("bf16", 64, "kv_lengths"), ("f16", 128, "dense"),
+                                       ("bf16", 24, "none"), ("f32", 16, "dense")])
+def test_every_output_element_is_written(dt, D, kind):
+    say(f"NaN-prefilled outputs {dt} D={D} {kind}")
+    c = wl.make_case(2, 2, 2, 131, 77, D, dt, kind, seed=9).to("cuda")
+    out = torch.full_like(c.q, float("nan"))
+    lse = torch.full(c.q.shape[:4], float("nan"), device="cuda")
+    mx = torch.full(c.q.shape[:4], float("nan"), device="cuda")
+    desc = None
+    if c.mask is not None:
+        m = c.mask.contiguous().view(torch.uint8)
+        desc = nat.TriAttnMask()
+        desc.kind = nat.TRIATTN_MASK_DENSE
+        desc.dense = m.data_ptr()
+    elif c.kv_lengths is not None:
+        ln = c.kv_lengths.contiguous()
+        desc = nat.TriAttnMask()
+        desc.kind = nat.TRIATTN_MASK_KV_LENGTHS
+        desc.kv_lengths = ln.data_ptr()
+    B, N, H, Q, K, D = c.shape
+    st = mat.tri_attn_fwd(nat.TriAttnShape(B, N, H, Q, K, D), nat.DTYPE_CODES[c.q.dtype],
+                          c.q, c.k, c.v, c.bias, desc, math.nan, out, lse, mx, None)
+    torch.cuda.synchronize()
+    assert st == mat.TRIATTN_OK
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all() and \
+        torch.isfinite(mx).all()
+
+
+def test_optional_aux_outputs_and_invalid_args_write_nothing():
+    say("null lse/max; rejected call writes nothing")
+    c = wl.make_case(1, 2, 2, 64, 64, 64, "bf16", "none", seed=10).to("cuda")
+    out = torch.zeros_like(c.q)
+    B, N, H, Q, K, D = c.shape
+    shp = nat.TriAttnShape(B, N, H, Q, K, D)
+    assert mat.tri_attn_fwd(shp, nat.TRIATTN_BF16, c.q, c.k, c.v, c.bias, None, math.nan,
+                            out, None, None, None) == mat.TRIATTN_OK
+    torch.cuda.synchronize()
+    ref = run_gpu(c.to("cpu"), scale=None)
+    assert torch.equal(out.cpu(), ref[0])
+    poison = torch.full_like(c.q, 7.0)
+    bad = nat.TriAttnShape(B, N, H, Q, K, 72)  # D % 8 != 0 for bf16... 72 % 8 == 0, use 68
+    bad.D = 68
+    assert mat.tri_attn_fwd(bad, nat.TRIATTN_BF16, c.q, c.k, c.v, c.bias, None, math.nan,
+                            poison, None, None, None) == mat.TRIATTN_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(poison == 7.0)
+
+
+def test_four_d_inputs_and_side_stream():
+    say("4-D inputs (B=1) on a side stream")
+    c = wl.make_case(1, 3, 2, 80, 80, 64, "bf16", "kv_lengths", seed=11)
+    ref = run_gpu(c)
+    g = c.to("cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, lse, mx = mat.triangle_attention(g.q[0], g.k[0], g.v[0], g.bias[0],
+                                              kv_lengths=g.kv_lengths[0], scale=g.scale,
+                                              return_aux=True)
+    s.synchronize()
+    assert out.shape == g.q.shape[1:] and lse.shape == (3, 2, 80, 1)
+    assert torch.equal(out.cpu(), ref[0][0]) and torch.equal(lse.cpu(), ref[1][0])
+
+
+def test_mask_to_kv_lengths():
+    say("mask_to_kv_lengths")
+    lens = torch.tensor([0, 1, 5, 64, 100, 129, 130], dtype=torch.int32)
+    K = 130
+    mask = (torch.arange(K).view(1, 1, K) < lens.view(1, 7, 1)).view(1, 7, 1, 1, K)
+    got = mat.mask_to_kv_lengths(mask.cuda())
+    assert torch.equal(got.cpu().view(-1), lens)
+    holey = mask.clone()
+    holey[0, 3, 0, 0, 70] = True  # a valid key after the first masked one
+    with pytest.raises(ValueError):
+        mat.mask_to_kv_lengths(holey.cuda())
+    got4 = mat.mask_to_kv_lengths(mask[0].cuda())
+    assert got4.shape == (7, 1, 1, 1)
+
+
+def test_blockmask_with_callable_causal_and_tuple_block_size():
+    say("BlockMask causal callable")
+    g = torch.Generator().manual_seed(12)
+    c = wl.make_case(1, 1, 2, 256, 256, 64, "bf16", "none", seed=12, bias=False)
+    lists = wl.causal_block_lists(g, 2, 128, 128)
+    bm = mat.BlockMask.from_kv_blocks(lists.kv_num_blocks.cuda(), lists.kv_indices.cuda(),
+                                      lists.full_kv_num_blocks.cuda(),
+                                      lists.full_kv_indices.cuda(), BLOCK_SIZE=(128, 128),
+                                      mask_mod=mat.causal_mask)
+    gq = c.to("cuda")
+    out = mat.triangle_attention(gq.q, gq.k, gq.v, None, block_mask=bm)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        c.q.float(), c.k.float(), c.v.float(), is_causal=True)
+    assert (out.cpu().float() - ref).abs().max() < 2e-2

@@ -1,0 +1,159 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element.
+
+Small cases are compared in full; the five named workloads run at their full
+sizes (the launch the benchmark times) and are compared on sampled rows,
+which the oracle computes one by one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from masked_attention_tri_amd import workloads as wl
+from tests import helpers as hp
+from tests.gpu_common import assert_parity, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+# ---- the five named workloads -------------------------------------------
+
+def test_config1_fp32_dense_ones():
+    say("config 1")
+    assert_parity(wl.make_config(1))
+
+
+def test_config1_fp32_no_mask():
+    say("config 1 without mask")
+    c = wl.make_config(1)
+    c.mask = None
+    assert_parity(c)
+
+
+def test_config2_fp16_kv_lengths():
+    say("config 2")
+    assert_parity(wl.make_config(2))
+
+
+def test_config3_bf16_dense_fully_masked_rows():
+    say("config 3")
+    c = wl.make_config(3)
+    gpu = run_gpu(c)
+    dead = c.meta["fully_masked_rows"]
+    g = torch.Generator().manual_seed(5)
+    keep = sorted(set(dead) | set(torch.randperm(384, generator=g)[:12].tolist()))
+    sub = wl.Case(c.name + " (n sample)", c.dtype, c.q[:, keep], c.k[:, keep], c.v[:, keep],
+                  c.bias, mask=c.mask[:, keep], scale=c.scale)
+    sub_gpu = tuple(x[:, keep] for x in gpu)
+    assert_parity(sub, gpu=sub_gpu)
+    # the fully masked rows: uniform weights over all K keys
+    for n in dead:
+        assert torch.all(gpu[2][0, n] == -1.0e9)
+        assert torch.all(gpu[1][0, n] == -1.0e9)
+
+
+def test_config4_bf16_kv_lengths_sampled():
+    say("config 4 (full size, sampled rows)")
+    c = wl.make_config(4)
+    gpu = run_gpu(c)
+    lens = c.kv_lengths.view(-1)
+    g = torch.Generator().manual_seed(6)
+    ns = set(torch.randperm(768, generator=g)[:20].tolist())
+    ns |= {int(lens.argmin()), int(lens.argmax()), 0, 767}
+    ns = sorted(ns)
+    qs = sorted(set(torch.randperm(768, generator=g)[:62].tolist()) | {0, 767})
+    sub = wl.Case(c.name + " (sample)", c.dtype, c.q[:, ns], c.k[:, ns], c.v[:, ns], c.bias,
+                  kv_lengths=c.kv_lengths[:, ns], scale=c.scale)
+    H, Q = 4, 768
+    rows = np.array([(i * H + h) * Q + q for i in range(len(ns)) for h in range(H) for q in qs])
+    sub_gpu = tuple(x[:, ns] for x in gpu)
+    assert_parity(sub, gpu=sub_gpu, rows=rows)
+
+
+def test_config5_bf16_causal_blockmask_sampled():
+    say("config 5 (full size, sampled rows)")
+    c = wl.make_config(5)
+    gpu = run_gpu(c)
+    B, N, H, Q = 2, 1, 8, 4096
+    qs = [0, 1, 63, 64, 127, 128, 129, 1000, 2047, 2048, 3071, 4000, 4095]
+    rows = np.array([((b * N) * H + h) * Q + q for b in range(B) for h in (0, 3, 7) for q in qs])
+    assert_parity(c, gpu=gpu, rows=rows)
+
+
+# ---- random shapes through both kernels ------------------------------------
+
+MFMA_CASES = [
+    # (B, N, H, Q, K, D, dtype, kind, extra)
+    (2, 3, 2, 200, 150, 64, "bf16", "kv_lengths", {}),
+    (1, 2, 3, 130, 200, 64, "f16", "dense", {}),
+    (2, 2, 2, 129, 64, 32, "bf16", "none", {}),
+    (1, 3, 2, 96, 77, 128, "bf16", "dense", {"bias_sigma": 2.0}),
+    (1, 2, 2, 256, 256, 128, "f16", "kv_lengths", {"len_range": (0, 256)}),
+    (2, 1, 2, 256, 320, 64, "bf16", "block", {"q_block": 128, "kv_block": 64,
+                                               "mask_mod": "causal"}),
+    (1, 2, 2, 256, 256, 32, "f16", "block", {"q_block": 128, "kv_block": 128}),
+    (1, 2, 3, 384, 250, 64, "bf16", "block", {"q_block": 256, "kv_block": 64,
+                                               "mask_mod": "causal", "block_broadcast": True}),
+    (2, 2, 2, 100, 100, 64, "bf16", "none", {"bias": False, "scale": 0.3}),
+    (1, 4, 2, 64, 1, 64, "bf16", "none", {}),
+    (1, 2, 2, 1, 100, 128, "f16", "kv_lengths", {}),
+    (1, 2, 2, 70, 33, 32, "bf16", "kv_lengths", {"len_range": (-3, 0)}),
+    (1, 3, 2, 150, 130, 64, "bf16", "dense", {"p_valid": 0.02}),
+    (1, 2, 2, 128, 131, 64, "bf16", "none", {}),  # K % 4 != 0: scalar bias loads
+]
+
+GENERIC_CASES = [
+    (2, 2, 3, 37, 29, 8, "bf16", "kv_lengths", {}),
+    (1, 2, 2, 50, 70, 24, "f16", "dense", {}),
+    (1, 2, 2, 33, 41, 40, "bf16", "none", {}),
+    (1, 2, 1, 20, 130, 120, "f16", "kv_lengths", {}),
+    (2, 2, 2, 40, 37, 16, "bf16", "block", {"q_block": 16, "kv_block": 8, "mask_mod": "causal"}),
+    (1, 2, 2, 64, 64, 64, "bf16", "block", {"q_block": 32, "kv_block": 32}),
+    (2, 3, 2, 19, 23, 12, "f32", "dense", {}),
+    (1, 2, 2, 40, 40, 32, "f32", "kv_lengths", {"len_range": (-2, 45)}),
+    (1, 1, 2, 30, 30, 4, "f32", "block", {"q_block": 8, "kv_block": 4, "mask_mod": "causal"}),
+    (1, 2, 2, 9, 1, 32, "f32", "none", {}),
+]
+
+
+def _case_id(c):
+    B, N, H, Q, K, D, dt, kind, extra = c
+    return f"B{B}N{N}H{H}Q{Q}K{K}D{D}-{dt}-{kind}" + ("-" + "-".join(
+        f"{k}" for k in extra) if extra else "")
+
+
+@pytest.mark.parametrize("spec", MFMA_CASES + GENERIC_CASES,
+                         ids=[_case_id(c) for c in MFMA_CASES + GENERIC_CASES])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_random_shapes(spec, seed):
+    B, N, H, Q, K, D, dt, kind, extra = spec
+    c = wl.make_case(B, N, H, Q, K, D, dt, kind, seed=seed, **extra)
+    say(c.name)
+    assert_parity(c)
+
+
+def test_p1_example_shapes_and_lengths():
+    """The triangle_attention page's example: fp16, seq 128, 2 heads, D 32,
+    lengths 96 built as a right-padded mask and turned into kv_lengths."""
+    import json
+    import os
+
+    import masked_attention_tri_amd as mat
+
+    say("P1 example")
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "p1_example_shapes.json")))
+    c = wl.make_config(2)
+    assert list(c.q.shape) == g["q_shape"] and list(c.bias.shape) == g["bias_shape"]
+    pos = torch.arange(128)
+    mask = (pos.view(1, 128) < 96).view(1, 128, 1, 1, 1) & (pos.view(1, 128) < 96).view(
+        1, 1, 1, 1, 128)
+    lens = mat.mask_to_kv_lengths(mask.cuda())
+    assert list(lens.shape) == g["kv_lengths_shape"]
+    expect = torch.where(pos < 96, 96, 0).view(1, 128, 1, 1, 1).to(torch.int32)
+    assert torch.equal(lens.cpu(), expect)
+    c.kv_lengths = lens.cpu()
+    gpu = run_gpu(c)
+    assert list(gpu[0].shape) == g["output_shape"]
+    assert_parity(c, gpu=gpu)  # rows n >= 96 have no valid key
