@@ -25,6 +25,9 @@ FLAGS = [
     "-shared",
     # packed fp32 instructions are disabled for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: the softmax reads and rescales them
+    # with VALU instructions, and AGPR accumulators cost a copy each way
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall",
     "-Wno-unused-function",
     f"-I{INCLUDE}",

@@ -6,20 +6,48 @@
 // max-shifted softmax; the page fixes the result, not the schedule).
 //
 // Work decomposition: one workgroup of 4 wavefronts owns 128 query rows of
-// one (b, n, h); wave w owns rows 32w .. 32w+31.  Key tiles of 64 keys are
-// staged in LDS, double-buffered, straight from the row-major HBM layout.
+// one (b, n, h); wave w owns rows 32w .. 32w+31.  Keys go in tiles of 64.
 //
 // Both contractions run on v_mfma_f32_32x32x16_{bf16,f16}:
-//   S^T = K . Q^T   A = K rows from LDS (16-byte reads), B = Q^T held in
+//   S^T = K . Q^T + C   A = K rows from LDS (16-byte reads), B = Q^T held in
 //                   registers for the whole key loop.  The accumulator puts
 //                   one query per lane and 16 keys per lane in registers, so
-//                   the softmax row reductions are in-lane plus one exchange
-//                   with the partner lane (lane ^ 32).
+//                   the softmax row reductions are in-lane plus one
+//                   v_permlane32_swap with the partner lane (lane ^ 32).
+//                   C is the fp32 bias tile itself, so the bias add costs no
+//                   vector instruction.
 //   O^T = V^T . P^T B = P^T taken directly from the S^T registers (converted
 //                   to bf16/fp16), A = V^T read from the row-major V tile with
 //                   ds_read_b64_tr_b16, which hands each lane four keys of
 //                   one column.  The query stays in the lane, so the running
 //                   rescale of O is a per-lane scalar.
+//
+// Data movement: every tile arrives by LDS DMA (buffer_load ... lds), never
+// through registers.  K and V tiles are shared by the workgroup and double
+// buffered.  The fp32 bias is the largest stream (it is re-read for every n):
+// the accumulator layout would make each lane fetch 16 bytes from its own
+// query row, 32 rows per instruction, which saturates the L1 address path.
+// Instead each wave DMAs its 32 x 64 bias block with whole rows per lane
+// group (8 cache lines per instruction) into its own LDS region, reads it
+// back in the accumulator layout, and immediately refills the region with
+// the next tile's block.  LDS rows are unpadded; 16-byte chunks are stored
+// XOR-swizzled by row so that the operand reads are bank-conflict free.
+//
+// Buffer descriptors bound every access to its (b, n, h) slice.  The range
+// check covers the per-lane offset (not the scalar one), so all variable
+// offsets go in the per-lane offset: reads past a slice return 0 and touch
+// no memory, and ragged tiles need no clamping (those keys are masked).
+//
+// Scale: z = s*(Q.K) + B.  When s is 0 or a power of two, s*Q is exact in the
+// input format, so Q is scaled once at load and S = (sQ).K + B is z itself.
+// Otherwise C holds B/s and z = s*S.  Either way the exponent is one FMA:
+// p = exp2(S*c - m*c) with c = s_eff*log2(e).
+//
+// Softmax bookkeeping per query row: the exact running max (the "max"
+// output) and a reference max used in the exponent.  The reference is only
+// raised, and O and the sum rescaled, when a tile's max exceeds it by more
+// than ln(256); so p <= 256 and the rescale is rare.  The sum is taken over
+// the fp32 p, before they are rounded for the P.V contraction.
 //
 // Masks: kv_lengths and block lists cut whole tiles (tiles past the length,
 // blocks not listed); element masks are applied only on tiles that need
@@ -47,6 +75,8 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -54,6 +84,9 @@ constexpr int kQTile = 32 * kWaves;  // query rows per workgroup
 constexpr int kKTile = 64;           // keys per K/V tile
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyLog = 5.545177444479562f;  // ln(256): largest p before a rescale
+
+enum BiasMode { kNoBias = 0, kBiasLds = 1, kBiasScalar = 2 };
 
 template <typename T>
 struct Mma;
@@ -72,20 +105,38 @@ struct Mma<_Float16> {
     }
 };
 
+// LDS geometry and XOR swizzles of one head dimension.  Rows are stored
+// unpadded; the 16-byte chunk c of row r lives at chunk position c ^ f(r).
 template <int D>
-struct Tile {
-    // LDS row pitches: K rows are read 16 bytes per lane down 8-row groups,
-    // V rows 4x8 bytes by the transposing read; the pads keep both
-    // bank-conflict free.
-    static constexpr int kPitch = 2 * D + 16;
-    static constexpr int vPitch = 2 * D + 32;
-    static constexpr int kBytes = kKTile * kPitch;
-    static constexpr int vBytes = kKTile * vPitch;
-    static constexpr int stage = kBytes + vBytes;
-    static constexpr int chunksPerRow = D / 8;                  // 16-byte chunks
-    static constexpr int perThread = kKTile * chunksPerRow / kThreads;
-    static_assert(perThread * kThreads == kKTile * chunksPerRow, "tile split");
+struct Geo {
+    static constexpr int rowBytes = 2 * D;              // one K or V row
+    static constexpr int chunks = D / 8;                 // 16-byte chunks per row
+    static constexpr int tileBytes = kKTile * rowBytes;  // one K (or V) tile
+    static constexpr int stageBytes = 2 * tileBytes;     // K + V
+    static constexpr int dmaPerWave = tileBytes / 1024 / kWaves;  // per tile, K or V
+    static_assert(dmaPerWave * 1024 * kWaves == tileBytes, "DMA split");
+    // K is read 16 bytes per lane down consecutive rows (8 or 16 lanes per
+    // LDS cycle at one chunk): consecutive rows must land on distinct banks.
+    static __device__ __forceinline__ int fk(int r) {
+        if (D == 32) return ((r >> 1) ^ (r >> 3)) & 3;
+        if (D == 64) return (r + (r >> 3)) & 7;
+        return r & 15;
+    }
+    // V is read by ds_read_b64_tr_b16: each 16 lanes take 4 consecutive rows
+    // (first one a multiple of 4) x 2 adjacent chunks, and 32 lanes 4 rows x
+    // 4 adjacent chunks.
+    static __device__ __forceinline__ int fv(int r) {
+        if (D == 32) return r & 2;
+        if (D == 64) return 2 * (r & 3) + ((r >> 2) & 1);
+        return (r & 3) == 0 ? 0 : (r & 3) == 1 ? 6 : (r & 3) == 2 ? 12 : 10;
+    }
 };
+
+// The per-wave bias block: 32 query rows x 64 keys of fp32 = 256-byte rows,
+// read 16 bytes per lane down consecutive rows.
+constexpr int kBiasRowBytes = kKTile * 4;
+constexpr int kBiasWaveBytes = 32 * kBiasRowBytes;  // 8 KiB
+__device__ __forceinline__ int fb(int r) { return r & 15; }
 
 __device__ __forceinline__ bool bit_set(const uint32_t* bits, int64_t i) {
     return (bits[i >> 5] >> (i & 31)) & 1u;
@@ -116,22 +167,62 @@ __device__ void mark_list(uint32_t* bits, const int32_t* counts, const int32_t* 
     }
 }
 
-template <typename T, int D, int KIND, bool BIAS_VEC>
+// Buffer resources: a 128-bit scalar descriptor (base, size in bytes).  Word
+// 3 selects 32-bit data format, untyped access.  The scalar offset of every
+// access below is 0; the whole offset is per lane and range-checked.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                             kRsrcWord3);
+}
+__device__ __forceinline__ float bload32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+// 16 bytes per lane from byte offset voff into LDS at dst + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                             voff, 0, 0, 0);
+}
+// Wait until this wave's vector-memory operations (the DMAs) have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// IEEE maximum (NaN-propagating); lowers to v_maximum3_f32 chains without the
+// NaN-quieting instructions fmaxf needs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Value of x in the partner lane (lane ^ 32) combined with x: both halves of
+// the wave hold the same query column, each for half of the keys.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <typename T, int D, int KIND, int BIAS, bool EXACT>
 __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
     using M = Mma<T>;
     using v8 = typename M::v8;
-    using L = Tile<D>;
+    using G = Geo<D>;
     constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);
     constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK;
+    constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
+    constexpr int kBiasBytes = BIAS == kBiasLds ? kWaves * kBiasWaveBytes : 0;
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * L::stage];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * G::stageBytes + kBiasBytes];
     __shared__ uint32_t listed_bits[kBlock ? kWords : 1];
     __shared__ uint32_t full_bits[kBlock ? kWords : 1];
     __shared__ float mean_v[D];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
     const int col = lane & 31;  // this lane's query within the wave
     const int half = lane >> 5;
 
@@ -141,33 +232,42 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
     const int64_t w = blockIdx.x;
     const int64_t xcd = w % kXcds, slot = w / kXcds;
     const int64_t per = W / kXcds, rem = W % kXcds;
-    const int64_t lid = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+    const int64_t lid =
+        xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
     const int64_t qt = lid % n_qt;
     const int64_t n = (lid / n_qt) % p.N;
     const int64_t h = (lid / (n_qt * p.N)) % p.H;
     const int64_t b = lid / (n_qt * p.N * p.H);
 
-    const int64_t K = p.K, Q = p.Q;
+    // Per-(b,n,h) bases; offsets inside one slice fit in 32 bits (checked on
+    // the host).
+    const int K = static_cast<int>(p.K), Q = static_cast<int>(p.Q);
     const int64_t bnh = (b * p.N + n) * p.H + h;
-    const T* kbase = static_cast<const T*>(p.k) + bnh * K * D;
-    const T* vbase = static_cast<const T*>(p.v) + bnh * K * D;
-    const int64_t q0 = qt * kQTile;
-    const int64_t q0w = q0 + 32 * wave;
-    const int64_t qrow = q0w + col;  // this lane's query
+    const T* kbase = static_cast<const T*>(p.k) + bnh * p.K * D;
+    const T* vbase = static_cast<const T*>(p.v) + bnh * p.K * D;
+    const float* bslice = BIAS != kNoBias ? p.bias + (b * p.H + h) * p.Q * p.K : nullptr;
+    const int q0 = static_cast<int>(qt) * kQTile;
+    const int q0w = q0 + 32 * wave;
+    const int qrow = q0w + col;  // this lane's query
     const bool row_ok = qrow < Q;
-    const int64_t qload = row_ok ? qrow : Q - 1;
-    const float* brow = p.bias ? p.bias + ((b * p.H + h) * Q + qload) * K : nullptr;
+    const int qload = row_ok ? qrow : Q - 1;
+
+    // Scale handling (see the header comment).
+    const float zscale = EXACT ? 1.0f : p.scale;        // z = zscale * S
+    const float c_exp = zscale * kLog2e;                 // exponent slope in S units
+    const float lazy_s = kLazyLog / zscale;              // rescale threshold in S units
+    const float inv_s = EXACT ? 1.0f : 1.0f / p.scale;   // bias -> S units
 
     // ---- visited key range / tile list -------------------------------
-    int64_t limit = K;  // keys >= limit are never valid
-    if (KIND == TRIATTN_MASK_KV_LENGTHS) {
+    int limit = K;  // keys >= limit are never valid
+    if (KIND == TRIATTN_MASK_KV_LENGTHS && p.kv_lengths) {
         const int64_t len = p.kv_lengths[b * p.N + n];
-        limit = len < 0 ? 0 : (len > K ? K : len);
+        limit = len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
     }
-    const int64_t n_tiles_all = (limit + kKTile - 1) / kKTile;
-    int64_t tiles_per_block = 1;
+    const int n_tiles_all = (limit + kKTile - 1) / kKTile;
+    int tiles_per_block = 1;
     if (kBlock) {
-        tiles_per_block = p.kv_block / kKTile;
+        tiles_per_block = static_cast<int>(p.kv_block / kKTile);
         const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
         for (int i = tid; i < words; i += kThreads) {
             listed_bits[i] = 0u;
@@ -186,220 +286,296 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
         }
         __syncthreads();
     }
-    auto first_tile = [&]() -> int64_t {
+    auto first_tile = [&]() -> int {
         if (!kBlock) return n_tiles_all > 0 ? 0 : -1;
         const int64_t blk = next_set(listed_bits, 0, p.n_kv_blocks);
-        return blk < 0 ? -1 : blk * tiles_per_block;
+        return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
     };
-    auto next_tile = [&](int64_t t) -> int64_t {
+    auto next_tile = [&](int t) -> int {
         if (!kBlock) return t + 1 < n_tiles_all ? t + 1 : -1;
         if ((t + 1) % tiles_per_block != 0 && t + 1 < n_tiles_all) return t + 1;
         const int64_t blk = next_set(listed_bits, t / tiles_per_block + 1, p.n_kv_blocks);
-        return blk < 0 ? -1 : blk * tiles_per_block;
+        return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
     };
 
     // ---- Q^T operand: registers for the whole key loop ----------------
     v8 qop[D / 16];
     {
-        const T* qp = static_cast<const T*>(p.q) + (bnh * Q + qload) * D + 8 * half;
+        const T* qp = static_cast<const T*>(p.q) + (bnh * p.Q + qload) * D + 8 * half;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * st);
-            if (!row_ok) raw = u32x4{0u, 0u, 0u, 0u};
-            qop[st] = __builtin_bit_cast(v8, raw);
+            v8 x = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(qp + 16 * st));
+            if (EXACT) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] = static_cast<T>(static_cast<float>(x[j]) * p.scale);
+            }
+            qop[st] = x;
         }
     }
 
-    // ---- K/V staging ---------------------------------------------------
-    u32x4 kreg[L::perThread], vreg[L::perThread];
-    auto load_tile = [&](int64_t t) {
+    // ---- LDS regions and DMA address tables ------------------------------
+    lds_char* lds = (lds_char*)smem;
+    lds_char* bias_lds = lds + 2 * G::stageBytes + wave * kBiasWaveBytes;  // this wave's block
+    const uint32_t kv_bytes = static_cast<uint32_t>(p.K * D * sizeof(T));
+    const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kbase, kv_bytes);
+    const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(vbase, kv_bytes);
+    const __amdgpu_buffer_rsrc_t bias_rsrc =
+        make_rsrc(bslice, BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * 4) : 0u);
+
+    // K/V DMA: this wave issues DMA instructions I = wave*dmaPerWave + j of
+    // each tile; lane l of instruction I fills LDS slot s = 64 I + l, i.e.
+    // row s / chunks, stored chunk s % chunks, which holds source chunk
+    // (s % chunks) ^ f(row).
+    uint32_t k_src[G::dmaPerWave], v_src[G::dmaPerWave];
 #pragma unroll
-        for (int i = 0; i < L::perThread; ++i) {
-            const int c = tid + kThreads * i;
-            const int r = c / L::chunksPerRow, cc = c % L::chunksPerRow;
-            const int64_t key = t * kKTile + r;
-            if (key < K) {
-                kreg[i] = *reinterpret_cast<const u32x4*>(kbase + key * D + cc * 8);
-                vreg[i] = *reinterpret_cast<const u32x4*>(vbase + key * D + cc * 8);
-            } else {
-                kreg[i] = u32x4{0u, 0u, 0u, 0u};
-                vreg[i] = u32x4{0u, 0u, 0u, 0u};
-            }
+    for (int j = 0; j < G::dmaPerWave; ++j) {
+        const int s = 64 * (wave * G::dmaPerWave + j) + lane;
+        const int r = s / G::chunks, c = s % G::chunks;
+        k_src[j] = static_cast<uint32_t>(r * G::rowBytes + 16 * (c ^ G::fk(r)));
+        v_src[j] = static_cast<uint32_t>(r * G::rowBytes + 16 * (c ^ G::fv(r)));
+    }
+    auto dma_kv = [&](int t, int buf) {
+        const uint32_t toff = static_cast<uint32_t>(t) * G::tileBytes;
+        lds_char* kdst = lds + buf * G::stageBytes;
+#pragma unroll
+        for (int j = 0; j < G::dmaPerWave; ++j) {
+            const int I = wave * G::dmaPerWave + j;
+            dma16(k_rsrc, kdst + 1024 * I, k_src[j] + toff);
+            dma16(v_rsrc, kdst + G::tileBytes + 1024 * I, v_src[j] + toff);
         }
     };
-    lds_char* lds = (lds_char*)smem;
-    auto store_tile = [&](int buf) {
+    // Bias DMA: 8 instructions of 4 rows x 256 bytes; lane l of instruction j
+    // fills row r = 4j + l/16 of the wave's block, stored chunk l%16, holding
+    // source chunk (l%16) ^ fb(r).  Rows past Q read past the slice and land
+    // as zeros; keys past K read the next row (masked).
+    uint32_t b_src[8];
 #pragma unroll
-        for (int i = 0; i < L::perThread; ++i) {
-            const int c = tid + kThreads * i;
-            const int r = c / L::chunksPerRow, cc = c % L::chunksPerRow;
-            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-                lds + buf * L::stage + r * L::kPitch + cc * 16) = kreg[i];
-            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-                lds + buf * L::stage + L::kBytes + r * L::vPitch + cc * 16) = vreg[i];
-        }
+    for (int j = 0; j < 8; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        b_src[j] = static_cast<uint32_t>(q0w + r) * static_cast<uint32_t>(K) * 4u +
+                   16u * static_cast<uint32_t>((lane & 15) ^ fb(r));
+    }
+    auto dma_bias = [&](int t) {
+        const uint32_t toff = static_cast<uint32_t>(t) * kBiasRowBytes;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma16(bias_rsrc, bias_lds + 1024 * j, b_src[j] + toff);
+    };
+    // Bias read into the accumulator layout: register 4g+e of key block kb is
+    // key 32kb + 8g + 4half + e, i.e. source chunk 8kb + 2g + half of row col.
+    auto read_bias = [&](f32x16 (&dst)[2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int chunk = (8 * kb + 2 * g + half) ^ fb(col);
+                const f32x4 bv = __builtin_bit_cast(
+                    f32x4, *reinterpret_cast<const lds_u32x4*>(bias_lds + col * kBiasRowBytes +
+                                                               16 * chunk));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[kb][4 * g + e] = bv[e];
+            }
+    };
+    // Bias for K % 4 != 0 (rows not 16-byte aligned): plain per-lane loads.
+    const uint32_t bias_lane_scalar =
+        static_cast<uint32_t>(qload) * static_cast<uint32_t>(K) * 4u + 16u * half;
+    auto load_bias_scalar = [&](int t, f32x16 (&dst)[2]) {
+        const uint32_t base = bias_lane_scalar + static_cast<uint32_t>(t) * kKTile * 4u;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[kb][4 * g + e] = bload32(bias_rsrc, base + 4u * (32 * kb + 8 * g + e));
     };
 
-    // Per-lane LDS offsets of the operand reads.
-    const int k_off = col * L::kPitch + 16 * half;  // K row `col`, d-slot 8*half
-    // Transposing read: lane s names row 4*(s/32) + (s%16)/4 and column
-    // 16*((s/16)%2) + 4*(s%4) of a 16-key x 32-column block; the result in
-    // lane l is then V[key(slot)][32*db + (l % 32)] for its 4 key slots.
-    const int v_off = (4 * half + (lane & 15) / 4) * L::vPitch + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    // Per-lane LDS offsets of the operand reads (within a stage).
+    // K: row 32kb + col, source chunk 2st + half.
+    int k_off[2][D / 16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+            const int r = 32 * kb + col;
+            k_off[kb][st] = r * G::rowBytes + 16 * ((2 * st + half) ^ G::fk(r));
+        }
+    // V (transposing read): lane s names row 32kb + 16t + 8u + 4half + (s%16)/4
+    // and column 32db + 16((s/16)%2) + 4(s%4), i.e. byte 8(s%2) of source
+    // chunk 4db + 2((s/16)%2) + (s%4)/2; lane l then receives V[key][32db + l%32]
+    // for the 4 keys of its slots 4u..4u+3.
+    int v_off[2][2][2][D / 32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const int r = 32 * kb + 16 * t + 8 * u + 4 * half + ((lane & 15) >> 2);
+                    const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+                    v_off[kb][t][u][db] =
+                        G::tileBytes + r * G::rowBytes + 16 * (chunk ^ G::fv(r)) + 8 * (lane & 1);
+                }
+    const uint8_t* dense_row = kDense ? p.dense + (b * p.N + n) * p.K : nullptr;
 
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m_run = -INFINITY;  // running max of this lane's query row
-    float l_run = 0.f;        // this lane's half of the running sum
+    float m_true = -INFINITY;  // exact running max of this row, S units
+    float m_ref = -INFINITY;   // reference max of the exponent, S units
+    float l_run = 0.f;         // this lane's half of the running sum
 
-    int64_t tile = first_tile();
-    if (tile >= 0) {
-        load_tile(tile);
-        store_tile(0);
-    }
-    __syncthreads();
-    int buf = 0;
-    while (tile >= 0) {
-        const int64_t nxt = next_tile(tile);
-        if (nxt >= 0) load_tile(nxt);  // in flight while this tile computes
+    // One key tile, computed from LDS buffer `buf`; DMAs for the next tile go
+    // to the other K/V buffer and (after this tile's bias is read) to this
+    // wave's bias region.  Returns the next tile (or -1).
+    auto step = [&](int tile, int buf) -> int {
+        tile = __builtin_amdgcn_readfirstlane(tile);
+        const int nxt = __builtin_amdgcn_readfirstlane(next_tile(tile));
+        const int k0 = tile * kKTile;
+        // This tile's DMAs (issued one tile ago) have landed, for every wave.
+        wait_vmem();
+        __syncthreads();
+        if (nxt >= 0) dma_kv(nxt, buf ^ 1);  // that buffer was last read one tile ago
 
-        const int64_t k0 = tile * kKTile;
-        // ---- which element mask this tile needs (wave-uniform) ---------
+        // ---- S^T = K . Q^T + bias --------------------------------------
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+        if (BIAS == kBiasLds) {
+            read_bias(s);
+            wait_lds();
+            if (nxt >= 0) dma_bias(nxt);  // the region is free again
+        } else if (BIAS == kBiasScalar) {
+            load_bias_scalar(tile, s);
+        }
+        if (BIAS != kNoBias && !EXACT) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb] *= inv_s;
+        }
+        const lds_char* stage = lds + buf * G::stageBytes;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const v8 a = __builtin_bit_cast(
+                    v8, *reinterpret_cast<const lds_u32x4*>(stage + k_off[kb][st]));
+                s[kb] = M::run(a, qop[st], s[kb]);
+            }
+        }
+
+        // ---- element mask (only on tiles that need one) -------------------
         bool need_mask = k0 + kKTile > limit;
         bool causal = false;
         uint64_t dense_bits = ~0ull;
-        if (KIND == TRIATTN_MASK_DENSE) {
-            const int64_t key = k0 + lane;
-            const bool ok = key < K && p.dense[(b * p.N + n) * K + key] != 0;
+        if (kDense) {
+            const int key = k0 + lane;
+            const int kc = key < K ? key : K - 1;
+            const bool ok = key < K && dense_row[kc] != 0;
             dense_bits = __ballot(ok);
-            need_mask = true;
+            need_mask = dense_bits != ~0ull;
         }
         if (kBlock && p.mask_mod == TRIATTN_MOD_CAUSAL &&
             !bit_set(full_bits, tile / tiles_per_block) && k0 + kKTile - 1 > q0w) {
             causal = true;
             need_mask = true;
         }
-        const bool skip = KIND == TRIATTN_MASK_DENSE && dense_bits == 0ull;
-
-        if (!skip) {
-            // ---- bias for this lane's query and its 32 keys ------------
-            float bias_v[2][16];
-            if (brow) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int64_t key = k0 + 32 * kb + 8 * g + 4 * half;
-                        if (BIAS_VEC) {
-                            f32x4 bv = f32x4{0.f, 0.f, 0.f, 0.f};
-                            if (key < K) bv = *reinterpret_cast<const f32x4*>(brow + key);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) bias_v[kb][4 * g + e] = bv[e];
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                bias_v[kb][4 * g + e] = key + e < K ? brow[key + e] : 0.f;
-                        }
-                    }
-            }
-
-            // ---- S^T = K . Q^T ------------------------------------------
-            const lds_char* kl = lds + buf * L::stage;
-            f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const v8 a = __builtin_bit_cast(
-                        v8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
-                                kl + k_off + kb * 32 * L::kPitch + 32 * st));
-                    s[kb] = M::run(a, qop[st], s[kb]);
-                }
-            }
-
-            // ---- logits, mask, running max -------------------------------
-            float mloc = -INFINITY;
+        if (need_mask) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    float z = brow ? fmaf(s[kb][r], p.scale, bias_v[kb][r]) : s[kb][r] * p.scale;
-                    if (need_mask) {
-                        const int kl_idx = 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
-                        const int64_t key = k0 + kl_idx;
-                        bool ok = key < limit;
-                        if (KIND == TRIATTN_MASK_DENSE) ok = ok && ((dense_bits >> kl_idx) & 1ull);
-                        if (causal) ok = ok && qrow >= key;
-                        z = ok ? z : -INFINITY;
-                    }
-                    s[kb][r] = z;
-                    mloc = fmaxf(mloc, z);
+                    const int kl_idx = 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
+                    const int key = k0 + kl_idx;
+                    bool ok = key < limit;
+                    if (kDense) ok = ok && ((dense_bits >> kl_idx) & 1ull);
+                    if (causal) ok = ok && qrow >= key;
+                    s[kb][r] = ok ? s[kb][r] : -INFINITY;
                 }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            const float m_new = fmaxf(m_run, mloc);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float mb = m_use * kLog2e;
-            const float alpha = __builtin_amdgcn_exp2f(m_run * kLog2e - mb);
-            m_run = m_new;
+        }
 
-            // ---- probabilities, running sum, P^T operands ----------------
-            v8 pop[2][2];
-            float lsum = 0.f;
+        // ---- row max; lazily raised reference ------------------------------
+        float mloc = vmax(s[0][0], s[0][1]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = kb == 0 ? 2 : 0; r < 16; r += 2) mloc = vmax(mloc, vmax(s[kb][r], s[kb][r + 1]));
+        mloc = max_halves(mloc);
+        m_true = vmax(m_true, mloc);
+        const bool raise = mloc > m_ref + lazy_s;  // false while mloc == -inf
+        if (__ballot(raise)) {
+            // lanes that do not raise keep alpha = 1 exactly (their m_ref may
+            // still be -inf); a raising lane with m_ref = -inf gets alpha = 0
+            const float m_new = raise ? mloc : m_ref;
+            const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mloc) * c_exp) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+            m_ref = m_new;
+        }
+        const float mb = (m_ref == -INFINITY ? 0.f : m_ref) * c_exp;
+
+        // ---- probabilities, their fp32 sum, P^T operands (rounded) ---------
+        // The sum must use the unrounded p: rounding each p to bf16 moves
+        // lse by up to ~2^-9, past its tolerance on short rows.
+        v8 pop[2][2];
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int j = 0; j < 8; j += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + j], c_exp, -mb));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + j + 1], c_exp, -mb));
+                    psum += p0 + p1;
+                    pop[kb][t][j] = static_cast<T>(p0);
+                    pop[kb][t][j + 1] = static_cast<T>(p1);
+                }
+        l_run += psum;
+
+        // ---- O^T += V^T . P^T ----------------------------------------------
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float pz = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + j], kLog2e, -mb));
-                        lsum += pz;
-                        pop[kb][t][j] = static_cast<T>(pz);
-                    }
-            l_run = l_run * alpha + lsum;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+                for (int t = 0; t < 2; ++t) {
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(stage + v_off[kb][t][0][db]));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4*)(stage + v_off[kb][t][1][db]));
+                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+                    const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+                    const v8 a = __builtin_bit_cast(v8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+                    oacc[db] = M::run(a, pop[kb][t], oacc[db]);
+                }
+        return nxt;
+    };
 
-            // ---- O^T += V^T . P^T ----------------------------------------
-            const lds_char* vl = lds + buf * L::stage + L::kBytes;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const lds_char* base = vl + v_off + (32 * kb + 16 * t) * L::vPitch + 64 * db;
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(base));
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(base + 8 * L::vPitch));
-                        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-                        const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-                        const v8 a = __builtin_bit_cast(v8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-                        oacc[db] = M::run(a, pop[kb][t], oacc[db]);
-                    }
-        }
-
-        if (nxt >= 0) store_tile(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
-        tile = nxt;
+    int tile = first_tile();
+    if (tile >= 0) {
+        dma_kv(tile, 0);
+        if (BIAS == kBiasLds) dma_bias(tile);
+    }
+    while (tile >= 0) {
+        tile = step(tile, 0);
+        if (tile < 0) break;
+        tile = step(tile, 1);
     }
 
     // ---- epilogue ---------------------------------------------------------
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    const bool dead = m_run == -INFINITY;
+    const float l_tot = sum_halves(l_run);
+    const bool dead = m_true == -INFINITY;
     if (__syncthreads_or(dead && row_ok)) {
         // Some row saw no valid key: its weights are uniform over all K keys.
         for (int d = tid; d < D; d += kThreads) {
             float acc = 0.f;
-            for (int64_t kk = 0; kk < K; ++kk) acc += static_cast<float>(vbase[kk * D + d]);
+            for (int kk = 0; kk < K; ++kk) acc += static_cast<float>(vbase[kk * D + d]);
             mean_v[d] = acc / static_cast<float>(K);
         }
         __syncthreads();
     }
     if (!row_ok) return;
-    T* orow = static_cast<T*>(p.out) + (bnh * Q + qrow) * D;
+    T* orow = static_cast<T*>(p.out) + (bnh * p.Q + qrow) * D;
     const float inv = dead ? 0.f : 1.0f / l_tot;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -413,47 +589,69 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
             *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, o4);
         }
     if (half == 0) {
-        const int64_t ridx = bnh * Q + qrow;
-        if (p.lse) p.lse[ridx] = dead ? kMaskedLogit + logf(static_cast<float>(K)) : m_run + logf(l_tot);
-        if (p.mx) p.mx[ridx] = dead ? kMaskedLogit : m_run;
+        const int64_t ridx = bnh * p.Q + qrow;
+        if (p.lse)
+            p.lse[ridx] = dead ? kMaskedLogit + logf(static_cast<float>(K))
+                               : m_ref * zscale + logf(l_tot);
+        if (p.mx) p.mx[ridx] = dead ? kMaskedLogit : m_true * zscale;
     }
 }
 
-template <typename T, int D, int KIND>
-hipError_t launch_kind(const Params& p, bool bias_vec, dim3 grid, hipStream_t stream) {
-    if (bias_vec)
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, true>), grid, dim3(kThreads), 0, stream, p);
+template <typename T, int D, int KIND, int BIAS>
+hipError_t launch_bias(const Params& p, bool exact, dim3 grid, hipStream_t stream) {
+    if (exact)
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true>), grid, dim3(kThreads), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, false>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false>), grid, dim3(kThreads), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
+template <typename T, int D, int KIND>
+hipError_t launch_kind(const Params& p, bool exact, dim3 grid, hipStream_t stream) {
+    if (!p.bias) return launch_bias<T, D, KIND, kNoBias>(p, exact, grid, stream);
+    // The DMA path moves 16-byte chunks of bias rows: rows must be 16-byte
+    // aligned.
+    const bool rows16 = p.K % 4 == 0 && reinterpret_cast<uintptr_t>(p.bias) % 16 == 0;
+    if (rows16) return launch_bias<T, D, KIND, kBiasLds>(p, exact, grid, stream);
+    return launch_bias<T, D, KIND, kBiasScalar>(p, exact, grid, stream);
+}
+
 template <typename T, int D>
-hipError_t launch_d(const Params& p, bool bias_vec, dim3 grid, hipStream_t stream) {
+hipError_t launch_d(const Params& p, bool exact, dim3 grid, hipStream_t stream) {
     switch (p.mask_kind) {
-    case TRIATTN_MASK_NONE:
-        return launch_kind<T, D, TRIATTN_MASK_NONE>(p, bias_vec, grid, stream);
-    case TRIATTN_MASK_DENSE:
-        return launch_kind<T, D, TRIATTN_MASK_DENSE>(p, bias_vec, grid, stream);
+    case TRIATTN_MASK_NONE:  // a kv_lengths mask with no lengths: limit = K
     case TRIATTN_MASK_KV_LENGTHS:
-        return launch_kind<T, D, TRIATTN_MASK_KV_LENGTHS>(p, bias_vec, grid, stream);
+        return launch_kind<T, D, TRIATTN_MASK_KV_LENGTHS>(p, exact, grid, stream);
+    case TRIATTN_MASK_DENSE:
+        return launch_kind<T, D, TRIATTN_MASK_DENSE>(p, exact, grid, stream);
     case TRIATTN_MASK_BLOCK:
-        return launch_kind<T, D, TRIATTN_MASK_BLOCK>(p, bias_vec, grid, stream);
+        return launch_kind<T, D, TRIATTN_MASK_BLOCK>(p, exact, grid, stream);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t launch_t(const Params& p, bool bias_vec, dim3 grid, hipStream_t stream) {
+hipError_t launch_t(const Params& p, bool exact, dim3 grid, hipStream_t stream) {
     switch (p.D) {
     case 32:
-        return launch_d<T, 32>(p, bias_vec, grid, stream);
+        return launch_d<T, 32>(p, exact, grid, stream);
     case 64:
-        return launch_d<T, 64>(p, bias_vec, grid, stream);
+        return launch_d<T, 64>(p, exact, grid, stream);
     case 128:
-        return launch_d<T, 128>(p, bias_vec, grid, stream);
+        return launch_d<T, 128>(p, exact, grid, stream);
     }
     return hipErrorInvalidValue;
+}
+
+// s*x is exact for every x of the input format when s is 0 or a power of two
+// (no bf16/fp16 input is near enough to the format limits to matter: fp16
+// results that fall below its normal range keep their subnormal value).
+bool scale_is_exact(float s) {
+    if (s == 0.0f) return true;
+    int e = 0;
+    return std::fabs(std::frexp(s, &e)) == 0.5f;
 }
 
 }  // namespace
@@ -465,6 +663,17 @@ bool mfma_supports(const Params& p, int32_t dtype) {
         // one block row per workgroup, whole tiles per kv block
         if (p.q_block % kQTile != 0 || p.kv_block % kKTile != 0) return false;
     }
+    // Byte offsets within one (b, n, h) or (b, h) slice, including the
+    // overhang of a ragged last tile and of the last query tile, must fit
+    // the 32-bit per-lane offset.
+    const int64_t kpad = (p.K + kKTile - 1) / kKTile * kKTile;
+    const int64_t qpad = (p.Q + kQTile - 1) / kQTile * kQTile;
+    const int64_t lim = int64_t(1) << 31;
+    if (kpad * p.D * 2 >= lim || qpad * p.D * 2 >= lim || (qpad + 1) * kpad * 4 >= lim)
+        return false;
+    // a negative non-power-of-two scale would flip the max; the generic
+    // kernel handles it
+    if (!(p.scale > 0.0f) && !scale_is_exact(p.scale)) return false;
     return true;
 }
 
@@ -473,9 +682,9 @@ hipError_t launch_mfma(const Params& p, int32_t dtype, hipStream_t stream) {
     const int64_t groups = p.B * p.N * p.H * n_qt;
     if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(groups));
-    const bool bias_vec = p.bias && (p.K % 4 == 0) && (reinterpret_cast<uintptr_t>(p.bias) % 16 == 0);
-    if (dtype == TRIATTN_BF16) return launch_t<__bf16>(p, bias_vec, grid, stream);
-    return launch_t<_Float16>(p, bias_vec, grid, stream);
+    const bool exact = scale_is_exact(p.scale);
+    if (dtype == TRIATTN_BF16) return launch_t<__bf16>(p, exact, grid, stream);
+    return launch_t<_Float16>(p, exact, grid, stream);
 }
 
 }  // namespace triattn

@@ -118,8 +118,9 @@ Params make_params(const tri_attn_shape* s, const void* q, const void* k, const 
     p.q_block = p.kv_block = p.max_blocks = p.full_max_blocks = 1;
     p.n_q_rows = p.n_kv_blocks = 1;
     if (mask) {
-        p.dense = mask->dense;
-        p.kv_lengths = mask->kv_lengths;
+        // only the arrays of the selected kind are forwarded to the kernels
+        if (mask->kind == TRIATTN_MASK_DENSE) p.dense = mask->dense;
+        if (mask->kind == TRIATTN_MASK_KV_LENGTHS) p.kv_lengths = mask->kv_lengths;
         if (mask->kind == TRIATTN_MASK_BLOCK) {
             p.mask_mod = mask->mask_mod;
             p.kv_num_blocks = mask->kv_num_blocks;
