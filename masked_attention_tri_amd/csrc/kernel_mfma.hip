@@ -6,7 +6,9 @@
 // max-shifted softmax; the page fixes the result, not the schedule).
 //
 // Work decomposition: one workgroup of 4 wavefronts owns 128 query rows of
-// one (b, n, h); wave w owns rows 32w .. 32w+31.  Keys go in tiles of 64.
+// one (b, n, h); wave w owns rows 32w .. 32w+31.  Keys go in tiles of 32,
+// which keeps the LDS footprint (and register state) small enough for four
+// workgroups per CU.
 //
 // Both contractions run on v_mfma_f32_32x32x16_{bf16,f16}:
 //   S^T = K . Q^T + C   A = K rows from LDS (16-byte reads), B = Q^T held in
@@ -27,7 +29,7 @@
 // buffered.  The fp32 bias is the largest stream (it is re-read for every n):
 // the accumulator layout would make each lane fetch 16 bytes from its own
 // query row, 32 rows per instruction, which saturates the L1 address path.
-// Instead each wave DMAs its 32 x 64 bias block with whole rows per lane
+// Instead each wave DMAs its 32 x 32 bias block with whole rows per lane
 // group (8 cache lines per instruction) into its own LDS region, reads it
 // back in the accumulator layout, and immediately refills the region with
 // the next tile's block.  LDS rows are unpadded; 16-byte chunks are stored
@@ -81,7 +83,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQTile = 32 * kWaves;  // query rows per workgroup
-constexpr int kKTile = 64;           // keys per K/V tile
+constexpr int kKTile = 32;           // keys per K/V tile
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog = 5.545177444479562f;  // ln(256): largest p before a rescale
@@ -113,8 +115,11 @@ struct Geo {
     static constexpr int chunks = D / 8;                 // 16-byte chunks per row
     static constexpr int tileBytes = kKTile * rowBytes;  // one K (or V) tile
     static constexpr int stageBytes = 2 * tileBytes;     // K + V
-    static constexpr int dmaPerWave = tileBytes / 1024 / kWaves;  // per tile, K or V
-    static_assert(dmaPerWave * 1024 * kWaves == tileBytes, "DMA split");
+    // A stage is 2*tileBytes/1024 DMA instructions (K first, then V), dealt
+    // round-robin to the waves.
+    static constexpr int kDma = tileBytes / 1024;
+    static constexpr int dmaPerWave = 2 * kDma / kWaves;
+    static_assert(kDma * 1024 == tileBytes && dmaPerWave * kWaves == 2 * kDma, "DMA split");
     // K is read 16 bytes per lane down consecutive rows (8 or 16 lanes per
     // LDS cycle at one chunk): consecutive rows must land on distinct banks.
     static __device__ __forceinline__ int fk(int r) {
@@ -132,11 +137,12 @@ struct Geo {
     }
 };
 
-// The per-wave bias block: 32 query rows x 64 keys of fp32 = 256-byte rows,
-// read 16 bytes per lane down consecutive rows.
+// The per-wave bias block: 32 query rows x 32 keys of fp32 = 128-byte rows,
+// read 16 bytes per lane down consecutive rows (the K-read pattern of D=64).
 constexpr int kBiasRowBytes = kKTile * 4;
-constexpr int kBiasWaveBytes = 32 * kBiasRowBytes;  // 8 KiB
-__device__ __forceinline__ int fb(int r) { return r & 15; }
+constexpr int kBiasWaveBytes = 32 * kBiasRowBytes;  // 4 KiB
+constexpr int kBiasDma = kBiasWaveBytes / 1024;
+__device__ __forceinline__ int fb(int r) { return (r + (r >> 3)) & 7; }
 
 __device__ __forceinline__ bool bit_set(const uint32_t* bits, int64_t i) {
     return (bits[i >> 5] >> (i & 31)) & 1u;
@@ -322,101 +328,94 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t bias_rsrc =
         make_rsrc(bslice, BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * 4) : 0u);
 
-    // K/V DMA: this wave issues DMA instructions I = wave*dmaPerWave + j of
-    // each tile; lane l of instruction I fills LDS slot s = 64 I + l, i.e.
-    // row s / chunks, stored chunk s % chunks, which holds source chunk
-    // (s % chunks) ^ f(row).
-    uint32_t k_src[G::dmaPerWave], v_src[G::dmaPerWave];
+    // K/V DMA: instruction I of a stage (I < kDma: K, else V) is issued by
+    // wave I % kWaves; lane l of it fills LDS slot s = 64 (I % kDma) + l of
+    // that tile, i.e. row s / chunks, stored chunk s % chunks, which holds
+    // source chunk (s % chunks) ^ f(row).
+    uint32_t kv_src[G::dmaPerWave];
 #pragma unroll
     for (int j = 0; j < G::dmaPerWave; ++j) {
-        const int s = 64 * (wave * G::dmaPerWave + j) + lane;
+        const int I = wave + kWaves * j;
+        const bool is_v = I >= G::kDma;
+        const int s = 64 * (I % G::kDma) + lane;
         const int r = s / G::chunks, c = s % G::chunks;
-        k_src[j] = static_cast<uint32_t>(r * G::rowBytes + 16 * (c ^ G::fk(r)));
-        v_src[j] = static_cast<uint32_t>(r * G::rowBytes + 16 * (c ^ G::fv(r)));
+        kv_src[j] = static_cast<uint32_t>(r * G::rowBytes +
+                                          16 * (c ^ (is_v ? G::fv(r) : G::fk(r))));
     }
     auto dma_kv = [&](int t, int buf) {
         const uint32_t toff = static_cast<uint32_t>(t) * G::tileBytes;
-        lds_char* kdst = lds + buf * G::stageBytes;
+        lds_char* dst = lds + buf * G::stageBytes;
 #pragma unroll
         for (int j = 0; j < G::dmaPerWave; ++j) {
-            const int I = wave * G::dmaPerWave + j;
-            dma16(k_rsrc, kdst + 1024 * I, k_src[j] + toff);
-            dma16(v_rsrc, kdst + G::tileBytes + 1024 * I, v_src[j] + toff);
+            const int I = wave + kWaves * j;  // wave-uniform
+            if (I < G::kDma)
+                dma16(k_rsrc, dst + 1024 * I, kv_src[j] + toff);
+            else
+                dma16(v_rsrc, dst + 1024 * I, kv_src[j] + toff);  // V follows K in the stage
         }
     };
-    // Bias DMA: 8 instructions of 4 rows x 256 bytes; lane l of instruction j
-    // fills row r = 4j + l/16 of the wave's block, stored chunk l%16, holding
-    // source chunk (l%16) ^ fb(r).  Rows past Q read past the slice and land
-    // as zeros; keys past K read the next row (masked).
-    uint32_t b_src[8];
+    // Bias DMA: kBiasDma instructions of 8 rows x 128 bytes; lane l of
+    // instruction j fills row r = 8j + l/8 of the wave's block, stored chunk
+    // l%8, holding source chunk (l%8) ^ fb(r).  Rows past Q read past the
+    // slice and land as zeros; keys past K read the next row (masked).
+    uint32_t b_src[kBiasDma];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = 4 * j + (lane >> 4);
+    for (int j = 0; j < kBiasDma; ++j) {
+        const int r = 8 * j + (lane >> 3);
         b_src[j] = static_cast<uint32_t>(q0w + r) * static_cast<uint32_t>(K) * 4u +
-                   16u * static_cast<uint32_t>((lane & 15) ^ fb(r));
+                   16u * static_cast<uint32_t>((lane & 7) ^ fb(r));
     }
     auto dma_bias = [&](int t) {
         const uint32_t toff = static_cast<uint32_t>(t) * kBiasRowBytes;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dma16(bias_rsrc, bias_lds + 1024 * j, b_src[j] + toff);
+        for (int j = 0; j < kBiasDma; ++j) dma16(bias_rsrc, bias_lds + 1024 * j, b_src[j] + toff);
     };
-    // Bias read into the accumulator layout: register 4g+e of key block kb is
-    // key 32kb + 8g + 4half + e, i.e. source chunk 8kb + 2g + half of row col.
-    auto read_bias = [&](f32x16 (&dst)[2]) {
+    // Bias read into the accumulator layout: register 4g+e is key
+    // 8g + 4half + e, i.e. source chunk 2g + half of row col.
+    auto read_bias = [&](f32x16& dst) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int g = 0; g < 4; ++g) {
+            const int chunk = (2 * g + half) ^ fb(col);
+            const f32x4 bv = __builtin_bit_cast(
+                f32x4,
+                *reinterpret_cast<const lds_u32x4*>(bias_lds + col * kBiasRowBytes + 16 * chunk));
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int chunk = (8 * kb + 2 * g + half) ^ fb(col);
-                const f32x4 bv = __builtin_bit_cast(
-                    f32x4, *reinterpret_cast<const lds_u32x4*>(bias_lds + col * kBiasRowBytes +
-                                                               16 * chunk));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dst[kb][4 * g + e] = bv[e];
-            }
+            for (int e = 0; e < 4; ++e) dst[4 * g + e] = bv[e];
+        }
     };
     // Bias for K % 4 != 0 (rows not 16-byte aligned): plain per-lane loads.
     const uint32_t bias_lane_scalar =
         static_cast<uint32_t>(qload) * static_cast<uint32_t>(K) * 4u + 16u * half;
-    auto load_bias_scalar = [&](int t, f32x16 (&dst)[2]) {
+    auto load_bias_scalar = [&](int t, f32x16& dst) {
         const uint32_t base = bias_lane_scalar + static_cast<uint32_t>(t) * kKTile * 4u;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dst[kb][4 * g + e] = bload32(bias_rsrc, base + 4u * (32 * kb + 8 * g + e));
+            for (int e = 0; e < 4; ++e) dst[4 * g + e] = bload32(bias_rsrc, base + 4u * (8 * g + e));
     };
 
     // Per-lane LDS offsets of the operand reads (within a stage).
-    // K: row 32kb + col, source chunk 2st + half.
-    int k_off[2][D / 16];
+    // K: row col, source chunk 2st + half.
+    int k_off[D / 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const int r = 32 * kb + col;
-            k_off[kb][st] = r * G::rowBytes + 16 * ((2 * st + half) ^ G::fk(r));
-        }
-    // V (transposing read): lane s names row 32kb + 16t + 8u + 4half + (s%16)/4
-    // and column 32db + 16((s/16)%2) + 4(s%4), i.e. byte 8(s%2) of source
-    // chunk 4db + 2((s/16)%2) + (s%4)/2; lane l then receives V[key][32db + l%32]
+    for (int st = 0; st < D / 16; ++st)
+        k_off[st] = col * G::rowBytes + 16 * ((2 * st + half) ^ G::fk(col));
+    // V (transposing read): lane s names row 16t + 8u + 4half + (s%16)/4 and
+    // column 32db + 16((s/16)%2) + 4(s%4), i.e. byte 8(s%2) of source chunk
+    // 4db + 2((s/16)%2) + (s%4)/2; lane l then receives V[key][32db + l%32]
     // for the 4 keys of its slots 4u..4u+3.
-    int v_off[2][2][2][D / 32];
+    int v_off[2][2][D / 32];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const int r = 32 * kb + 16 * t + 8 * u + 4 * half + ((lane & 15) >> 2);
-                    const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-                    v_off[kb][t][u][db] =
-                        G::tileBytes + r * G::rowBytes + 16 * (chunk ^ G::fv(r)) + 8 * (lane & 1);
-                }
+            for (int db = 0; db < D / 32; ++db) {
+                const int r = 16 * t + 8 * u + 4 * half + ((lane & 15) >> 2);
+                const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+                v_off[t][u][db] =
+                    G::tileBytes + r * G::rowBytes + 16 * (chunk ^ G::fv(r)) + 8 * (lane & 1);
+            }
     const uint8_t* dense_row = kDense ? p.dense + (b * p.N + n) * p.K : nullptr;
 
     f32x16 oacc[D / 32];
@@ -439,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
         if (nxt >= 0) dma_kv(nxt, buf ^ 1);  // that buffer was last read one tile ago
 
         // ---- S^T = K . Q^T + bias --------------------------------------
-        f32x16 s[2] = {f32x16{}, f32x16{}};
+        f32x16 s = f32x16{};
         if (BIAS == kBiasLds) {
             read_bias(s);
             wait_lds();
@@ -447,19 +446,13 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
         } else if (BIAS == kBiasScalar) {
             load_bias_scalar(tile, s);
         }
-        if (BIAS != kNoBias && !EXACT) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) s[kb] *= inv_s;
-        }
+        if (BIAS != kNoBias && !EXACT) s *= inv_s;
         const lds_char* stage = lds + buf * G::stageBytes;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const v8 a = __builtin_bit_cast(
-                    v8, *reinterpret_cast<const lds_u32x4*>(stage + k_off[kb][st]));
-                s[kb] = M::run(a, qop[st], s[kb]);
-            }
+            const v8 a =
+                __builtin_bit_cast(v8, *reinterpret_cast<const lds_u32x4*>(stage + k_off[st]));
+            s = M::run(a, qop[st], s);
         }
 
         // ---- element mask (only on tiles that need one) -------------------
@@ -467,11 +460,12 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
         bool causal = false;
         uint64_t dense_bits = ~0ull;
         if (kDense) {
-            const int key = k0 + lane;
+            // bit i = key k0 + i valid (both wave halves read the same 32 keys)
+            const int key = k0 + (lane & 31);
             const int kc = key < K ? key : K - 1;
             const bool ok = key < K && dense_row[kc] != 0;
-            dense_bits = __ballot(ok);
-            need_mask = dense_bits != ~0ull;
+            dense_bits = __ballot(ok) & 0xFFFFFFFFull;
+            need_mask = dense_bits != 0xFFFFFFFFull;
         }
         if (kBlock && p.mask_mod == TRIATTN_MOD_CAUSAL &&
             !bit_set(full_bits, tile / tiles_per_block) && k0 + kKTile - 1 > q0w) {
@@ -480,24 +474,20 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
         }
         if (need_mask) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kl_idx = 32 * kb + 8 * (r / 4) + 4 * half + (r % 4);
-                    const int key = k0 + kl_idx;
-                    bool ok = key < limit;
-                    if (kDense) ok = ok && ((dense_bits >> kl_idx) & 1ull);
-                    if (causal) ok = ok && qrow >= key;
-                    s[kb][r] = ok ? s[kb][r] : -INFINITY;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int kl_idx = 8 * (r / 4) + 4 * half + (r % 4);
+                const int key = k0 + kl_idx;
+                bool ok = key < limit;
+                if (kDense) ok = ok && ((dense_bits >> kl_idx) & 1ull);
+                if (causal) ok = ok && qrow >= key;
+                s[r] = ok ? s[r] : -INFINITY;
+            }
         }
 
         // ---- row max; lazily raised reference ------------------------------
-        float mloc = vmax(s[0][0], s[0][1]);
+        float mloc = vmax(s[0], s[1]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = kb == 0 ? 2 : 0; r < 16; r += 2) mloc = vmax(mloc, vmax(s[kb][r], s[kb][r + 1]));
+        for (int r = 2; r < 16; r += 2) mloc = vmax(mloc, vmax(s[r], s[r + 1]));
         mloc = max_halves(mloc);
         m_true = vmax(m_true, mloc);
         const bool raise = mloc > m_ref + lazy_s;  // false while mloc == -inf
@@ -516,38 +506,34 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
         // ---- probabilities, their fp32 sum, P^T operands (rounded) ---------
         // The sum must use the unrounded p: rounding each p to bf16 moves
         // lse by up to ~2^-9, past its tolerance on short rows.
-        v8 pop[2][2];
+        v8 pop[2];
         float psum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int j = 0; j < 8; j += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + j], c_exp, -mb));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * t + j + 1], c_exp, -mb));
-                    psum += p0 + p1;
-                    pop[kb][t][j] = static_cast<T>(p0);
-                    pop[kb][t][j + 1] = static_cast<T>(p1);
-                }
+            for (int j = 0; j < 8; j += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * t + j], c_exp, -mb));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * t + j + 1], c_exp, -mb));
+                psum += p0 + p1;
+                pop[t][j] = static_cast<T>(p0);
+                pop[t][j + 1] = static_cast<T>(p1);
+            }
         l_run += psum;
 
         // ---- O^T += V^T . P^T ----------------------------------------------
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)(stage + v_off[kb][t][0][db]));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4*)(stage + v_off[kb][t][1][db]));
-                    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-                    const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-                    const v8 a = __builtin_bit_cast(v8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-                    oacc[db] = M::run(a, pop[kb][t], oacc[db]);
-                }
+            for (int t = 0; t < 2; ++t) {
+                const i16x4 lo =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + v_off[t][0][db]));
+                const i16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + v_off[t][1][db]));
+                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
+                const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
+                const v8 a = __builtin_bit_cast(v8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+                oacc[db] = M::run(a, pop[t], oacc[db]);
+            }
         return nxt;
     };
 
