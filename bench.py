@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBPS = 8000.0
 METRIC = "fwd TFLOP/s + % bf16 MFMA peak, triangle attn N=Q=K=768 H=4 D=64"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_config4.json")
+PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "masked_attention_tri_amd", "csrc", "kernel_mfma.hip")
 
 
@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=4, help="named workload (4 = headline)")
+    ap.add_argument("--workload", default=None,
+                    help="named workload (default: the headline bf16 kv_lengths N768 D64 one)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -87,12 +88,13 @@ def work_counts(case):
     return nominal, alg, qo + kv + bias + aux + mask
 
 
-def traffic_entry():
-    """Measured HBM bytes per launch, if the counters were taken on this
-    exact kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_entry(workload):
+    """Measured HBM bytes per launch of the MFMA kernel on this workload, if
+    the counters were taken on this exact kernel source; else None."""
+    path = os.path.join(PROFILES, f"traffic_mfma_fwd_{workload}.json")
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
     src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
     if t.get("kernel_source_sha256") != src:
@@ -149,7 +151,8 @@ def main():
     mat.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    case = wl.make_config(args.config)
+    key = args.workload or wl.HEADLINE
+    case = wl.make_workload(key)
     g = case.to(dev)
     B, N, H, Q, K, D = case.shape
     out = torch.empty_like(g.q)
@@ -217,7 +220,7 @@ def main():
     sec = ms * 1e-3
     value = nominal / sec / 1e12
     alg_tflops = alg / sec / 1e12
-    tr = traffic_entry()
+    tr = traffic_entry(key)
     traffic = None if tr is None else tr["bytes_per_launch"]
     res = {
         "metric": METRIC,
@@ -239,7 +242,7 @@ def main():
         "hbm_GBps_algorithmic": round(alg_bytes / sec / 1e9, 1),
         "config": {
             "workload": case.name,
-            "config_index": args.config,
+            "key": key,
             "B": B, "N": N, "H": H, "Q": Q, "K": K, "D": D,
             "nominal_flop": nominal,
             "algorithmic_flop": alg,

@@ -3,7 +3,7 @@
 This module only draws random tensors; it holds none of the attention
 arithmetic, so both the GPU path and the CPU oracle can consume its output.
 
-Recipe (one CPU ``torch.Generator`` per case, seeded ``1000 + config``):
+Recipe (one CPU ``torch.Generator`` per case, with the seed listed per workload):
   * draws in the fixed order q, k, v, bias, then the mask / kv_lengths;
   * q, k, v ~ N(0, 1) drawn in fp32, then rounded (RNE) to the case dtype;
   * bias ~ N(0, sigma^2) in fp32, shape (B, 1, H, Q, K), shared over N;
@@ -107,47 +107,52 @@ def causal_block_lists(gen, n_rows: int, q_block: int = 128, kv_block: int = 128
                       q_block, kv_block, "causal")
 
 
-# name, dtype, B, N, H, Q=K, D
-CONFIGS = {
-    1: ("fp32 dense-ones B1 N32 H2 Q=K=32 D32", "f32", 1, 32, 2, 32, 32),
-    2: ("fp16 kv_lengths=96 B1 N128 H2 Q=K=128 D32", "f16", 1, 128, 2, 128, 32),
-    3: ("bf16 dense Bernoulli(0.5) B1 N384 H4 Q=K=384 D32", "bf16", 1, 384, 4, 384, 32),
-    4: ("bf16 kv_lengths U{384..768 step 8} B1 N768 H4 Q=K=768 D64", "bf16", 1, 768, 4, 768, 64),
-    5: ("bf16 causal BlockMask 128 no-bias B2 N1 H8 Q=K=4096 D128", "bf16", 2, 1, 8, 4096, 128),
+# key -> (description, seed, dtype, B, N, H, Q=K, D)
+WORKLOADS = {
+    "fp32_dense_ones": ("fp32 dense-ones B1 N32 H2 Q=K=32 D32", 1001, "f32", 1, 32, 2, 32, 32),
+    "fp16_lens96": ("fp16 kv_lengths=96 B1 N128 H2 Q=K=128 D32", 1002, "f16", 1, 128, 2, 128,
+                    32),
+    "bf16_dense_half": ("bf16 dense Bernoulli(0.5) B1 N384 H4 Q=K=384 D32", 1003, "bf16", 1,
+                        384, 4, 384, 32),
+    "bf16_lens_d64": ("bf16 kv_lengths U{384..768 step 8} B1 N768 H4 Q=K=768 D64", 1004,
+                      "bf16", 1, 768, 4, 768, 64),
+    "bf16_causal_blocks_d128": ("bf16 causal BlockMask 128 no-bias B2 N1 H8 Q=K=4096 D128",
+                                1005, "bf16", 2, 1, 8, 4096, 128),
 }
+HEADLINE = "bf16_lens_d64"
 
 
-def make_config(cfg: int) -> Case:
+def make_workload(key: str) -> Case:
     """The five named workloads, bit-for-bit reproducible."""
-    name, dt, B, N, H, S, D = CONFIGS[cfg]
+    name, seed, dt, B, N, H, S, D = WORKLOADS[key]
     dtype = DTYPES[dt]
-    gen = torch.Generator().manual_seed(1000 + cfg)
+    gen = torch.Generator().manual_seed(seed)
     q, k, v = _qkv(gen, B, N, H, S, S, D, dtype)
-    meta = {"config": cfg}
-    if cfg == 1:
+    meta = {"workload": key}
+    if key == "fp32_dense_ones":
         bias = _bias(gen, B, H, S, S, 1.0)
         mask = torch.ones(B, N, 1, 1, S, dtype=torch.bool)
         return Case(name, dtype, q, k, v, bias, mask=mask, scale=1.0 / 32 ** 0.5, meta=meta)
-    if cfg == 2:
+    if key == "fp16_lens96":
         bias = _bias(gen, B, H, S, S, 1.0)
         lens = torch.full((B, N, 1, 1, 1), 96, dtype=torch.int32)
         return Case(name, dtype, q, k, v, bias, kv_lengths=lens, scale=1.0 / 32 ** 0.5,
                     meta=meta)
-    if cfg == 3:
+    if key == "bf16_dense_half":
         bias = _bias(gen, B, H, S, S, 2.0)
         mask = torch.rand(B, N, 1, 1, S, generator=gen) < 0.5
         dead = torch.randperm(N, generator=gen)[:4]
         mask[:, dead] = False
         meta["fully_masked_rows"] = sorted(int(x) for x in dead)
         return Case(name, dtype, q, k, v, bias, mask=mask, meta=meta)
-    if cfg == 4:
+    if key == "bf16_lens_d64":
         bias = _bias(gen, B, H, S, S, 1.0)
         lens = (8 * torch.randint(48, 97, (B, N, 1, 1, 1), generator=gen)).to(torch.int32)
         return Case(name, dtype, q, k, v, bias, kv_lengths=lens, scale=1.0 / 8.0, meta=meta)
-    if cfg == 5:
+    if key == "bf16_causal_blocks_d128":
         block = causal_block_lists(gen, S // 128)
         return Case(name, dtype, q, k, v, None, block=block, scale=None, meta=meta)
-    raise KeyError(cfg)
+    raise KeyError(key)
 
 
 def make_case(B, N, H, Q, K, D, dtype="bf16", mask_kind="none", seed=0, bias=True,

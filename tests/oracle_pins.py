@@ -252,7 +252,7 @@ def check_blocks(fwd, seed=0):
     cb = wl.make_case(1, 3, 2, 24, 24, 8, "f32", "block", seed=seed + 5, q_block=8,
                       kv_block=8, mask_mod="causal", block_broadcast=True)
     check_against_library(fwd, cb)
-    # causal lists (config-5 style) equal the library's is_causal
+    # causal lists (as in the block-sparse workload) equal the library's is_causal
     g = torch.Generator().manual_seed(seed + 9)
     c = wl.make_case(1, 1, 2, 64, 64, 16, "bf16", "none", seed=seed + 9, bias=False)
     c.block = wl.causal_block_lists(g, 4, 16, 16)

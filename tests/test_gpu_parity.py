@@ -19,26 +19,26 @@ pytestmark = pytest.mark.gpu
 
 # ---- the five named workloads -------------------------------------------
 
-def test_config1_fp32_dense_ones():
-    say("config 1")
-    assert_parity(wl.make_config(1))
+def test_fp32_dense_ones():
+    say("fp32 dense-ones workload")
+    assert_parity(wl.make_workload("fp32_dense_ones"))
 
 
-def test_config1_fp32_no_mask():
-    say("config 1 without mask")
-    c = wl.make_config(1)
+def test_fp32_dense_ones_without_mask():
+    say("fp32 workload without mask")
+    c = wl.make_workload("fp32_dense_ones")
     c.mask = None
     assert_parity(c)
 
 
-def test_config2_fp16_kv_lengths():
-    say("config 2")
-    assert_parity(wl.make_config(2))
+def test_fp16_lens96():
+    say("fp16 kv_lengths=96 workload")
+    assert_parity(wl.make_workload("fp16_lens96"))
 
 
-def test_config3_bf16_dense_fully_masked_rows():
-    say("config 3")
-    c = wl.make_config(3)
+def test_bf16_dense_half_with_fully_masked_rows():
+    say("bf16 dense-mask workload")
+    c = wl.make_workload("bf16_dense_half")
     gpu = run_gpu(c)
     dead = c.meta["fully_masked_rows"]
     g = torch.Generator().manual_seed(5)
@@ -53,9 +53,9 @@ def test_config3_bf16_dense_fully_masked_rows():
         assert torch.all(gpu[1][0, n] == -1.0e9)
 
 
-def test_config4_bf16_kv_lengths_sampled():
-    say("config 4 (full size, sampled rows)")
-    c = wl.make_config(4)
+def test_bf16_lens_d64_headline_sampled():
+    say("bf16 kv_lengths N768 D64 workload (full size, sampled rows)")
+    c = wl.make_workload("bf16_lens_d64")
     gpu = run_gpu(c)
     lens = c.kv_lengths.view(-1)
     g = torch.Generator().manual_seed(6)
@@ -71,9 +71,9 @@ def test_config4_bf16_kv_lengths_sampled():
     assert_parity(sub, gpu=sub_gpu, rows=rows)
 
 
-def test_config5_bf16_causal_blockmask_sampled():
-    say("config 5 (full size, sampled rows)")
-    c = wl.make_config(5)
+def test_bf16_causal_blocks_d128_sampled():
+    say("bf16 causal BlockMask Q4096 D128 workload (full size, sampled rows)")
+    c = wl.make_workload("bf16_causal_blocks_d128")
     gpu = run_gpu(c)
     B, N, H, Q = 2, 1, 8, 4096
     qs = [0, 1, 63, 64, 127, 128, 129, 1000, 2047, 2048, 3071, 4000, 4095]
@@ -144,7 +144,7 @@ def test_p1_example_shapes_and_lengths():
     say("P1 example")
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
                                     "p1_example_shapes.json")))
-    c = wl.make_config(2)
+    c = wl.make_workload("fp16_lens96")
     assert list(c.q.shape) == g["q_shape"] and list(c.bias.shape) == g["bias_shape"]
     pos = torch.arange(128)
     mask = (pos.view(1, 128) < 96).view(1, 128, 1, 1, 1) & (pos.view(1, 128) < 96).view(

@@ -22,27 +22,27 @@ def test_oracle_library_random_seeds(seed):
         pins.check_against_library(orc.oracle_fwd, c)
 
 
-def test_oracle_small_configs_against_library():
-    # config 1 (fp32, dense all-ones mask) and config 2 (fp16, kv_lengths = 96)
-    for cfg in (1, 2):
-        pins.check_against_library(orc.oracle_fwd, wl.make_config(cfg))
+def test_oracle_small_workloads_against_library():
+    # fp32 with a dense all-ones mask, and fp16 with kv_lengths = 96
+    for key in ("fp32_dense_ones", "fp16_lens96"):
+        pins.check_against_library(orc.oracle_fwd, wl.make_workload(key))
 
 
-def test_oracle_config3_rows_against_library():
-    # config 3 restricted to a few n rows, including the four fully masked ones
-    c = wl.make_config(3)
+def test_oracle_dense_half_rows_against_library():
+    # the bf16 dense-mask workload restricted to a few n rows, including the four fully masked ones
+    c = wl.make_workload("bf16_dense_half")
     keep = sorted(set(c.meta["fully_masked_rows"]) | {0, 1, 200, 383})
     sub = wl.Case(c.name, c.dtype, c.q[:, keep], c.k[:, keep], c.v[:, keep], c.bias,
                   mask=c.mask[:, keep], scale=c.scale)
     pins.check_against_library(orc.oracle_fwd, sub)
 
 
-def test_oracle_config5_rows_against_causal_library():
-    # config 5's lists are causal; sampled q rows against is_causal on b=0,h=0
+def test_oracle_causal_blocks_rows_against_causal_library():
+    # the block workload's lists are causal; sampled q rows against is_causal on b=0,h=0
     import torch
     import torch.nn.functional as F
 
-    c = wl.make_config(5)
+    c = wl.make_workload("bf16_causal_blocks_d128")
     qs = [0, 1, 127, 128, 129, 2047, 4095]
     rows = [q for q in qs]  # b = 0, n = 0, h = 0
     O, lse, mx = hp.run_oracle(c, rows=rows)
