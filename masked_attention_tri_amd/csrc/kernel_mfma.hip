@@ -138,11 +138,14 @@ struct Geo {
 };
 
 // The per-wave bias block: 32 query rows x 32 keys of fp32 = 128-byte rows,
-// read 16 bytes per lane down consecutive rows (the K-read pattern of D=64).
+// read 16 bytes per lane down consecutive rows.  Of 16 lanes served
+// together, the 8 even rows land on one half of the 64 banks and the 8 odd
+// rows on the other, so the swizzle must differ across each of the two
+// groups: (r >> 1) & 7 does.
 constexpr int kBiasRowBytes = kKTile * 4;
 constexpr int kBiasWaveBytes = 32 * kBiasRowBytes;  // 4 KiB
 constexpr int kBiasDma = kBiasWaveBytes / 1024;
-__device__ __forceinline__ int fb(int r) { return (r + (r >> 3)) & 7; }
+__device__ __forceinline__ int fb(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ bool bit_set(const uint32_t* bits, int64_t i) {
     return (bits[i >> 5] >> (i & 31)) & 1u;
@@ -163,11 +166,12 @@ __device__ int64_t next_set(const uint32_t* bits, int64_t from, int64_t n) {
 }
 
 __device__ void mark_list(uint32_t* bits, const int32_t* counts, const int32_t* ids,
-                          int64_t list_row, int64_t width, int64_t n_blocks, int tid) {
+                          int64_t list_row, int64_t width, int64_t n_blocks, int tid,
+                          int n_threads) {
     int64_t count = counts[list_row];
     count = count < 0 ? 0 : (count > width ? width : count);
     const int32_t* row = ids + list_row * width;
-    for (int64_t j = tid; j < count; j += kThreads) {
+    for (int64_t j = tid; j < count; j += n_threads) {
         const int64_t id = row[j];
         if (id >= 0 && id < n_blocks) atomicOr(&bits[id >> 5], 1u << (id & 31));
     }
@@ -211,29 +215,63 @@ __device__ __forceinline__ float sum_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <typename T, int D, int KIND, int BIAS, bool EXACT>
-__global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
+template <int V>
+struct Par {
+    static constexpr int value = V;
+};
+
+// G = number of n rows per workgroup (1 or 2).  With G = 2 the two rows
+// share every fp32 bias block (the bias does not depend on n), which halves
+// the bias bytes each CU pulls from L2.
+// Waves per SIMD the register budget must allow: four (128 VGPRs) for
+// D <= 64, two for D = 128 (whose O accumulator alone takes 64 VGPRs).
+template <int D>
+constexpr int min_waves_per_simd() {
+    return D <= 64 ? 4 : 2;
+}
+
+template <typename T, int D, int KIND, int BIAS, bool EXACT, int G>
+__global__ __launch_bounds__(kThreads* G)
+__attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kernel(Params p) {
     using M = Mma<T>;
     using v8 = typename M::v8;
-    using G = Geo<D>;
+    using Ge = Geo<D>;
     constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);
     constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK;
     constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
-    constexpr int kBiasBytes = BIAS == kBiasLds ? kWaves * kBiasWaveBytes : 0;
-
-    __shared__ __attribute__((aligned(1024))) char smem[2 * G::stageBytes + kBiasBytes];
+    constexpr int kT = kThreads * G;
+    static_assert(G == 1 || (G == 2 && !kBlock), "n-sharing needs a tile list shared by both rows");
+    // LDS: two buffers (positions of even and odd parity) each of the G
+    // rows' K tiles and of their V tiles, and the bias blocks (one 32 x 32
+    // block per query group).  With G = 1 each wave owns its bias block and
+    // refills it as soon as it has read it, so one buffer suffices; with
+    // G = 2 two waves read each block and it is double buffered.  Every
+    // buffer is its own object: the compiler then knows that a DMA into one
+    // buffer does not write the others, and does not wait for it before
+    // reading them.
+    constexpr bool kBiasSingle = G == 1;
+    constexpr int kBiasBuf = BIAS == kBiasLds ? kWaves * kBiasWaveBytes : 16;
+    __shared__ __attribute__((aligned(1024))) char k_lds0[G * Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[G * Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[G * Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[G * Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char b_lds0[kBiasBuf];
+    __shared__ __attribute__((aligned(1024))) char b_lds1[kBiasSingle ? 16 : kBiasBuf];
     __shared__ uint32_t listed_bits[kBlock ? kWords : 1];
     __shared__ uint32_t full_bits[kBlock ? kWords : 1];
-    __shared__ float mean_v[D];
+    __shared__ float mean_v[G][D];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
+    const int ng = wave / kWaves;                                 // which of the G rows
+    const int qg = wave % kWaves;                                 // which 32-query group
     const int col = lane & 31;  // this lane's query within the wave
     const int half = lane >> 5;
 
-    // ---- workgroup -> (b, n, h, q tile), XCD-contiguous order -----------
+    // ---- workgroup -> (b, h, n group, q tile), XCD-contiguous order ----------
     const int64_t n_qt = (p.Q + kQTile - 1) / kQTile;
+    const int64_t n_grp = (p.N + G - 1) / G;
     const int64_t W = gridDim.x;
     const int64_t w = blockIdx.x;
     const int64_t xcd = w % kXcds, slot = w / kXcds;
@@ -241,22 +279,24 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
     const int64_t lid =
         xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
     const int64_t qt = lid % n_qt;
-    const int64_t n = (lid / n_qt) % p.N;
-    const int64_t h = (lid / (n_qt * p.N)) % p.H;
-    const int64_t b = lid / (n_qt * p.N * p.H);
+    const int64_t ngrp = (lid / n_qt) % n_grp;
+    const int64_t h = (lid / (n_qt * n_grp)) % p.H;
+    const int64_t b = lid / (n_qt * n_grp * p.H);
+    const int64_t n0 = ngrp * G;
+    const int64_t n_raw = n0 + ng;
+    const bool n_ok = n_raw < p.N;
+    const int64_t n = n_ok ? n_raw : p.N - 1;  // a missing row reads a valid one, stores nothing
 
-    // Per-(b,n,h) bases; offsets inside one slice fit in 32 bits (checked on
-    // the host).
     const int K = static_cast<int>(p.K), Q = static_cast<int>(p.Q);
     const int64_t bnh = (b * p.N + n) * p.H + h;
     const T* kbase = static_cast<const T*>(p.k) + bnh * p.K * D;
     const T* vbase = static_cast<const T*>(p.v) + bnh * p.K * D;
     const float* bslice = BIAS != kNoBias ? p.bias + (b * p.H + h) * p.Q * p.K : nullptr;
     const int q0 = static_cast<int>(qt) * kQTile;
-    const int q0w = q0 + 32 * wave;
+    const int q0w = q0 + 32 * qg;
     const int qrow = q0w + col;  // this lane's query
-    const bool row_ok = qrow < Q;
-    const int qload = row_ok ? qrow : Q - 1;
+    const bool row_ok = qrow < Q && n_ok;
+    const int qload = qrow < Q ? qrow : Q - 1;
 
     // Scale handling (see the header comment).
     const float zscale = EXACT ? 1.0f : p.scale;        // z = zscale * S
@@ -265,17 +305,24 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
     const float inv_s = EXACT ? 1.0f : 1.0f / p.scale;   // bias -> S units
 
     // ---- visited key range / tile list -------------------------------
-    int limit = K;  // keys >= limit are never valid
-    if (KIND == TRIATTN_MASK_KV_LENGTHS && p.kv_lengths) {
-        const int64_t len = p.kv_lengths[b * p.N + n];
-        limit = len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
+    auto clamp_len = [&](int64_t nn) -> int {
+        if (KIND != TRIATTN_MASK_KV_LENGTHS || !p.kv_lengths) return K;
+        const int64_t len = p.kv_lengths[b * p.N + nn];
+        return len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
+    };
+    const int limit = clamp_len(n);  // keys >= limit are never valid for this wave's row
+    const int my_tiles = n_ok ? (limit + kKTile - 1) / kKTile : 0;
+    int wg_tiles = my_tiles;  // tiles any row of the workgroup visits
+    if (G == 2) {
+        const int64_t other = n0 + (1 - ng);
+        const int ot = other < p.N ? (clamp_len(other) + kKTile - 1) / kKTile : 0;
+        wg_tiles = __builtin_amdgcn_readfirstlane(my_tiles > ot ? my_tiles : ot);
     }
-    const int n_tiles_all = (limit + kKTile - 1) / kKTile;
     int tiles_per_block = 1;
     if (kBlock) {
         tiles_per_block = static_cast<int>(p.kv_block / kKTile);
         const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
-        for (int i = tid; i < words; i += kThreads) {
+        for (int i = tid; i < words; i += kT) {
             listed_bits[i] = 0u;
             full_bits[i] = 0u;
         }
@@ -283,26 +330,30 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
         const int64_t inst = b * p.stride_b + n * p.stride_n + h * p.stride_h;
         const int64_t list_row = inst * p.n_q_rows + q0 / p.q_block;
         mark_list(listed_bits, p.kv_num_blocks, p.kv_indices, list_row, p.max_blocks,
-                  p.n_kv_blocks, tid);
+                  p.n_kv_blocks, tid, kT);
         if (p.full_kv_num_blocks) {
             mark_list(full_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid);
+                      p.full_max_blocks, p.n_kv_blocks, tid, kT);
             mark_list(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid);
+                      p.full_max_blocks, p.n_kv_blocks, tid, kT);
         }
         __syncthreads();
     }
+    const int n_tiles_all = (K + kKTile - 1) / kKTile;
     auto first_tile = [&]() -> int {
-        if (!kBlock) return n_tiles_all > 0 ? 0 : -1;
+        if (!kBlock) return wg_tiles > 0 ? 0 : -1;
         const int64_t blk = next_set(listed_bits, 0, p.n_kv_blocks);
         return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
     };
     auto next_tile = [&](int t) -> int {
-        if (!kBlock) return t + 1 < n_tiles_all ? t + 1 : -1;
+        if (t < 0) return -1;
+        if (!kBlock) return t + 1 < wg_tiles ? t + 1 : -1;
         if ((t + 1) % tiles_per_block != 0 && t + 1 < n_tiles_all) return t + 1;
         const int64_t blk = next_set(listed_bits, t / tiles_per_block + 1, p.n_kv_blocks);
         return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
     };
+    // does this wave compute tile t (its row has keys there)?
+    auto mine = [&](int t) -> bool { return kBlock ? t >= 0 : (t >= 0 && t < my_tiles); };
 
     // ---- Q^T operand: registers for the whole key loop ----------------
     v8 qop[D / 16];
@@ -320,65 +371,75 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
     }
 
     // ---- LDS regions and DMA address tables ------------------------------
-    lds_char* lds = (lds_char*)smem;
-    lds_char* bias_lds = lds + 2 * G::stageBytes + wave * kBiasWaveBytes;  // this wave's block
     const uint32_t kv_bytes = static_cast<uint32_t>(p.K * D * sizeof(T));
     const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kbase, kv_bytes);
     const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(vbase, kv_bytes);
     const __amdgpu_buffer_rsrc_t bias_rsrc =
         make_rsrc(bslice, BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * 4) : 0u);
+    auto kbuf = [&](int x) { return (lds_char*)(x ? k_lds1 : k_lds0) + ng * Ge::tileBytes; };
+    auto vbuf = [&](int x) { return (lds_char*)(x ? v_lds1 : v_lds0) + ng * Ge::tileBytes; };
+    auto bbuf = [&](int x) {
+        return (lds_char*)(x && !kBiasSingle ? b_lds1 : b_lds0) + qg * kBiasWaveBytes;
+    };
 
-    // K/V DMA: instruction I of a stage (I < kDma: K, else V) is issued by
-    // wave I % kWaves; lane l of it fills LDS slot s = 64 (I % kDma) + l of
-    // that tile, i.e. row s / chunks, stored chunk s % chunks, which holds
-    // source chunk (s % chunks) ^ f(row).
-    uint32_t kv_src[G::dmaPerWave];
+    // K/V DMA of one tile of this wave's row: instruction I (I < kDma: K,
+    // else V) is issued by query group I % kWaves; lane l of it fills LDS
+    // slot s = 64 (I % kDma) + l of that tile, i.e. row s / chunks, stored
+    // chunk s % chunks, which holds source chunk (s % chunks) ^ f(row).
+    uint32_t kv_src[Ge::dmaPerWave];
 #pragma unroll
-    for (int j = 0; j < G::dmaPerWave; ++j) {
-        const int I = wave + kWaves * j;
-        const bool is_v = I >= G::kDma;
-        const int s = 64 * (I % G::kDma) + lane;
-        const int r = s / G::chunks, c = s % G::chunks;
-        kv_src[j] = static_cast<uint32_t>(r * G::rowBytes +
-                                          16 * (c ^ (is_v ? G::fv(r) : G::fk(r))));
+    for (int j = 0; j < Ge::dmaPerWave; ++j) {
+        const int I = qg + kWaves * j;
+        const bool is_v = I >= Ge::kDma;
+        const int s = 64 * (I % Ge::kDma) + lane;
+        const int r = s / Ge::chunks, c = s % Ge::chunks;
+        kv_src[j] = static_cast<uint32_t>(r * Ge::rowBytes +
+                                          16 * (c ^ (is_v ? Ge::fv(r) : Ge::fk(r))));
     }
-    auto dma_kv = [&](int t, int buf) {
-        const uint32_t toff = static_cast<uint32_t>(t) * G::tileBytes;
-        lds_char* dst = lds + buf * G::stageBytes;
+    auto dma_k = [&](int t, int x) {
+        const uint32_t toff = static_cast<uint32_t>(t) * Ge::tileBytes;
 #pragma unroll
-        for (int j = 0; j < G::dmaPerWave; ++j) {
-            const int I = wave + kWaves * j;  // wave-uniform
-            if (I < G::kDma)
-                dma16(k_rsrc, dst + 1024 * I, kv_src[j] + toff);
-            else
-                dma16(v_rsrc, dst + 1024 * I, kv_src[j] + toff);  // V follows K in the stage
+        for (int j = 0; j < Ge::dmaPerWave; ++j) {
+            const int I = qg + kWaves * j;  // wave-uniform
+            if (I < Ge::kDma) dma16(k_rsrc, kbuf(x) + 1024 * I, kv_src[j] + toff);
         }
     };
-    // Bias DMA: kBiasDma instructions of 8 rows x 128 bytes; lane l of
-    // instruction j fills row r = 8j + l/8 of the wave's block, stored chunk
-    // l%8, holding source chunk (l%8) ^ fb(r).  Rows past Q read past the
-    // slice and land as zeros; keys past K read the next row (masked).
-    uint32_t b_src[kBiasDma];
+    auto dma_v = [&](int t, int x) {
+        const uint32_t toff = static_cast<uint32_t>(t) * Ge::tileBytes;
 #pragma unroll
-    for (int j = 0; j < kBiasDma; ++j) {
-        const int r = 8 * j + (lane >> 3);
-        b_src[j] = static_cast<uint32_t>(q0w + r) * static_cast<uint32_t>(K) * 4u +
-                   16u * static_cast<uint32_t>((lane & 7) ^ fb(r));
-    }
-    auto dma_bias = [&](int t) {
+        for (int j = 0; j < Ge::dmaPerWave; ++j) {
+            const int I = qg + kWaves * j;
+            if (I >= Ge::kDma) dma16(v_rsrc, vbuf(x) + 1024 * (I - Ge::kDma), kv_src[j] + toff);
+        }
+    };
+    // Bias DMA: a query group's block is kBiasDma instructions of 8 rows x
+    // 128 bytes, dealt to the G waves of that group; lane l of instruction
+    // j fills row r = 8j + l/8, stored chunk l%8, holding source chunk
+    // (l%8) ^ fb(r) = (l%8) ^ (l/16) ^ 4(j%2).  Rows past Q read past the
+    // slice and land as zeros; keys past K read the next row (masked).
+    constexpr int kBiasPerWave = kBiasDma / G;
+    const uint32_t b_row = static_cast<uint32_t>(q0w + (lane >> 3)) * static_cast<uint32_t>(K) * 4u;
+    const uint32_t b_src_even = b_row + 16u * static_cast<uint32_t>((lane & 7) ^ (lane >> 4));
+    const uint32_t b_src_odd = b_row + 16u * static_cast<uint32_t>((lane & 7) ^ (lane >> 4) ^ 4);
+    auto dma_bias = [&](int t, int x) {
+        if (BIAS != kBiasLds) return;
         const uint32_t toff = static_cast<uint32_t>(t) * kBiasRowBytes;
 #pragma unroll
-        for (int j = 0; j < kBiasDma; ++j) dma16(bias_rsrc, bias_lds + 1024 * j, b_src[j] + toff);
+        for (int i = 0; i < kBiasPerWave; ++i) {
+            const int j = ng * kBiasPerWave + i;
+            const uint32_t rows = static_cast<uint32_t>(8 * j) * static_cast<uint32_t>(K) * 4u;
+            dma16(bias_rsrc, bbuf(x) + 1024 * j, ((j & 1) ? b_src_odd : b_src_even) + rows + toff);
+        }
     };
     // Bias read into the accumulator layout: register 4g+e is key
     // 8g + 4half + e, i.e. source chunk 2g + half of row col.
-    auto read_bias = [&](f32x16& dst) {
+    auto read_bias = [&](f32x16& dst, int x) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int chunk = (2 * g + half) ^ fb(col);
             const f32x4 bv = __builtin_bit_cast(
                 f32x4,
-                *reinterpret_cast<const lds_u32x4*>(bias_lds + col * kBiasRowBytes + 16 * chunk));
+                *reinterpret_cast<const lds_u32x4*>(bbuf(x) + col * kBiasRowBytes + 16 * chunk));
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[4 * g + e] = bv[e];
         }
@@ -394,29 +455,29 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
             for (int e = 0; e < 4; ++e) dst[4 * g + e] = bload32(bias_rsrc, base + 4u * (8 * g + e));
     };
 
-    // Per-lane LDS offsets of the operand reads (within a stage).
-    // K: row col, source chunk 2st + half.
-    int k_off[D / 16];
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-        k_off[st] = col * G::rowBytes + 16 * ((2 * st + half) ^ G::fk(col));
+    // Per-lane LDS offsets of the operand reads (within a tile).
+    // K: row col, source chunk 2st + half, stored at chunk (2st + half) ^
+    // fk(col) = 2st ^ (half ^ fk(col)); the row, the chunk and its high
+    // bits occupy disjoint bits of the offset, so the offset of k-step st is
+    // k_base ^ 32st.
+    const int k_base = col * Ge::rowBytes + 16 * (half ^ Ge::fk(col));
     // V (transposing read): lane s names row 16t + 8u + 4half + (s%16)/4 and
     // column 32db + 16((s/16)%2) + 4(s%4), i.e. byte 8(s%2) of source chunk
     // 4db + 2((s/16)%2) + (s%4)/2; lane l then receives V[key][32db + l%32]
-    // for the 4 keys of its slots 4u..4u+3.
-    int v_off[2][2][D / 32];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const int r = 16 * t + 8 * u + 4 * half + ((lane & 15) >> 2);
-                const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-                v_off[t][u][db] =
-                    G::tileBytes + r * G::rowBytes + 16 * (chunk ^ G::fv(r)) + 8 * (lane & 1);
-            }
+    // for the 4 keys of its slots 4u..4u+3.  The swizzle of row r depends on
+    // r % 8 only, which t and u do not change: they add (16t + 8u) rows.
+    // As for K, the column block db only flips bits of the stored chunk:
+    // the offset for db is v_base ^ 64db.
+    const int v_base = [&] {
+        const int r = 4 * half + ((lane & 15) >> 2);
+        const int chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+        return r * Ge::rowBytes + 16 * (chunk ^ Ge::fv(r)) + 8 * (lane & 1);
+    }();
     const uint8_t* dense_row = kDense ? p.dense + (b * p.N + n) * p.K : nullptr;
+    auto dense_byte = [&](int t) -> bool {
+        const int key = t * kKTile + (lane & 31);
+        return key < K && dense_row[key] != 0;
+    };
 
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -425,61 +486,53 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
     float m_ref = -INFINITY;   // reference max of the exponent, S units
     float l_run = 0.f;         // this lane's half of the running sum
 
-    // One key tile, computed from LDS buffer `buf`; DMAs for the next tile go
-    // to the other K/V buffer and (after this tile's bias is read) to this
-    // wave's bias region.  Returns the next tile (or -1).
-    auto step = [&](int tile, int buf) -> int {
-        tile = __builtin_amdgcn_readfirstlane(tile);
-        const int nxt = __builtin_amdgcn_readfirstlane(next_tile(tile));
-        const int k0 = tile * kKTile;
-        // This tile's DMAs (issued one tile ago) have landed, for every wave.
-        wait_vmem();
-        __syncthreads();
-        if (nxt >= 0) dma_kv(nxt, buf ^ 1);  // that buffer was last read one tile ago
-
-        // ---- S^T = K . Q^T + bias --------------------------------------
-        f32x16 s = f32x16{};
-        if (BIAS == kBiasLds) {
-            read_bias(s);
-            wait_lds();
-            if (nxt >= 0) dma_bias(nxt);  // the region is free again
-        } else if (BIAS == kBiasScalar) {
-            load_bias_scalar(tile, s);
-        }
+    // S^T = K . Q^T + bias for tile t from K buffer / bias buffer x.
+    auto qk = [&](f32x16& s, int t, int x) {
+        s = f32x16{};
+        if (BIAS == kBiasLds) read_bias(s, x);
+        if (BIAS == kBiasScalar) load_bias_scalar(t, s);
         if (BIAS != kNoBias && !EXACT) s *= inv_s;
-        const lds_char* stage = lds + buf * G::stageBytes;
+        const lds_char* kt = kbuf(x);
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
             const v8 a =
-                __builtin_bit_cast(v8, *reinterpret_cast<const lds_u32x4*>(stage + k_off[st]));
+                __builtin_bit_cast(v8, *reinterpret_cast<const lds_u32x4*>(kt + (k_base ^ (32 * st))));
             s = M::run(a, qop[st], s);
         }
+    };
 
+    // Softmax of tile t (logits in s) and O^T += V^T . P^T from V buffer x.
+    auto softmax_pv = [&](f32x16& s, int t, int x, bool dvalid) {
+        const int k0 = t * kKTile;
         // ---- element mask (only on tiles that need one) -------------------
+        // Register r holds key k0 + 8(r/4) + r%4 in lanes 0-31 and that key
+        // + 4 in lanes 32-63, so the length and dense-mask tests are uniform
+        // per wave half: they become one 64-bit lane mask per register,
+        // built with scalar instructions and applied by one select.
         bool need_mask = k0 + kKTile > limit;
         bool causal = false;
-        uint64_t dense_bits = ~0ull;
+        uint32_t dense_bits = ~0u;
         if (kDense) {
-            // bit i = key k0 + i valid (both wave halves read the same 32 keys)
-            const int key = k0 + (lane & 31);
-            const int kc = key < K ? key : K - 1;
-            const bool ok = key < K && dense_row[kc] != 0;
-            dense_bits = __ballot(ok) & 0xFFFFFFFFull;
-            need_mask = dense_bits != 0xFFFFFFFFull;
+            // bit i = key k0 + i valid (both wave halves hold the same 32 keys)
+            dense_bits = static_cast<uint32_t>(__ballot(dvalid));
+            need_mask = dense_bits != ~0u;
         }
         if (kBlock && p.mask_mod == TRIATTN_MOD_CAUSAL &&
-            !bit_set(full_bits, tile / tiles_per_block) && k0 + kKTile - 1 > q0w) {
+            !bit_set(full_bits, t / tiles_per_block) && k0 + kKTile - 1 > q0w) {
             causal = true;
             need_mask = true;
         }
         if (need_mask) {
+            constexpr uint64_t kLo = 0x00000000FFFFFFFFull, kHi = 0xFFFFFFFF00000000ull;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int kl_idx = 8 * (r / 4) + 4 * half + (r % 4);
-                const int key = k0 + kl_idx;
-                bool ok = key < limit;
-                if (kDense) ok = ok && ((dense_bits >> kl_idx) & 1ull);
-                if (causal) ok = ok && qrow >= key;
+                const int ka = 8 * (r / 4) + (r % 4);  // key offset in lanes 0-31
+                uint64_t lanes = (k0 + ka < limit ? kLo : 0ull) | (k0 + ka + 4 < limit ? kHi : 0ull);
+                if (kDense)
+                    lanes &= (((dense_bits >> ka) & 1u) ? kLo : 0ull) |
+                             (((dense_bits >> (ka + 4)) & 1u) ? kHi : 0ull);
+                bool ok = __builtin_amdgcn_inverse_ballot_w64(lanes);
+                if (causal) ok = ok && qrow >= k0 + ka + 4 * half;
                 s[r] = ok ? s[r] : -INFINITY;
             }
         }
@@ -509,43 +562,92 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
         v8 pop[2];
         float psum = 0.f;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * t + j], c_exp, -mb));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * t + j + 1], c_exp, -mb));
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * tt + j], c_exp, -mb));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * tt + j + 1], c_exp, -mb));
                 psum += p0 + p1;
-                pop[t][j] = static_cast<T>(p0);
-                pop[t][j + 1] = static_cast<T>(p1);
+                pop[tt][j] = static_cast<T>(p0);
+                pop[tt][j + 1] = static_cast<T>(p1);
             }
         l_run += psum;
 
         // ---- O^T += V^T . P^T ----------------------------------------------
+        const lds_char* vt = vbuf(x);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const i16x4 lo =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + v_off[t][0][db]));
-                const i16x4 hi =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + v_off[t][1][db]));
+            for (int tt = 0; tt < 2; ++tt) {
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(vt + (v_base ^ (64 * db)) + 16 * tt * Ge::rowBytes));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4*)(vt + (v_base ^ (64 * db)) + (16 * tt + 8) * Ge::rowBytes));
                 const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
                 const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
                 const v8 a = __builtin_bit_cast(v8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-                oacc[db] = M::run(a, pop[t], oacc[db]);
+                oacc[db] = M::run(a, pop[tt], oacc[db]);
             }
-        return nxt;
     };
 
-    int tile = first_tile();
-    if (tile >= 0) {
-        dma_kv(tile, 0);
-        if (BIAS == kBiasLds) dma_bias(tile);
+    // ---- key loop ---------------------------------------------------------
+    // Position j of the tile sequence keeps K, V (and, with G = 2, bias) in
+    // buffers j % 2.  At position j the logits of tile cur = t_j are in
+    // registers; the loop first computes the logits of t_{j+1} (K buffer
+    // (j+1) % 2) and then the softmax and P.V of t_j (V buffer j % 2), so the
+    // QK contraction of one tile overlaps the softmax of the previous one.
+    // DMAs run one position ahead: K and bias of t_{j+2}, V of t_{j+1}; a
+    // single bias buffer is refilled right after the logits have read it.
+    f32x16 sa, sb;
+    int cur = first_tile();
+    int nxt = next_tile(cur);
+    bool dv_cur = false, dv_nxt = false;
+    if (cur >= 0) {
+        if (mine(cur)) dma_k(cur, 0);
+        dma_bias(cur, 0);
+        if (kDense && mine(cur)) dv_cur = dense_byte(cur);
+        wait_vmem();
+        __syncthreads();
+        if (nxt >= 0) {
+            if (mine(nxt)) dma_k(nxt, 1);
+            if (!kBiasSingle) dma_bias(nxt, 1);
+        }
+        if (mine(cur)) dma_v(cur, 0);
+        if (mine(cur)) qk(sa, cur, 0);
+        if (kBiasSingle && nxt >= 0) {
+            wait_lds();  // the bias reads are done before the region is refilled
+            dma_bias(nxt, 0);
+        }
     }
-    while (tile >= 0) {
-        tile = step(tile, 0);
-        if (tile < 0) break;
-        tile = step(tile, 1);
+    auto step = [&](auto X, f32x16& s_cur, f32x16& s_nxt) {
+        constexpr int x = decltype(X)::value;
+        const int nxt2 = __builtin_amdgcn_readfirstlane(next_tile(nxt));
+        // K/bias of nxt and V of cur (issued one position ago) have landed for
+        // every wave, and every wave is done with the buffers refilled below.
+        wait_vmem();
+        __syncthreads();
+        if (nxt2 >= 0) {
+            if (mine(nxt2)) dma_k(nxt2, x);
+            if (!kBiasSingle) dma_bias(nxt2, x);
+        }
+        if (mine(nxt)) {
+            dma_v(nxt, x ^ 1);
+            if (kDense) dv_nxt = dense_byte(nxt);
+        }
+        if (mine(nxt)) qk(s_nxt, nxt, x ^ 1);
+        if (kBiasSingle && nxt2 >= 0) {
+            wait_lds();  // the bias reads are done before the region is refilled
+            dma_bias(nxt2, 0);
+        }
+        if (mine(cur)) softmax_pv(s_cur, cur, x, dv_cur);
+        cur = nxt;
+        nxt = nxt2;
+        dv_cur = dv_nxt;
+    };
+    while (cur >= 0) {
+        step(Par<0>{}, sa, sb);
+        if (cur < 0) break;
+        step(Par<1>{}, sb, sa);
     }
 
     // ---- epilogue ---------------------------------------------------------
@@ -553,10 +655,13 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
     const bool dead = m_true == -INFINITY;
     if (__syncthreads_or(dead && row_ok)) {
         // Some row saw no valid key: its weights are uniform over all K keys.
-        for (int d = tid; d < D; d += kThreads) {
+        for (int i = tid; i < G * D; i += kT) {
+            const int g = i / D, d = i % D;
+            const int64_t nn = n0 + g < p.N ? n0 + g : p.N - 1;
+            const T* vb = static_cast<const T*>(p.v) + ((b * p.N + nn) * p.H + h) * p.K * D;
             float acc = 0.f;
-            for (int kk = 0; kk < K; ++kk) acc += static_cast<float>(vbase[kk * D + d]);
-            mean_v[d] = acc / static_cast<float>(K);
+            for (int kk = 0; kk < K; ++kk) acc += static_cast<float>(vb[kk * D + d]);
+            mean_v[g][d] = acc / static_cast<float>(K);
         }
         __syncthreads();
     }
@@ -571,7 +676,7 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
             T o4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                o4[e] = static_cast<T>(dead ? mean_v[d0 + e] : oacc[db][4 * g + e] * inv);
+                o4[e] = static_cast<T>(dead ? mean_v[ng][d0 + e] : oacc[db][4 * g + e] * inv);
             *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, o4);
         }
     if (half == 0) {
@@ -583,61 +688,76 @@ __global__ __launch_bounds__(kThreads) void mfma_fwd_kernel(Params p) {
     }
 }
 
+// n rows per workgroup.  The kernel supports G = 2 (two rows sharing each
+// bias block, half the bias bytes per CU), but rows of unequal length then
+// leave waves idle behind the longer one; on right-padded rows G = 1 is
+// faster, and it is used throughout.
+template <int KIND, int BIAS>
+constexpr int groups_of() {
+    return 1;
+}
+
 template <typename T, int D, int KIND, int BIAS>
-hipError_t launch_bias(const Params& p, bool exact, dim3 grid, hipStream_t stream) {
+hipError_t launch_bias(const Params& p, bool exact, hipStream_t stream) {
+    constexpr int G = groups_of<KIND, BIAS>();
+    const int64_t n_qt = (p.Q + kQTile - 1) / kQTile;
+    const int64_t groups = p.B * ((p.N + G - 1) / G) * p.H * n_qt;
+    if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(groups));
     if (exact)
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true>), grid, dim3(kThreads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, G>), grid, dim3(kThreads * G),
+                           0, stream, p);
     else
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false>), grid, dim3(kThreads), 0,
-                           stream, p);
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false, G>), grid,
+                           dim3(kThreads * G), 0, stream, p);
     return hipGetLastError();
 }
 
 template <typename T, int D, int KIND>
-hipError_t launch_kind(const Params& p, bool exact, dim3 grid, hipStream_t stream) {
-    if (!p.bias) return launch_bias<T, D, KIND, kNoBias>(p, exact, grid, stream);
+hipError_t launch_kind(const Params& p, bool exact, hipStream_t stream) {
+    if (!p.bias) return launch_bias<T, D, KIND, kNoBias>(p, exact, stream);
     // The DMA path moves 16-byte chunks of bias rows: rows must be 16-byte
     // aligned.
     const bool rows16 = p.K % 4 == 0 && reinterpret_cast<uintptr_t>(p.bias) % 16 == 0;
-    if (rows16) return launch_bias<T, D, KIND, kBiasLds>(p, exact, grid, stream);
-    return launch_bias<T, D, KIND, kBiasScalar>(p, exact, grid, stream);
+    if (rows16) return launch_bias<T, D, KIND, kBiasLds>(p, exact, stream);
+    return launch_bias<T, D, KIND, kBiasScalar>(p, exact, stream);
 }
 
 template <typename T, int D>
-hipError_t launch_d(const Params& p, bool exact, dim3 grid, hipStream_t stream) {
+hipError_t launch_d(const Params& p, bool exact, hipStream_t stream) {
     switch (p.mask_kind) {
     case TRIATTN_MASK_NONE:  // a kv_lengths mask with no lengths: limit = K
     case TRIATTN_MASK_KV_LENGTHS:
-        return launch_kind<T, D, TRIATTN_MASK_KV_LENGTHS>(p, exact, grid, stream);
+        return launch_kind<T, D, TRIATTN_MASK_KV_LENGTHS>(p, exact, stream);
     case TRIATTN_MASK_DENSE:
-        return launch_kind<T, D, TRIATTN_MASK_DENSE>(p, exact, grid, stream);
+        return launch_kind<T, D, TRIATTN_MASK_DENSE>(p, exact, stream);
     case TRIATTN_MASK_BLOCK:
-        return launch_kind<T, D, TRIATTN_MASK_BLOCK>(p, exact, grid, stream);
+        return launch_kind<T, D, TRIATTN_MASK_BLOCK>(p, exact, stream);
     }
     return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t launch_t(const Params& p, bool exact, dim3 grid, hipStream_t stream) {
+hipError_t launch_t(const Params& p, bool exact, hipStream_t stream) {
     switch (p.D) {
     case 32:
-        return launch_d<T, 32>(p, exact, grid, stream);
+        return launch_d<T, 32>(p, exact, stream);
     case 64:
-        return launch_d<T, 64>(p, exact, grid, stream);
+        return launch_d<T, 64>(p, exact, stream);
     case 128:
-        return launch_d<T, 128>(p, exact, grid, stream);
+        return launch_d<T, 128>(p, exact, stream);
     }
     return hipErrorInvalidValue;
 }
 
-// s*x is exact for every x of the input format when s is 0 or a power of two
-// (no bf16/fp16 input is near enough to the format limits to matter: fp16
-// results that fall below its normal range keep their subnormal value).
+// s*x is exact for every normal x of the input format when s is 0 or a power
+// of two with |s| <= 1 (so s*x cannot overflow).  An fp16 product that falls
+// below the normal range is rounded to a subnormal, an absolute error of at
+// most 2^-25 per element of Q, far below the output tolerance.
 bool scale_is_exact(float s) {
     if (s == 0.0f) return true;
     int e = 0;
-    return std::fabs(std::frexp(s, &e)) == 0.5f;
+    return std::fabs(std::frexp(s, &e)) == 0.5f && std::fabs(s) <= 1.0f;
 }
 
 }  // namespace
@@ -657,20 +777,16 @@ bool mfma_supports(const Params& p, int32_t dtype) {
     const int64_t lim = int64_t(1) << 31;
     if (kpad * p.D * 2 >= lim || qpad * p.D * 2 >= lim || (qpad + 1) * kpad * 4 >= lim)
         return false;
-    // a negative non-power-of-two scale would flip the max; the generic
-    // kernel handles it
-    if (!(p.scale > 0.0f) && !scale_is_exact(p.scale)) return false;
+    // Other scales run as z = s * (Q.K + B/s): a negative s would flip the
+    // max and a tiny one would overflow B/s; the generic kernel takes both.
+    if (!scale_is_exact(p.scale) && !(p.scale >= 0x1p-40f)) return false;
     return true;
 }
 
 hipError_t launch_mfma(const Params& p, int32_t dtype, hipStream_t stream) {
-    const int64_t n_qt = (p.Q + kQTile - 1) / kQTile;
-    const int64_t groups = p.B * p.N * p.H * n_qt;
-    if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid(static_cast<unsigned>(groups));
     const bool exact = scale_is_exact(p.scale);
-    if (dtype == TRIATTN_BF16) return launch_t<__bf16>(p, exact, grid, stream);
-    return launch_t<_Float16>(p, exact, grid, stream);
+    if (dtype == TRIATTN_BF16) return launch_t<__bf16>(p, exact, stream);
+    return launch_t<_Float16>(p, exact, stream);
 }
 
 }  // namespace triattn
