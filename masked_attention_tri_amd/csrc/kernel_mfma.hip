@@ -25,8 +25,9 @@
 //                   rescale of O is a per-lane scalar.
 //
 // Data movement: every tile arrives by LDS DMA (buffer_load ... lds), never
-// through registers.  K and V tiles are shared by the workgroup and double
-// buffered.  The fp32 bias is the largest stream (it is re-read for every n):
+// through registers.  K and V tiles are shared by the workgroup in rings of
+// three buffers, loaded two tiles ahead.  The fp32 bias is the largest
+// stream (it is re-read for every n):
 // the accumulator layout would make each lane fetch 16 bytes from its own
 // query row, 32 rows per instruction, which saturates the L1 address path.
 // Instead each wave DMAs its 32 x 32 bias block with whole rows per lane
@@ -88,6 +89,8 @@ constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog = 5.545177444479562f;  // ln(256): largest p before a rescale
 
+// Bias paths: none; staged through LDS by DMA; per-lane 4-byte loads (rows
+// not 16-byte aligned).
 enum BiasMode { kNoBias = 0, kBiasLds = 1, kBiasScalar = 2 };
 
 template <typename T>
@@ -188,15 +191,37 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ float bload32(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
 }
-// 16 bytes per lane from byte offset voff into LDS at dst + 16 * lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, lds_char* dst, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
-                                             voff, 0, 0, 0);
+// The same descriptor as four dwords, for the DMA below.
+__device__ __forceinline__ u32x4 make_desc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xFFFFu, bytes,
+                 static_cast<uint32_t>(kRsrcWord3)};
+}
+// 16 bytes per lane from byte offset voff into LDS at dst + 16 * lane
+// (buffer_load_dwordx4 ... lds; M0 holds the LDS address).  Written as
+// inline assembly so that the compiler does not track these LDS writes: it
+// would otherwise wait for every DMA in flight before any later LDS read,
+// which defeats prefetching more than one tile ahead.  The key loop waits
+// for them explicitly (vmcnt) and fences with barriers instead.
+__device__ __forceinline__ void dma16(const u32x4& r, lds_char* dst, uint32_t voff) {
+    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(r)
+                 : "memory");
 }
 // Wait until this wave's vector-memory operations (the DMAs) have landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Wait until this wave's LDS reads have returned.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// s_waitcnt immediate that waits until at most N vector-memory operations of
+// this wave are outstanding (vmcnt: bits 3:0 and 15:14; lgkmcnt and expcnt
+// left at their maxima).
+template <int N>
+constexpr int kVmcntWait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    return (N & 15) | ((N >> 4) << 14) | 0x0F70;
+}
 
 // IEEE maximum (NaN-propagating); lowers to v_maximum3_f32 chains without the
 // NaN-quieting instructions fmaxf needs.
@@ -220,9 +245,6 @@ struct Par {
     static constexpr int value = V;
 };
 
-// G = number of n rows per workgroup (1 or 2).  With G = 2 the two rows
-// share every fp32 bias block (the bias does not depend on n), which halves
-// the bias bytes each CU pulls from L2.
 // Waves per SIMD the register budget must allow: four (128 VGPRs) for
 // D <= 64, two for D = 128 (whose O accumulator alone takes 64 VGPRs).
 template <int D>
@@ -230,8 +252,12 @@ constexpr int min_waves_per_simd() {
     return D <= 64 ? 4 : 2;
 }
 
-template <typename T, int D, int KIND, int BIAS, bool EXACT, int G>
-__global__ __launch_bounds__(kThreads* G)
+// An offset past every buffer's range: a DMA with it reads nothing (the
+// buffer range check returns zeros) and only fills a dead LDS buffer.
+constexpr uint32_t kNoTile = 0x80000000u;
+
+template <typename T, int D, int KIND, int BIAS, bool EXACT>
+__global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kernel(Params p) {
     using M = Mma<T>;
     using v8 = typename M::v8;
@@ -239,39 +265,33 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);
     constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK;
     constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
-    constexpr int kT = kThreads * G;
-    static_assert(G == 1 || (G == 2 && !kBlock), "n-sharing needs a tile list shared by both rows");
-    // LDS: two buffers (positions of even and odd parity) each of the G
-    // rows' K tiles and of their V tiles, and the bias blocks (one 32 x 32
-    // block per query group).  With G = 1 each wave owns its bias block and
-    // refills it as soon as it has read it, so one buffer suffices; with
-    // G = 2 two waves read each block and it is double buffered.  Every
-    // buffer is its own object: the compiler then knows that a DMA into one
-    // buffer does not write the others, and does not wait for it before
-    // reading them.
-    constexpr bool kBiasSingle = G == 1;
+    // LDS: a ring of three buffers for K tiles and three for V tiles, and one
+    // 32 x 32 fp32 bias block per wave (each wave refills its block as soon
+    // as it has read it).  Every buffer is its own object, so the compiler
+    // knows that a DMA into one buffer does not write the others and does
+    // not wait for it before reading them.
     constexpr int kBiasBuf = BIAS == kBiasLds ? kWaves * kBiasWaveBytes : 16;
-    __shared__ __attribute__((aligned(1024))) char k_lds0[G * Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char k_lds1[G * Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char v_lds0[G * Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char v_lds1[G * Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char b_lds0[kBiasBuf];
-    __shared__ __attribute__((aligned(1024))) char b_lds1[kBiasSingle ? 16 : kBiasBuf];
+    __shared__ __attribute__((aligned(1024))) char k_lds0[Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char k_lds1[Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char k_lds2[Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds0[Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds1[Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char v_lds2[Ge::tileBytes];
+    __shared__ __attribute__((aligned(1024))) char b_lds[kBiasBuf];
     __shared__ uint32_t listed_bits[kBlock ? kWords : 1];
     __shared__ uint32_t full_bits[kBlock ? kWords : 1];
-    __shared__ float mean_v[G][D];
+    // after the key loop, the first K buffer holds the mean of V
+    float* const mean_v = reinterpret_cast<float*>(k_lds0);
+    static_assert(D * 4 <= Ge::tileBytes, "mean of V fits a K buffer");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
-    const int ng = wave / kWaves;                                 // which of the G rows
-    const int qg = wave % kWaves;                                 // which 32-query group
     const int col = lane & 31;  // this lane's query within the wave
     const int half = lane >> 5;
 
-    // ---- workgroup -> (b, h, n group, q tile), XCD-contiguous order ----------
+    // ---- workgroup -> (b, h, n, q tile), XCD-contiguous order ---------------
     const int64_t n_qt = (p.Q + kQTile - 1) / kQTile;
-    const int64_t n_grp = (p.N + G - 1) / G;
     const int64_t W = gridDim.x;
     const int64_t w = blockIdx.x;
     const int64_t xcd = w % kXcds, slot = w / kXcds;
@@ -279,13 +299,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     const int64_t lid =
         xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
     const int64_t qt = lid % n_qt;
-    const int64_t ngrp = (lid / n_qt) % n_grp;
-    const int64_t h = (lid / (n_qt * n_grp)) % p.H;
-    const int64_t b = lid / (n_qt * n_grp * p.H);
-    const int64_t n0 = ngrp * G;
-    const int64_t n_raw = n0 + ng;
-    const bool n_ok = n_raw < p.N;
-    const int64_t n = n_ok ? n_raw : p.N - 1;  // a missing row reads a valid one, stores nothing
+    const int64_t n = (lid / n_qt) % p.N;
+    const int64_t h = (lid / (n_qt * p.N)) % p.H;
+    const int64_t b = lid / (n_qt * p.N * p.H);
 
     const int K = static_cast<int>(p.K), Q = static_cast<int>(p.Q);
     const int64_t bnh = (b * p.N + n) * p.H + h;
@@ -293,10 +309,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     const T* vbase = static_cast<const T*>(p.v) + bnh * p.K * D;
     const float* bslice = BIAS != kNoBias ? p.bias + (b * p.H + h) * p.Q * p.K : nullptr;
     const int q0 = static_cast<int>(qt) * kQTile;
-    const int q0w = q0 + 32 * qg;
+    const int q0w = q0 + 32 * wave;
     const int qrow = q0w + col;  // this lane's query
-    const bool row_ok = qrow < Q && n_ok;
-    const int qload = qrow < Q ? qrow : Q - 1;
+    const bool row_ok = qrow < Q;
+    const int qload = row_ok ? qrow : Q - 1;
 
     // Scale handling (see the header comment).
     const float zscale = EXACT ? 1.0f : p.scale;        // z = zscale * S
@@ -305,24 +321,19 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     const float inv_s = EXACT ? 1.0f : 1.0f / p.scale;   // bias -> S units
 
     // ---- visited key range / tile list -------------------------------
-    auto clamp_len = [&](int64_t nn) -> int {
-        if (KIND != TRIATTN_MASK_KV_LENGTHS || !p.kv_lengths) return K;
-        const int64_t len = p.kv_lengths[b * p.N + nn];
-        return len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
-    };
-    const int limit = clamp_len(n);  // keys >= limit are never valid for this wave's row
-    const int my_tiles = n_ok ? (limit + kKTile - 1) / kKTile : 0;
-    int wg_tiles = my_tiles;  // tiles any row of the workgroup visits
-    if (G == 2) {
-        const int64_t other = n0 + (1 - ng);
-        const int ot = other < p.N ? (clamp_len(other) + kKTile - 1) / kKTile : 0;
-        wg_tiles = __builtin_amdgcn_readfirstlane(my_tiles > ot ? my_tiles : ot);
+    int limit = K;  // keys >= limit are never valid
+    if (KIND == TRIATTN_MASK_KV_LENGTHS && p.kv_lengths) {
+        const int64_t len = p.kv_lengths[b * p.N + n];
+        limit = len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
     }
+    const int n_tiles = (limit + kKTile - 1) / kKTile;
+    const int n_tiles_all = (K + kKTile - 1) / kKTile;
     int tiles_per_block = 1;
-    if (kBlock) {
+    // (if constexpr keeps the block bitmaps out of the other kinds' LDS)
+    if constexpr (kBlock) {
         tiles_per_block = static_cast<int>(p.kv_block / kKTile);
         const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
-        for (int i = tid; i < words; i += kT) {
+        for (int i = tid; i < words; i += kThreads) {
             listed_bits[i] = 0u;
             full_bits[i] = 0u;
         }
@@ -330,30 +341,33 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         const int64_t inst = b * p.stride_b + n * p.stride_n + h * p.stride_h;
         const int64_t list_row = inst * p.n_q_rows + q0 / p.q_block;
         mark_list(listed_bits, p.kv_num_blocks, p.kv_indices, list_row, p.max_blocks,
-                  p.n_kv_blocks, tid, kT);
+                  p.n_kv_blocks, tid, kThreads);
         if (p.full_kv_num_blocks) {
             mark_list(full_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid, kT);
+                      p.full_max_blocks, p.n_kv_blocks, tid, kThreads);
             mark_list(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid, kT);
+                      p.full_max_blocks, p.n_kv_blocks, tid, kThreads);
         }
         __syncthreads();
     }
-    const int n_tiles_all = (K + kKTile - 1) / kKTile;
     auto first_tile = [&]() -> int {
-        if (!kBlock) return wg_tiles > 0 ? 0 : -1;
-        const int64_t blk = next_set(listed_bits, 0, p.n_kv_blocks);
-        return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
+        if constexpr (!kBlock) {
+            return n_tiles > 0 ? 0 : -1;
+        } else {
+            const int64_t blk = next_set(listed_bits, 0, p.n_kv_blocks);
+            return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
+        }
     };
     auto next_tile = [&](int t) -> int {
         if (t < 0) return -1;
-        if (!kBlock) return t + 1 < wg_tiles ? t + 1 : -1;
-        if ((t + 1) % tiles_per_block != 0 && t + 1 < n_tiles_all) return t + 1;
-        const int64_t blk = next_set(listed_bits, t / tiles_per_block + 1, p.n_kv_blocks);
-        return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
+        if constexpr (!kBlock) {
+            return t + 1 < n_tiles ? t + 1 : -1;
+        } else {
+            if ((t + 1) % tiles_per_block != 0 && t + 1 < n_tiles_all) return t + 1;
+            const int64_t blk = next_set(listed_bits, t / tiles_per_block + 1, p.n_kv_blocks);
+            return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
+        }
     };
-    // does this wave compute tile t (its row has keys there)?
-    auto mine = [&](int t) -> bool { return kBlock ? t >= 0 : (t >= 0 && t < my_tiles); };
 
     // ---- Q^T operand: registers for the whole key loop ----------------
     v8 qop[D / 16];
@@ -372,24 +386,25 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
 
     // ---- LDS regions and DMA address tables ------------------------------
     const uint32_t kv_bytes = static_cast<uint32_t>(p.K * D * sizeof(T));
-    const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kbase, kv_bytes);
-    const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(vbase, kv_bytes);
-    const __amdgpu_buffer_rsrc_t bias_rsrc =
-        make_rsrc(bslice, BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * 4) : 0u);
-    auto kbuf = [&](int x) { return (lds_char*)(x ? k_lds1 : k_lds0) + ng * Ge::tileBytes; };
-    auto vbuf = [&](int x) { return (lds_char*)(x ? v_lds1 : v_lds0) + ng * Ge::tileBytes; };
-    auto bbuf = [&](int x) {
-        return (lds_char*)(x && !kBiasSingle ? b_lds1 : b_lds0) + qg * kBiasWaveBytes;
-    };
+    const uint32_t bias_bytes = BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * 4) : 0u;
+    const u32x4 k_desc = make_desc(kbase, kv_bytes);
+    const u32x4 v_desc = make_desc(vbase, kv_bytes);
+    const u32x4 bias_desc = make_desc(bslice, bias_bytes);
+    const __amdgpu_buffer_rsrc_t bias_rsrc = make_rsrc(bslice, bias_bytes);
+    auto kbuf = [&](int x) { return (lds_char*)(x == 0 ? k_lds0 : x == 1 ? k_lds1 : k_lds2); };
+    auto vbuf = [&](int x) { return (lds_char*)(x == 0 ? v_lds0 : x == 1 ? v_lds1 : v_lds2); };
+    lds_char* const bias_lds = (lds_char*)b_lds + wave * kBiasWaveBytes;  // this wave's block
 
-    // K/V DMA of one tile of this wave's row: instruction I (I < kDma: K,
-    // else V) is issued by query group I % kWaves; lane l of it fills LDS
-    // slot s = 64 (I % kDma) + l of that tile, i.e. row s / chunks, stored
-    // chunk s % chunks, which holds source chunk (s % chunks) ^ f(row).
+    // K/V DMA of one tile: instruction I (I < kDma: K, else V) is issued by
+    // wave I % kWaves; lane l of it fills LDS slot s = 64 (I % kDma) + l of
+    // that tile, i.e. row s / chunks, stored chunk s % chunks, which holds
+    // source chunk (s % chunks) ^ f(row).  Every wave issues its
+    // instructions for every position, with kNoTile when there is no tile,
+    // so the count of DMAs in flight per position is fixed.
     uint32_t kv_src[Ge::dmaPerWave];
 #pragma unroll
     for (int j = 0; j < Ge::dmaPerWave; ++j) {
-        const int I = qg + kWaves * j;
+        const int I = wave + kWaves * j;
         const bool is_v = I >= Ge::kDma;
         const int s = 64 * (I % Ge::kDma) + lane;
         const int r = s / Ge::chunks, c = s % Ge::chunks;
@@ -397,49 +412,47 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
                                           16 * (c ^ (is_v ? Ge::fv(r) : Ge::fk(r))));
     }
     auto dma_k = [&](int t, int x) {
-        const uint32_t toff = static_cast<uint32_t>(t) * Ge::tileBytes;
+        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * Ge::tileBytes : kNoTile;
 #pragma unroll
         for (int j = 0; j < Ge::dmaPerWave; ++j) {
-            const int I = qg + kWaves * j;  // wave-uniform
-            if (I < Ge::kDma) dma16(k_rsrc, kbuf(x) + 1024 * I, kv_src[j] + toff);
+            const int I = wave + kWaves * j;  // wave-uniform
+            if (I < Ge::kDma) dma16(k_desc, kbuf(x) + 1024 * I, kv_src[j] + toff);
         }
     };
     auto dma_v = [&](int t, int x) {
-        const uint32_t toff = static_cast<uint32_t>(t) * Ge::tileBytes;
+        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * Ge::tileBytes : kNoTile;
 #pragma unroll
         for (int j = 0; j < Ge::dmaPerWave; ++j) {
-            const int I = qg + kWaves * j;
-            if (I >= Ge::kDma) dma16(v_rsrc, vbuf(x) + 1024 * (I - Ge::kDma), kv_src[j] + toff);
+            const int I = wave + kWaves * j;
+            if (I >= Ge::kDma) dma16(v_desc, vbuf(x) + 1024 * (I - Ge::kDma), kv_src[j] + toff);
         }
     };
-    // Bias DMA: a query group's block is kBiasDma instructions of 8 rows x
-    // 128 bytes, dealt to the G waves of that group; lane l of instruction
-    // j fills row r = 8j + l/8, stored chunk l%8, holding source chunk
-    // (l%8) ^ fb(r) = (l%8) ^ (l/16) ^ 4(j%2).  Rows past Q read past the
-    // slice and land as zeros; keys past K read the next row (masked).
-    constexpr int kBiasPerWave = kBiasDma / G;
+    // Bias DMA: the wave's block is kBiasDma instructions of 8 rows x 128
+    // bytes; lane l of instruction j fills row r = 8j + l/8, stored chunk
+    // l%8, holding source chunk (l%8) ^ fb(r) = (l%8) ^ (l/16) ^ 4(j%2).
+    // Rows past Q read past the slice and land as zeros; keys past K read
+    // the next row (masked).
     const uint32_t b_row = static_cast<uint32_t>(q0w + (lane >> 3)) * static_cast<uint32_t>(K) * 4u;
     const uint32_t b_src_even = b_row + 16u * static_cast<uint32_t>((lane & 7) ^ (lane >> 4));
     const uint32_t b_src_odd = b_row + 16u * static_cast<uint32_t>((lane & 7) ^ (lane >> 4) ^ 4);
-    auto dma_bias = [&](int t, int x) {
+    auto dma_bias = [&](int t) {
         if (BIAS != kBiasLds) return;
         const uint32_t toff = static_cast<uint32_t>(t) * kBiasRowBytes;
 #pragma unroll
-        for (int i = 0; i < kBiasPerWave; ++i) {
-            const int j = ng * kBiasPerWave + i;
+        for (int j = 0; j < kBiasDma; ++j) {
             const uint32_t rows = static_cast<uint32_t>(8 * j) * static_cast<uint32_t>(K) * 4u;
-            dma16(bias_rsrc, bbuf(x) + 1024 * j, ((j & 1) ? b_src_odd : b_src_even) + rows + toff);
+            dma16(bias_desc, bias_lds + 1024 * j, ((j & 1) ? b_src_odd : b_src_even) + rows + toff);
         }
     };
     // Bias read into the accumulator layout: register 4g+e is key
     // 8g + 4half + e, i.e. source chunk 2g + half of row col.
-    auto read_bias = [&](f32x16& dst, int x) {
+    auto read_bias = [&](f32x16& dst) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int chunk = (2 * g + half) ^ fb(col);
             const f32x4 bv = __builtin_bit_cast(
                 f32x4,
-                *reinterpret_cast<const lds_u32x4*>(bbuf(x) + col * kBiasRowBytes + 16 * chunk));
+                *reinterpret_cast<const lds_u32x4*>(bias_lds + col * kBiasRowBytes + 16 * chunk));
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[4 * g + e] = bv[e];
         }
@@ -447,6 +460,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     // Bias for K % 4 != 0 (rows not 16-byte aligned): plain per-lane loads.
     const uint32_t bias_lane_scalar =
         static_cast<uint32_t>(qload) * static_cast<uint32_t>(K) * 4u + 16u * half;
+
     auto load_bias_scalar = [&](int t, f32x16& dst) {
         const uint32_t base = bias_lane_scalar + static_cast<uint32_t>(t) * kKTile * 4u;
 #pragma unroll
@@ -486,10 +500,11 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     float m_ref = -INFINITY;   // reference max of the exponent, S units
     float l_run = 0.f;         // this lane's half of the running sum
 
-    // S^T = K . Q^T + bias for tile t from K buffer / bias buffer x.
+    // S^T = K . Q^T + bias for tile t from K buffer x and this wave's bias
+    // block.
     auto qk = [&](f32x16& s, int t, int x) {
         s = f32x16{};
-        if (BIAS == kBiasLds) read_bias(s, x);
+        if (BIAS == kBiasLds) read_bias(s);
         if (BIAS == kBiasScalar) load_bias_scalar(t, s);
         if (BIAS != kNoBias && !EXACT) s *= inv_s;
         const lds_char* kt = kbuf(x);
@@ -517,10 +532,12 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
             dense_bits = static_cast<uint32_t>(__ballot(dvalid));
             need_mask = dense_bits != ~0u;
         }
-        if (kBlock && p.mask_mod == TRIATTN_MOD_CAUSAL &&
-            !bit_set(full_bits, t / tiles_per_block) && k0 + kKTile - 1 > q0w) {
-            causal = true;
-            need_mask = true;
+        if constexpr (kBlock) {
+            if (p.mask_mod == TRIATTN_MOD_CAUSAL && !bit_set(full_bits, t / tiles_per_block) &&
+                k0 + kKTile - 1 > q0w) {
+                causal = true;
+                need_mask = true;
+            }
         }
         if (need_mask) {
             constexpr uint64_t kLo = 0x00000000FFFFFFFFull, kHi = 0xFFFFFFFF00000000ull;
@@ -591,77 +608,98 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     };
 
     // ---- key loop ---------------------------------------------------------
-    // Position j of the tile sequence keeps K, V (and, with G = 2, bias) in
-    // buffers j % 2.  At position j the logits of tile cur = t_j are in
-    // registers; the loop first computes the logits of t_{j+1} (K buffer
-    // (j+1) % 2) and then the softmax and P.V of t_j (V buffer j % 2), so the
-    // QK contraction of one tile overlaps the softmax of the previous one.
-    // DMAs run one position ahead: K and bias of t_{j+2}, V of t_{j+1}; a
-    // single bias buffer is refilled right after the logits have read it.
+    // Position j of the tile sequence t_0, t_1, ... keeps K(t_j) and V(t_j)
+    // in ring buffers j % 3.  At position j the logits of cur = t_j are in
+    // registers; the loop computes the logits of nxt = t_{j+1} (K buffer
+    // (j+1) % 3, bias block) and then the softmax and P.V of t_j (V buffer
+    // j % 3), so the QK contraction of one tile overlaps the softmax of the
+    // previous one.  K/V DMAs run two positions ahead (K of t_{j+3}, V of
+    // t_{j+2}); the bias block is refilled with t_{j+2} right after the
+    // logits of t_{j+1} have read it.  Each position first waits for all of
+    // this wave's DMAs but the K/V ones of the previous position.
+    constexpr int kKvInFlight = Ge::dmaPerWave;  // K/V DMAs a wave issues per position
     f32x16 sa, sb;
     int cur = first_tile();
     int nxt = next_tile(cur);
+    int nxt2 = next_tile(nxt);
     bool dv_cur = false, dv_nxt = false;
     if (cur >= 0) {
-        if (mine(cur)) dma_k(cur, 0);
-        dma_bias(cur, 0);
-        if (kDense && mine(cur)) dv_cur = dense_byte(cur);
+        // prologue: K(t0), bias(t0) | K(t1), V(t0) | logits of t0 | bias(t1) |
+        // K(t2), V(t1)
+        dma_k(cur, 0);
+        if (BIAS == kBiasLds) dma_bias(cur);
+        if (kDense) dv_cur = dense_byte(cur);
+        dma_k(nxt, 1);
+        dma_v(cur, 0);
         wait_vmem();
         __syncthreads();
-        if (nxt >= 0) {
-            if (mine(nxt)) dma_k(nxt, 1);
-            if (!kBiasSingle) dma_bias(nxt, 1);
+        qk(sa, cur, 0);
+        if (BIAS == kBiasLds && nxt >= 0) {
+            wait_lds();  // the bias reads are done before the block is refilled
+            dma_bias(nxt);
         }
-        if (mine(cur)) dma_v(cur, 0);
-        if (mine(cur)) qk(sa, cur, 0);
-        if (kBiasSingle && nxt >= 0) {
-            wait_lds();  // the bias reads are done before the region is refilled
-            dma_bias(nxt, 0);
-        }
+        if (kDense && nxt >= 0) dv_nxt = dense_byte(nxt);
+        dma_k(nxt2, 2);
+        dma_v(nxt, 1);
     }
     auto step = [&](auto X, f32x16& s_cur, f32x16& s_nxt) {
-        constexpr int x = decltype(X)::value;
-        const int nxt2 = __builtin_amdgcn_readfirstlane(next_tile(nxt));
-        // K/bias of nxt and V of cur (issued one position ago) have landed for
-        // every wave, and every wave is done with the buffers refilled below.
-        wait_vmem();
+        constexpr int x = decltype(X)::value;  // j % 3
+        const int nxt3 = __builtin_amdgcn_readfirstlane(next_tile(nxt2));
+        // Everything but the last position's K/V DMAs has landed: K(nxt),
+        // V(cur) and the bias block of nxt, for every wave once all have
+        // passed the barrier, which also means every wave is done with the
+        // buffers refilled below.
+        __builtin_amdgcn_s_waitcnt(kVmcntWait<kKvInFlight>());
         __syncthreads();
-        if (nxt2 >= 0) {
-            if (mine(nxt2)) dma_k(nxt2, x);
-            if (!kBiasSingle) dma_bias(nxt2, x);
+        if (nxt >= 0) qk(s_nxt, nxt, (x + 1) % 3);
+        if (BIAS == kBiasLds && nxt2 >= 0) {
+            wait_lds();
+            dma_bias(nxt2);
         }
-        if (mine(nxt)) {
-            dma_v(nxt, x ^ 1);
-            if (kDense) dv_nxt = dense_byte(nxt);
-        }
-        if (mine(nxt)) qk(s_nxt, nxt, x ^ 1);
-        if (kBiasSingle && nxt2 >= 0) {
-            wait_lds();  // the bias reads are done before the region is refilled
-            dma_bias(nxt2, 0);
-        }
-        if (mine(cur)) softmax_pv(s_cur, cur, x, dv_cur);
+        bool dv_nxt2 = false;
+        if (kDense && nxt2 >= 0) dv_nxt2 = dense_byte(nxt2);
+        dma_k(nxt3, x);           // K(t_j) was last read one position ago
+        dma_v(nxt2, (x + 2) % 3);  // V(t_{j-1}) likewise
+        softmax_pv(s_cur, cur, x, dv_cur);
         cur = nxt;
         nxt = nxt2;
+        nxt2 = nxt3;
         dv_cur = dv_nxt;
+        dv_nxt = dv_nxt2;
     };
     while (cur >= 0) {
         step(Par<0>{}, sa, sb);
         if (cur < 0) break;
         step(Par<1>{}, sb, sa);
+        if (cur < 0) break;
+        step(Par<2>{}, sa, sb);
+        if (cur < 0) break;
+        step(Par<0>{}, sb, sa);
+        if (cur < 0) break;
+        step(Par<1>{}, sa, sb);
+        if (cur < 0) break;
+        step(Par<2>{}, sb, sa);
     }
 
     // ---- epilogue ---------------------------------------------------------
     const float l_tot = sum_halves(l_run);
     const bool dead = m_true == -INFINITY;
-    if (__syncthreads_or(dead && row_ok)) {
+    // Does any row of the workgroup lack a valid key?  The flag lives in a K
+    // buffer: after this wave's DMAs have landed and every wave has left the
+    // loop, the ring is free.
+    wait_vmem();
+    __syncthreads();
+    int* const any_dead = reinterpret_cast<int*>(k_lds1);
+    if (tid == 0) *any_dead = 0;
+    __syncthreads();
+    if (__ballot(dead && row_ok) && lane == 0) *any_dead = 1;
+    __syncthreads();
+    if (*any_dead) {
         // Some row saw no valid key: its weights are uniform over all K keys.
-        for (int i = tid; i < G * D; i += kT) {
-            const int g = i / D, d = i % D;
-            const int64_t nn = n0 + g < p.N ? n0 + g : p.N - 1;
-            const T* vb = static_cast<const T*>(p.v) + ((b * p.N + nn) * p.H + h) * p.K * D;
+        for (int d = tid; d < D; d += kThreads) {
             float acc = 0.f;
-            for (int kk = 0; kk < K; ++kk) acc += static_cast<float>(vb[kk * D + d]);
-            mean_v[g][d] = acc / static_cast<float>(K);
+            for (int kk = 0; kk < K; ++kk) acc += static_cast<float>(vbase[kk * D + d]);
+            mean_v[d] = acc / static_cast<float>(K);
         }
         __syncthreads();
     }
@@ -676,7 +714,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
             T o4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                o4[e] = static_cast<T>(dead ? mean_v[ng][d0 + e] : oacc[db][4 * g + e] * inv);
+                o4[e] = static_cast<T>(dead ? mean_v[d0 + e] : oacc[db][4 * g + e] * inv);
             *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, o4);
         }
     if (half == 0) {
@@ -688,28 +726,18 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     }
 }
 
-// n rows per workgroup.  The kernel supports G = 2 (two rows sharing each
-// bias block, half the bias bytes per CU), but rows of unequal length then
-// leave waves idle behind the longer one; on right-padded rows G = 1 is
-// faster, and it is used throughout.
-template <int KIND, int BIAS>
-constexpr int groups_of() {
-    return 1;
-}
-
 template <typename T, int D, int KIND, int BIAS>
 hipError_t launch_bias(const Params& p, bool exact, hipStream_t stream) {
-    constexpr int G = groups_of<KIND, BIAS>();
     const int64_t n_qt = (p.Q + kQTile - 1) / kQTile;
-    const int64_t groups = p.B * ((p.N + G - 1) / G) * p.H * n_qt;
+    const int64_t groups = p.B * p.N * p.H * n_qt;
     if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(groups));
     if (exact)
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, G>), grid, dim3(kThreads * G),
-                           0, stream, p);
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true>), grid, dim3(kThreads), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false, G>), grid,
-                           dim3(kThreads * G), 0, stream, p);
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false>), grid, dim3(kThreads), 0,
+                           stream, p);
     return hipGetLastError();
 }
 
