@@ -81,9 +81,9 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kQTile = 32 * kWaves;  // query rows per workgroup
+// A workgroup has W waves (4 or 8) and owns 32 W query rows; block masks use
+// W = 4 (128-row blocks hold whole workgroups).
+constexpr int kQTileBlock = 128;  // query rows per workgroup with block masks
 constexpr int kKTile = 32;           // keys per K/V tile
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -121,8 +121,7 @@ struct Geo {
     // A stage is 2*tileBytes/1024 DMA instructions (K first, then V), dealt
     // round-robin to the waves.
     static constexpr int kDma = tileBytes / 1024;
-    static constexpr int dmaPerWave = 2 * kDma / kWaves;
-    static_assert(kDma * 1024 == tileBytes && dmaPerWave * kWaves == 2 * kDma, "DMA split");
+    static_assert(kDma * 1024 == tileBytes, "whole DMA instructions per tile");
     // K is read 16 bytes per lane down consecutive rows (8 or 16 lanes per
     // LDS cycle at one chunk): consecutive rows must land on distinct banks.
     static __device__ __forceinline__ int fk(int r) {
@@ -256,12 +255,19 @@ constexpr int min_waves_per_simd() {
 // buffer range check returns zeros) and only fills a dead LDS buffer.
 constexpr uint32_t kNoTile = 0x80000000u;
 
-template <typename T, int D, int KIND, int BIAS, bool EXACT>
-__global__ __launch_bounds__(kThreads)
+template <typename T, int D, int KIND, int BIAS, bool EXACT, int W>
+__global__ __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kernel(Params p) {
     using M = Mma<T>;
     using v8 = typename M::v8;
     using Ge = Geo<D>;
+    constexpr int kWaves = W;
+    constexpr int kThreads = 64 * W;
+    constexpr int kQTile = 32 * W;  // query rows per workgroup
+    // The K and V DMA instructions of a tile are dealt evenly to the waves,
+    // so every wave has the same number in flight.
+    constexpr int kDmaPerWave = 2 * Ge::kDma / W;
+    static_assert(kDmaPerWave * W == 2 * Ge::kDma, "K/V DMAs split evenly over the waves");
     constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);
     constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK;
     constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
@@ -292,10 +298,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
 
     // ---- workgroup -> (b, h, n, q tile), XCD-contiguous order ---------------
     const int64_t n_qt = (p.Q + kQTile - 1) / kQTile;
-    const int64_t W = gridDim.x;
+    const int64_t n_wg = gridDim.x;
     const int64_t w = blockIdx.x;
     const int64_t xcd = w % kXcds, slot = w / kXcds;
-    const int64_t per = W / kXcds, rem = W % kXcds;
+    const int64_t per = n_wg / kXcds, rem = n_wg % kXcds;
     const int64_t lid =
         xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
     const int64_t qt = lid % n_qt;
@@ -401,9 +407,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     // source chunk (s % chunks) ^ f(row).  Every wave issues its
     // instructions for every position, with kNoTile when there is no tile,
     // so the count of DMAs in flight per position is fixed.
-    uint32_t kv_src[Ge::dmaPerWave];
+    uint32_t kv_src[kDmaPerWave];
 #pragma unroll
-    for (int j = 0; j < Ge::dmaPerWave; ++j) {
+    for (int j = 0; j < kDmaPerWave; ++j) {
         const int I = wave + kWaves * j;
         const bool is_v = I >= Ge::kDma;
         const int s = 64 * (I % Ge::kDma) + lane;
@@ -414,7 +420,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     auto dma_k = [&](int t, int x) {
         const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * Ge::tileBytes : kNoTile;
 #pragma unroll
-        for (int j = 0; j < Ge::dmaPerWave; ++j) {
+        for (int j = 0; j < kDmaPerWave; ++j) {
             const int I = wave + kWaves * j;  // wave-uniform
             if (I < Ge::kDma) dma16(k_desc, kbuf(x) + 1024 * I, kv_src[j] + toff);
         }
@@ -422,7 +428,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     auto dma_v = [&](int t, int x) {
         const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * Ge::tileBytes : kNoTile;
 #pragma unroll
-        for (int j = 0; j < Ge::dmaPerWave; ++j) {
+        for (int j = 0; j < kDmaPerWave; ++j) {
             const int I = wave + kWaves * j;
             if (I >= Ge::kDma) dma16(v_desc, vbuf(x) + 1024 * (I - Ge::kDma), kv_src[j] + toff);
         }
@@ -617,7 +623,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     // t_{j+2}); the bias block is refilled with t_{j+2} right after the
     // logits of t_{j+1} have read it.  Each position first waits for all of
     // this wave's DMAs but the K/V ones of the previous position.
-    constexpr int kKvInFlight = Ge::dmaPerWave;  // K/V DMAs a wave issues per position
+    constexpr int kKvInFlight = kDmaPerWave;  // K/V DMAs a wave issues per position
     f32x16 sa, sb;
     int cur = first_tile();
     int nxt = next_tile(cur);
@@ -696,10 +702,34 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     __syncthreads();
     if (*any_dead) {
         // Some row saw no valid key: its weights are uniform over all K keys.
+        // Thread (key phase ph, 16-byte chunk c) sums rows ph, ph + P, ...;
+        // lanes holding the same chunk are then summed by shuffles, and the
+        // per-wave partial sums in LDS.
+        constexpr int kChunks = D / 8;
+        constexpr int kPhases = kThreads / kChunks;
+        const int c = tid % kChunks, ph = tid / kChunks;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int kk = ph; kk < K; kk += kPhases) {
+            const v8 x = __builtin_bit_cast(
+                v8, *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(kk) * D + 8 * c));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += static_cast<float>(x[e]);
+        }
+#pragma unroll
+        for (int off = kChunks; off < 64; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+        float* const part = reinterpret_cast<float*>(k_lds2);  // kWaves x D partial sums
+        static_assert(kWaves * D * 4 <= Ge::tileBytes, "partial sums fit a K buffer");
+        if (lane < kChunks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[wave * D + 8 * lane + e] = acc[e];
+        }
+        __syncthreads();
         for (int d = tid; d < D; d += kThreads) {
-            float acc = 0.f;
-            for (int kk = 0; kk < K; ++kk) acc += static_cast<float>(vbase[kk * D + d]);
-            mean_v[d] = acc / static_cast<float>(K);
+            float sum = 0.f;
+            for (int w2 = 0; w2 < kWaves; ++w2) sum += part[w2 * D + d];
+            mean_v[d] = sum / static_cast<float>(K);
         }
         __syncthreads();
     }
@@ -726,17 +756,27 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     }
 }
 
+// Waves per workgroup.  The kernel also runs with 8 (256 query rows sharing
+// each K/V tile, half the K/V bytes per wave); on the kv_lengths workload at
+// D = 64 that measured no faster than 4, which wastes fewer rows when Q is
+// not a multiple of 256, so 4 is used.
+template <int D, int KIND>
+constexpr int waves_of() {
+    return 4;
+}
+
 template <typename T, int D, int KIND, int BIAS>
 hipError_t launch_bias(const Params& p, bool exact, hipStream_t stream) {
-    const int64_t n_qt = (p.Q + kQTile - 1) / kQTile;
+    constexpr int W = waves_of<D, KIND>();
+    const int64_t n_qt = (p.Q + 32 * W - 1) / (32 * W);
     const int64_t groups = p.B * p.N * p.H * n_qt;
     if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(groups));
     if (exact)
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true>), grid, dim3(kThreads), 0,
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, W>), grid, dim3(64 * W), 0,
                            stream, p);
     else
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false>), grid, dim3(kThreads), 0,
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false, W>), grid, dim3(64 * W), 0,
                            stream, p);
     return hipGetLastError();
 }
@@ -795,13 +835,13 @@ bool mfma_supports(const Params& p, int32_t dtype) {
     if (p.D != 32 && p.D != 64 && p.D != 128) return false;
     if (p.mask_kind == TRIATTN_MASK_BLOCK) {
         // one block row per workgroup, whole tiles per kv block
-        if (p.q_block % kQTile != 0 || p.kv_block % kKTile != 0) return false;
+        if (p.q_block % kQTileBlock != 0 || p.kv_block % kKTile != 0) return false;
     }
     // Byte offsets within one (b, n, h) or (b, h) slice, including the
     // overhang of a ragged last tile and of the last query tile, must fit
     // the 32-bit per-lane offset.
     const int64_t kpad = (p.K + kKTile - 1) / kKTile * kKTile;
-    const int64_t qpad = (p.Q + kQTile - 1) / kQTile * kQTile;
+    const int64_t qpad = (p.Q + 255) / 256 * 256;  // the largest query tile
     const int64_t lim = int64_t(1) << 31;
     if (kpad * p.D * 2 >= lim || qpad * p.D * 2 >= lim || (qpad + 1) * kpad * 4 >= lim)
         return false;
