@@ -504,6 +504,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
     float m_true = -INFINITY;  // exact running max of this row, S units
     float m_ref = -INFINITY;   // reference max of the exponent, S units
+    float m_thr = -INFINITY;   // m_ref + the lazy-rescale margin
+    float m_exp = 0.f;         // m_ref * c_exp (0 while m_ref is -inf)
     float l_run = 0.f;         // this lane's half of the running sum
 
     // S^T = K . Q^T + bias for tile t from K buffer x and this wave's bias
@@ -561,23 +563,30 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         }
 
         // ---- row max; lazily raised reference ------------------------------
-        float mloc = vmax(s[0], s[1]);
-#pragma unroll
-        for (int r = 2; r < 16; r += 2) mloc = vmax(mloc, vmax(s[r], s[r + 1]));
+        // a tree of three-input maxima (8 instructions for 16 values)
+        const float m0 = vmax(vmax(s[0], s[1]), s[2]);
+        const float m1 = vmax(vmax(s[3], s[4]), s[5]);
+        const float m2 = vmax(vmax(s[6], s[7]), s[8]);
+        const float m3 = vmax(vmax(s[9], s[10]), s[11]);
+        const float m4 = vmax(vmax(s[12], s[13]), s[14]);
+        float mloc = vmax(vmax(vmax(m0, m1), m2), vmax(vmax(m3, m4), s[15]));
         mloc = max_halves(mloc);
         m_true = vmax(m_true, mloc);
-        const bool raise = mloc > m_ref + lazy_s;  // false while mloc == -inf
+        const bool raise = mloc > m_thr;  // false while mloc == -inf
         if (__ballot(raise)) {
             // lanes that do not raise keep alpha = 1 exactly (their m_ref may
             // still be -inf); a raising lane with m_ref = -inf gets alpha = 0
-            const float m_new = raise ? mloc : m_ref;
             const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mloc) * c_exp) : 1.0f;
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-            m_ref = m_new;
+            if (raise) {
+                m_ref = mloc;
+                m_thr = mloc + lazy_s;
+                m_exp = mloc * c_exp;
+            }
         }
-        const float mb = (m_ref == -INFINITY ? 0.f : m_ref) * c_exp;
+        const float mb = m_exp;
 
         // ---- probabilities, their fp32 sum, P^T operands (rounded) ---------
         // The sum must use the unrounded p: rounding each p to bf16 moves
