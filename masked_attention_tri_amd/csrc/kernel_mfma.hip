@@ -493,10 +493,36 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         const int chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
         return r * Ge::rowBytes + 16 * (chunk ^ Ge::fv(r)) + 8 * (lane & 1);
     }();
+    // Dense key mask as bits: lane i of dense_word holds bit j = key
+    // 32(64c + i) + j valid, for the chunk c = dense_chunk of 64 tiles.  The
+    // loop reads a tile's word with one readlane, so it issues no memory
+    // operation for the mask; a chunk is rebuilt from the byte mask (32
+    // coalesced byte loads and ballots per 64 tiles) when the key loop
+    // reaches it.  The loads of a rebuild are waited for at once.
     const uint8_t* dense_row = kDense ? p.dense + (b * p.N + n) * p.K : nullptr;
-    auto dense_byte = [&](int t) -> bool {
-        const int key = t * kKTile + (lane & 31);
-        return key < K && dense_row[key] != 0;
+    uint32_t dense_word = 0;
+    int dense_chunk = -1;
+    auto load_dense_chunk = [&](int c) {
+        const int t0 = 64 * c;
+        const int nt = min(64, n_tiles_all - t0);
+        uint32_t w = 0;
+        for (int i0 = 0; i0 < nt; i0 += 16) {
+            bool v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // the 64 lanes cover tiles t0 + i0 + 2j and t0 + i0 + 2j + 1
+                const int key = (t0 + i0 + 2 * j) * kKTile + lane;
+                v[j] = key < K && dense_row[key] != 0;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint64_t bits = __ballot(v[j]);
+                w = lane == i0 + 2 * j ? static_cast<uint32_t>(bits) : w;
+                w = lane == i0 + 2 * j + 1 ? static_cast<uint32_t>(bits >> 32) : w;
+            }
+        }
+        dense_word = w;
+        dense_chunk = c;
     };
 
     f32x16 oacc[D / 32];
@@ -525,7 +551,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     };
 
     // Softmax of tile t (logits in s) and O^T += V^T . P^T from V buffer x.
-    auto softmax_pv = [&](f32x16& s, int t, int x, bool dvalid) {
+    auto softmax_pv = [&](f32x16& s, int t, int x) {
         const int k0 = t * kKTile;
         // ---- element mask (only on tiles that need one) -------------------
         // Register r holds key k0 + 8(r/4) + r%4 in lanes 0-31 and that key
@@ -537,7 +563,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         uint32_t dense_bits = ~0u;
         if (kDense) {
             // bit i = key k0 + i valid (both wave halves hold the same 32 keys)
-            dense_bits = static_cast<uint32_t>(__ballot(dvalid));
+            if ((t >> 6) != dense_chunk) load_dense_chunk(t >> 6);
+            dense_bits = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dense_word), t & 63));
             need_mask = dense_bits != ~0u;
         }
         if constexpr (kBlock) {
@@ -548,15 +575,18 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
             }
         }
         if (need_mask) {
-            constexpr uint64_t kLo = 0x00000000FFFFFFFFull, kHi = 0xFFFFFFFF00000000ull;
+            // bit i of w: key k0 + i passes the length and dense tests
+            const int room = limit - k0;
+            uint32_t w = room >= kKTile ? ~0u : room <= 0 ? 0u : (1u << room) - 1u;
+            if (kDense) w &= dense_bits;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ka = 8 * (r / 4) + (r % 4);  // key offset in lanes 0-31
-                uint64_t lanes = (k0 + ka < limit ? kLo : 0ull) | (k0 + ka + 4 < limit ? kHi : 0ull);
-                if (kDense)
-                    lanes &= (((dense_bits >> ka) & 1u) ? kLo : 0ull) |
-                             (((dense_bits >> (ka + 4)) & 1u) ? kHi : 0ull);
-                bool ok = __builtin_amdgcn_inverse_ballot_w64(lanes);
+                // lanes 0-31 take bit ka, lanes 32-63 bit ka + 4, each spread
+                // over its 32 lanes by sign-extending the one-bit field
+                const uint32_t lo = static_cast<uint32_t>(static_cast<int32_t>(w << (31 - ka)) >> 31);
+                const uint32_t hi = static_cast<uint32_t>(static_cast<int32_t>(w << (27 - ka)) >> 31);
+                bool ok = __builtin_amdgcn_inverse_ballot_w64(lo | (static_cast<uint64_t>(hi) << 32));
                 if (causal) ok = ok && qrow >= k0 + ka + 4 * half;
                 s[r] = ok ? s[r] : -INFINITY;
             }
@@ -637,13 +667,12 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     int cur = first_tile();
     int nxt = next_tile(cur);
     int nxt2 = next_tile(nxt);
-    bool dv_cur = false, dv_nxt = false;
     if (cur >= 0) {
         // prologue: K(t0), bias(t0) | K(t1), V(t0) | logits of t0 | bias(t1) |
         // K(t2), V(t1)
+        if constexpr (kDense) load_dense_chunk(cur >> 6);  // before any DMA is in flight
         dma_k(cur, 0);
         if (BIAS == kBiasLds) dma_bias(cur);
-        if (kDense) dv_cur = dense_byte(cur);
         dma_k(nxt, 1);
         dma_v(cur, 0);
         wait_vmem();
@@ -653,7 +682,6 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
             wait_lds();  // the bias reads are done before the block is refilled
             dma_bias(nxt);
         }
-        if (kDense && nxt >= 0) dv_nxt = dense_byte(nxt);
         dma_k(nxt2, 2);
         dma_v(nxt, 1);
     }
@@ -671,16 +699,12 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
             wait_lds();
             dma_bias(nxt2);
         }
-        bool dv_nxt2 = false;
-        if (kDense && nxt2 >= 0) dv_nxt2 = dense_byte(nxt2);
         dma_k(nxt3, x);           // K(t_j) was last read one position ago
         dma_v(nxt2, (x + 2) % 3);  // V(t_{j-1}) likewise
-        softmax_pv(s_cur, cur, x, dv_cur);
+        softmax_pv(s_cur, cur, x);
         cur = nxt;
         nxt = nxt2;
         nxt2 = nxt3;
-        dv_cur = dv_nxt;
-        dv_nxt = dv_nxt2;
     };
     while (cur >= 0) {
         step(Par<0>{}, sa, sb);

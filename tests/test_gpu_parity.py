@@ -101,6 +101,9 @@ MFMA_CASES = [
     (1, 2, 2, 70, 33, 32, "bf16", "kv_lengths", {"len_range": (-3, 0)}),
     (1, 3, 2, 150, 130, 64, "bf16", "dense", {"p_valid": 0.02}),
     (1, 2, 2, 128, 131, 64, "bf16", "none", {}),  # K % 4 != 0: scalar bias loads
+    # dense masks past 64 key tiles: the mask bits are rebuilt per 64 tiles
+    (1, 1, 2, 64, 4200, 64, "bf16", "dense", {}),
+    (1, 2, 1, 96, 2090, 32, "bf16", "dense", {"p_valid": 0.9}),
 ]
 
 GENERIC_CASES = [
