@@ -534,24 +534,41 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     float m_exp = 0.f;         // m_ref * c_exp (0 while m_ref is -inf)
     float l_run = 0.f;         // this lane's half of the running sum
 
+    // At D = 64 the QK MFMAs of one tile are interleaved with the
+    // exponentials of the previous one (softmax_pv below); at D = 32 and 128
+    // that measured slower than issuing them as one group.  The per-lane
+    // bias loads keep the grouped order: interleaved, their registers spill.
+    constexpr bool kInterleave = D == 64 && BIAS != kBiasScalar;
+
     // S^T = K . Q^T + bias for tile t from K buffer x and this wave's bias
-    // block.
-    auto qk = [&](f32x16& s, int t, int x) {
+    // block.  qk_load reads the bias into s and the K operands into kop;
+    // the key loop issues the MFMAs later, between the exponentials of the
+    // previous tile (qk does both at once, for the first tile).
+    v8 kop[D / 16];
+    auto qk_load = [&](f32x16& s, int t, int x) {
         s = f32x16{};
         if (BIAS == kBiasLds) read_bias(s);
         if (BIAS == kBiasScalar) load_bias_scalar(t, s);
         if (BIAS != kNoBias && !EXACT) s *= inv_s;
         const lds_char* kt = kbuf(x);
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const v8 a =
-                __builtin_bit_cast(v8, *reinterpret_cast<const lds_u32x4*>(kt + (k_base ^ (32 * st))));
-            s = M::run(a, qop[st], s);
-        }
+        for (int st = 0; st < D / 16; ++st)
+            kop[st] = __builtin_bit_cast(v8, *reinterpret_cast<const lds_u32x4*>(kt + (k_base ^ (32 * st))));
+    };
+    auto qk = [&](f32x16& s, int t, int x) {
+        qk_load(s, t, x);
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) s = M::run(kop[st], qop[st], s);
     };
 
     // Softmax of tile t (logits in s) and O^T += V^T . P^T from V buffer x.
-    auto softmax_pv = [&](f32x16& s, int t, int x) {
+    // Between the row max and the exponentials it calls dma() (this
+    // position's DMAs, issued once the bias reads have long returned).  With
+    // kInterleave the MFMAs of the next tile's logits (operands already in
+    // kop and s_nxt) are interleaved with the exponentials, one MFMA per few
+    // vector instructions, so that the matrix core runs them while the wave
+    // keeps issuing the softmax instead of stalling on their dependent chain.
+    auto softmax_pv = [&](f32x16& s, int t, int x, f32x16& s_nxt, auto dma) {
         const int k0 = t * kKTile;
         // ---- element mask (only on tiles that need one) -------------------
         // Register r holds key k0 + 8(r/4) + r%4 in lanes 0-31 and that key
@@ -617,6 +634,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
             }
         }
         const float mb = m_exp;
+        dma();
 
         // ---- probabilities, their fp32 sum, P^T operands (rounded) ---------
         // The sum must use the unrounded p: rounding each p to bf16 moves
@@ -634,6 +652,17 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
                 pop[tt][j + 1] = static_cast<T>(p1);
             }
         l_run += psum;
+        // ---- S^T of the next tile, interleaved with the code above ----------
+        if constexpr (kInterleave) {
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) s_nxt = M::run(kop[st], qop[st], s_nxt);
+            // scheduling pattern: (1 MFMA, 7 VALU) per k-step
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+            }
+        }
 
         // ---- O^T += V^T . P^T ----------------------------------------------
         const lds_char* vt = vbuf(x);
@@ -656,9 +685,15 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     // Position j of the tile sequence t_0, t_1, ... keeps K(t_j) and V(t_j)
     // in ring buffers j % 3.  At position j the logits of cur = t_j are in
     // registers; the loop computes the logits of nxt = t_{j+1} (K buffer
-    // (j+1) % 3, bias block) and then the softmax and P.V of t_j (V buffer
-    // j % 3), so the QK contraction of one tile overlaps the softmax of the
-    // previous one.  K/V DMAs run two positions ahead (K of t_{j+3}, V of
+    // (j+1) % 3, bias block) and the softmax and P.V of t_j (V buffer j % 3),
+    // so the QK contraction of one tile overlaps the softmax of the previous
+    // one.  With kInterleave it reads the operands of the logits of t_{j+1},
+    // takes the row max of t_j, issues the DMAs and then runs the
+    // exponentials of t_j with the QK MFMAs of t_{j+1} between them; when
+    // there is no t_{j+1} those reads and MFMAs still run, on stale buffers
+    // that no DMA is writing, and their result is never used: that keeps the
+    // exponentials and the MFMAs in one scheduling region.  Otherwise the
+    // QK MFMAs go first and the DMAs follow them.  K/V DMAs run two positions ahead (K of t_{j+3}, V of
     // t_{j+2}); the bias block is refilled with t_{j+2} right after the
     // logits of t_{j+1} have read it.  Each position first waits for all of
     // this wave's DMAs but the K/V ones of the previous position.
@@ -694,14 +729,22 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         // buffers refilled below.
         __builtin_amdgcn_s_waitcnt(kVmcntWait<kKvInFlight>());
         __syncthreads();
-        if (nxt >= 0) qk(s_nxt, nxt, (x + 1) % 3);
-        if (BIAS == kBiasLds && nxt2 >= 0) {
-            wait_lds();
-            dma_bias(nxt2);
+        auto dma = [&]() {  // this position's DMAs
+            if (BIAS == kBiasLds && nxt2 >= 0) {
+                wait_lds();
+                dma_bias(nxt2);
+            }
+            dma_k(nxt3, x);           // K(t_j) was last read one position ago
+            dma_v(nxt2, (x + 2) % 3);  // V(t_{j-1}) likewise
+        };
+        if constexpr (kInterleave) {
+            qk_load(s_nxt, nxt, (x + 1) % 3);
+            softmax_pv(s_cur, cur, x, s_nxt, dma);
+        } else {
+            if (nxt >= 0) qk(s_nxt, nxt, (x + 1) % 3);
+            dma();
+            softmax_pv(s_cur, cur, x, s_nxt, [] {});
         }
-        dma_k(nxt3, x);           // K(t_j) was last read one position ago
-        dma_v(nxt2, (x + 2) % 3);  // V(t_{j-1}) likewise
-        softmax_pv(s_cur, cur, x);
         cur = nxt;
         nxt = nxt2;
         nxt2 = nxt3;
