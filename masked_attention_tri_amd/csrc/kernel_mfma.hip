@@ -62,7 +62,8 @@
 // Grid: one workgroup per (b, n, h, query tile), remapped so that each of the
 // 8 XCDs walks a contiguous range of (b, h, n, q-tile) order: the q-tiles of
 // one (n, h) share K/V in that XCD's L2 and a head's fp32 bias (shared by
-// every n) stays resident there.
+// every n) stays resident there.  Within one (b, n, h) the q-tiles alternate
+// between the two ends, which balances causal block masks across CUs.
 #include <math.h>
 
 #include "triattn_internal.h"
@@ -304,7 +305,16 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     const int64_t per = n_wg / kXcds, rem = n_wg % kXcds;
     const int64_t lid =
         xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-    const int64_t qt = lid % n_qt;
+    // Query tiles of one (b, n, h) are taken in the order 0, T-1, 1, T-2, ...
+    // and every other (b, n, h) in the reverse of that.  Work per tile is the
+    // same for dense masks and lengths, but with a causal block mask tile i
+    // visits i + 1 blocks; when the whole grid is resident at once (512
+    // workgroups at two per CU), this puts heavy and light tiles side by side
+    // on a CU, whichever way the dispatcher fills its slots (consecutive
+    // workgroups, or workgroups one round apart).
+    const int64_t qr = lid % n_qt;
+    const int64_t qt0 = (qr & 1) ? n_qt - 1 - qr / 2 : qr / 2;
+    const int64_t qt = ((lid / n_qt) & 1) ? n_qt - 1 - qt0 : qt0;
     const int64_t n = (lid / n_qt) % p.N;
     const int64_t h = (lid / (n_qt * p.N)) % p.H;
     const int64_t b = lid / (n_qt * p.N * p.H);
