@@ -143,9 +143,14 @@ typedef struct tri_attn_mask {
  * `scale`: s in the equation; NaN selects the page's default 1/sqrt(D)
  * (computed in double, then rounded to float).  `mask` NULL means no mask.
  *
- * Returns TRIATTN_ERR_INVALID_ARG for: a NULL shape / q / k / v / out; a
- * negative size, K < 1 or D < 1; an unknown dtype or mask kind; a misaligned
- * pointer; a mask kind whose required arrays are NULL; only one of the
+ * When B, N, H or Q is 0 there is no query row: the call does nothing and
+ * returns TRIATTN_OK, and q, k, v, out and the mask's arrays may be NULL (an
+ * empty tensor's address); every other rule below still applies.
+ *
+ * Returns TRIATTN_ERR_INVALID_ARG for: a NULL shape; a NULL q / k / v / out
+ * when there is a query row; a negative size, K < 1 or D < 1; an unknown
+ * dtype or mask kind; a misaligned pointer; a mask kind whose required
+ * arrays are NULL when there is a query row; only one of the
  * full_kv pair (the BlockMask constructor rejects that too); q_block,
  * kv_block or max_blocks below 1; an unknown mask_mod; a negative stride;
  * an infinite scale.  TRIATTN_ERR_UNSUPPORTED for (dtype, D) outside the

@@ -27,10 +27,14 @@ triattn_status check_impl(const tri_attn_shape* shape, int32_t dtype, const void
                           const void* k, const void* v, const float* bias,
                           const tri_attn_mask* mask, float scale, const void* out,
                           const float* lse, const float* mx) {
-    if (!shape || !q || !k || !v || !out) return TRIATTN_ERR_INVALID_ARG;
+    if (!shape) return TRIATTN_ERR_INVALID_ARG;
     const int64_t B = shape->B, N = shape->N, H = shape->H, Q = shape->Q, K = shape->K,
                   D = shape->D;
     if (B < 0 || N < 0 || H < 0 || Q < 0 || K < 1 || D < 1) return TRIATTN_ERR_INVALID_ARG;
+    // With no query row there is nothing to read or write: arrays with no
+    // elements may then be NULL (what an empty tensor hands over).
+    const bool empty = B == 0 || N == 0 || H == 0 || Q == 0;
+    if (!empty && (!q || !k || !v || !out)) return TRIATTN_ERR_INVALID_ARG;
     if (dtype != TRIATTN_F32 && dtype != TRIATTN_F16 && dtype != TRIATTN_BF16)
         return TRIATTN_ERR_INVALID_ARG;
     if (isinf(scale)) return TRIATTN_ERR_INVALID_ARG;
@@ -44,13 +48,14 @@ triattn_status check_impl(const tri_attn_shape* shape, int32_t dtype, const void
             break;
         case TRIATTN_MASK_DENSE:
             // a dense mask and kv_lengths are mutually exclusive
-            if (!mask->dense || mask->kv_lengths) return TRIATTN_ERR_INVALID_ARG;
+            if ((!mask->dense && !empty) || mask->kv_lengths) return TRIATTN_ERR_INVALID_ARG;
             break;
         case TRIATTN_MASK_KV_LENGTHS:
-            if (!mask->kv_lengths || mask->dense) return TRIATTN_ERR_INVALID_ARG;
+            if ((!mask->kv_lengths && !empty) || mask->dense) return TRIATTN_ERR_INVALID_ARG;
             break;
         case TRIATTN_MASK_BLOCK:
-            if (!mask->kv_num_blocks || !mask->kv_indices) return TRIATTN_ERR_INVALID_ARG;
+            if (!empty && (!mask->kv_num_blocks || !mask->kv_indices))
+                return TRIATTN_ERR_INVALID_ARG;
             if (mask->dense || mask->kv_lengths) return TRIATTN_ERR_INVALID_ARG;
             if ((mask->full_kv_num_blocks == nullptr) != (mask->full_kv_indices == nullptr))
                 return TRIATTN_ERR_INVALID_ARG;

@@ -85,6 +85,34 @@ def test_check_accepts_valid_arguments():
     assert check(mask=d) == nat.TRIATTN_OK
 
 
+def test_check_empty_work_accepts_null_arrays():
+    """No query row (B, N, H or Q is 0): the arrays an empty tensor hands over
+    may be NULL; the other rules still apply."""
+    none = dict(q=0, k=0, v=0, out=0, bias=0, lse=0, mx=0)
+    for shp in (shape(N=0), shape(Q=0), shape(B=0), shape(H=0)):
+        assert check(shp, **none) == nat.TRIATTN_OK
+        for kind, field in ((nat.TRIATTN_MASK_DENSE, "dense"),
+                            (nat.TRIATTN_MASK_KV_LENGTHS, "kv_lengths")):
+            d = nat.TriAttnMask()
+            d.kind = kind
+            assert check(shp, mask=d, **none) == nat.TRIATTN_OK, field
+        d = nat.TriAttnMask()
+        d.kind = nat.TRIATTN_MASK_BLOCK
+        d.q_block = d.kv_block = 128
+        d.max_blocks = 4
+        assert check(shp, mask=d, **none) == nat.TRIATTN_OK
+        # still rejected: sizes, dtype, scale, both mask sources at once
+        assert check(shape(N=0, K=0), **none) == nat.TRIATTN_ERR_INVALID_ARG
+        assert check(shp, dtype=9, **none) == nat.TRIATTN_ERR_INVALID_ARG
+        assert check(shp, scale=math.inf, **none) == nat.TRIATTN_ERR_INVALID_ARG
+        d = nat.TriAttnMask()
+        d.kind = nat.TRIATTN_MASK_DENSE
+        d.kv_lengths = A
+        assert check(shp, mask=d, **none) == nat.TRIATTN_ERR_INVALID_ARG
+    # with a query row the NULL arrays are errors again
+    assert check(q=0) == nat.TRIATTN_ERR_INVALID_ARG
+
+
 @pytest.mark.parametrize("kw", [
     dict(q=0), dict(k=0), dict(v=0), dict(out=0),
     dict(q=A + 8), dict(out=A + 2), dict(bias=A + 2), dict(lse=A + 1), dict(mx=A + 3),

@@ -153,3 +153,25 @@ def test_blockmask_with_callable_causal_and_tuple_block_size():
     ref = torch.nn.functional.scaled_dot_product_attention(
         c.q.float(), c.k.float(), c.v.float(), is_causal=True)
     assert (out.cpu().float() - ref).abs().max() < 2e-2
+
+
+@pytest.mark.parametrize("B,N,H,Q,K,D,dt", [(1, 0, 2, 16, 8, 64, "bf16"), (1, 2, 2, 0, 8, 64, "f16"),
+                                            (0, 2, 2, 16, 8, 32, "f32"), (1, 2, 0, 16, 8, 32, "bf16")])
+def test_empty_work_returns_empty_outputs(B, N, H, Q, K, D, dt):
+    """No query row: every mask kind returns outputs of the right (empty)
+    shape and launches nothing; empty tensors hand over NULL addresses."""
+    say(f"empty work B{B} N{N} H{H} Q{Q} K{K} D{D} {dt}")
+    dtype = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
+    q = torch.randn(B, N, H, Q, D, device="cuda").to(dtype)
+    k = torch.randn(B, N, H, K, D, device="cuda").to(dtype)
+    v = torch.randn(B, N, H, K, D, device="cuda").to(dtype)
+    bias = torch.randn(B, 1, H, Q, K, device="cuda")
+    lens = torch.full((B, N, 1, 1, 1), 3, device="cuda", dtype=torch.int32)
+    mask = torch.ones(B, N, 1, 1, K, device="cuda", dtype=torch.bool)
+    for kw in ({}, {"kv_lengths": lens}, {"mask": mask}):
+        out, lse, mx = mat.triangle_attention(q, k, v, bias, return_aux=True, **kw)
+        torch.cuda.synchronize()
+        assert out.shape == q.shape and out.dtype == dtype
+        assert lse.shape == (B, N, H, Q, 1) and mx.shape == (B, N, H, Q, 1)
+    lens2 = mat.mask_to_kv_lengths(mask)
+    assert lens2.shape == (B, N, 1, 1, 1)

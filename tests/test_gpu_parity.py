@@ -95,6 +95,9 @@ MFMA_CASES = [
     (1, 2, 2, 256, 256, 32, "f16", "block", {"q_block": 128, "kv_block": 128}),
     (1, 2, 3, 384, 250, 64, "bf16", "block", {"q_block": 256, "kv_block": 64,
                                                "mask_mod": "causal", "block_broadcast": True}),
+    # an odd number of query tiles per row (the tile order alternates ends)
+    (2, 3, 2, 640, 640, 64, "bf16", "block", {"q_block": 128, "kv_block": 128,
+                                               "mask_mod": "causal"}),
     (2, 2, 2, 100, 100, 64, "bf16", "none", {"bias": False, "scale": 0.3}),
     (1, 4, 2, 64, 1, 64, "bf16", "none", {}),
     (1, 2, 2, 1, 100, 128, "f16", "kv_lengths", {}),
