@@ -24,9 +24,11 @@
  *   lse, max (B, N, H, Q)     fp32; each may be NULL (not written)
  * q, k, v and out must be 16-byte aligned; bias, lse and max 4-byte aligned.
  *
- * Supported envelope (the triangle_attention page, Notes item 3):
+ * Supported envelope (the triangle_attention page, Notes item 3: its
+ * standard kernels' fp32 bound, and for the half types the wider forward
+ * bound it gives its newest kernels):
  *   TRIATTN_F32:            D <= 32 and D % 4 == 0
- *   TRIATTN_F16 / BF16:     D <= 128 and D % 8 == 0
+ *   TRIATTN_F16 / BF16:     D <= 256 and D % 8 == 0
  * Anything else returns TRIATTN_ERR_UNSUPPORTED; the library has no slower
  * fallback implementation.
  *

@@ -1,8 +1,10 @@
 // Generic forward kernel: one wavefront per query row, fp32 arithmetic.
 //
 // Serves every (dtype, D) in the envelope of the triangle_attention page
-// (Notes item 3) and every mask form; it is the path for fp32 inputs and
-// for shapes the MFMA kernel is not instantiated for.  Lanes split the keys
+// (Notes item 3: D <= 32 for fp32, D <= 256 for the half types, the wider
+// bound being the one that page gives its newest forward kernels) and every
+// mask form; it is the path for fp32 inputs and for shapes the MFMA kernel
+// is not instantiated for.  Lanes split the keys
 // for the logits and the d coordinates for P.V; the softmax runs online over
 // chunks of 64 keys with a running max and sum (the max-shifted evaluation of
 // the page's softmax), so a row of any length needs O(D) state.
@@ -49,7 +51,8 @@ __device__ void mark_list(uint32_t* bits, const int32_t* counts, const int32_t* 
     }
 }
 
-template <typename T>
+// kOut output coordinates per lane: 2 covers D <= 128, 4 covers D <= 256.
+template <typename T, int kOut>
 __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
     __shared__ uint32_t listed_bits[kWaves][kWords];
     __shared__ uint32_t full_bits[kWaves][kWords];
@@ -106,8 +109,14 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
 
     float m = -INFINITY;  // running max of the valid logits
     float l = 0.f;        // running sum of exp(z - m)
-    float o0 = 0.f, o1 = 0.f;  // O[lane], O[lane + 64]
-    const bool has0 = lane < D, has1 = lane + 64 < D;
+    // O[lane + 64 i], i < kOut: up to 256 coordinates
+    float o[kOut];
+    bool has[kOut];
+#pragma unroll
+    for (int i = 0; i < kOut; ++i) {
+        o[i] = 0.f;
+        has[i] = lane + 64 * i < D;
+    }
 
     for (int64_t c0 = 0; c0 < limit; c0 += 64) {
         const int64_t kk = c0 + lane;
@@ -133,15 +142,16 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
         const float alpha = expf(m - m_use);
         const float pz = valid ? expf(z - m_use) : 0.f;
         l = l * alpha + wave_sum(pz);
-        o0 *= alpha;
-        o1 *= alpha;
+#pragma unroll
+        for (int i = 0; i < kOut; ++i) o[i] *= alpha;
         const int64_t jmax = (limit - c0) < 64 ? (limit - c0) : 64;
         for (int j = 0; j < jmax; ++j) {
             const float pj = __shfl(pz, j);
             if (pj == 0.f) continue;  // uniform: pj is the same in every lane
             const T* vrow = vbase + (c0 + j) * D;
-            if (has0) o0 = fmaf(pj, to_f32(vrow[lane]), o0);
-            if (has1) o1 = fmaf(pj, to_f32(vrow[lane + 64]), o1);
+#pragma unroll
+            for (int i = 0; i < kOut; ++i)
+                if (has[i]) o[i] = fmaf(pj, to_f32(vrow[lane + 64 * i]), o[i]);
         }
         m = m_new;
     }
@@ -150,27 +160,30 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
     if (m == -INFINITY) {
         // No valid key: every logit is the -1e9 replacement, so the softmax
         // is uniform over all K keys.
-        o0 = o1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < kOut; ++i) o[i] = 0.f;
         for (int64_t kk = 0; kk < K; ++kk) {
             const T* vrow = vbase + kk * D;
-            if (has0) o0 += to_f32(vrow[lane]);
-            if (has1) o1 += to_f32(vrow[lane + 64]);
+#pragma unroll
+            for (int i = 0; i < kOut; ++i)
+                if (has[i]) o[i] += to_f32(vrow[lane + 64 * i]);
         }
         const float inv = 1.0f / static_cast<float>(K);
-        o0 *= inv;
-        o1 *= inv;
+#pragma unroll
+        for (int i = 0; i < kOut; ++i) o[i] *= inv;
         mx = kMaskedLogit;
         lse = kMaskedLogit + logf(static_cast<float>(K));
     } else {
         const float inv = 1.0f / l;
-        o0 *= inv;
-        o1 *= inv;
+#pragma unroll
+        for (int i = 0; i < kOut; ++i) o[i] *= inv;
         mx = m;
         lse = m + logf(l);
     }
     T* orow = static_cast<T*>(p.out) + r * D;
-    if (has0) orow[lane] = static_cast<T>(o0);
-    if (has1) orow[lane + 64] = static_cast<T>(o1);
+#pragma unroll
+    for (int i = 0; i < kOut; ++i)
+        if (has[i]) orow[lane + 64 * i] = static_cast<T>(o[i]);
     if (lane == 0) {
         if (p.lse) p.lse[r] = lse;
         if (p.mx) p.mx[r] = mx;
@@ -184,15 +197,22 @@ hipError_t launch_generic(const Params& p, int32_t dtype, hipStream_t stream) {
     const int64_t blocks = (rows + kWaves - 1) / kWaves;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kWaves);
+    const bool wide = p.D > 128;
     switch (dtype) {
     case TRIATTN_F32:
-        hipLaunchKernelGGL(generic_fwd_kernel<float>, grid, block, 0, stream, p);
+        hipLaunchKernelGGL((generic_fwd_kernel<float, 2>), grid, block, 0, stream, p);
         break;
     case TRIATTN_F16:
-        hipLaunchKernelGGL(generic_fwd_kernel<_Float16>, grid, block, 0, stream, p);
+        if (wide)
+            hipLaunchKernelGGL((generic_fwd_kernel<_Float16, 4>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((generic_fwd_kernel<_Float16, 2>), grid, block, 0, stream, p);
         break;
     case TRIATTN_BF16:
-        hipLaunchKernelGGL(generic_fwd_kernel<__bf16>, grid, block, 0, stream, p);
+        if (wide)
+            hipLaunchKernelGGL((generic_fwd_kernel<__bf16, 4>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((generic_fwd_kernel<__bf16, 2>), grid, block, 0, stream, p);
         break;
     default:
         return hipErrorInvalidValue;

@@ -84,7 +84,7 @@ triattn_status check_impl(const tri_attn_shape* shape, int32_t dtype, const void
     if (dtype == TRIATTN_F32) {
         if (D > 32 || D % 4 != 0) return TRIATTN_ERR_UNSUPPORTED;
     } else {
-        if (D > 128 || D % 8 != 0) return TRIATTN_ERR_UNSUPPORTED;
+        if (D > 256 || D % 8 != 0) return TRIATTN_ERR_UNSUPPORTED;
     }
 
     // Index range: element counts must fit comfortably in int64, and the

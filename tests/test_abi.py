@@ -132,11 +132,19 @@ def test_check_rejects_shape_null():
 
 @pytest.mark.parametrize("dtype,D", [
     (nat.TRIATTN_F32, 36), (nat.TRIATTN_F32, 30), (nat.TRIATTN_F32, 64),
-    (nat.TRIATTN_BF16, 136), (nat.TRIATTN_F16, 60), (nat.TRIATTN_BF16, 4),
+    (nat.TRIATTN_BF16, 264), (nat.TRIATTN_F16, 60), (nat.TRIATTN_BF16, 4),
+    (nat.TRIATTN_F16, 260),
 ])
 def test_check_envelope(dtype, D):
-    # triangle_attention page, Notes item 3: fp32 D<=32, D%4==0; half D<=128, D%8==0
+    # triangle_attention page, Notes item 3: fp32 D<=32, D%4==0; half types
+    # D<=256 (the page's forward bound for its newest kernels), D%8==0
     assert check(shape(D=D), dtype=dtype) == nat.TRIATTN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype,D", [(nat.TRIATTN_BF16, 136), (nat.TRIATTN_F16, 256),
+                                     (nat.TRIATTN_BF16, 8), (nat.TRIATTN_F32, 32)])
+def test_check_envelope_accepts(dtype, D):
+    assert check(shape(D=D), dtype=dtype) == nat.TRIATTN_OK
 
 
 def test_check_mask_descriptors():

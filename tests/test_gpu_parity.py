@@ -120,6 +120,11 @@ GENERIC_CASES = [
     (1, 2, 2, 40, 40, 32, "f32", "kv_lengths", {"len_range": (-2, 45)}),
     (1, 1, 2, 30, 30, 4, "f32", "block", {"q_block": 8, "kv_block": 4, "mask_mod": "causal"}),
     (1, 2, 2, 9, 1, 32, "f32", "none", {}),
+    # head dimensions past 128 (half types, up to 256)
+    (1, 2, 2, 70, 90, 256, "bf16", "kv_lengths", {}),
+    (1, 2, 2, 40, 33, 192, "f16", "dense", {}),
+    (1, 2, 2, 30, 50, 256, "bf16", "dense", {"p_valid": 0.02}),
+    (1, 1, 2, 64, 64, 136, "bf16", "block", {"q_block": 32, "kv_block": 16, "mask_mod": "causal"}),
 ]
 
 
