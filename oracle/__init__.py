@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the masked, biased triangle-attention forward.
+"""fp64 CPU oracle for the masked, biased triangle-attention forward and its
+gradient.
 
 TEST INFRASTRUCTURE ONLY: the checker that the GPU library is compared
 against.  Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline
@@ -14,7 +15,9 @@ from .oracle import (  # noqa: F401
     MOD_NONE,
     OracleBlockMask,
     build,
+    build_bwd,
     default_threads,
     load_library,
+    oracle_bwd,
     oracle_fwd,
 )

@@ -31,7 +31,10 @@ MOD_CAUSAL = 1
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "triattn_oracle.c")
 _LIB = os.path.join(_HERE, "libtriattn_oracle.so")
+_SRC_BWD = os.path.join(_HERE, "triattn_oracle_bwd.c")
+_LIB_BWD = os.path.join(_HERE, "libtriattn_oracle_bwd.so")
 _lib = None
+_lib_bwd = None
 
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
@@ -65,6 +68,32 @@ def _load():
         build()
     _lib = load_library(_LIB)
     return _lib
+
+
+def build_bwd(src: str = _SRC_BWD, out: str = _LIB_BWD) -> str:
+    """Compile the backward oracle (its own library)."""
+    return build(src, out)
+
+
+def load_library_bwd(path: str):
+    lib = ctypes.CDLL(path)
+    i64, ptr, c_int, dbl = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    lib.tri_oracle_bwd.restype = c_int
+    lib.tri_oracle_bwd.argtypes = (
+        [i64] * 6 + [ptr] * 4 + [c_int] + [ptr] * 6 + [i64] * 4 + [c_int] + [i64] * 3
+        + [dbl] + [ptr] * 5 + [c_int]
+    )
+    return lib
+
+
+def _load_bwd():
+    global _lib_bwd
+    if _lib_bwd is not None:
+        return _lib_bwd
+    if not os.path.exists(_LIB_BWD) or os.path.getmtime(_LIB_BWD) < os.path.getmtime(_SRC_BWD):
+        build_bwd()
+    _lib_bwd = load_library_bwd(_LIB_BWD)
+    return _lib_bwd
 
 
 def default_threads() -> int:
@@ -109,30 +138,8 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def oracle_fwd(q, k, v, bias=None, *, mask=None, kv_lengths=None,
-               block: Optional[OracleBlockMask] = None, scale: Optional[float] = None,
-               rows=None, threads: int = 0, lib=None):
-    """Return (O, lse, max) in fp64.
-
-    q: (B,N,H,Q,D); k, v: (B,N,H,K,D); bias: (B,1,H,Q,K) or None;
-    mask: (B,N,K) or (B,N,1,1,K), nonzero = valid; kv_lengths: (B,N) or
-    (B,N,1,1,1); block: OracleBlockMask.  At most one mask form may be given.
-    rows: optional flat (b,n,h,q) row indices; then O is (len(rows), D) and
-    lse/max are (len(rows),), else O is (B,N,H,Q,D) and lse/max (B,N,H,Q).
-    ``lib`` selects another compiled copy of the oracle (used to check that
-    the pins reject deliberately broken copies).
-    """
-    lib = lib or _load()
-    qn, kn, vn = _np(q, np.float64), _np(k, np.float64), _np(v, np.float64)
-    if qn.ndim != 5 or kn.ndim != 5 or vn.ndim != 5:
-        raise ValueError("q, k, v must be 5-D (B,N,H,Q|K,D)")
-    B, N, H, Q, D = qn.shape
-    K = kn.shape[3]
-    if kn.shape != (B, N, H, K, D) or vn.shape != kn.shape:
-        raise ValueError("k/v shape mismatch")
-    bn = _np(bias, np.float64)
-    if bn is not None and bn.shape != (B, 1, H, Q, K):
-        raise ValueError(f"bias must be (B,1,H,Q,K), got {bn.shape}")
+def _mask_args(B, N, K, mask, kv_lengths, block):
+    """Mask kind and the C arguments of one of the three mask forms."""
     given = sum(x is not None for x in (mask, kv_lengths, block))
     if given > 1:
         raise ValueError("pass at most one of mask, kv_lengths, block")
@@ -163,6 +170,35 @@ def oracle_fwd(q, k, v, bias=None, *, mask=None, kv_lengths=None,
                     int(block.mask_mod), int(block.stride_b), int(block.stride_n),
                     int(block.stride_h)]
 
+    return kind, dense, lens, blk_args, keep
+
+
+def oracle_fwd(q, k, v, bias=None, *, mask=None, kv_lengths=None,
+               block: Optional[OracleBlockMask] = None, scale: Optional[float] = None,
+               rows=None, threads: int = 0, lib=None):
+    """Return (O, lse, max) in fp64.
+
+    q: (B,N,H,Q,D); k, v: (B,N,H,K,D); bias: (B,1,H,Q,K) or None;
+    mask: (B,N,K) or (B,N,1,1,K), nonzero = valid; kv_lengths: (B,N) or
+    (B,N,1,1,1); block: OracleBlockMask.  At most one mask form may be given.
+    rows: optional flat (b,n,h,q) row indices; then O is (len(rows), D) and
+    lse/max are (len(rows),), else O is (B,N,H,Q,D) and lse/max (B,N,H,Q).
+    ``lib`` selects another compiled copy of the oracle (used to check that
+    the pins reject deliberately broken copies).
+    """
+    lib = lib or _load()
+    qn, kn, vn = _np(q, np.float64), _np(k, np.float64), _np(v, np.float64)
+    if qn.ndim != 5 or kn.ndim != 5 or vn.ndim != 5:
+        raise ValueError("q, k, v must be 5-D (B,N,H,Q|K,D)")
+    B, N, H, Q, D = qn.shape
+    K = kn.shape[3]
+    if kn.shape != (B, N, H, K, D) or vn.shape != kn.shape:
+        raise ValueError("k/v shape mismatch")
+    bn = _np(bias, np.float64)
+    if bn is not None and bn.shape != (B, 1, H, Q, K):
+        raise ValueError(f"bias must be (B,1,H,Q,K), got {bn.shape}")
+    kind, dense, lens, blk_args, keep = _mask_args(B, N, K, mask, kv_lengths, block)
+
     if rows is None:
         n_rows = B * N * H * Q
         rows_arr = None
@@ -181,3 +217,35 @@ def oracle_fwd(q, k, v, bias=None, *, mask=None, kv_lengths=None,
     if rows is None:
         return out.reshape(B, N, H, Q, D), lse.reshape(B, N, H, Q), mx.reshape(B, N, H, Q)
     return out, lse, mx
+
+
+def oracle_bwd(q, k, v, bias=None, *, dout, mask=None, kv_lengths=None,
+               block: Optional[OracleBlockMask] = None, scale: Optional[float] = None,
+               threads: int = 0, lib=None):
+    """Return (dQ, dK, dV, dBias) in fp64: the gradient of O = forward(q, k,
+    v, bias) against the incoming gradient ``dout`` (B,N,H,Q,D).  dBias is
+    (B,1,H,Q,K), or None without a bias.  Arguments as for oracle_fwd."""
+    lib = lib or _load_bwd()
+    qn, kn, vn = _np(q, np.float64), _np(k, np.float64), _np(v, np.float64)
+    B, N, H, Q, D = qn.shape
+    K = kn.shape[3]
+    if kn.shape != (B, N, H, K, D) or vn.shape != kn.shape:
+        raise ValueError("k/v shape mismatch")
+    bn = _np(bias, np.float64)
+    if bn is not None and bn.shape != (B, 1, H, Q, K):
+        raise ValueError(f"bias must be (B,1,H,Q,K), got {bn.shape}")
+    gn = _np(dout, np.float64)
+    if gn.shape != qn.shape:
+        raise ValueError("dout must have q's shape")
+    kind, dense, lens, blk_args, keep = _mask_args(B, N, K, mask, kv_lengths, block)
+    dq = np.empty_like(qn)
+    dk = np.empty_like(kn)
+    dv = np.empty_like(vn)
+    db = np.empty((B, 1, H, Q, K), dtype=np.float64) if bn is not None else None
+    s = math.nan if scale is None else float(scale)
+    rc = lib.tri_oracle_bwd(B, N, H, Q, K, D, _ptr(qn), _ptr(kn), _ptr(vn), _ptr(bn), kind,
+                            _ptr(dense), _ptr(lens), *blk_args, s, _ptr(gn), _ptr(dq),
+                            _ptr(dk), _ptr(dv), _ptr(db), int(threads))
+    if rc != 0:
+        raise RuntimeError(f"tri_oracle_bwd failed with status {rc}")
+    return dq, dk, dv, db
