@@ -175,6 +175,35 @@ triattn_status tri_attn_fwd(const tri_attn_shape* shape, int32_t dtype, const vo
                             float* max, hipStream_t stream);
 
 /*
+ * Backward of the forward's output O (the page's backward pass; lse and max
+ * carry no incoming gradient).  Per (b,n,h,q) row, with P the forward's
+ * softmax weights rebuilt from lse (P_k = exp(z_k - lse)) and Delta = dO.O:
+ *   dV_k += P_k dO;   dz_k = P_k (dO.V_k - Delta);
+ *   for valid keys only: dQ += s dz_k K_k, dK_k += s dz_k Q, dbias_qk += dz_k,
+ * dbias summed over n (the bias is shared by every n).  A row whose forward
+ * max is the -1e9 replacement had no valid key: its weights are 1/K and it
+ * adds dO/K to every dV_k and nothing else.
+ *
+ * Inputs: q, k, v, bias, mask, scale exactly as given to tri_attn_fwd; out,
+ * lse and max as tri_attn_fwd wrote them for those inputs (all three
+ * required here); dout (B,N,H,Q,D) of type `dtype`, 16-byte aligned.
+ * Outputs (written in full, caller-owned): dq (B,N,H,Q,D), dk and dv
+ * (B,N,H,K,D), all of type `dtype` and 16-byte aligned; dbias (B,1,H,Q,K)
+ * fp32, or NULL to skip it.  All device memory; enqueued on `stream`.
+ *
+ * Errors: those of tri_attn_check for the forward's arguments, and
+ * TRIATTN_ERR_INVALID_ARG for a NULL dout / lse / max / dq / dk / dv when
+ * there is a query row, or a misaligned one; nothing is launched then.
+ * TRIATTN_ERR_HIP if a launch fails.  With no query row the call does
+ * nothing.  The kernels compute in fp32 (plain vector code).
+ */
+triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                            const void* k, const void* v, const float* bias,
+                            const tri_attn_mask* mask, float scale, const void* out,
+                            const void* dout, const float* lse, const float* max, void* dq,
+                            void* dk, void* dv, float* dbias, hipStream_t stream);
+
+/*
  * Count the valid prefix of each dense key-mask row: the page's
  * mask_to_kv_lengths helper, which turns a right-padded (B,N,1,1,K) bool mask
  * into (B,N,1,1,1) int32 lengths.  `mask`: rows*K bytes (nonzero = valid);

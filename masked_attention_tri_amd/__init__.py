@@ -35,14 +35,16 @@ from ._native import (  # noqa: F401
     TriAttnMask,
     TriAttnShape,
     load_library,
+    tri_attn_bwd,
     tri_attn_check,
     tri_attn_fwd,
     tri_attn_mask_to_kv_lengths,
     tri_attn_status_str,
 )
 
-__all__ = ["triangle_attention", "mask_to_kv_lengths", "BlockMask", "causal_mask",
-           "tri_attn_fwd", "tri_attn_check", "tri_attn_status_str",
+__all__ = ["triangle_attention", "triangle_attention_backward", "mask_to_kv_lengths",
+           "BlockMask", "causal_mask", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_check",
+           "tri_attn_status_str",
            "tri_attn_mask_to_kv_lengths", "load_library"]
 
 
@@ -190,19 +192,9 @@ def _as5(x, name):
     return x
 
 
-def triangle_attention(q, k, v, bias=None, mask=None, scale: Optional[float] = None,
-                       return_aux: bool = False, *, kv_lengths=None,
-                       block_mask: Optional[BlockMask] = None, stream=None):
-    """Attention_q = sum_k softmax_k(s Q_q.K_k + B_qk if key k is valid else
-    -1e9) V_k over (B, N, H, Q, D) tensors.
-
-    q (B,N,H,Q,D); k, v (B,N,H,K,D); bias (B,1,H,Q,K) (cast to fp32) or None;
-    mask (B,N,1,1,K) (cast to bool) | kv_lengths (B,N,1,1,1) int32 |
-    block_mask: at most one.  4-D inputs are accepted when B = 1.  scale None
-    means 1/sqrt(D).  Returns O (q's dtype), or (O, lse, max) with fp32 lse
-    and max of shape (B,N,H,Q,1) when return_aux.  Runs on `stream` (torch's
-    current stream by default) and does not synchronise.
-    """
+def _prepare(q, k, v, bias, mask, kv_lengths, block_mask):
+    """Shape and dtype checks, 5-D views, contiguous copies, and the mask
+    descriptor (with the tensors it points at, which must stay alive)."""
     if mask is not None and kv_lengths is not None:
         raise ValueError("pass either mask or kv_lengths, not both")
     if block_mask is not None and (mask is not None or kv_lengths is not None):
@@ -249,6 +241,27 @@ def triangle_attention(q, k, v, bias=None, mask=None, scale: Optional[float] = N
         desc, conv = block_mask._descriptor(B, N, H, Q, K, dev)
         keep.extend(conv)
 
+    return four_d, q5, k5, v5, bias5, desc, keep
+
+
+def triangle_attention(q, k, v, bias=None, mask=None, scale: Optional[float] = None,
+                       return_aux: bool = False, *, kv_lengths=None,
+                       block_mask: Optional[BlockMask] = None, stream=None):
+    """Attention_q = sum_k softmax_k(s Q_q.K_k + B_qk if key k is valid else
+    -1e9) V_k over (B, N, H, Q, D) tensors.
+
+    q (B,N,H,Q,D); k, v (B,N,H,K,D); bias (B,1,H,Q,K) (cast to fp32) or None;
+    mask (B,N,1,1,K) (cast to bool) | kv_lengths (B,N,1,1,1) int32 |
+    block_mask: at most one.  4-D inputs are accepted when B = 1.  scale None
+    means 1/sqrt(D).  Returns O (q's dtype), or (O, lse, max) with fp32 lse
+    and max of shape (B,N,H,Q,1) when return_aux.  Runs on `stream` (torch's
+    current stream by default) and does not synchronise.
+    """
+    four_d, q5, k5, v5, bias5, desc, keep = _prepare(q, k, v, bias, mask, kv_lengths,
+                                                     block_mask)
+    B, N, H, Q, D = q5.shape
+    K = k5.shape[3]
+    dev = q5.device
     out = torch.empty_like(q5)
     lse = torch.empty(B, N, H, Q, 1, device=dev, dtype=torch.float32)
     mx = torch.empty(B, N, H, Q, 1, device=dev, dtype=torch.float32)
@@ -286,3 +299,39 @@ def mask_to_kv_lengths(mask):
         raise ValueError(f"{int(bad.item())} mask rows are not right-padded prefixes; "
                          "pass the dense mask instead")
     return lens.squeeze(0) if four_d else lens
+
+
+def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
+                                scale: Optional[float] = None, *, kv_lengths=None,
+                                block_mask: Optional[BlockMask] = None, stream=None):
+    """Gradients of O = triangle_attention(q, k, v, bias, mask, scale, ...)
+    for the incoming gradient dout: returns (dq, dk, dv, dbias), dq/dk/dv in
+    q's dtype and dbias fp32 of shape (B,1,H,Q,K) (None when bias is None).
+    out, lse and mx are the forward's (O, lse, max) for the same arguments
+    (from return_aux=True).  Every step runs in the library's HIP kernels.
+    """
+    four_d, q5, k5, v5, bias5, desc, keep = _prepare(q, k, v, bias, mask, kv_lengths,
+                                                     block_mask)
+    B, N, H, Q, D = q5.shape
+    K = k5.shape[3]
+    o5, g5 = _as5(out, "out").contiguous(), _as5(dout, "dout").contiguous()
+    if tuple(o5.shape) != (B, N, H, Q, D) or tuple(g5.shape) != (B, N, H, Q, D):
+        raise ValueError(f"out and dout must be (B,N,H,Q,D) = {(B, N, H, Q, D)}")
+    if o5.dtype != q5.dtype or g5.dtype != q5.dtype:
+        raise ValueError("out and dout must have q's dtype")
+    lse5 = _as5(lse, "lse").to(torch.float32).contiguous()
+    mx5 = _as5(mx, "max").to(torch.float32).contiguous()
+    if lse5.numel() != B * N * H * Q or mx5.numel() != B * N * H * Q:
+        raise ValueError("lse and max must hold one value per (b, n, h, q) row")
+    dq, dk, dv = torch.empty_like(q5), torch.empty_like(k5), torch.empty_like(v5)
+    dbias = (torch.empty(B, 1, H, Q, K, device=q5.device, dtype=torch.float32)
+             if bias5 is not None else None)
+    s = math.nan if scale is None else float(scale)
+    st = tri_attn_bwd(TriAttnShape(B, N, H, Q, K, D), _native.DTYPE_CODES[q5.dtype], q5, k5, v5,
+                      bias5, desc, s, o5, g5, lse5, mx5, dq, dk, dv, dbias, stream)
+    if st != TRIATTN_OK:
+        raise RuntimeError(f"tri_attn_bwd: {tri_attn_status_str(st)}")
+    if four_d:
+        dq, dk, dv = dq.squeeze(0), dk.squeeze(0), dv.squeeze(0)
+        dbias = dbias.squeeze(0) if dbias is not None else None
+    return dq, dk, dv, dbias

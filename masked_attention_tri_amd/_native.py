@@ -32,7 +32,7 @@ TRIATTN_MASK_BLOCK = 3
 TRIATTN_MOD_NONE = 0
 TRIATTN_MOD_CAUSAL = 1
 
-EXPORTED = ("tri_attn_check", "tri_attn_fwd", "tri_attn_mask_to_kv_lengths",
+EXPORTED = ("tri_attn_check", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_mask_to_kv_lengths",
             "tri_attn_status_str")
 
 DTYPE_CODES = {torch.float32: TRIATTN_F32, torch.float16: TRIATTN_F16,
@@ -86,6 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_check.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P]
     lib.tri_attn_fwd.restype = I32
     lib.tri_attn_fwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P]
+    lib.tri_attn_bwd.restype = I32
+    lib.tri_attn_bwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P, P, P, P]
     lib.tri_attn_mask_to_kv_lengths.restype = I32
     lib.tri_attn_mask_to_kv_lengths.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P]
     lib.tri_attn_status_str.restype = ctypes.c_char_p
@@ -137,4 +139,17 @@ def tri_attn_mask_to_kv_lengths(mask, rows: int, K: int, kv_lengths, nonprefix_r
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     return int(load_library().tri_attn_mask_to_kv_lengths(
         _ptr(mask), int(rows), int(K), _ptr(kv_lengths), _ptr(nonprefix_rows),
+        ctypes.c_void_p(handle)))
+
+
+def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: float, out, dout,
+                 lse, mx, dq, dk, dv, dbias, stream) -> int:
+    """Enqueue the backward pass on `stream` (as tri_attn_fwd)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return int(load_library().tri_attn_bwd(
+        ctypes.byref(shape), int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+        ctypes.byref(mask) if mask is not None else None, ctypes.c_float(scale), _ptr(out),
+        _ptr(dout), _ptr(lse), _ptr(mx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
         ctypes.c_void_p(handle)))

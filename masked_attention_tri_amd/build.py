@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtriattn.so")
-SOURCES = ["triattn_api.hip", "kernel_generic.hip", "kernel_mfma.hip", "kernel_util.hip"]
+SOURCES = ["triattn_api.hip", "kernel_generic.hip", "kernel_mfma.hip", "kernel_util.hip",
+           "kernel_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -171,6 +171,34 @@ triattn_status tri_attn_fwd(const tri_attn_shape* shape, int32_t dtype, const vo
     return err == hipSuccess ? TRIATTN_OK : TRIATTN_ERR_HIP;
 }
 
+triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                            const void* k, const void* v, const float* bias,
+                            const tri_attn_mask* mask, float scale, const void* out,
+                            const void* dout, const float* lse, const float* max, void* dq,
+                            void* dk, void* dv, float* dbias, hipStream_t stream) {
+    // The forward's arguments (out is read, not written, here).
+    triattn_status st = check_impl(shape, dtype, q, k, v, bias, mask, scale, out, lse, max);
+    if (st != TRIATTN_OK) return st;
+    const bool empty = shape->B == 0 || shape->N == 0 || shape->H == 0 || shape->Q == 0;
+    if (!empty && (!dout || !lse || !max || !dq || !dk || !dv)) return TRIATTN_ERR_INVALID_ARG;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(dbias, 4))
+        return TRIATTN_ERR_INVALID_ARG;
+    if (empty) return TRIATTN_OK;
+    const Params p = make_params(shape, q, k, v, bias, mask, scale, nullptr, nullptr, nullptr);
+    triattn::BwdParams g{};
+    g.out = out;
+    g.dout = dout;
+    g.lse = lse;
+    g.mx = max;
+    g.dq = dq;
+    g.dk = dk;
+    g.dv = dv;
+    g.dbias = dbias;
+    const hipError_t err = triattn::launch_bwd(p, g, dtype, stream);
+    return err == hipSuccess ? TRIATTN_OK : TRIATTN_ERR_HIP;
+}
+
 triattn_status tri_attn_mask_to_kv_lengths(const uint8_t* mask, int64_t rows, int64_t K,
                                            int32_t* kv_lengths, int32_t* nonprefix_rows,
                                            hipStream_t stream) {

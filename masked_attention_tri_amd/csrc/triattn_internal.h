@@ -35,6 +35,20 @@ struct Params {
     int64_t n_kv_blocks;  // ceil(K / kv_block) (block kind)
 };
 
+// The extra arguments of one backward call: the forward's output and the
+// incoming gradient (inputs), lse and max read through Params, and the
+// gradients (outputs; dbias may be nullptr).
+struct BwdParams {
+    const void* out;
+    const void* dout;
+    const float* lse;
+    const float* mx;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dbias;
+};
+
 // Masked logits are carried as -inf inside the kernels: when a row has at
 // least one valid key this gives exactly the weights of the -1e9
 // replacement (exp underflows to 0 either way); rows with no valid key are
@@ -49,6 +63,7 @@ constexpr int64_t kMaxKvBlocks = 8192;
 hipError_t launch_generic(const Params& p, int32_t dtype, hipStream_t stream);
 hipError_t launch_mfma(const Params& p, int32_t dtype, hipStream_t stream);
 bool mfma_supports(const Params& p, int32_t dtype);
+hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, hipStream_t stream);
 hipError_t launch_mask_to_kv_lengths(const uint8_t* mask, int64_t rows, int64_t K,
                                      int32_t* kv_lengths, int32_t* nonprefix_rows,
                                      hipStream_t stream);
