@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 flop/clk)
 METRIC = "fwd TFLOP/s + % bf16 MFMA peak, triangle attn N=Q=K=768 H=4 D=64"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "masked_attention_tri_amd", "csrc", "kernel_mfma.hip")
@@ -35,11 +36,13 @@ KERNEL_SRC = os.path.join(ROOT, "masked_attention_tri_amd", "csrc", "kernel_mfma
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=None, help="default 100 (backward: 10)")
     # Under this load the GPU's clock first dips and then settles over a few
     # tens of milliseconds; the default warmup covers that, so the timed
     # steps see the steady clock.
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=None, help="default 200 (backward: 3)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time tri_attn_bwd (dQ, dK, dV, dBias) instead of the forward")
     ap.add_argument("--workload", default=None,
                     help="named workload (default: the headline bf16 kv_lengths N768 D64 one)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -47,7 +50,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 10 if args.backward else 100
+    if args.warmup is None:
+        args.warmup = 3 if args.backward else 200
+    return args
 
 
 def work_counts(case):
@@ -138,6 +146,85 @@ def cpu_baseline(case, target_s):
     }, ns, out
 
 
+def bench_backward(args, case, g, key, shape, dtype, desc, scale, out, lse, mx, stream, fwd):
+    """One step = one tri_attn_bwd call (dQ, dK, dV, dBias) on the workload,
+    after one forward for O, lse and max; inputs resident in HBM."""
+    import torch
+
+    import masked_attention_tri_amd as mat
+    from masked_attention_tri_amd import _native as nat
+
+    B, N, H, Q, K, D = case.shape
+    fwd()
+    gen = torch.Generator().manual_seed(4242)
+    dout = torch.randn(g.q.shape, generator=gen).to(g.q.dtype).to(g.q.device)
+    dq, dk, dv = torch.empty_like(g.q), torch.empty_like(g.k), torch.empty_like(g.v)
+    dbias = torch.empty_like(g.bias) if g.bias is not None else None
+
+    def step():
+        st = mat.tri_attn_bwd(shape, dtype, g.q, g.k, g.v, g.bias, desc, scale, out, dout, lse,
+                              mx, dq, dk, dv, dbias, stream)
+        if st != nat.TRIATTN_OK:
+            raise RuntimeError(mat.tri_attn_status_str(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] backward: {ms:.4f} ms/step", file=sys.stderr, flush=True)
+    # Algorithmic work: 10 D flops per visited (query, key) pair (recomputed
+    # logits, dP = dO.V, dV, dQ and dK, 2 D each), i.e. 2.5x the forward's.
+    _, alg_fwd, _ = work_counts(case)
+    alg = 2.5 * alg_fwd
+    tflops = alg / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "bwd TFLOP/s (10 D flops per visited query-key pair), triangle attn",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[case.dtype],
+        "data": "synthetic",
+        "config": {"workload": case.name, "key": key, "B": B, "N": N, "H": H, "Q": Q, "K": K,
+                   "D": D, "algorithmic_flop": alg},
+        # the backward kernels are plain fp32 vector code
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_FP32_VALU_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_VALU_TFLOPS, 5),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        print("[bench] timing the CPU backward oracle baseline", file=sys.stderr, flush=True)
+        threads = oracle.default_threads()
+
+        def run(ns):
+            t0 = time.perf_counter()
+            oracle.oracle_bwd(case.q[:, :ns], case.k[:, :ns], case.v[:, :ns], case.bias,
+                              dout=dout.cpu()[:, :ns],
+                              kv_lengths=None if case.kv_lengths is None else case.kv_lengths[:, :ns],
+                              mask=None if case.mask is None else case.mask[:, :ns],
+                              scale=case.scale, threads=threads)
+            return time.perf_counter() - t0
+
+        dt1 = run(1)
+        ns = max(1, min(N, int(args.cpu_seconds / max(dt1, 1e-3))))
+        dt = run(ns)
+        alg_s = alg * ns / N
+        res["cpu_baseline"] = {"value": round(alg_s / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": min(threads, B * H), "kind": "oracle",
+                               "sample": f"first {ns} of {N} n rows, fp64, {dt:.1f} s",
+                               "seconds": round(dt, 3)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -190,6 +277,10 @@ def main():
                               stream)
         if st != nat.TRIATTN_OK:
             raise RuntimeError(mat.tri_attn_status_str(st))
+
+    if args.backward:
+        return bench_backward(args, case, g, key, shape, dtype, desc, scale, out, lse, mx,
+                              stream, step)
 
     for _ in range(args.warmup):
         step()
