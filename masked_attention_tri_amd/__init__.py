@@ -42,7 +42,8 @@ from ._native import (  # noqa: F401
     tri_attn_status_str,
 )
 
-__all__ = ["triangle_attention", "triangle_attention_backward", "mask_to_kv_lengths",
+__all__ = ["triangle_attention", "triangle_attention_backward", "triangle_attention_autograd",
+           "mask_to_kv_lengths",
            "BlockMask", "causal_mask", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_check",
            "tri_attn_status_str",
            "tri_attn_mask_to_kv_lengths", "load_library"]
@@ -335,3 +336,38 @@ def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
         dq, dk, dv = dq.squeeze(0), dk.squeeze(0), dv.squeeze(0)
         dbias = dbias.squeeze(0) if dbias is not None else None
     return dq, dk, dv, dbias
+
+
+class _TriangleAttentionFn(torch.autograd.Function):
+    """Forward through tri_attn_fwd, backward through tri_attn_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, bias, mask, scale, kv_lengths, block_mask):
+        out, lse, mx = triangle_attention(q, k, v, bias, mask, scale, return_aux=True,
+                                          kv_lengths=kv_lengths, block_mask=block_mask)
+        ctx.save_for_backward(q, k, v, bias, out, lse, mx)
+        ctx.mask, ctx.scale, ctx.kv_lengths, ctx.block_mask = mask, scale, kv_lengths, block_mask
+        ctx.bias_dtype = None if bias is None else bias.dtype
+        ctx.mark_non_differentiable(lse, mx)
+        return out, lse, mx
+
+    @staticmethod
+    def backward(ctx, dout, _dlse, _dmx):
+        q, k, v, bias, out, lse, mx = ctx.saved_tensors
+        dq, dk, dv, dbias = triangle_attention_backward(
+            q, k, v, bias, out, dout.to(q.dtype).contiguous(), lse, mx, ctx.mask, ctx.scale,
+            kv_lengths=ctx.kv_lengths, block_mask=ctx.block_mask)
+        if dbias is not None:
+            dbias = dbias.to(ctx.bias_dtype)
+        return dq, dk, dv, dbias, None, None, None, None
+
+
+def triangle_attention_autograd(q, k, v, bias=None, mask=None, scale: Optional[float] = None,
+                                return_aux: bool = False, *, kv_lengths=None,
+                                block_mask: Optional[BlockMask] = None):
+    """triangle_attention with gradients: O (or (O, lse, max)) recorded for
+    torch.autograd, whose backward runs tri_attn_bwd.  Gradients flow to q,
+    k, v and bias (its gradient is summed over n and cast to bias's dtype);
+    lse and max are not differentiable."""
+    out, lse, mx = _TriangleAttentionFn.apply(q, k, v, bias, mask, scale, kv_lengths, block_mask)
+    return (out, lse, mx) if return_aux else out

@@ -91,3 +91,27 @@ def test_backward_workload_kv_lengths_fp16():
     c = wl.make_workload("fp16_lens96")
     say(f"backward {c.name}")
     _check(c, seed=29)
+
+
+@pytest.mark.parametrize("four_d", [False, True])
+def test_autograd_wrapper(four_d):
+    """torch.autograd through triangle_attention_autograd gives the oracle's
+    gradients of sum(O * G); 4-D (B = 1) inputs keep their rank."""
+    c = wl.make_case(1, 2, 2, 40, 50, 64, "bf16", "kv_lengths", seed=31)
+    say(f"autograd {c.name} four_d={four_d}")
+    g = torch.Generator().manual_seed(37)
+    dout = torch.randn(c.q.shape, generator=g).to(c.q.dtype)
+    sq = (lambda t: t.squeeze(0)) if four_d else (lambda t: t)
+    q, k, v = (sq(x).cuda().requires_grad_() for x in (c.q, c.k, c.v))
+    bias = sq(c.bias).cuda().requires_grad_()
+    lens = sq(c.kv_lengths).cuda()
+    out = mat.triangle_attention_autograd(q, k, v, bias, kv_lengths=lens, scale=c.scale)
+    assert out.shape == q.shape
+    out.backward(sq(dout).cuda())
+    ref = orc.oracle_bwd(c.q, c.k, c.v, c.bias, dout=dout, kv_lengths=c.kv_lengths, scale=c.scale)
+    for name, t, want in zip(("dq", "dk", "dv", "dbias"), (q, k, v, bias), ref):
+        got = t.grad.detach().cpu().double().reshape(want.shape).numpy()
+        err = float(np.abs(got - want).max())
+        bound = 2e-2 * (1 + float(np.abs(want).max()))
+        say(f"autograd {name}: err {err:.3g} bound {bound:.3g}")
+        assert err <= bound, f"{name}: {err} > {bound}"
