@@ -14,15 +14,16 @@
 // every key and it passes nothing to Q, K or the bias.  The bias is shared by
 // every n, so dB sums over n.
 //
-// Three plain fp32 kernels, one wavefront per output row, no atomics:
-//   dq_kernel    one (b,n,h,q) row: lanes split the keys (chunks of 64) for
-//                z and dz, then broadcast dz_j to accumulate dQ over d.
-//   dkdv_kernel  one (b,n,h,k) key: lanes split the query rows, then
-//                broadcast to accumulate dK and dV over d.
-//   dbias_kernel one (b,h,q) row: lanes split the keys and each lane sums
-//                dz over n for its key.
-// Each lane holds up to kOut = 4 coordinates of a D <= 256 vector (d = lane +
-// 64 i).  These are correctness-first VALU kernels, not tuned.
+// Three fp32 vector kernels on 32 x 32 (query, key) tiles staged in LDS (see
+// Tiles below), no atomics:
+//   dq_kernel    one (b, n, h, 32 query rows) per workgroup, looping over
+//                key tiles: dQ = s dz K.
+//   dkdv_kernel  one (b, n, h, 32 keys), looping over query tiles:
+//                dV = P^T dO, dK = s dz^T Q.
+//   dbias_kernel one (b, h, 32 query rows, 32 keys), looping over n: the sum
+//                of dz.
+// Global memory is read only by coalesced tile loads.  Not MFMA code: the
+// contractions run as fp32 FMAs from LDS.
 #include <math.h>
 
 #include "triattn_internal.h"
@@ -30,17 +31,13 @@
 namespace triattn {
 namespace {
 
-constexpr int kWaves = 4;
+// Each thread accumulates columns d = part + 8 i of one row, i < 8 kOut:
+// kOut = 4 covers D <= 256.
 constexpr int kOut = 4;
 
 template <typename T>
 __device__ __forceinline__ float f32(T x) {
     return static_cast<float>(x);
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
 }
 
 // Is block `blk` among the first count entries of list row `row`?
@@ -81,165 +78,283 @@ __device__ bool key_valid(const Params& p, int64_t b, int64_t n, int64_t h, int6
     }
 }
 
-template <typename T>
-__device__ __forceinline__ float dot_rows(const T* a, const T* b, int64_t D) {
-    float acc = 0.f;
-    for (int64_t d = 0; d < D; ++d) acc = fmaf(f32(a[d]), f32(b[d]), acc);
-    return acc;
+// ---- tiled kernels --------------------------------------------------------
+// A workgroup of 256 threads works on 32 x 32 (query, key) tiles.  Rows of
+// Q, dO (32 query rows) and K, V (32 keys) are staged in LDS as fp32 with a
+// padded row stride (D + 1 floats, so the column reads below hit distinct
+// banks), together with Delta = dO.O, lse and a no-valid-key flag per query
+// row.  pair_tile then gives thread t the pairs (t / 8, t % 8 + 8 j), j < 4,
+// computes z, P, dP and dz for them from LDS and stores P and dz in 32 x 33
+// LDS arrays for the accumulation step of each kernel.
+constexpr int kT = 32;        // tile rows (queries) and columns (keys)
+constexpr int kThreads = 256;
+
+struct Tiles {
+    float* qs;   // kT x (D + 1)
+    float* gos;  // kT x (D + 1): dO
+    float* ks;   // kT x (D + 1)
+    float* vs;   // kT x (D + 1)
+    float* ps;   // kT x (kT + 1): P
+    float* dzs;  // kT x (kT + 1): dz
+    float* delta;  // kT
+    float* lse;    // kT
+    float* dead;   // kT: 1 when the row has no valid key
+};
+
+__device__ __forceinline__ Tiles carve(float* lds, int64_t D) {
+    const int64_t ld = D + 1;
+    Tiles t;
+    t.qs = lds;
+    t.gos = t.qs + kT * ld;
+    t.ks = t.gos + kT * ld;
+    t.vs = t.ks + kT * ld;
+    t.ps = t.vs + kT * ld;
+    t.dzs = t.ps + kT * (kT + 1);
+    t.delta = t.dzs + kT * (kT + 1);
+    t.lse = t.delta + kT;
+    t.dead = t.lse + kT;
+    return t;
 }
 
-// dQ: one wave per (b, n, h, q) row.
-template <typename T>
-__global__ __launch_bounds__(64 * kWaves) void dq_kernel(Params p, BwdParams g) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (row >= p.B * p.N * p.H * p.Q) return;
-    const int64_t qi = row % p.Q, h = (row / p.Q) % p.H, n = (row / (p.Q * p.H)) % p.N,
-                  b = row / (p.Q * p.H * p.N);
-    const int64_t D = p.D, K = p.K, bnh = (b * p.N + n) * p.H + h;
-    const T* qr = static_cast<const T*>(p.q) + row * D;
-    const T* go = static_cast<const T*>(g.dout) + row * D;
-    const T* o = static_cast<const T*>(g.out) + row * D;
-    const T* kb = static_cast<const T*>(p.k) + bnh * K * D;
-    const T* vb = static_cast<const T*>(p.v) + bnh * K * D;
-    const float* br = p.bias ? p.bias + ((b * p.H + h) * p.Q + qi) * K : nullptr;
-    T* dqr = static_cast<T*>(g.dq) + row * D;
+size_t lds_bytes(int64_t D) {
+    return static_cast<size_t>(4 * kT * (D + 1) + 2 * kT * (kT + 1) + 3 * kT) * sizeof(float);
+}
 
-    float acc[kOut];
+// Stage `rows` rows (from row r0 of a (rows_total, D) array) into dst as
+// fp32, zero past rows_total.  Coalesced: consecutive threads take
+// consecutive elements.
+template <typename T>
+__device__ __forceinline__ void stage(float* dst, const T* src, int64_t r0, int64_t rows_total,
+                                      int64_t D) {
+    for (int64_t e = threadIdx.x; e < kT * D; e += kThreads) {
+        const int64_t r = e / D, d = e % D;
+        dst[r * (D + 1) + d] = r0 + r < rows_total ? f32(src[(r0 + r) * D + d]) : 0.f;
+    }
+}
+
+// Delta, lse and the no-valid-key flag of query rows q0 .. q0 + kT - 1 of
+// slice bnh (8 threads per row, d strided by 8, reduced by shuffles).
+template <typename T>
+__device__ __forceinline__ void stage_rows(const Params& p, const BwdParams& g, Tiles t,
+                                           int64_t bnh, int64_t q0) {
+    const int r = threadIdx.x >> 3, part = threadIdx.x & 7;
+    const int64_t qi = q0 + r, D = p.D;
+    float acc = 0.f;
+    if (qi < p.Q) {
+        const T* go = static_cast<const T*>(g.dout) + (bnh * p.Q + qi) * D;
+        const T* o = static_cast<const T*>(g.out) + (bnh * p.Q + qi) * D;
+        for (int64_t d = part; d < D; d += 8) acc = fmaf(f32(go[d]), f32(o[d]), acc);
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (part == 0) {
+        const int64_t row = bnh * p.Q + qi;
+        t.delta[r] = acc;
+        t.lse[r] = qi < p.Q ? g.lse[row] : 0.f;
+        t.dead[r] = qi < p.Q && g.mx[row] == kMaskedLogit ? 1.f : 0.f;
+    }
+}
+
+// P and dz of the tile's pairs, from the staged rows (see Tiles).
+__device__ __forceinline__ void pair_tile(const Params& p, Tiles t, int64_t b, int64_t n,
+                                          int64_t h, int64_t q0, int64_t k0) {
+    const int64_t D = p.D, ld = D + 1;
+    const int ql = threadIdx.x >> 3, kb = threadIdx.x & 7;
+    float z[4] = {0.f, 0.f, 0.f, 0.f}, dp[4] = {0.f, 0.f, 0.f, 0.f};
+    const float* qr = t.qs + ql * ld;
+    const float* gr = t.gos + ql * ld;
+    for (int64_t d = 0; d < D; ++d) {
+        const float qd = qr[d], gd = gr[d];
 #pragma unroll
-    for (int i = 0; i < kOut; ++i) acc[i] = 0.f;
-    const bool dead = g.mx[row] == kMaskedLogit;
-    if (!dead) {
-        const float lse = g.lse[row];
-        const float delta = dot_rows(go, o, D);  // dO . O
-        for (int64_t c0 = 0; c0 < K; c0 += 64) {
-            const int64_t kk = c0 + lane;
-            float dz = 0.f;
-            if (kk < K && key_valid(p, b, n, h, qi, kk)) {
-                const float z = fmaf(dot_rows(qr, kb + kk * D, D), p.scale, br ? br[kk] : 0.f);
-                const float pr = expf(z - lse);
-                dz = pr * (dot_rows(go, vb + kk * D, D) - delta);
+        for (int j = 0; j < 4; ++j) {
+            const int kl = kb + 8 * j;
+            z[j] = fmaf(qd, t.ks[kl * ld + d], z[j]);
+            dp[j] = fmaf(gd, t.vs[kl * ld + d], dp[j]);
+        }
+    }
+    const int64_t qi = q0 + ql;
+    const bool dead = t.dead[ql] != 0.f;
+    const float inv_k = 1.0f / static_cast<float>(p.K);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int kl = kb + 8 * j;
+        const int64_t kk = k0 + kl;
+        float pr = 0.f, dz = 0.f;
+        if (qi < p.Q && kk < p.K) {
+            if (dead) {
+                pr = inv_k;
+            } else if (key_valid(p, b, n, h, qi, kk)) {
+                const float bias = p.bias ? p.bias[((b * p.H + h) * p.Q + qi) * p.K + kk] : 0.f;
+                pr = expf(fmaf(z[j], p.scale, bias) - t.lse[ql]);
+                dz = pr * (dp[j] - t.delta[ql]);
             }
-            const int jmax = (K - c0) < 64 ? static_cast<int>(K - c0) : 64;
-            for (int j = 0; j < jmax; ++j) {
-                const float dzj = __shfl(dz, j);
-                if (dzj == 0.f) continue;  // uniform across the wave
-                const T* krow = kb + (c0 + j) * D;
+        }
+        t.ps[ql * (kT + 1) + kl] = pr;
+        t.dzs[ql * (kT + 1) + kl] = dz;
+    }
+}
+
+// dQ: one workgroup per (b, n, h, 32 query rows); loops over key tiles.
+// Thread t owns row t / 8 and columns d = t % 8 + 8 i.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
+    extern __shared__ float lds[];
+    const int64_t D = p.D, ld = D + 1;
+    const Tiles t = carve(lds, D);
+    const int64_t n_qt = (p.Q + kT - 1) / kT;
+    const int64_t bnh = blockIdx.x / n_qt, q0 = (blockIdx.x % n_qt) * kT;
+    const int64_t h = bnh % p.H, n = (bnh / p.H) % p.N, b = bnh / (p.H * p.N);
+    stage(t.qs, static_cast<const T*>(p.q) + bnh * p.Q * D, q0, p.Q, D);
+    stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
+    stage_rows<T>(p, g, t, bnh, q0);
+    const int r = threadIdx.x >> 3, part = threadIdx.x & 7;
+    float acc[kOut * 8];
 #pragma unroll
-                for (int i = 0; i < kOut; ++i)
-                    if (lane + 64 * i < D) acc[i] = fmaf(dzj, f32(krow[lane + 64 * i]), acc[i]);
+    for (int i = 0; i < kOut * 8; ++i) acc[i] = 0.f;
+    for (int64_t k0 = 0; k0 < p.K; k0 += kT) {
+        __syncthreads();  // previous tile's reads done
+        stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
+        stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
+        __syncthreads();
+        pair_tile(p, t, b, n, h, q0, k0);
+        __syncthreads();
+        for (int kl = 0; kl < kT; ++kl) {
+            const float dz = t.dzs[r * (kT + 1) + kl];
+            const float* kr = t.ks + kl * ld;
+#pragma unroll
+            for (int i = 0; i < kOut * 8; ++i) {
+                const int64_t d = part + 8 * i;
+                if (d < D) acc[i] = fmaf(dz, kr[d], acc[i]);
             }
         }
     }
+    const int64_t qi = q0 + r;
+    if (qi >= p.Q) return;
+    T* dqr = static_cast<T*>(g.dq) + (bnh * p.Q + qi) * D;
 #pragma unroll
-    for (int i = 0; i < kOut; ++i)
-        if (lane + 64 * i < D) dqr[lane + 64 * i] = static_cast<T>(acc[i] * p.scale);
+    for (int i = 0; i < kOut * 8; ++i) {
+        const int64_t d = part + 8 * i;
+        if (d < D) dqr[d] = static_cast<T>(acc[i] * p.scale);
+    }
 }
 
-// dK and dV: one wave per (b, n, h, k) key row.
+// dK and dV: one workgroup per (b, n, h, 32 keys); loops over query tiles.
+// Thread t owns key t / 8 and columns d = t % 8 + 8 i.
 template <typename T>
-__global__ __launch_bounds__(64 * kWaves) void dkdv_kernel(Params p, BwdParams g) {
-    const int lane = threadIdx.x & 63;
-    const int64_t krow_i = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (krow_i >= p.B * p.N * p.H * p.K) return;
-    const int64_t kk = krow_i % p.K, h = (krow_i / p.K) % p.H, n = (krow_i / (p.K * p.H)) % p.N,
-                  b = krow_i / (p.K * p.H * p.N);
-    const int64_t D = p.D, Q = p.Q, bnh = (b * p.N + n) * p.H + h;
-    const T* kr = static_cast<const T*>(p.k) + krow_i * D;
-    const T* vr = static_cast<const T*>(p.v) + krow_i * D;
-    const T* qb = static_cast<const T*>(p.q) + bnh * Q * D;
-    const T* gob = static_cast<const T*>(g.dout) + bnh * Q * D;
-    const T* ob = static_cast<const T*>(g.out) + bnh * Q * D;
-    const float inv_k = 1.0f / static_cast<float>(p.K);
-
-    float dk[kOut], dv[kOut];
+__global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
+    extern __shared__ float lds[];
+    const int64_t D = p.D, ld = D + 1;
+    const Tiles t = carve(lds, D);
+    const int64_t n_kt = (p.K + kT - 1) / kT;
+    const int64_t bnh = blockIdx.x / n_kt, k0 = (blockIdx.x % n_kt) * kT;
+    const int64_t h = bnh % p.H, n = (bnh / p.H) % p.N, b = bnh / (p.H * p.N);
+    stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
+    stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
+    const int kr = threadIdx.x >> 3, part = threadIdx.x & 7;
+    float dk[kOut * 8], dv[kOut * 8];
 #pragma unroll
-    for (int i = 0; i < kOut; ++i) dk[i] = dv[i] = 0.f;
-    for (int64_t c0 = 0; c0 < Q; c0 += 64) {
-        const int64_t qi = c0 + lane;
-        float pr = 0.f, dz = 0.f;
-        if (qi < Q) {
-            const int64_t row = bnh * Q + qi;
-            if (g.mx[row] == kMaskedLogit) {
-                pr = inv_k;  // no valid key in this row: uniform weights
-            } else if (key_valid(p, b, n, h, qi, kk)) {
-                const float bias = p.bias ? p.bias[((b * p.H + h) * Q + qi) * p.K + kk] : 0.f;
-                const float z = fmaf(dot_rows(qb + qi * D, kr, D), p.scale, bias);
-                pr = expf(z - g.lse[row]);
-                dz = pr * (dot_rows(gob + qi * D, vr, D) - dot_rows(gob + qi * D, ob + qi * D, D));
-            }
-        }
-        const int jmax = (Q - c0) < 64 ? static_cast<int>(Q - c0) : 64;
-        for (int j = 0; j < jmax; ++j) {
-            const float pj = __shfl(pr, j), dzj = __shfl(dz, j);
-            if (pj == 0.f && dzj == 0.f) continue;  // uniform across the wave
-            const T* gq = gob + (c0 + j) * D;
-            const T* qq = qb + (c0 + j) * D;
+    for (int i = 0; i < kOut * 8; ++i) dk[i] = dv[i] = 0.f;
+    for (int64_t q0 = 0; q0 < p.Q; q0 += kT) {
+        __syncthreads();
+        stage(t.qs, static_cast<const T*>(p.q) + bnh * p.Q * D, q0, p.Q, D);
+        stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
+        stage_rows<T>(p, g, t, bnh, q0);
+        __syncthreads();
+        pair_tile(p, t, b, n, h, q0, k0);
+        __syncthreads();
+        for (int ql = 0; ql < kT; ++ql) {
+            const float pr = t.ps[ql * (kT + 1) + kr], dz = t.dzs[ql * (kT + 1) + kr];
+            const float* qrow = t.qs + ql * ld;
+            const float* grow = t.gos + ql * ld;
 #pragma unroll
-            for (int i = 0; i < kOut; ++i) {
-                const int64_t d = lane + 64 * i;
+            for (int i = 0; i < kOut * 8; ++i) {
+                const int64_t d = part + 8 * i;
                 if (d < D) {
-                    dv[i] = fmaf(pj, f32(gq[d]), dv[i]);
-                    dk[i] = fmaf(dzj, f32(qq[d]), dk[i]);
+                    dv[i] = fmaf(pr, grow[d], dv[i]);
+                    dk[i] = fmaf(dz, qrow[d], dk[i]);
                 }
             }
         }
     }
-    T* dkr = static_cast<T*>(g.dk) + krow_i * D;
-    T* dvr = static_cast<T*>(g.dv) + krow_i * D;
+    const int64_t kk = k0 + kr;
+    if (kk >= p.K) return;
+    T* dkr = static_cast<T*>(g.dk) + (bnh * p.K + kk) * D;
+    T* dvr = static_cast<T*>(g.dv) + (bnh * p.K + kk) * D;
 #pragma unroll
-    for (int i = 0; i < kOut; ++i)
-        if (lane + 64 * i < D) {
-            dkr[lane + 64 * i] = static_cast<T>(dk[i] * p.scale);
-            dvr[lane + 64 * i] = static_cast<T>(dv[i]);
+    for (int i = 0; i < kOut * 8; ++i) {
+        const int64_t d = part + 8 * i;
+        if (d < D) {
+            dkr[d] = static_cast<T>(dk[i] * p.scale);
+            dvr[d] = static_cast<T>(dv[i]);
         }
+    }
 }
 
-// dBias: one wave per (b, h, q) row; each lane sums dz over n for its keys.
+// dBias: one workgroup per (b, h, 32 query rows, 32 keys); loops over n and
+// sums dz; thread t owns the pairs of pair_tile.
 template <typename T>
-__global__ __launch_bounds__(64 * kWaves) void dbias_kernel(Params p, BwdParams g) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-    if (r >= p.B * p.H * p.Q) return;
-    const int64_t qi = r % p.Q, h = (r / p.Q) % p.H, b = r / (p.Q * p.H);
-    const int64_t D = p.D, K = p.K;
-    const float* br = p.bias ? p.bias + r * K : nullptr;  // (B,1,H,Q,K): row r
-    float* dbr = g.dbias + r * K;
-    for (int64_t c0 = 0; c0 < K; c0 += 64) {
-        const int64_t kk = c0 + lane;
-        float acc = 0.f;
-        if (kk < K) {
-            for (int64_t n = 0; n < p.N; ++n) {
-                const int64_t bnh = (b * p.N + n) * p.H + h;
-                const int64_t row = bnh * p.Q + qi;
-                if (g.mx[row] == kMaskedLogit || !key_valid(p, b, n, h, qi, kk)) continue;
-                const T* qr = static_cast<const T*>(p.q) + row * D;
-                const T* go = static_cast<const T*>(g.dout) + row * D;
-                const T* o = static_cast<const T*>(g.out) + row * D;
-                const T* krow = static_cast<const T*>(p.k) + (bnh * K + kk) * D;
-                const T* vrow = static_cast<const T*>(p.v) + (bnh * K + kk) * D;
-                const float z = fmaf(dot_rows(qr, krow, D), p.scale, br ? br[kk] : 0.f);
-                const float pr = expf(z - g.lse[row]);
-                acc += pr * (dot_rows(go, vrow, D) - dot_rows(go, o, D));
-            }
-            dbr[kk] = acc;
-        }
+__global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) {
+    extern __shared__ float lds[];
+    const int64_t D = p.D;
+    const Tiles t = carve(lds, D);
+    const int64_t n_qt = (p.Q + kT - 1) / kT, n_kt = (p.K + kT - 1) / kT;
+    const int64_t bh = blockIdx.x / (n_qt * n_kt);
+    const int64_t q0 = ((blockIdx.x / n_kt) % n_qt) * kT, k0 = (blockIdx.x % n_kt) * kT;
+    const int64_t h = bh % p.H, b = bh / p.H;
+    const int ql = threadIdx.x >> 3, kb = threadIdx.x & 7;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t n = 0; n < p.N; ++n) {
+        const int64_t bnh = (b * p.N + n) * p.H + h;
+        __syncthreads();
+        stage(t.qs, static_cast<const T*>(p.q) + bnh * p.Q * D, q0, p.Q, D);
+        stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
+        stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
+        stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
+        stage_rows<T>(p, g, t, bnh, q0);
+        __syncthreads();
+        pair_tile(p, t, b, n, h, q0, k0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += t.dzs[ql * (kT + 1) + kb + 8 * j];
+    }
+    const int64_t qi = q0 + ql;
+    if (qi >= p.Q) return;
+    float* dbr = g.dbias + (bh * p.Q + qi) * p.K;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t kk = k0 + kb + 8 * j;
+        if (kk < p.K) dbr[kk] = acc[j];
     }
 }
 
 template <typename T>
 hipError_t launch_t(const Params& p, const BwdParams& g, hipStream_t stream) {
-    const dim3 block(64 * kWaves);
-    auto grid = [](int64_t rows) { return (rows + kWaves - 1) / kWaves; };
-    const int64_t gq = grid(p.B * p.N * p.H * p.Q), gk = grid(p.B * p.N * p.H * p.K),
-                  gb = grid(p.B * p.H * p.Q);
+    const int64_t n_qt = (p.Q + kT - 1) / kT, n_kt = (p.K + kT - 1) / kT;
+    const int64_t gq = p.B * p.N * p.H * n_qt, gk = p.B * p.N * p.H * n_kt,
+                  gb = p.B * p.H * n_qt * n_kt;
     if (gq > 0x7fffffff || gk > 0x7fffffff || gb > 0x7fffffff)
         return hipErrorInvalidConfiguration;
-    if (gq > 0) hipLaunchKernelGGL(dq_kernel<T>, dim3(static_cast<unsigned>(gq)), block, 0, stream, p, g);
+    const size_t shm = lds_bytes(p.D);
+    const dim3 block(kThreads);
+    if (shm > 65536) {
+        // more than 64 KiB of LDS per workgroup (D > 64; gfx950 has 160 KiB)
+        const int b = static_cast<int>(shm);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dq_kernel<T>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, b);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(dkdv_kernel<T>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, b);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(dbias_kernel<T>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, b);
+        if (e != hipSuccess) return e;
+    }
+    if (gq > 0)
+        hipLaunchKernelGGL(dq_kernel<T>, dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
     if (gk > 0)
-        hipLaunchKernelGGL(dkdv_kernel<T>, dim3(static_cast<unsigned>(gk)), block, 0, stream, p, g);
+        hipLaunchKernelGGL(dkdv_kernel<T>, dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
     if (g.dbias && gb > 0)
-        hipLaunchKernelGGL(dbias_kernel<T>, dim3(static_cast<unsigned>(gb)), block, 0, stream, p, g);
+        hipLaunchKernelGGL(dbias_kernel<T>, dim3(static_cast<unsigned>(gb)), block, shm, stream, p, g);
     return hipGetLastError();
 }
 
