@@ -78,6 +78,15 @@ __device__ bool key_valid(const Params& p, int64_t b, int64_t n, int64_t h, int6
     }
 }
 
+// Keys at or past this limit are never valid in slice (b, n): the clamped
+// length with kv_lengths, else K.  With kv_lengths and a limit of 0 every row
+// of the slice has no valid key.
+__device__ __forceinline__ int64_t key_limit(const Params& p, int64_t b, int64_t n) {
+    if (p.mask_kind != TRIATTN_MASK_KV_LENGTHS || !p.kv_lengths) return p.K;
+    const int64_t len = p.kv_lengths[b * p.N + n];
+    return len < 0 ? 0 : (len > p.K ? p.K : len);
+}
+
 // ---- tiled kernels --------------------------------------------------------
 // A workgroup of 256 threads works on 32 x 32 (query, key) tiles.  Rows of
 // Q, dO (32 query rows) and K, V (32 keys) are staged in LDS as fp32 with a
@@ -212,7 +221,8 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
     float acc[kOut * 8];
 #pragma unroll
     for (int i = 0; i < kOut * 8; ++i) acc[i] = 0.f;
-    for (int64_t k0 = 0; k0 < p.K; k0 += kT) {
+    const int64_t k_end = key_limit(p, b, n);  // dz is 0 past it (and everywhere if 0)
+    for (int64_t k0 = 0; k0 < k_end; k0 += kT) {
         __syncthreads();  // previous tile's reads done
         stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
         stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
@@ -255,7 +265,12 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
     float dk[kOut * 8], dv[kOut * 8];
 #pragma unroll
     for (int i = 0; i < kOut * 8; ++i) dk[i] = dv[i] = 0.f;
-    for (int64_t q0 = 0; q0 < p.Q; q0 += kT) {
+    // A key tile at or past a nonzero length limit gets P = dz = 0 from every
+    // row: dK = dV = 0 without the loop (a zero limit means rows without a
+    // valid key, whose uniform weights reach every key).
+    const int64_t lim = key_limit(p, b, n);
+    const int64_t q_end = (lim > 0 && k0 >= lim) ? 0 : p.Q;
+    for (int64_t q0 = 0; q0 < q_end; q0 += kT) {
         __syncthreads();
         stage(t.qs, static_cast<const T*>(p.q) + bnh * p.Q * D, q0, p.Q, D);
         stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
@@ -306,6 +321,8 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int64_t n = 0; n < p.N; ++n) {
         const int64_t bnh = (b * p.N + n) * p.H + h;
+        const int64_t lim = key_limit(p, b, n);
+        if (lim == 0 || k0 >= lim) continue;  // dz = 0 for the whole tile (uniform)
         __syncthreads();
         stage(t.qs, static_cast<const T*>(p.q) + bnh * p.Q * D, q0, p.Q, D);
         stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
