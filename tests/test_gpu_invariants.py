@@ -175,3 +175,47 @@ def test_empty_work_returns_empty_outputs(B, N, H, Q, K, D, dt):
         assert lse.shape == (B, N, H, Q, 1) and mx.shape == (B, N, H, Q, 1)
     lens2 = mat.mask_to_kv_lengths(mask)
     assert lens2.shape == (B, N, 1, 1, 1)
+
+
+def test_graph_capture_replays_match_eager():
+    """tri_attn_fwd and tri_attn_bwd allocate nothing and launch only
+    kernels, so they can be captured in a HIP graph: every replay, with eager
+    work and synchronisations between replays, equals the eager result
+    bitwise."""
+    say("graph capture of forward and backward")
+    c = wl.make_case(1, 4, 2, 96, 80, 64, "bf16", "kv_lengths", seed=41).to("cuda")
+    dout = torch.randn(c.q.shape, generator=torch.Generator().manual_seed(43)).to(c.q.dtype).cuda()
+    B, N, H, Q, K, D = c.shape
+    desc = nat.TriAttnMask()
+    desc.kind = nat.TRIATTN_MASK_KV_LENGTHS
+    desc.kv_lengths = c.kv_lengths.data_ptr()
+    shape = nat.TriAttnShape(B, N, H, Q, K, D)
+    dt = nat.DTYPE_CODES[c.q.dtype]
+    out, lse, mx = torch.empty_like(c.q), torch.empty(B, N, H, Q, device="cuda"), \
+        torch.empty(B, N, H, Q, device="cuda")
+    dq, dk, dv = torch.empty_like(c.q), torch.empty_like(c.k), torch.empty_like(c.v)
+    db = torch.empty_like(c.bias)
+
+    def run(stream):
+        assert mat.tri_attn_fwd(shape, dt, c.q, c.k, c.v, c.bias, desc, math.nan, out, lse, mx,
+                                stream) == mat.TRIATTN_OK
+        assert mat.tri_attn_bwd(shape, dt, c.q, c.k, c.v, c.bias, desc, math.nan, out, dout,
+                                lse, mx, dq, dk, dv, db, stream) == mat.TRIATTN_OK
+
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        run(side)
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (out, lse, mx, dq, dk, dv, db)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        run(side)
+    for rep in range(3):
+        for t in (out, lse, mx, dq, dk, dv, db):
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (out, lse, mx, dq, dk, dv, db)
+        assert all(torch.equal(a, b) for a, b in zip(got, eager)), f"replay {rep} differs"
+        torch.cuda.synchronize()
+        _ = (c.q.float() * 2).sum().item()  # eager work between replays
