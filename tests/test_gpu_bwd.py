@@ -115,3 +115,31 @@ def test_autograd_wrapper(four_d):
         bound = 2e-2 * (1 + float(np.abs(want).max()))
         say(f"autograd {name}: err {err:.3g} bound {bound:.3g}")
         assert err <= bound, f"{name}: {err} > {bound}"
+
+
+def test_backward_headline_size_sampled():
+    """The headline workload at full size (B1 N768 H4 Q=K=768 D64, bf16,
+    kv_lengths): the GPU backward of every slice, with dQ, dK and dV of the
+    first two n compared element by element with the oracle run on those
+    slices alone (each (b, n, h) slice's dQ, dK, dV depend only on that
+    slice; dBias, a sum over all n, is checked on the smaller cases)."""
+    c = wl.make_workload("bf16_lens_d64")
+    say(f"backward sampled {c.name}")
+    g = torch.Generator().manual_seed(47)
+    dout = torch.randn(c.q.shape, generator=g).to(c.q.dtype)
+    gc = c.to("cuda")
+    out, lse, mx = mat.triangle_attention(gc.q, gc.k, gc.v, gc.bias, scale=gc.scale,
+                                          return_aux=True, kv_lengths=gc.kv_lengths)
+    dq, dk, dv, _ = mat.triangle_attention_backward(gc.q, gc.k, gc.v, gc.bias, out, dout.cuda(),
+                                                    lse, mx, scale=gc.scale,
+                                                    kv_lengths=gc.kv_lengths)
+    torch.cuda.synchronize()
+    ns = 2
+    ref = orc.oracle_bwd(c.q[:, :ns], c.k[:, :ns], c.v[:, :ns], c.bias, dout=dout[:, :ns],
+                         kv_lengths=c.kv_lengths[:, :ns], scale=c.scale)
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        got = got[:, :ns].cpu().double().numpy()
+        err = float(np.abs(got - want).max())
+        bound = 2e-2 * (1 + float(np.abs(want).max()))
+        say(f"headline sampled {name}: err {err:.3g} bound {bound:.3g}")
+        assert err <= bound, f"{name}: {err} > {bound}"
