@@ -113,6 +113,17 @@ def traffic_entry(workload):
     return t
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, target_s):
     """Time the fp64 oracle on the first n rows of the workload."""
     import numpy as np
@@ -122,14 +133,35 @@ def cpu_baseline(case, target_s):
 
     B, N, H, Q, K, D = case.shape
     threads = oracle.default_threads()
+    blk = None
+    if case.block is not None:
+        # BlockMask lists with leading dims (B|1, N|1, H|1), flattened to
+        # instances with strides (0 broadcasts)
+        b = case.block
+        lb, ln, lh = b.kv_num_blocks.shape[:3]
+        sh = 1 if lh == H and H > 1 else 0
+        sn = lh if ln == N and N > 1 else 0
+        sb = ln * lh if lb == B and B > 1 else 0
+        rows = b.kv_num_blocks.shape[3]
+        flat = lambda t, *tail: None if t is None else t.reshape(-1, rows, *tail).cpu()
+        blk = oracle.OracleBlockMask(
+            flat(b.kv_num_blocks), flat(b.kv_indices, b.kv_indices.shape[-1]),
+            flat(b.full_kv_num_blocks),
+            None if b.full_kv_indices is None else flat(b.full_kv_indices,
+                                                       b.full_kv_indices.shape[-1]),
+            q_block=b.q_block, kv_block=b.kv_block,
+            mask_mod=oracle.MOD_CAUSAL if b.mask_mod == "causal" else oracle.MOD_NONE,
+            stride_b=sb, stride_n=sn, stride_h=sh)
 
     def run(ns):
+        if blk is not None and blk.stride_n != 0:
+            ns = N  # per-n lists: the instance strides assume every n
         sub_q, sub_k, sub_v = case.q[:, :ns], case.k[:, :ns], case.v[:, :ns]
         lens = case.kv_lengths[:, :ns] if case.kv_lengths is not None else None
         mask = case.mask[:, :ns] if case.mask is not None else None
         t0 = time.perf_counter()
         out = oracle.oracle_fwd(sub_q, sub_k, sub_v, case.bias, kv_lengths=lens, mask=mask,
-                                scale=case.scale, threads=threads)
+                                block=blk, scale=case.scale, threads=threads)
         return time.perf_counter() - t0, out
 
     dt1, _ = run(1)
@@ -287,7 +319,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    # HIP events on the stream the kernel is launched on.
+    # HIP events on the stream the kernel is launched on, around the K steps.
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -299,6 +331,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
+    # A second pass, after the timed one, with an event after every step for
+    # the median and minimum step time (the extra events add gaps between
+    # launches, so they stay out of the timed pass).
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     print(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall:.3f} s)",
           file=sys.stderr, flush=True)
 
@@ -324,6 +366,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_median": round(per_step[len(per_step) // 2], 5),
+        "ms_min": round(per_step[0], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -356,12 +400,27 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
         cb, ns, oracle_out = cpu_baseline(case, args.cpu_seconds)
-        # the same rows of the GPU result, for reference
+        # the same rows of the GPU result against the oracle: O max-abs
+        # against the unrounded fp64 oracle, lse and max against the oracle
+        # rounded to fp32
         import numpy as np
 
         go = out[:, :ns].double().cpu().numpy()
-        cb["max_abs_err_O_vs_gpu"] = float(np.abs(go - oracle_out[0]).max())
+        gl = lse[:, :ns].double().cpu().numpy()
+        gm = mx[:, :ns].double().cpu().numpy()
+        f32 = lambda a: np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+        err_o = float(np.abs(go - oracle_out[0]).max())
+        err_l = float(np.abs(gl - f32(oracle_out[1])).max())
+        err_m = float(np.abs(gm - f32(oracle_out[2])).max())
+        tol = ({"o": 1e-5, "lse": 1e-5, "max": 1e-5} if case.dtype == torch.float32
+               else {"o": 2e-2, "lse": 1e-3, "max": 1e-3})
+        cb["max_abs_err_O_vs_gpu"] = err_o
+        cb["cpu_model"] = cpu_model()
         res["cpu_baseline"] = cb
+        res["parity"] = {"rows": f"first {ns} of {N} n rows (all b, h, q)", "err_O": err_o,
+                         "err_lse": err_l, "err_max": err_m, "tol": tol,
+                         "pass": err_o <= tol["o"] and err_l <= tol["lse"]
+                         and err_m <= tol["max"]}
     print(json.dumps(res), flush=True)
 
 
