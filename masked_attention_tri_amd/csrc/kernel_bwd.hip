@@ -26,14 +26,15 @@
 // contractions run as fp32 FMAs from LDS.
 #include <math.h>
 
+#include <type_traits>
+
 #include "triattn_internal.h"
 
 namespace triattn {
 namespace {
 
-// Each thread accumulates columns d = part + 8 i of one row, i < 8 kOut:
-// kOut = 4 covers D <= 256.
-constexpr int kOut = 4;
+// Each thread accumulates columns d = part + 8 i of one row, i < NC (a
+// template parameter: D <= 8 NC, NC in {4, 8, 16, 32}).
 
 template <typename T>
 __device__ __forceinline__ float f32(T x) {
@@ -135,9 +136,11 @@ size_t lds_bytes(int64_t D) {
 template <typename T>
 __device__ __forceinline__ void stage(float* dst, const T* src, int64_t r0, int64_t rows_total,
                                       int64_t D) {
-    for (int64_t e = threadIdx.x; e < kT * D; e += kThreads) {
-        const int64_t r = e / D, d = e % D;
-        dst[r * (D + 1) + d] = r0 + r < rows_total ? f32(src[(r0 + r) * D + d]) : 0.f;
+    const int d32 = static_cast<int>(D);
+    const int64_t valid_rows = rows_total - r0;  // rows of this tile that exist
+    for (int e = threadIdx.x; e < kT * d32; e += kThreads) {
+        const int r = e / d32, d = e - r * d32;
+        dst[r * (d32 + 1) + d] = r < valid_rows ? f32(src[(r0 + r) * D + d]) : 0.f;
     }
 }
 
@@ -165,21 +168,85 @@ __device__ __forceinline__ void stage_rows(const Params& p, const BwdParams& g, 
     }
 }
 
-// P and dz of the tile's pairs, from the staged rows (see Tiles).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <typename T>
+struct Mma;
+template <>
+struct Mma<__bf16> {
+    using v8 = bf16x8;
+    static __device__ __forceinline__ f32x16 run(v8 a, v8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mma<_Float16> {
+    using v8 = f16x8;
+    static __device__ __forceinline__ f32x16 run(v8 a, v8 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// One wave: dst[j][i] = sum_d a[i][d] b[j][d] for the 32 staged rows of a
+// and of b (fp32 in LDS, stride ld), on v_mfma_f32_32x32x16 with a as the A
+// operand and b transposed as the B operand.  The staged values are exact
+// conversions of T, so converting them back is exact.  Lane l supplies row
+// l % 32, coordinates 16 st + 8 (l / 32) .. + 7 (zero past D); its result
+// register r is dst[l % 32][8 (r / 4) + 4 (l / 32) + r % 4].
+template <typename T>
+__device__ __forceinline__ void mfma_rows(const float* a, const float* b, int64_t D, int64_t ld,
+                                          float* dst) {
+    using M = Mma<T>;
+    using v8 = typename M::v8;
+    const int lane = threadIdx.x & 63, row = lane & 31, half = lane >> 5;
+    f32x16 acc = {};
+    for (int64_t st = 0; st < D; st += 16) {
+        v8 va, vb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t d = st + 8 * half + e;
+            va[e] = static_cast<T>(d < D ? a[row * ld + d] : 0.f);
+            vb[e] = static_cast<T>(d < D ? b[row * ld + d] : 0.f);
+        }
+        acc = M::run(va, vb, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[row * (kT + 1) + 8 * (r / 4) + 4 * half + (r % 4)] = acc[r];
+}
+
+// P and dz of the tile's pairs, from the staged rows (see Tiles).  z = Q.K
+// and dP = dO.V come from two MFMA waves for the half types (through the ps
+// and dzs arrays, which every thread then overwrites only at its own
+// pairs), and from fp32 FMAs for fp32 inputs.  Every thread of the
+// workgroup must call it (it holds a barrier for the half types).
+template <typename T>
 __device__ __forceinline__ void pair_tile(const Params& p, Tiles t, int64_t b, int64_t n,
                                           int64_t h, int64_t q0, int64_t k0) {
     const int64_t D = p.D, ld = D + 1;
     const int ql = threadIdx.x >> 3, kb = threadIdx.x & 7;
     float z[4] = {0.f, 0.f, 0.f, 0.f}, dp[4] = {0.f, 0.f, 0.f, 0.f};
-    const float* qr = t.qs + ql * ld;
-    const float* gr = t.gos + ql * ld;
-    for (int64_t d = 0; d < D; ++d) {
-        const float qd = qr[d], gd = gr[d];
+    if constexpr (std::is_same<T, float>::value) {
+        const float* qr = t.qs + ql * ld;
+        const float* gr = t.gos + ql * ld;
+        for (int64_t d = 0; d < D; ++d) {
+            const float qd = qr[d], gd = gr[d];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int kl = kb + 8 * j;
+                z[j] = fmaf(qd, t.ks[kl * ld + d], z[j]);
+                dp[j] = fmaf(gd, t.vs[kl * ld + d], dp[j]);
+            }
+        }
+    } else {
+        const int wave = threadIdx.x >> 6;
+        if (wave == 0) mfma_rows<T>(t.ks, t.qs, D, ld, t.ps);
+        if (wave == 1) mfma_rows<T>(t.vs, t.gos, D, ld, t.dzs);
+        __syncthreads();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int kl = kb + 8 * j;
-            z[j] = fmaf(qd, t.ks[kl * ld + d], z[j]);
-            dp[j] = fmaf(gd, t.vs[kl * ld + d], dp[j]);
+            z[j] = t.ps[ql * (kT + 1) + kb + 8 * j];
+            dp[j] = t.dzs[ql * (kT + 1) + kb + 8 * j];
         }
     }
     const int64_t qi = q0 + ql;
@@ -206,7 +273,7 @@ __device__ __forceinline__ void pair_tile(const Params& p, Tiles t, int64_t b, i
 
 // dQ: one workgroup per (b, n, h, 32 query rows); loops over key tiles.
 // Thread t owns row t / 8 and columns d = t % 8 + 8 i.
-template <typename T>
+template <typename T, int NC>
 __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
     extern __shared__ float lds[];
     const int64_t D = p.D, ld = D + 1;
@@ -218,22 +285,22 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
     stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
     stage_rows<T>(p, g, t, bnh, q0);
     const int r = threadIdx.x >> 3, part = threadIdx.x & 7;
-    float acc[kOut * 8];
+    float acc[NC];
 #pragma unroll
-    for (int i = 0; i < kOut * 8; ++i) acc[i] = 0.f;
+    for (int i = 0; i < NC; ++i) acc[i] = 0.f;
     const int64_t k_end = key_limit(p, b, n);  // dz is 0 past it (and everywhere if 0)
     for (int64_t k0 = 0; k0 < k_end; k0 += kT) {
         __syncthreads();  // previous tile's reads done
         stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
         stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
         __syncthreads();
-        pair_tile(p, t, b, n, h, q0, k0);
+        pair_tile<T>(p, t, b, n, h, q0, k0);
         __syncthreads();
         for (int kl = 0; kl < kT; ++kl) {
             const float dz = t.dzs[r * (kT + 1) + kl];
             const float* kr = t.ks + kl * ld;
 #pragma unroll
-            for (int i = 0; i < kOut * 8; ++i) {
+            for (int i = 0; i < NC; ++i) {
                 const int64_t d = part + 8 * i;
                 if (d < D) acc[i] = fmaf(dz, kr[d], acc[i]);
             }
@@ -243,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
     if (qi >= p.Q) return;
     T* dqr = static_cast<T*>(g.dq) + (bnh * p.Q + qi) * D;
 #pragma unroll
-    for (int i = 0; i < kOut * 8; ++i) {
+    for (int i = 0; i < NC; ++i) {
         const int64_t d = part + 8 * i;
         if (d < D) dqr[d] = static_cast<T>(acc[i] * p.scale);
     }
@@ -251,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
 
 // dK and dV: one workgroup per (b, n, h, 32 keys); loops over query tiles.
 // Thread t owns key t / 8 and columns d = t % 8 + 8 i.
-template <typename T>
+template <typename T, int NC>
 __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
     extern __shared__ float lds[];
     const int64_t D = p.D, ld = D + 1;
@@ -262,9 +329,9 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
     stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
     stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
     const int kr = threadIdx.x >> 3, part = threadIdx.x & 7;
-    float dk[kOut * 8], dv[kOut * 8];
+    float dk[NC], dv[NC];
 #pragma unroll
-    for (int i = 0; i < kOut * 8; ++i) dk[i] = dv[i] = 0.f;
+    for (int i = 0; i < NC; ++i) dk[i] = dv[i] = 0.f;
     // A key tile at or past a nonzero length limit gets P = dz = 0 from every
     // row: dK = dV = 0 without the loop (a zero limit means rows without a
     // valid key, whose uniform weights reach every key).
@@ -276,14 +343,14 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
         stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
         stage_rows<T>(p, g, t, bnh, q0);
         __syncthreads();
-        pair_tile(p, t, b, n, h, q0, k0);
+        pair_tile<T>(p, t, b, n, h, q0, k0);
         __syncthreads();
         for (int ql = 0; ql < kT; ++ql) {
             const float pr = t.ps[ql * (kT + 1) + kr], dz = t.dzs[ql * (kT + 1) + kr];
             const float* qrow = t.qs + ql * ld;
             const float* grow = t.gos + ql * ld;
 #pragma unroll
-            for (int i = 0; i < kOut * 8; ++i) {
+            for (int i = 0; i < NC; ++i) {
                 const int64_t d = part + 8 * i;
                 if (d < D) {
                     dv[i] = fmaf(pr, grow[d], dv[i]);
@@ -297,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
     T* dkr = static_cast<T*>(g.dk) + (bnh * p.K + kk) * D;
     T* dvr = static_cast<T*>(g.dv) + (bnh * p.K + kk) * D;
 #pragma unroll
-    for (int i = 0; i < kOut * 8; ++i) {
+    for (int i = 0; i < NC; ++i) {
         const int64_t d = part + 8 * i;
         if (d < D) {
             dkr[d] = static_cast<T>(dk[i] * p.scale);
@@ -308,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
 
 // dBias: one workgroup per (b, h, 32 query rows, 32 keys); loops over n and
 // sums dz; thread t owns the pairs of pair_tile.
-template <typename T>
+template <typename T, int NC>
 __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) {
     extern __shared__ float lds[];
     const int64_t D = p.D;
@@ -330,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
         stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
         stage_rows<T>(p, g, t, bnh, q0);
         __syncthreads();
-        pair_tile(p, t, b, n, h, q0, k0);
+        pair_tile<T>(p, t, b, n, h, q0, k0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] += t.dzs[ql * (kT + 1) + kb + 8 * j];
     }
@@ -344,8 +411,8 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
     }
 }
 
-template <typename T>
-hipError_t launch_t(const Params& p, const BwdParams& g, hipStream_t stream) {
+template <typename T, int NC>
+hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
     const int64_t n_qt = (p.Q + kT - 1) / kT, n_kt = (p.K + kT - 1) / kT;
     const int64_t gq = p.B * p.N * p.H * n_qt, gk = p.B * p.N * p.H * n_kt,
                   gb = p.B * p.H * n_qt * n_kt;
@@ -356,23 +423,31 @@ hipError_t launch_t(const Params& p, const BwdParams& g, hipStream_t stream) {
     if (shm > 65536) {
         // more than 64 KiB of LDS per workgroup (D > 64; gfx950 has 160 KiB)
         const int b = static_cast<int>(shm);
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dq_kernel<T>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(dq_kernel<T, NC>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, b);
         if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(dkdv_kernel<T>),
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(dkdv_kernel<T, NC>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, b);
         if (e == hipSuccess)
-            e = hipFuncSetAttribute(reinterpret_cast<const void*>(dbias_kernel<T>),
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(dbias_kernel<T, NC>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, b);
         if (e != hipSuccess) return e;
     }
     if (gq > 0)
-        hipLaunchKernelGGL(dq_kernel<T>, dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
+        hipLaunchKernelGGL((dq_kernel<T, NC>), dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
     if (gk > 0)
-        hipLaunchKernelGGL(dkdv_kernel<T>, dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
+        hipLaunchKernelGGL((dkdv_kernel<T, NC>), dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
     if (g.dbias && gb > 0)
-        hipLaunchKernelGGL(dbias_kernel<T>, dim3(static_cast<unsigned>(gb)), block, shm, stream, p, g);
+        hipLaunchKernelGGL((dbias_kernel<T, NC>), dim3(static_cast<unsigned>(gb)), block, shm, stream, p, g);
     return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const Params& p, const BwdParams& g, hipStream_t stream) {
+    if (p.D <= 32) return launch_nc<T, 4>(p, g, stream);
+    if (p.D <= 64) return launch_nc<T, 8>(p, g, stream);
+    if (p.D <= 128) return launch_nc<T, 16>(p, g, stream);
+    return launch_nc<T, 32>(p, g, stream);
 }
 
 }  // namespace
