@@ -215,6 +215,38 @@ __device__ __forceinline__ void mfma_rows(const float* a, const float* b, int64_
     for (int r = 0; r < 16; ++r) dst[row * (kT + 1) + 8 * (r / 4) + 4 * half + (r % 4)] = acc[r];
 }
 
+// acc += A . B over c < 32 on v_mfma_f32_32x32x16, for the 32-column block
+// jb of the output: A(i, c) = a[i ars + c acs] (i < 32), B(c, j) =
+// b[c brs + j] with j = 32 jb + lane % 32 (zero at j >= D); A and B are
+// rounded to T (P and dz enter the contraction in the input type, the
+// usual choice).  Lane l then holds out[8 (r / 4) + 4 (l / 32) + r % 4][j]
+// in register r.
+template <typename T>
+__device__ __forceinline__ f32x16 mfma_acc(f32x16 acc, const float* a, int ars, int acs,
+                                           const float* b, int64_t brs, int jb, int64_t D) {
+    using M = Mma<T>;
+    using v8 = typename M::v8;
+    const int lane = threadIdx.x & 63, row = lane & 31, half = lane >> 5;
+    const int64_t j = 32 * jb + row;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        v8 va, vb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = 16 * st + 8 * half + e;
+            va[e] = static_cast<T>(a[row * ars + c * acs]);
+            vb[e] = static_cast<T>(j < D ? b[c * brs + j] : 0.f);
+        }
+        acc = M::run(va, vb, acc);
+    }
+    return acc;
+}
+
+// Row index of register r of lane l in an MFMA result block.
+__device__ __forceinline__ int mfma_row(int r, int lane) {
+    return 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+}
+
 // P and dz of the tile's pairs, from the staged rows (see Tiles).  z = Q.K
 // and dP = dO.V come from two MFMA waves for the half types (through the ps
 // and dzs arrays, which every thread then overwrites only at its own
@@ -285,9 +317,17 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
     stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
     stage_rows<T>(p, g, t, bnh, q0);
     const int r = threadIdx.x >> 3, part = threadIdx.x & 7;
-    float acc[NC];
+    constexpr bool kMfma = !std::is_same<T, float>::value;
+    // half types: wave w accumulates the 32-column blocks w, w + 4, ... of dQ
+    constexpr int kPer = NC >= 32 ? 2 : 1;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n_jb = static_cast<int>((D + 31) / 32);
+    f32x16 macc[kPer];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) acc[i] = 0.f;
+    for (int m = 0; m < kPer; ++m) macc[m] = f32x16{};
+    float acc[kMfma ? 1 : NC];
+#pragma unroll
+    for (int i = 0; i < (kMfma ? 1 : NC); ++i) acc[i] = 0.f;
     const int64_t k_end = key_limit(p, b, n);  // dz is 0 past it (and everywhere if 0)
     for (int64_t k0 = 0; k0 < k_end; k0 += kT) {
         __syncthreads();  // previous tile's reads done
@@ -296,21 +336,46 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
         __syncthreads();
         pair_tile<T>(p, t, b, n, h, q0, k0);
         __syncthreads();
-        for (int kl = 0; kl < kT; ++kl) {
-            const float dz = t.dzs[r * (kT + 1) + kl];
-            const float* kr = t.ks + kl * ld;
+        if constexpr (kMfma) {
+            // dQ(q, d) += sum_k dz(q, k) K(k, d)
 #pragma unroll
-            for (int i = 0; i < NC; ++i) {
-                const int64_t d = part + 8 * i;
-                if (d < D) acc[i] = fmaf(dz, kr[d], acc[i]);
+            for (int m = 0; m < kPer; ++m) {
+                const int jb = wave + 4 * m;
+                if (jb < n_jb) macc[m] = mfma_acc<T>(macc[m], t.dzs, kT + 1, 1, t.ks, ld, jb, D);
+            }
+        } else {
+            for (int kl = 0; kl < kT; ++kl) {
+                const float dz = t.dzs[r * (kT + 1) + kl];
+                const float* kr = t.ks + kl * ld;
+#pragma unroll
+                for (int i = 0; i < NC; ++i) {
+                    const int64_t d = part + 8 * i;
+                    if (d < D) acc[i] = fmaf(dz, kr[d], acc[i]);
+                }
             }
         }
+    }
+    if constexpr (kMfma) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int jb = wave + 4 * m;
+            const int64_t d = 32 * jb + (lane & 31);
+            if (jb >= n_jb || d >= D) continue;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int64_t qi = q0 + mfma_row(rr, lane);
+                if (qi < p.Q)
+                    static_cast<T*>(g.dq)[(bnh * p.Q + qi) * D + d] =
+                        static_cast<T>(macc[m][rr] * p.scale);
+            }
+        }
+        return;
     }
     const int64_t qi = q0 + r;
     if (qi >= p.Q) return;
     T* dqr = static_cast<T*>(g.dq) + (bnh * p.Q + qi) * D;
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
+    for (int i = 0; i < (kMfma ? 1 : NC); ++i) {
         const int64_t d = part + 8 * i;
         if (d < D) dqr[d] = static_cast<T>(acc[i] * p.scale);
     }
@@ -329,9 +394,20 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
     stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
     stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
     const int kr = threadIdx.x >> 3, part = threadIdx.x & 7;
-    float dk[NC], dv[NC];
+    constexpr bool kMfma = !std::is_same<T, float>::value;
+    // half types: waves 0-1 accumulate dV, waves 2-3 dK, each over the
+    // 32-column blocks (w % 2), (w % 2) + 2, ...
+    constexpr int kPer = NC >= 16 ? NC / 8 : 1;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n_jb = static_cast<int>((D + 31) / 32);
+    const bool wave_dk = wave >= 2;
+    f32x16 macc[kPer];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) dk[i] = dv[i] = 0.f;
+    for (int m = 0; m < kPer; ++m) macc[m] = f32x16{};
+    constexpr int kF = kMfma ? 1 : NC;
+    float dk[kF], dv[kF];
+#pragma unroll
+    for (int i = 0; i < kF; ++i) dk[i] = dv[i] = 0.f;
     // A key tile at or past a nonzero length limit gets P = dz = 0 from every
     // row: dK = dV = 0 without the loop (a zero limit means rows without a
     // valid key, whose uniform weights reach every key).
@@ -345,26 +421,53 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
         __syncthreads();
         pair_tile<T>(p, t, b, n, h, q0, k0);
         __syncthreads();
-        for (int ql = 0; ql < kT; ++ql) {
-            const float pr = t.ps[ql * (kT + 1) + kr], dz = t.dzs[ql * (kT + 1) + kr];
-            const float* qrow = t.qs + ql * ld;
-            const float* grow = t.gos + ql * ld;
+        if constexpr (kMfma) {
+            // dV(k, d) += sum_q P(q, k) dO(q, d);  dK(k, d) += sum_q dz(q, k) Q(q, d)
 #pragma unroll
-            for (int i = 0; i < NC; ++i) {
-                const int64_t d = part + 8 * i;
-                if (d < D) {
-                    dv[i] = fmaf(pr, grow[d], dv[i]);
-                    dk[i] = fmaf(dz, qrow[d], dk[i]);
+            for (int m = 0; m < kPer; ++m) {
+                const int jb = (wave & 1) + 2 * m;
+                if (jb < n_jb)
+                    macc[m] = wave_dk ? mfma_acc<T>(macc[m], t.dzs, 1, kT + 1, t.qs, ld, jb, D)
+                                      : mfma_acc<T>(macc[m], t.ps, 1, kT + 1, t.gos, ld, jb, D);
+            }
+        } else {
+            for (int ql = 0; ql < kT; ++ql) {
+                const float pr = t.ps[ql * (kT + 1) + kr], dz = t.dzs[ql * (kT + 1) + kr];
+                const float* qrow = t.qs + ql * ld;
+                const float* grow = t.gos + ql * ld;
+#pragma unroll
+                for (int i = 0; i < kF; ++i) {
+                    const int64_t d = part + 8 * i;
+                    if (d < D) {
+                        dv[i] = fmaf(pr, grow[d], dv[i]);
+                        dk[i] = fmaf(dz, qrow[d], dk[i]);
+                    }
                 }
             }
         }
+    }
+    if constexpr (kMfma) {
+        T* dst = static_cast<T*>(wave_dk ? g.dk : g.dv);
+        const float mul = wave_dk ? p.scale : 1.0f;
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int jb = (wave & 1) + 2 * m;
+            const int64_t d = 32 * jb + (lane & 31);
+            if (jb >= n_jb || d >= D) continue;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int64_t kk2 = k0 + mfma_row(rr, lane);
+                if (kk2 < p.K) dst[(bnh * p.K + kk2) * D + d] = static_cast<T>(macc[m][rr] * mul);
+            }
+        }
+        return;
     }
     const int64_t kk = k0 + kr;
     if (kk >= p.K) return;
     T* dkr = static_cast<T*>(g.dk) + (bnh * p.K + kk) * D;
     T* dvr = static_cast<T*>(g.dv) + (bnh * p.K + kk) * D;
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
+    for (int i = 0; i < kF; ++i) {
         const int64_t d = part + 8 * i;
         if (d < D) {
             dkr[d] = static_cast<T>(dk[i] * p.scale);
