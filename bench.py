@@ -216,6 +216,7 @@ def bench_backward(args, case, g, key, shape, dtype, desc, scale, out, lse, mx, 
     _, alg_fwd, _ = work_counts(case)
     alg = 2.5 * alg_fwd
     tflops = alg / (ms * 1e-3) / 1e12
+    peak = PEAK_FP32_VALU_TFLOPS if case.dtype == torch.float32 else PEAK_BF16_TFLOPS
     res = {
         "metric": "bwd TFLOP/s (10 D flops per visited query-key pair), triangle attn",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -225,10 +226,11 @@ def bench_backward(args, case, g, key, shape, dtype, desc, scale, out, lse, mx, 
         "data": "synthetic",
         "config": {"workload": case.name, "key": key, "B": B, "N": N, "H": H, "Q": Q, "K": K,
                    "D": D, "algorithmic_flop": alg},
-        # the backward kernels are plain fp32 vector code
-        "roofline": {"bound": "alu", "achieved": round(tflops, 3), "peak": PEAK_FP32_VALU_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP32_VALU_TFLOPS, 5),
-                     "traffic": None},
+        # bf16/fp16: every contraction of the backward runs on MFMA; fp32
+        # inputs run them as vector FMAs
+        "roofline": {"bound": "alu" if case.dtype == torch.float32 else "mfma",
+                     "achieved": round(tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 5), "traffic": None},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
