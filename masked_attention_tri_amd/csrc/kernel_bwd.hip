@@ -476,49 +476,62 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
     }
 }
 
-// dBias: one workgroup per (b, h, 32 query rows, 32 keys); loops over n and
-// sums dz; thread t owns the pairs of pair_tile.
+// dBias: one workgroup per (b, h, 32 query rows, kChunk key tiles); loops
+// over n (in order) and, for each n, over its key tiles, adding dz into its
+// own block of the output (zeroed first).  Q, dO and Delta are staged once
+// per n for all the key tiles of the chunk.  Deterministic: every element
+// is owned by one thread of one workgroup and summed in n order.
+constexpr int kChunk = 4;  // key tiles per dBias workgroup
+
 template <typename T, int NC>
 __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) {
     extern __shared__ float lds[];
     const int64_t D = p.D;
     const Tiles t = carve(lds, D);
-    const int64_t n_qt = (p.Q + kT - 1) / kT, n_kt = (p.K + kT - 1) / kT;
-    const int64_t bh = blockIdx.x / (n_qt * n_kt);
-    const int64_t q0 = ((blockIdx.x / n_kt) % n_qt) * kT, k0 = (blockIdx.x % n_kt) * kT;
+    const int64_t n_qt = (p.Q + kT - 1) / kT;
+    const int64_t n_kc = (p.K + kT * kChunk - 1) / (kT * kChunk);
+    const int64_t bh = blockIdx.x / (n_qt * n_kc);
+    const int64_t q0 = ((blockIdx.x / n_kc) % n_qt) * kT;
+    const int64_t kc0 = (blockIdx.x % n_kc) * kT * kChunk;
+    const int64_t kc1 = kc0 + kT * kChunk < p.K ? kc0 + kT * kChunk : p.K;
     const int64_t h = bh % p.H, b = bh / p.H;
     const int ql = threadIdx.x >> 3, kb = threadIdx.x & 7;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t qi = q0 + ql;
+    float* dbr = g.dbias + (bh * p.Q + qi) * p.K;  // this thread's row (when qi < Q)
+    if (qi < p.Q)
+        for (int64_t kk = kc0 + kb; kk < kc1; kk += 8) dbr[kk] = 0.f;
     for (int64_t n = 0; n < p.N; ++n) {
         const int64_t bnh = (b * p.N + n) * p.H + h;
         const int64_t lim = key_limit(p, b, n);
-        if (lim == 0 || k0 >= lim) continue;  // dz = 0 for the whole tile (uniform)
+        const int64_t k_end = kc1 < lim ? kc1 : lim;  // dz = 0 at and past lim (all if 0)
+        if (k_end <= kc0) continue;  // uniform
         __syncthreads();
         stage(t.qs, static_cast<const T*>(p.q) + bnh * p.Q * D, q0, p.Q, D);
         stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
-        stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
-        stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
         stage_rows<T>(p, g, t, bnh, q0);
-        __syncthreads();
-        pair_tile<T>(p, t, b, n, h, q0, k0);
+        for (int64_t k0 = kc0; k0 < k_end; k0 += kT) {
+            __syncthreads();
+            stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
+            stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
+            __syncthreads();
+            pair_tile<T>(p, t, b, n, h, q0, k0);
+            if (qi < p.Q) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += t.dzs[ql * (kT + 1) + kb + 8 * j];
-    }
-    const int64_t qi = q0 + ql;
-    if (qi >= p.Q) return;
-    float* dbr = g.dbias + (bh * p.Q + qi) * p.K;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t kk = k0 + kb + 8 * j;
-        if (kk < p.K) dbr[kk] = acc[j];
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t kk = k0 + kb + 8 * j;
+                    if (kk < p.K) dbr[kk] += t.dzs[ql * (kT + 1) + kb + 8 * j];
+                }
+            }
+        }
     }
 }
 
 template <typename T, int NC>
 hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
     const int64_t n_qt = (p.Q + kT - 1) / kT, n_kt = (p.K + kT - 1) / kT;
+    const int64_t n_kc = (p.K + kT * kChunk - 1) / (kT * kChunk);
     const int64_t gq = p.B * p.N * p.H * n_qt, gk = p.B * p.N * p.H * n_kt,
-                  gb = p.B * p.H * n_qt * n_kt;
+                  gb = p.B * p.H * n_qt * n_kc;
     if (gq > 0x7fffffff || gk > 0x7fffffff || gb > 0x7fffffff)
         return hipErrorInvalidConfiguration;
     const size_t shm = lds_bytes(p.D);
