@@ -262,8 +262,8 @@ def bench_backward(args, case, g, key, shape, dtype, desc, scale, out, lse, mx, 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build "
-              "has no multi-GPU path)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library "
+              "has no multi-GPU path: rows shard over N with no exchange step)", file=sys.stderr)
         sys.exit(2)
 
     import torch
