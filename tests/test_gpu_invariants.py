@@ -1,8 +1,11 @@
 """GPU invariants of the library that hold at any size (mostly bitwise)."""
 import math
 
+import numpy as np
 import pytest
 import torch
+
+import oracle as orc
 
 import masked_attention_tri_amd as mat
 from masked_attention_tri_amd import _native as nat
@@ -219,3 +222,28 @@ def test_graph_capture_replays_match_eager():
         assert all(torch.equal(a, b) for a, b in zip(got, eager)), f"replay {rep} differs"
         torch.cuda.synchronize()
         _ = (c.q.float() * 2).sum().item()  # eager work between replays
+
+
+def test_slices_past_32_bit_offsets():
+    """K = 2^24 keys at D = 64 (each (b, n, h) slice of k and v is 2 GiB, so
+    offsets pass 2^31 bytes): the library routes this to the kernel with
+    64-bit addressing, and with every length at most 100 the result must
+    equal the oracle on the first 100 keys alone (later keys never count)."""
+    say("K = 2^24, D = 64, bf16, kv_lengths <= 100")
+    B, N, H, Q, K, D = 1, 1, 2, 8, 1 << 24, 64
+    g = torch.Generator(device="cuda").manual_seed(53)
+    q = torch.randn(B, N, H, Q, D, device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn(B, N, H, K, D, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(B, N, H, K, D, device="cuda", generator=g).to(torch.bfloat16)
+    lens = torch.tensor([77], dtype=torch.int32, device="cuda").view(1, 1, 1, 1, 1)
+    out, lse, mx = mat.triangle_attention(q, k, v, None, kv_lengths=lens, return_aux=True)
+    torch.cuda.synchronize()
+    k100, v100 = k[:, :, :, :100].cpu(), v[:, :, :, :100].cpu()
+    del k, v
+    O, L, M = orc.oracle_fwd(q.cpu(), k100, v100, None, kv_lengths=lens.cpu(),
+                             scale=1 / math.sqrt(D))
+    assert np.abs(out.cpu().double().numpy() - O).max() <= TOL[torch.bfloat16]["o"]
+    assert np.abs(lse.cpu().double().numpy().reshape(L.shape)
+                  - L.astype(np.float32)).max() <= TOL[torch.bfloat16]["lse"]
+    assert np.abs(mx.cpu().double().numpy().reshape(M.shape)
+                  - M.astype(np.float32)).max() <= TOL[torch.bfloat16]["mx"]
