@@ -191,17 +191,29 @@ triattn_status tri_attn_fwd(const tri_attn_shape* shape, int32_t dtype, const vo
  * (B,N,H,K,D), all of type `dtype` and 16-byte aligned; dbias (B,1,H,Q,K)
  * fp32, or NULL to skip it.  All device memory; enqueued on `stream`.
  *
+ * Workspace (used only when dbias is not NULL): NULL, or device memory of
+ * at least 4*B*N*H*Q*K bytes, 16-byte aligned, caller-owned, whose contents
+ * on entry do not matter and on return are unspecified.  With it, the dQ
+ * pass stores every dz and dbias is their sum over n, read back at HBM
+ * bandwidth; without it, dbias is recomputed per block by a latency-bound
+ * walk over n (no extra memory).  Both routes add the same values in the
+ * same order (n ascending) and give the same bits.  Calls that share one
+ * workspace must not overlap.
+ *
  * Errors: those of tri_attn_check for the forward's arguments, and
  * TRIATTN_ERR_INVALID_ARG for a NULL dout / lse / max / dq / dk / dv when
- * there is a query row, or a misaligned one; nothing is launched then.
- * TRIATTN_ERR_HIP if a launch fails.  With no query row the call does
- * nothing.  The kernels compute in fp32 (plain vector code).
+ * there is a query row, a misaligned pointer, or a workspace smaller than
+ * the size above (TRIATTN_ERR_UNSUPPORTED if that size overflows int64);
+ * nothing is launched then.  TRIATTN_ERR_HIP if a launch fails.  With no
+ * query row the call does nothing.  Products of bf16/fp16 tiles run on
+ * MFMA with fp32 accumulation, fp32 inputs on fp32 FMAs.
  */
 triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const void* q,
                             const void* k, const void* v, const float* bias,
                             const tri_attn_mask* mask, float scale, const void* out,
                             const void* dout, const float* lse, const float* max, void* dq,
-                            void* dk, void* dv, float* dbias, hipStream_t stream);
+                            void* dk, void* dv, float* dbias, float* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Count the valid prefix of each dense key-mask row: the page's

@@ -302,14 +302,24 @@ def mask_to_kv_lengths(mask):
     return lens.squeeze(0) if four_d else lens
 
 
+# Largest dz workspace triangle_attention_backward allocates by itself.
+_DBIAS_WORKSPACE_AUTO_BYTES = 16 << 30
+
+
 def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
                                 scale: Optional[float] = None, *, kv_lengths=None,
-                                block_mask: Optional[BlockMask] = None, stream=None):
+                                block_mask: Optional[BlockMask] = None, stream=None,
+                                dbias_workspace: Optional[bool] = None):
     """Gradients of O = triangle_attention(q, k, v, bias, mask, scale, ...)
     for the incoming gradient dout: returns (dq, dk, dv, dbias), dq/dk/dv in
     q's dtype and dbias fp32 of shape (B,1,H,Q,K) (None when bias is None).
     out, lse and mx are the forward's (O, lse, max) for the same arguments
     (from return_aux=True).  Every step runs in the library's HIP kernels.
+
+    dbias_workspace: give the library a 4*B*N*H*Q*K-byte workspace so that
+    dbias is summed from stored dz at HBM bandwidth (True) or recomputed
+    without extra memory (False); None picks True up to 16 GiB.  Both give
+    the same bits.
     """
     four_d, q5, k5, v5, bias5, desc, keep = _prepare(q, k, v, bias, mask, kv_lengths,
                                                      block_mask)
@@ -328,8 +338,13 @@ def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
     dbias = (torch.empty(B, 1, H, Q, K, device=q5.device, dtype=torch.float32)
              if bias5 is not None else None)
     s = math.nan if scale is None else float(scale)
+    ws_elems = B * N * H * Q * K
+    if dbias_workspace is None:
+        dbias_workspace = 4 * ws_elems <= _DBIAS_WORKSPACE_AUTO_BYTES
+    ws = (torch.empty(ws_elems, device=q5.device, dtype=torch.float32)
+          if dbias is not None and dbias_workspace and ws_elems > 0 else None)
     st = tri_attn_bwd(TriAttnShape(B, N, H, Q, K, D), _native.DTYPE_CODES[q5.dtype], q5, k5, v5,
-                      bias5, desc, s, o5, g5, lse5, mx5, dq, dk, dv, dbias, stream)
+                      bias5, desc, s, o5, g5, lse5, mx5, dq, dk, dv, dbias, stream, workspace=ws)
     if st != TRIATTN_OK:
         raise RuntimeError(f"tri_attn_bwd: {tri_attn_status_str(st)}")
     if four_d:

@@ -87,7 +87,8 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_fwd.restype = I32
     lib.tri_attn_fwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P]
     lib.tri_attn_bwd.restype = I32
-    lib.tri_attn_bwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P, P, P, P]
+    lib.tri_attn_bwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P, P, P, P,
+                                  ctypes.c_size_t, P]
     lib.tri_attn_mask_to_kv_lengths.restype = I32
     lib.tri_attn_mask_to_kv_lengths.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P]
     lib.tri_attn_status_str.restype = ctypes.c_char_p
@@ -143,8 +144,9 @@ def tri_attn_mask_to_kv_lengths(mask, rows: int, K: int, kv_lengths, nonprefix_r
 
 
 def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: float, out, dout,
-                 lse, mx, dq, dk, dv, dbias, stream) -> int:
-    """Enqueue the backward pass on `stream` (as tri_attn_fwd)."""
+                 lse, mx, dq, dk, dv, dbias, stream, workspace=None) -> int:
+    """Enqueue the backward pass on `stream` (as tri_attn_fwd); `workspace`
+    is a tensor of at least 4*B*N*H*Q*K bytes or None."""
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -152,4 +154,6 @@ def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: fl
         ctypes.byref(shape), int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
         ctypes.byref(mask) if mask is not None else None, ctypes.c_float(scale), _ptr(out),
         _ptr(dout), _ptr(lse), _ptr(mx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
+        _ptr(workspace),
+        ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size()),
         ctypes.c_void_p(handle)))

@@ -20,10 +20,14 @@
 //                key tiles: dQ = s dz K.
 //   dkdv_kernel  one (b, n, h, 32 keys), looping over query tiles:
 //                dV = P^T dO, dK = s dz^T Q.
-//   dbias_kernel one (b, h, 32 query rows, 32 keys), looping over n: the sum
-//                of dz.
-// Global memory is read only by coalesced tile loads.  Not MFMA code: the
-// contractions run as fp32 FMAs from LDS.
+//   dbias_kernel one (b, h, 32 query rows, 128 keys), looping over n: the
+//                sum of dz, recomputed per n.
+// With a dz workspace, dq_kernel also stores every dz it computes (fp32,
+// (B,N,H,Q,K)) and dbias_sum_kernel sums it over n instead of dbias_kernel:
+// the same values added in the same order, so the two routes give the same
+// bits; the workspace route is bound by HBM bandwidth, the other by latency.
+// Global memory is read by coalesced tile loads.  The contractions run on
+// MFMA for bf16/fp16 and as fp32 FMAs from LDS for fp32.
 #include <math.h>
 
 #include <type_traits>
@@ -335,6 +339,15 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
         stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
         __syncthreads();
         pair_tile<T>(p, t, b, n, h, q0, k0);
+        if (g.dz && q0 + r < p.Q) {
+            // this thread's own pairs (row r, keys part + 8 j), as pair_tile stored them
+            float* zr = g.dz + (bnh * p.Q + q0 + r) * p.K;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t kk = k0 + part + 8 * j;
+                if (kk < p.K) zr[kk] = t.dzs[r * (kT + 1) + part + 8 * j];
+            }
+        }
         __syncthreads();
         if constexpr (kMfma) {
             // dQ(q, d) += sum_k dz(q, k) K(k, d)
@@ -526,6 +539,26 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
     }
 }
 
+// dBias from the dz workspace: one thread per (b, h, q, k), summing over n
+// in order (dz is 0 at and past a row's key limit, where dq_kernel stored
+// nothing).  Consecutive threads take consecutive keys: every load of the
+// sum is one coalesced row segment.
+__global__ __launch_bounds__(256) void dbias_sum_kernel(Params p, BwdParams g) {
+    const int64_t total = p.B * p.H * p.Q * p.K;
+    const int64_t plane = p.H * p.Q * p.K;  // stride of n in the workspace
+    for (int64_t e = blockIdx.x * int64_t(256) + threadIdx.x; e < total;
+         e += int64_t(gridDim.x) * 256) {
+        const int64_t kk = e % p.K, bhq = e / p.K;
+        const int64_t b = bhq / (p.H * p.Q), hq = bhq % (p.H * p.Q);
+        const float* src = g.dz + b * p.N * plane + hq * p.K + kk;
+        float acc = 0.f;
+#pragma unroll 8
+        for (int64_t n = 0; n < p.N; ++n)
+            if (kk < key_limit(p, b, n)) acc += src[n * plane];
+        g.dbias[e] = acc;
+    }
+}
+
 template <typename T, int NC>
 hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
     const int64_t n_qt = (p.Q + kT - 1) / kT, n_kt = (p.K + kT - 1) / kT;
@@ -553,8 +586,13 @@ hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
         hipLaunchKernelGGL((dq_kernel<T, NC>), dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
     if (gk > 0)
         hipLaunchKernelGGL((dkdv_kernel<T, NC>), dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
-    if (g.dbias && gb > 0)
+    if (g.dbias && g.dz) {
+        const int64_t total = p.B * p.H * p.Q * p.K, want = (total + 255) / 256;
+        const unsigned gs = static_cast<unsigned>(want < (1 << 20) ? want : (1 << 20));
+        if (gs > 0) hipLaunchKernelGGL(dbias_sum_kernel, dim3(gs), dim3(256), 0, stream, p, g);
+    } else if (g.dbias && gb > 0) {
         hipLaunchKernelGGL((dbias_kernel<T, NC>), dim3(static_cast<unsigned>(gb)), block, shm, stream, p, g);
+    }
     return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ struct BwdParams {
     void* dk;
     void* dv;
     float* dbias;
+    float* dz;  // (B,N,H,Q,K) fp32 dz from dq_kernel for the dBias sum, or null
 };
 
 // Masked logits are carried as -inf inside the kernels: when a row has at

@@ -2,6 +2,7 @@
 declared in include/*.h, and tri_attn_check (a pure host function) returns
 the documented status for each invalid-argument case.  No compute call is
 made here."""
+import ctypes
 import glob
 import math
 import os
@@ -232,3 +233,24 @@ def test_triangle_attention_argument_errors():
                                kv_lengths=torch.ones(1, 2, 1, 1, 1, dtype=torch.int32))
     with pytest.raises(ValueError):  # there is no CPU path
         mat.triangle_attention(q, q, q, None)
+
+
+def _bwd(shp, dbias=A, ws=None, ws_bytes=0):
+    lib = nat.load_library()
+    return lib.tri_attn_bwd(ctypes.byref(shp), nat.TRIATTN_BF16, A, A, A, A, None,
+                            ctypes.c_float(math.nan), A, A, A, A, A, A, A, dbias, ws,
+                            ctypes.c_size_t(ws_bytes), None)
+
+
+def test_bwd_workspace_validation():
+    """The dz workspace must hold 4 B N H Q K bytes and be 16-byte aligned;
+    a failing check launches nothing (these calls make no device call)."""
+    shp = shape(B=1, N=2, H=2, Q=8, K=8, D=32)
+    need = 4 * 1 * 2 * 2 * 8 * 8
+    assert _bwd(shp, ws=A, ws_bytes=need - 1) == nat.TRIATTN_ERR_INVALID_ARG
+    assert _bwd(shp, ws=A + 4, ws_bytes=need) == nat.TRIATTN_ERR_INVALID_ARG
+    # no query row: nothing to do, whatever the workspace
+    assert _bwd(shape(Q=0), ws=A, ws_bytes=0) == nat.TRIATTN_OK
+    # int64 overflow of the workspace size
+    big = shape(B=1 << 20, N=1 << 20, H=1, Q=1 << 12, K=1 << 12, D=32)
+    assert _bwd(big, ws=A, ws_bytes=0) == nat.TRIATTN_ERR_UNSUPPORTED

@@ -143,3 +143,46 @@ def test_backward_headline_size_sampled():
         bound = 2e-2 * (1 + float(np.abs(want).max()))
         say(f"headline sampled {name}: err {err:.3g} bound {bound:.3g}")
         assert err <= bound, f"{name}: {err} > {bound}"
+
+
+def _both_routes(c, seed):
+    """dbias from the dz workspace and from the walk over n."""
+    g = torch.Generator().manual_seed(seed)
+    dout = torch.randn(c.q.shape, generator=g).to(c.q.dtype).cuda()
+    gc = c.to("cuda")
+    bm = block_mask_of(gc)
+    out, lse, mx = mat.triangle_attention(gc.q, gc.k, gc.v, gc.bias, mask=gc.mask,
+                                          scale=gc.scale, return_aux=True,
+                                          kv_lengths=gc.kv_lengths, block_mask=bm)
+    res = []
+    for ws in (True, False):
+        res.append(mat.triangle_attention_backward(
+            gc.q, gc.k, gc.v, gc.bias, out, dout, lse, mx, mask=gc.mask, scale=gc.scale,
+            kv_lengths=gc.kv_lengths, block_mask=bm, dbias_workspace=ws))
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("spec", [s for s in CASES if s[8].get("bias", True)],
+                         ids=[f"B{c[0]}N{c[1]}H{c[2]}Q{c[3]}K{c[4]}D{c[5]}-{c[6]}-{c[7]}"
+                              for c in CASES if c[8].get("bias", True)])
+def test_dbias_routes_agree_bitwise(spec):
+    """dbias summed from the stored dz (workspace) and recomputed by the walk
+    over n add the same fp32 values in the same order: equal bits, and the
+    other gradients do not depend on the route."""
+    B, N, H, Q, K, D, dt, kind, extra = spec
+    c = wl.make_case(B, N, H, Q, K, D, dt, kind, seed=19, **extra)
+    say(f"dbias routes {c.name}")
+    (a, b) = _both_routes(c, seed=59)
+    for name, x, y in zip(("dq", "dk", "dv", "dbias"), a, b):
+        assert torch.equal(x, y), f"{c.name} {name}: routes differ"
+
+
+def test_dbias_routes_agree_headline_size():
+    """The same equality at the headline size (B1 N768 H4 Q=K=768 D64, bf16,
+    kv_lengths U{384..768}): every n contributes to each dbias element."""
+    c = wl.make_workload("bf16_lens_d64")
+    say(f"dbias routes {c.name}")
+    (a, b) = _both_routes(c, seed=61)
+    assert torch.equal(a[3], b[3]), "dbias routes differ"
+    assert float(a[3].abs().max()) > 0

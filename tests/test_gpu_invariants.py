@@ -198,12 +198,13 @@ def test_graph_capture_replays_match_eager():
         torch.empty(B, N, H, Q, device="cuda")
     dq, dk, dv = torch.empty_like(c.q), torch.empty_like(c.k), torch.empty_like(c.v)
     db = torch.empty_like(c.bias)
+    ws = torch.empty(B * N * H * Q * K, device="cuda")
 
     def run(stream):
         assert mat.tri_attn_fwd(shape, dt, c.q, c.k, c.v, c.bias, desc, math.nan, out, lse, mx,
                                 stream) == mat.TRIATTN_OK
         assert mat.tri_attn_bwd(shape, dt, c.q, c.k, c.v, c.bias, desc, math.nan, out, dout,
-                                lse, mx, dq, dk, dv, db, stream) == mat.TRIATTN_OK
+                                lse, mx, dq, dk, dv, db, stream, workspace=ws) == mat.TRIATTN_OK
 
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
