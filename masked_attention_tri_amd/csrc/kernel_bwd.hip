@@ -17,7 +17,9 @@
 // Three fp32 vector kernels on 32 x 32 (query, key) tiles staged in LDS (see
 // Tiles below), no atomics:
 //   dq_kernel    one (b, n, h, 32 query rows) per workgroup, looping over
-//                key tiles: dQ = s dz K.
+//                key tiles: dQ = s dz K.  bf16/fp16 at D in {32, 64, 128}
+//                use dq_mfma_kernel instead (128 rows, operands in
+//                registers, see there).
 //   dkdv_kernel  one (b, n, h, 32 keys), looping over query tiles:
 //                dV = P^T dO, dK = s dz^T Q.
 //   dbias_kernel one (b, h, 32 query rows, 128 keys), looping over n: the
@@ -394,6 +396,180 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
     }
 }
 
+// dQ for bf16/fp16 at D in {32, 64, 128}: one workgroup of 4 waves per
+// (b, n, h, 128 query rows), wave w owning rows 32 w .. 32 w + 31.  Each
+// lane keeps one query row of Q and dO as MFMA operands in registers (lane
+// l: row l % 32, coordinates 16 st + 8 (l / 32) + e), so z^T = K Q^T and
+// dP^T = V dO^T of a 32-key tile leave lane l with one query and 16 keys
+// (register r: key 8 (r / 4) + 4 (l / 32) + r % 4), P and dz are formed in
+// registers, and dQ^T += K^T dz^T takes dz straight from them: the
+// contraction over keys may run in any order as long as both operands use
+// the same one, so the A operand (K^T, from a transposed LDS copy) lists
+// the keys in the lanes' own order.  K and V tiles are double-buffered in
+// LDS and the next tile is loaded into registers while this one is used:
+// one barrier per tile.  Delta, lse and the no-valid-key flag come from
+// stage_rows, and z, dP, P and dz from the same MFMAs and expressions as
+// pair_tile, so the dz stored for dBias has the same bits as the one the
+// dBias walk recomputes.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void dq_mfma_kernel(Params p, BwdParams g) {
+    using M = Mma<T>;
+    using v8 = typename M::v8;
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    constexpr int kRows = 128;                 // query rows per workgroup
+    constexpr int LDK = D + 8;                 // K, V tile row stride (elements)
+    constexpr int LDT = kT + 8;                // transposed K tile row stride
+    constexpr int kChunks = kT * D / 8;        // 16-byte chunks per K (or V) tile
+    constexpr int kPerThr = (kChunks + kThreads - 1) / kThreads;
+    constexpr int kSt = D / 16, kJb = D / 32;
+    __shared__ __align__(16) T ks[2][kT * LDK];
+    __shared__ __align__(16) T vs[2][kT * LDK];
+    __shared__ __align__(16) T kts[2][D * LDT];
+    __shared__ float delta[kRows], lse[kRows], dead[kRows];
+
+    const int64_t n_qt = (p.Q + kRows - 1) / kRows;
+    const int64_t bnh = blockIdx.x / n_qt, q0 = (blockIdx.x % n_qt) * kRows;
+    const int64_t h = bnh % p.H, n = (bnh / p.H) % p.N, b = bnh / (p.H * p.N);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row = lane & 31, hf = lane >> 5;
+    const int ql = 32 * wave + row;            // this lane's query within the workgroup
+    const int64_t qi = q0 + ql;
+
+    {
+        Tiles t{};
+        for (int i = 0; i < kRows / kT; ++i) {
+            t.delta = delta + kT * i;
+            t.lse = lse + kT * i;
+            t.dead = dead + kT * i;
+            stage_rows<T>(p, g, t, bnh, q0 + kT * i);
+        }
+    }
+    const T* qb = static_cast<const T*>(p.q) + bnh * p.Q * D;
+    const T* gb = static_cast<const T*>(g.dout) + bnh * p.Q * D;
+    const T* kb = static_cast<const T*>(p.k) + bnh * p.K * D;
+    const T* vb = static_cast<const T*>(p.v) + bnh * p.K * D;
+    v8 qop[kSt], gop[kSt];
+#pragma unroll
+    for (int st = 0; st < kSt; ++st) {
+        qop[st] = v8{};
+        gop[st] = v8{};
+        if (qi < p.Q) {
+            qop[st] = *reinterpret_cast<const v8*>(qb + qi * D + 16 * st + 8 * hf);
+            gop[st] = *reinterpret_cast<const v8*>(gb + qi * D + 16 * st + 8 * hf);
+        }
+    }
+    f32x16 acc[kJb];
+#pragma unroll
+    for (int jb = 0; jb < kJb; ++jb) acc[jb] = f32x16{};
+
+    v8 kr[kPerThr], vr[kPerThr];
+    auto load = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < kPerThr; ++i) {
+            const int c = tid + kThreads * i;
+            const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+            kr[i] = v8{};
+            vr[i] = v8{};
+            if (c < kChunks && k0 + r < p.K) {
+                kr[i] = *reinterpret_cast<const v8*>(kb + (k0 + r) * D + col);
+                vr[i] = *reinterpret_cast<const v8*>(vb + (k0 + r) * D + col);
+            }
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kPerThr; ++i) {
+            const int c = tid + kThreads * i;
+            if (c >= kChunks) continue;
+            const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+            *reinterpret_cast<v8*>(&ks[buf][r * LDK + col]) = kr[i];
+            *reinterpret_cast<v8*>(&vs[buf][r * LDK + col]) = vr[i];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kts[buf][(col + e) * LDT + r] = kr[i][e];
+        }
+    };
+
+    const int64_t lim = key_limit(p, b, n);    // no valid key at or past it
+    const int64_t n_tiles = (lim + kT - 1) / kT;
+    if (n_tiles > 0) {
+        load(0);
+        store(0);
+        if (n_tiles > 1) load(kT);
+    }
+    __syncthreads();  // rows staged, first tile in LDS
+    const float d_q = delta[ql], l_q = lse[ql];
+    const bool dead_q = dead[ql] != 0.f, live = qi < p.Q && !dead_q;
+    const bool simple = p.mask_kind == TRIATTN_MASK_NONE || p.mask_kind == TRIATTN_MASK_KV_LENGTHS;
+    const float* brow = p.bias ? p.bias + ((b * p.H + h) * p.Q + qi) * p.K : nullptr;
+    float* zrow = g.dz ? g.dz + (bnh * p.Q + qi) * p.K : nullptr;
+
+    for (int64_t t = 0; t < n_tiles; ++t) {
+        const int buf = static_cast<int>(t & 1);
+        const int64_t k0 = t * kT;
+        f32x16 z{}, dp{};
+#pragma unroll
+        for (int st = 0; st < kSt; ++st) {
+            const v8 ka = *reinterpret_cast<const v8*>(&ks[buf][row * LDK + 16 * st + 8 * hf]);
+            z = M::run(ka, qop[st], z);
+        }
+#pragma unroll
+        for (int st = 0; st < kSt; ++st) {
+            const v8 va = *reinterpret_cast<const v8*>(&vs[buf][row * LDK + 16 * st + 8 * hf]);
+            dp = M::run(va, gop[st], dp);
+        }
+        float dz[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t kk = k0 + 8 * (r / 4) + 4 * hf + (r % 4);
+            float v = 0.f;
+            const bool ok = live && kk < p.K &&
+                            (simple ? kk < lim : key_valid(p, b, n, h, qi, kk));
+            if (ok) {
+                const float bias = brow ? brow[kk] : 0.f;
+                const float pr = expf(fmaf(z[r], p.scale, bias) - l_q);
+                v = pr * (dp[r] - d_q);
+            }
+            dz[r] = v;
+        }
+        if (zrow && qi < p.Q) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t kk = k0 + 8 * (r / 4) + 4 * hf + (r % 4);
+                if (kk < p.K) zrow[kk] = dz[r];
+            }
+        }
+        v8 dzop[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dzop[st][e] = static_cast<T>(dz[8 * st + e]);
+#pragma unroll
+        for (int jb = 0; jb < kJb; ++jb) {
+            const int d = 32 * jb + row;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                // keys 16 st + 4 hf + 0..3 and 16 st + 8 + 4 hf + 0..3: this lane's dz order
+                const v4 lo = *reinterpret_cast<const v4*>(&kts[buf][d * LDT + 16 * st + 4 * hf]);
+                const v4 hi = *reinterpret_cast<const v4*>(&kts[buf][d * LDT + 16 * st + 8 + 4 * hf]);
+                const v8 ka = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[jb] = M::run(ka, dzop[st], acc[jb]);
+            }
+        }
+        if (t + 1 < n_tiles) {
+            store(buf ^ 1);
+            if (t + 2 < n_tiles) load((t + 2) * kT);
+        }
+        __syncthreads();
+    }
+    if (qi >= p.Q) return;
+    T* dqr = static_cast<T*>(g.dq) + (bnh * p.Q + qi) * D;
+#pragma unroll
+    for (int jb = 0; jb < kJb; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            dqr[32 * jb + 8 * (r / 4) + 4 * hf + (r % 4)] = static_cast<T>(acc[jb][r] * p.scale);
+}
+
 // dK and dV: one workgroup per (b, n, h, 32 keys); loops over query tiles.
 // Thread t owns key t / 8 and columns d = t % 8 + 8 i.
 template <typename T, int NC>
@@ -582,8 +758,23 @@ hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
                                     hipFuncAttributeMaxDynamicSharedMemorySize, b);
         if (e != hipSuccess) return e;
     }
-    if (gq > 0)
-        hipLaunchKernelGGL((dq_kernel<T, NC>), dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
+    if (gq > 0) {
+        bool done = false;
+        if constexpr (!std::is_same<T, float>::value) {
+            const dim3 gm(static_cast<unsigned>(p.B * p.N * p.H * ((p.Q + 127) / 128)));
+            done = true;
+            if (p.D == 32)
+                hipLaunchKernelGGL((dq_mfma_kernel<T, 32>), gm, block, 0, stream, p, g);
+            else if (p.D == 64)
+                hipLaunchKernelGGL((dq_mfma_kernel<T, 64>), gm, block, 0, stream, p, g);
+            else if (p.D == 128)
+                hipLaunchKernelGGL((dq_mfma_kernel<T, 128>), gm, block, 0, stream, p, g);
+            else
+                done = false;
+        }
+        if (!done)
+            hipLaunchKernelGGL((dq_kernel<T, NC>), dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
+    }
     if (gk > 0)
         hipLaunchKernelGGL((dkdv_kernel<T, NC>), dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
     if (g.dbias && g.dz) {
