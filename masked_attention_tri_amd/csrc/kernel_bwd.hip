@@ -21,7 +21,8 @@
 //                use dq_mfma_kernel instead (128 rows, operands in
 //                registers, see there).
 //   dkdv_kernel  one (b, n, h, 32 keys), looping over query tiles:
-//                dV = P^T dO, dK = s dz^T Q.
+//                dV = P^T dO, dK = s dz^T Q.  bf16/fp16 at D in {32, 64} use
+//                dkdv_mfma_kernel instead (128 keys, operands in registers).
 //   dbias_kernel one (b, h, 32 query rows, 128 keys), looping over n: the
 //                sum of dz, recomputed per n.
 // With a dz workspace, dq_kernel also stores every dz it computes (fp32,
@@ -715,6 +716,189 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
     }
 }
 
+// dK and dV for bf16/fp16 at D in {32, 64}: one workgroup of 4 waves per
+// (b, n, h, 128 keys), wave w owning keys 32 w .. 32 w + 31.  The mirror of
+// dq_mfma_kernel: each lane keeps one key row of K and V as MFMA operands in
+// registers, so z = Q K^T and dP = dO V^T of a 32-query tile leave lane l
+// with one key and 16 queries (register r: query 8 (r / 4) + 4 (l / 32) +
+// r % 4); dV^T += dO^T P and dK^T += Q^T dz then take P and dz from the
+// registers, with the A operands (dO^T, Q^T) read from transposed LDS copies
+// in the lanes' own query order.  Q and dO tiles are double-buffered and the
+// next tile is loaded into registers while this one is used (one barrier
+// per tile); Delta = dO.O of the tile's rows is reduced from those same
+// registers (with O loaded beside dO), lse and the no-valid-key flag beside
+// them.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p, BwdParams g) {
+    using M = Mma<T>;
+    using v8 = typename M::v8;
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    constexpr int kKeys = 128;                 // keys per workgroup
+    constexpr int LDK = D + 8;                 // Q, dO tile row stride (elements)
+    constexpr int LDT = kT + 8;                // transposed tile row stride
+    constexpr int kCpr = D / 8;                // 16-byte chunks per row
+    constexpr int kChunks = kT * kCpr;         // per tile
+    static_assert(kChunks <= kThreads, "one chunk per thread");
+    constexpr int kSt = D / 16, kJb = D / 32;
+    __shared__ __align__(16) T qs[2][kT * LDK];
+    __shared__ __align__(16) T gs[2][kT * LDK];
+    __shared__ __align__(16) T qts[2][D * LDT];
+    __shared__ __align__(16) T gts[2][D * LDT];
+    __shared__ float delta[2][kT], lse[2][kT], dead[2][kT];
+
+    const int64_t n_kt = (p.K + kKeys - 1) / kKeys;
+    const int64_t bnh = blockIdx.x / n_kt, kw0 = (blockIdx.x % n_kt) * kKeys;
+    const int64_t h = bnh % p.H, n = (bnh / p.H) % p.N, b = bnh / (p.H * p.N);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row = lane & 31, hf = lane >> 5;
+    const int64_t kk = kw0 + 32 * wave + row;  // this lane's key
+
+    const T* qb = static_cast<const T*>(p.q) + bnh * p.Q * D;
+    const T* gb = static_cast<const T*>(g.dout) + bnh * p.Q * D;
+    const T* ob = static_cast<const T*>(g.out) + bnh * p.Q * D;
+    v8 kop[kSt], vop[kSt];
+#pragma unroll
+    for (int st = 0; st < kSt; ++st) {
+        kop[st] = v8{};
+        vop[st] = v8{};
+        if (kk < p.K) {
+            const int64_t off = (bnh * p.K + kk) * D + 16 * st + 8 * hf;
+            kop[st] = *reinterpret_cast<const v8*>(static_cast<const T*>(p.k) + off);
+            vop[st] = *reinterpret_cast<const v8*>(static_cast<const T*>(p.v) + off);
+        }
+    }
+    f32x16 ak[kJb], av[kJb];
+#pragma unroll
+    for (int jb = 0; jb < kJb; ++jb) {
+        ak[jb] = f32x16{};
+        av[jb] = f32x16{};
+    }
+
+    // thread tid < kChunks holds chunk tid: row tid / kCpr, columns 8 (tid % kCpr) ..
+    const int cr = tid / kCpr, cc = (tid % kCpr) * 8;
+    v8 qr{}, gr{}, orr{};
+    float lr = 0.f, mr = 0.f;
+    auto load = [&](int64_t q0) {
+        qr = v8{};
+        gr = v8{};
+        orr = v8{};
+        if (tid < kChunks && q0 + cr < p.Q) {
+            const int64_t off = (q0 + cr) * D + cc;
+            qr = *reinterpret_cast<const v8*>(qb + off);
+            gr = *reinterpret_cast<const v8*>(gb + off);
+            orr = *reinterpret_cast<const v8*>(ob + off);
+        }
+        if (tid < kT && q0 + tid < p.Q) {
+            lr = g.lse[bnh * p.Q + q0 + tid];
+            mr = g.mx[bnh * p.Q + q0 + tid];
+        }
+    };
+    auto store = [&](int buf, int64_t q0) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            part = fmaf(static_cast<float>(gr[e]), static_cast<float>(orr[e]), part);
+#pragma unroll
+        for (int s = 1; s < kCpr; s <<= 1) part += __shfl_xor(part, s);
+        if (tid < kChunks) {
+            *reinterpret_cast<v8*>(&qs[buf][cr * LDK + cc]) = qr;
+            *reinterpret_cast<v8*>(&gs[buf][cr * LDK + cc]) = gr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qts[buf][(cc + e) * LDT + cr] = qr[e];
+                gts[buf][(cc + e) * LDT + cr] = gr[e];
+            }
+            if (cc == 0) delta[buf][cr] = part;
+        }
+        if (tid < kT) {
+            const bool in = q0 + tid < p.Q;
+            lse[buf][tid] = in ? lr : 0.f;
+            dead[buf][tid] = in && mr == kMaskedLogit ? 1.f : 0.f;
+        }
+    };
+
+    const int64_t lim = key_limit(p, b, n);    // no valid key at or past it
+    // keys of this workgroup all past a nonzero limit get nothing (rows with
+    // no valid key, the only other source, exist only when lim is 0 here)
+    const int64_t n_tiles = (lim > 0 && kw0 >= lim) ? 0 : (p.Q + kT - 1) / kT;
+    if (n_tiles > 0) {
+        load(0);
+        store(0, 0);
+        if (n_tiles > 1) load(kT);
+    }
+    __syncthreads();
+    const bool simple = p.mask_kind == TRIATTN_MASK_NONE || p.mask_kind == TRIATTN_MASK_KV_LENGTHS;
+    const float inv_k = 1.0f / static_cast<float>(p.K);
+    const float* bcol = p.bias ? p.bias + (b * p.H + h) * p.Q * p.K + kk : nullptr;
+
+    for (int64_t t = 0; t < n_tiles; ++t) {
+        const int buf = static_cast<int>(t & 1);
+        const int64_t q0 = t * kT;
+        f32x16 z{}, dp{};
+#pragma unroll
+        for (int st = 0; st < kSt; ++st) {
+            const v8 qa = *reinterpret_cast<const v8*>(&qs[buf][row * LDK + 16 * st + 8 * hf]);
+            z = M::run(qa, kop[st], z);
+        }
+#pragma unroll
+        for (int st = 0; st < kSt; ++st) {
+            const v8 ga = *reinterpret_cast<const v8*>(&gs[buf][row * LDK + 16 * st + 8 * hf]);
+            dp = M::run(ga, vop[st], dp);
+        }
+        v8 pop[2], zop[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ql = 8 * (r / 4) + 4 * hf + (r % 4);
+            const int64_t qi = q0 + ql;
+            float pr = 0.f, dz = 0.f;
+            if (qi < p.Q && kk < p.K) {
+                if (dead[buf][ql] != 0.f) {
+                    pr = inv_k;
+                } else if (simple ? kk < lim : key_valid(p, b, n, h, qi, kk)) {
+                    const float bias = bcol ? bcol[qi * p.K] : 0.f;
+                    pr = expf(fmaf(z[r], p.scale, bias) - lse[buf][ql]);
+                    dz = pr * (dp[r] - delta[buf][ql]);
+                }
+            }
+            pop[r / 8][r % 8] = static_cast<T>(pr);
+            zop[r / 8][r % 8] = static_cast<T>(dz);
+        }
+#pragma unroll
+        for (int jb = 0; jb < kJb; ++jb) {
+            const int d = 32 * jb + row;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                // queries 16 st + 4 hf + 0..3 and 16 st + 8 + 4 hf + 0..3: this lane's order
+                const int c0 = d * LDT + 16 * st + 4 * hf;
+                const v4 glo = *reinterpret_cast<const v4*>(&gts[buf][c0]);
+                const v4 ghi = *reinterpret_cast<const v4*>(&gts[buf][c0 + 8]);
+                av[jb] = M::run(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7), pop[st],
+                                av[jb]);
+                const v4 qlo = *reinterpret_cast<const v4*>(&qts[buf][c0]);
+                const v4 qhi = *reinterpret_cast<const v4*>(&qts[buf][c0 + 8]);
+                ak[jb] = M::run(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), zop[st],
+                                ak[jb]);
+            }
+        }
+        if (t + 1 < n_tiles) {
+            store(buf ^ 1, q0 + kT);
+            if (t + 2 < n_tiles) load(q0 + 2 * kT);
+        }
+        __syncthreads();
+    }
+    if (kk >= p.K) return;
+    T* dkr = static_cast<T*>(g.dk) + (bnh * p.K + kk) * D;
+    T* dvr = static_cast<T*>(g.dv) + (bnh * p.K + kk) * D;
+#pragma unroll
+    for (int jb = 0; jb < kJb; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int d = 32 * jb + 8 * (r / 4) + 4 * hf + (r % 4);
+            dkr[d] = static_cast<T>(ak[jb][r] * p.scale);
+            dvr[d] = static_cast<T>(av[jb][r]);
+        }
+}
+
 // dBias from the dz workspace: one thread per (b, h, q, k), summing over n
 // in order (dz is 0 at and past a row's key limit, where dq_kernel stored
 // nothing).  Consecutive threads take consecutive keys: every load of the
@@ -775,8 +959,21 @@ hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
         if (!done)
             hipLaunchKernelGGL((dq_kernel<T, NC>), dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
     }
-    if (gk > 0)
-        hipLaunchKernelGGL((dkdv_kernel<T, NC>), dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
+    if (gk > 0) {
+        bool done = false;
+        if constexpr (!std::is_same<T, float>::value) {
+            const dim3 gm(static_cast<unsigned>(p.B * p.N * p.H * ((p.K + 127) / 128)));
+            done = true;
+            if (p.D == 32)
+                hipLaunchKernelGGL((dkdv_mfma_kernel<T, 32>), gm, block, 0, stream, p, g);
+            else if (p.D == 64)
+                hipLaunchKernelGGL((dkdv_mfma_kernel<T, 64>), gm, block, 0, stream, p, g);
+            else
+                done = false;
+        }
+        if (!done)
+            hipLaunchKernelGGL((dkdv_kernel<T, NC>), dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
+    }
     if (g.dbias && g.dz) {
         const int64_t total = p.B * p.H * p.Q * p.K, want = (total + 255) / 256;
         const unsigned gs = static_cast<unsigned>(want < (1 << 20) ? want : (1 << 20));
