@@ -533,10 +533,21 @@ __global__ __launch_bounds__(kThreads) void dq_mfma_kernel(Params p, BwdParams g
             dz[r] = v;
         }
         if (zrow && qi < p.Q) {
+            if ((p.K & 3) == 0) {
+                // registers 4 c .. 4 c + 3 are 4 consecutive keys from a multiple of 4
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t kk = k0 + 8 * (r / 4) + 4 * hf + (r % 4);
-                if (kk < p.K) zrow[kk] = dz[r];
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t kk = k0 + 8 * c + 4 * hf;
+                    if (kk < p.K)
+                        *reinterpret_cast<float4*>(zrow + kk) =
+                            make_float4(dz[4 * c], dz[4 * c + 1], dz[4 * c + 2], dz[4 * c + 3]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t kk = k0 + 8 * (r / 4) + 4 * hf + (r % 4);
+                    if (kk < p.K) zrow[kk] = dz[r];
+                }
             }
         }
         v8 dzop[2];
@@ -919,6 +930,33 @@ __global__ __launch_bounds__(256) void dbias_sum_kernel(Params p, BwdParams g) {
     }
 }
 
+// The same sum, 4 consecutive keys per thread with 16-byte loads and stores
+// (K a multiple of 4, dbias 16-byte aligned).  A group of 4 keys is read
+// when its first key is below the limit; its other keys then lie in a key
+// tile that dq_kernel visited, where it stored 0 for every invalid key.
+__global__ __launch_bounds__(256) void dbias_sum4_kernel(Params p, BwdParams g) {
+    const int64_t total = p.B * p.H * p.Q * p.K;
+    const int64_t plane = p.H * p.Q * p.K;
+    for (int64_t e = 4 * (blockIdx.x * int64_t(256) + threadIdx.x); e < total;
+         e += 4 * int64_t(gridDim.x) * 256) {
+        const int64_t kk = e % p.K, bhq = e / p.K;
+        const int64_t b = bhq / (p.H * p.Q), hq = bhq % (p.H * p.Q);
+        const float* src = g.dz + b * p.N * plane + hq * p.K + kk;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+        for (int64_t n = 0; n < p.N; ++n) {
+            if (kk < key_limit(p, b, n)) {
+                const float4 v = *reinterpret_cast<const float4*>(src + n * plane);
+                acc.x += v.x;
+                acc.y += v.y;
+                acc.z += v.z;
+                acc.w += v.w;
+            }
+        }
+        *reinterpret_cast<float4*>(g.dbias + e) = acc;
+    }
+}
+
 template <typename T, int NC>
 hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
     const int64_t n_qt = (p.Q + kT - 1) / kT, n_kt = (p.K + kT - 1) / kT;
@@ -975,9 +1013,14 @@ hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
             hipLaunchKernelGGL((dkdv_kernel<T, NC>), dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
     }
     if (g.dbias && g.dz) {
-        const int64_t total = p.B * p.H * p.Q * p.K, want = (total + 255) / 256;
+        const int64_t total = p.B * p.H * p.Q * p.K;
+        const bool vec4 = (p.K & 3) == 0 && (reinterpret_cast<uintptr_t>(g.dbias) & 15) == 0;
+        const int64_t want = (total / (vec4 ? 4 : 1) + 255) / 256;
         const unsigned gs = static_cast<unsigned>(want < (1 << 20) ? want : (1 << 20));
-        if (gs > 0) hipLaunchKernelGGL(dbias_sum_kernel, dim3(gs), dim3(256), 0, stream, p, g);
+        if (gs > 0 && vec4)
+            hipLaunchKernelGGL(dbias_sum4_kernel, dim3(gs), dim3(256), 0, stream, p, g);
+        else if (gs > 0)
+            hipLaunchKernelGGL(dbias_sum_kernel, dim3(gs), dim3(256), 0, stream, p, g);
     } else if (g.dbias && gb > 0) {
         hipLaunchKernelGGL((dbias_kernel<T, NC>), dim3(static_cast<unsigned>(gb)), block, shm, stream, p, g);
     }
