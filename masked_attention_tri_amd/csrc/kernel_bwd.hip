@@ -95,6 +95,16 @@ __device__ __forceinline__ int64_t key_limit(const Params& p, int64_t b, int64_t
     return len < 0 ? 0 : (len > p.K ? p.K : len);
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// P = exp(s z + bias - lse) of a valid key, formed as
+// 2^(z s2 + (bias log2 e - lse2)) on v_exp_f32 with s2 = s log2 e and
+// lse2 = lse log2 e.  Every kernel computes s2 and lse2 by the same fp32
+// products and calls this, so P (and dz) have the same bits in all of them.
+__device__ __forceinline__ float softmax_p(float z, float s2, float bias, float lse2) {
+    return __builtin_amdgcn_exp2f(fmaf(z, s2, fmaf(bias, kLog2e, -lse2)));
+}
+
 // ---- tiled kernels --------------------------------------------------------
 // A workgroup of 256 threads works on 32 x 32 (query, key) tiles.  Rows of
 // Q, dO (32 query rows) and K, V (32 keys) are staged in LDS as fp32 with a
@@ -301,7 +311,7 @@ __device__ __forceinline__ void pair_tile(const Params& p, Tiles t, int64_t b, i
                 pr = inv_k;
             } else if (key_valid(p, b, n, h, qi, kk)) {
                 const float bias = p.bias ? p.bias[((b * p.H + h) * p.Q + qi) * p.K + kk] : 0.f;
-                pr = expf(fmaf(z[j], p.scale, bias) - t.lse[ql]);
+                pr = softmax_p(z[j], p.scale * kLog2e, bias, t.lse[ql] * kLog2e);
                 dz = pr * (dp[j] - t.delta[ql]);
             }
         }
@@ -498,15 +508,36 @@ __global__ __launch_bounds__(kThreads) void dq_mfma_kernel(Params p, BwdParams g
         if (n_tiles > 1) load(kT);
     }
     __syncthreads();  // rows staged, first tile in LDS
-    const float d_q = delta[ql], l_q = lse[ql];
+    const float d_q = delta[ql], l2_q = lse[ql] * kLog2e, s2 = p.scale * kLog2e;
     const bool dead_q = dead[ql] != 0.f, live = qi < p.Q && !dead_q;
     const bool simple = p.mask_kind == TRIATTN_MASK_NONE || p.mask_kind == TRIATTN_MASK_KV_LENGTHS;
     const float* brow = p.bias ? p.bias + ((b * p.H + h) * p.Q + qi) * p.K : nullptr;
     float* zrow = g.dz ? g.dz + (bnh * p.Q + qi) * p.K : nullptr;
+    const bool bias4 = brow && (p.K & 3) == 0 && (reinterpret_cast<uintptr_t>(p.bias) & 15) == 0;
 
     for (int64_t t = 0; t < n_tiles; ++t) {
         const int buf = static_cast<int>(t & 1);
         const int64_t k0 = t * kT;
+        // this lane's 16 bias values, issued before the MFMAs
+        float bv[16];
+        if (bias4) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t kk = k0 + 8 * c + 4 * hf;  // 4 consecutive keys from here
+                const float4 v = live && kk < p.K ? *reinterpret_cast<const float4*>(brow + kk)
+                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+                bv[4 * c] = v.x;
+                bv[4 * c + 1] = v.y;
+                bv[4 * c + 2] = v.z;
+                bv[4 * c + 3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t kk = k0 + 8 * (r / 4) + 4 * hf + (r % 4);
+                bv[r] = brow && live && kk < p.K ? brow[kk] : 0.f;
+            }
+        }
         f32x16 z{}, dp{};
 #pragma unroll
         for (int st = 0; st < kSt; ++st) {
@@ -526,8 +557,7 @@ __global__ __launch_bounds__(kThreads) void dq_mfma_kernel(Params p, BwdParams g
             const bool ok = live && kk < p.K &&
                             (simple ? kk < lim : key_valid(p, b, n, h, qi, kk));
             if (ok) {
-                const float bias = brow ? brow[kk] : 0.f;
-                const float pr = expf(fmaf(z[r], p.scale, bias) - l_q);
+                const float pr = softmax_p(z[r], s2, bv[r], l2_q);
                 v = pr * (dp[r] - d_q);
             }
             dz[r] = v;
@@ -839,7 +869,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p, BwdParams
     }
     __syncthreads();
     const bool simple = p.mask_kind == TRIATTN_MASK_NONE || p.mask_kind == TRIATTN_MASK_KV_LENGTHS;
-    const float inv_k = 1.0f / static_cast<float>(p.K);
+    const float inv_k = 1.0f / static_cast<float>(p.K), s2 = p.scale * kLog2e;
     const float* bcol = p.bias ? p.bias + (b * p.H + h) * p.Q * p.K + kk : nullptr;
 
     for (int64_t t = 0; t < n_tiles; ++t) {
@@ -867,7 +897,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p, BwdParams
                     pr = inv_k;
                 } else if (simple ? kk < lim : key_valid(p, b, n, h, qi, kk)) {
                     const float bias = bcol ? bcol[qi * p.K] : 0.f;
-                    pr = expf(fmaf(z[r], p.scale, bias) - lse[buf][ql]);
+                    pr = softmax_p(z[r], s2, bias, lse[buf][ql] * kLog2e);
                     dz = pr * (dp[r] - delta[buf][ql]);
                 }
             }
