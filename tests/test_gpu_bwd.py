@@ -3,12 +3,13 @@ backward oracle.
 
 Each case runs the library's forward (O, lse, max), then its backward with a
 seeded incoming gradient dO, and compares every gradient element with the
-oracle's exact gradient of the same inputs.  Tolerance: the kernels work in
-fp32 and round dq, dk and dv once to the input type; the oracle is exact.
-For the half types the rounding alone is up to 2^-8 of the largest value
-(bf16), and Delta = dO . O inherits the forward's rounded O, so the bound is
-2e-2 of the tensor's largest magnitude (plus 2e-2 absolute); for fp32,
-1e-4 of it (plus 1e-4).  dbias is fp32 for every input type and gets the
+oracle's exact gradient of the same inputs.  Tolerance: the kernels
+accumulate in fp32 (for the half types, P and dz enter the MFMAs rounded to
+the input type) and round dq, dk and dv once to the input type; the oracle
+is exact.  For the half types the rounding alone is up to 2^-8 of the
+largest value (bf16), and Delta = dO . O inherits the forward's rounded O,
+so the bound is 2e-2 of the tensor's largest magnitude (plus 2e-2
+absolute); for fp32, 1e-4 of it (plus 1e-4).  dbias is fp32 for every input type and gets the
 same bound as its input type's gradients.
 """
 import numpy as np
