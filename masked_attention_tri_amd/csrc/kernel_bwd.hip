@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void dq_mfma_kernel(Params p, BwdParams g
     typedef T v4 __attribute__((ext_vector_type(4)));
     constexpr int kRows = 128;                 // query rows per workgroup
     constexpr int LDK = D + 8;                 // K, V tile row stride (elements)
-    constexpr int LDT = kT + 8;                // transposed K tile row stride
+    constexpr int LDT = kT + 4;                // transposed K tile row stride (see dkdv_mfma_kernel)
     constexpr int kChunks = kT * D / 8;        // 16-byte chunks per K (or V) tile
     constexpr int kPerThr = (kChunks + kThreads - 1) / kThreads;
     constexpr int kSt = D / 16, kJb = D / 32;
@@ -776,7 +776,10 @@ __global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p, BwdParams
     typedef T v4 __attribute__((ext_vector_type(4)));
     constexpr int kKeys = 128;                 // keys per workgroup
     constexpr int LDK = D + 8;                 // Q, dO tile row stride (elements)
-    constexpr int LDT = kT + 8;                // transposed tile row stride
+    // transposed tile row stride: 72 bytes keeps the 8-byte operand reads
+    // aligned and spreads the 2-byte transposed stores of one instruction
+    // (8 column blocks x 8 rows) over twice as many banks as 80 bytes would
+    constexpr int LDT = kT + 4;
     constexpr int kCpr = D / 8;                // 16-byte chunks per row
     constexpr int kChunks = kT * kCpr;         // per tile
     static_assert(kChunks <= kThreads, "one chunk per thread");
@@ -785,7 +788,8 @@ __global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p, BwdParams
     __shared__ __align__(16) T gs[2][kT * LDK];
     __shared__ __align__(16) T qts[2][D * LDT];
     __shared__ __align__(16) T gts[2][D * LDT];
-    __shared__ float delta[2][kT], lse[2][kT], dead[2][kT];
+    // per query row of the tile: Delta, lse log2 e, 1 when the row has no valid key
+    __shared__ __align__(16) float delta[2][kT], lse2[2][kT], dead[2][kT];
 
     const int64_t n_kt = (p.K + kKeys - 1) / kKeys;
     const int64_t bnh = blockIdx.x / n_kt, kw0 = (blockIdx.x % n_kt) * kKeys;
@@ -853,7 +857,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p, BwdParams
         }
         if (tid < kT) {
             const bool in = q0 + tid < p.Q;
-            lse[buf][tid] = in ? lr : 0.f;
+            lse2[buf][tid] = in ? lr * kLog2e : 0.f;
             dead[buf][tid] = in && mr == kMaskedLogit ? 1.f : 0.f;
         }
     };
@@ -887,22 +891,30 @@ __global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p, BwdParams
             dp = M::run(ga, vop[st], dp);
         }
         v8 pop[2], zop[2];
+        auto at = [](const float4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ql = 8 * (r / 4) + 4 * hf + (r % 4);
-            const int64_t qi = q0 + ql;
-            float pr = 0.f, dz = 0.f;
-            if (qi < p.Q && kk < p.K) {
-                if (dead[buf][ql] != 0.f) {
-                    pr = inv_k;
-                } else if (simple ? kk < lim : key_valid(p, b, n, h, qi, kk)) {
-                    const float bias = bcol ? bcol[qi * p.K] : 0.f;
-                    pr = softmax_p(z[r], s2, bias, lse[buf][ql] * kLog2e);
-                    dz = pr * (dp[r] - delta[buf][ql]);
+        for (int c = 0; c < 4; ++c) {
+            // registers 4 c .. 4 c + 3 hold queries 8 c + 4 hf + 0..3: one 16-byte read each
+            const float4 rl = *reinterpret_cast<const float4*>(&lse2[buf][8 * c + 4 * hf]);
+            const float4 rd = *reinterpret_cast<const float4*>(&delta[buf][8 * c + 4 * hf]);
+            const float4 rx = *reinterpret_cast<const float4*>(&dead[buf][8 * c + 4 * hf]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * c + i, ql = 8 * c + 4 * hf + i;
+                const int64_t qi = q0 + ql;
+                float pr = 0.f, dz = 0.f;
+                if (qi < p.Q && kk < p.K) {
+                    if (at(rx, i) != 0.f) {
+                        pr = inv_k;
+                    } else if (simple ? kk < lim : key_valid(p, b, n, h, qi, kk)) {
+                        const float bias = bcol ? bcol[qi * p.K] : 0.f;
+                        pr = softmax_p(z[r], s2, bias, at(rl, i));
+                        dz = pr * (dp[r] - at(rd, i));
+                    }
                 }
+                pop[r / 8][r % 8] = static_cast<T>(pr);
+                zop[r / 8][r % 8] = static_cast<T>(dz);
             }
-            pop[r / 8][r % 8] = static_cast<T>(pr);
-            zop[r / 8][r % 8] = static_cast<T>(dz);
         }
 #pragma unroll
         for (int jb = 0; jb < kJb; ++jb) {
