@@ -75,6 +75,14 @@ CASES = [
     (1, 2, 2, 48, 48, 64, "f16", "none", {"bias": False, "scale": 0.3}),
     (1, 2, 2, 20, 30, 256, "bf16", "kv_lengths", {}),
     (1, 2, 2, 16, 1, 32, "f32", "none", {}),
+    # register-resident MFMA kernels: ragged Q and K past 128, many rows with
+    # no valid key (lengths <= 0) and tiny lengths
+    (1, 6, 2, 130, 200, 64, "bf16", "kv_lengths", {"len_range": (-3, 3)}),
+    # D = 32, K not a multiple of 4 (scalar dz and dBias paths), about half
+    # the rows fully masked
+    (1, 3, 2, 40, 130, 32, "f16", "dense", {"p_valid": 0.005}),
+    # non-causal block mask at D = 64 through the validity predicate
+    (1, 2, 2, 96, 96, 64, "bf16", "block", {"q_block": 32, "kv_block": 32}),
 ]
 
 
