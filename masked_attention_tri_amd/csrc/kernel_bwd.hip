@@ -14,23 +14,22 @@
 // every key and it passes nothing to Q, K or the bias.  The bias is shared by
 // every n, so dB sums over n.
 //
-// Three fp32 vector kernels on 32 x 32 (query, key) tiles staged in LDS (see
-// Tiles below), no atomics:
-//   dq_kernel    one (b, n, h, 32 query rows) per workgroup, looping over
-//                key tiles: dQ = s dz K.  bf16/fp16 at D in {32, 64, 128}
-//                use dq_mfma_kernel instead (128 rows, operands in
-//                registers, see there).
-//   dkdv_kernel  one (b, n, h, 32 keys), looping over query tiles:
-//                dV = P^T dO, dK = s dz^T Q.  bf16/fp16 at D in {32, 64} use
-//                dkdv_mfma_kernel instead (128 keys, operands in registers).
-//   dbias_kernel one (b, h, 32 query rows, 128 keys), looping over n: the
-//                sum of dz, recomputed per n.
-// With a dz workspace, dq_kernel also stores every dz it computes (fp32,
-// (B,N,H,Q,K)) and dbias_sum_kernel sums it over n instead of dbias_kernel:
-// the same values added in the same order, so the two routes give the same
-// bits; the workspace route is bound by HBM bandwidth, the other by latency.
-// Global memory is read by coalesced tile loads.  The contractions run on
-// MFMA for bf16/fp16 and as fp32 FMAs from LDS for fp32.
+// Three launches per call, no atomics, every sum in a fixed order:
+//   dQ    dq_mfma_kernel (bf16/fp16, D in {32, 64, 128}): 128 query rows
+//         per workgroup, Q and dO in registers, looping over 32-key tiles;
+//         otherwise dq_kernel: 32 rows, fp32 tiles staged in LDS (see Tiles
+//         below).  dQ = s dz K.
+//   dK dV dkdv_mfma_kernel (bf16/fp16, D in {32, 64}): 128 keys per
+//         workgroup, K and V in registers, looping over 32-row query tiles;
+//         otherwise dkdv_kernel: 32 keys, LDS-staged.  dV = P^T dO,
+//         dK = s dz^T Q.
+//   dB    with a dz workspace, the dQ kernel also stores every dz (fp32,
+//         (B,N,H,Q,K)) and dbias_sum4_kernel / dbias_sum_kernel sum it over
+//         n (HBM-bound); without one, dbias_kernel recomputes dz per
+//         (b, h, 32 query rows, 128 keys) walking n (latency-bound).  Both
+//         add the same values in the same order and give the same bits.
+// The contractions run on MFMA for bf16/fp16 (P and dz rounded to the input
+// type as operands) and as fp32 FMAs from LDS for fp32.
 #include <math.h>
 
 #include <type_traits>
