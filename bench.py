@@ -41,6 +41,9 @@ def parse():
     # tens of milliseconds; the default warmup covers that, so the timed
     # steps see the steady clock.
     ap.add_argument("--warmup", type=int, default=None, help="default 200 (backward: 3)")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="keep warming up (after --warmup steps) until this much time has "
+                         "passed, so a short --warmup does not time the clock ramp")
     ap.add_argument("--backward", action="store_true",
                     help="time tri_attn_bwd (dQ, dK, dV, dBias) instead of the forward")
     ap.add_argument("--workload", default=None,
@@ -56,6 +59,26 @@ def parse():
     if args.warmup is None:
         args.warmup = 3 if args.backward else 200
     return args
+
+
+def warm_up(args, step):
+    """--warmup steps, then more until --warmup-seconds have passed (the
+    clock under this load dips and settles over tens of milliseconds).
+    Returns the number of warmup steps run."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    for _ in range(args.warmup):
+        step()
+        n += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < args.warmup_seconds:
+        for _ in range(10):
+            step()
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def work_counts(case):
@@ -202,9 +225,7 @@ def bench_backward(args, case, g, key, shape, dtype, desc, scale, out, lse, mx, 
         if st != nat.TRIATTN_OK:
             raise RuntimeError(mat.tri_attn_status_str(st))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_steps = warm_up(args, step)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
@@ -223,8 +244,8 @@ def bench_backward(args, case, g, key, shape, dtype, desc, scale, out, lse, mx, 
     res = {
         "metric": "bwd TFLOP/s (10 D flops per visited query-key pair), triangle attn",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
+        "warmup": args.warmup, "warmup_steps_run": warm_steps, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {torch.bfloat16: "bf16", torch.float16: "f16", torch.float32: "f32"}[case.dtype],
         "data": "synthetic",
         "config": {"workload": case.name, "key": key, "B": B, "N": N, "H": H, "Q": Q, "K": K,
@@ -319,10 +340,8 @@ def main():
         return bench_backward(args, case, g, key, shape, dtype, desc, scale, out, lse, mx,
                               stream, step)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    warm_steps = warm_up(args, step)
+    print(f"[bench] warmup done ({warm_steps} steps)", file=sys.stderr, flush=True)
 
     # HIP events on the stream the kernel is launched on, around the K steps.
     ev0 = torch.cuda.Event(enable_timing=True)
@@ -370,6 +389,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": warm_steps,
         "ms_per_step": round(ms, 5),
         "ms_median": round(per_step[len(per_step) // 2], 5),
         "ms_min": round(per_step[0], 5),

@@ -162,6 +162,11 @@ class BlockMask:
                 raise ValueError("block lists must be on the same device as q")
             t = t.to(torch.int32).contiguous()
             conv.append(t)
+        # every list is read with the kv_num_blocks instance strides, so all
+        # four must have the same leading shape (no separate broadcasting)
+        if conv[2] is not None and tuple(conv[2].shape) != tuple(self.kv_num_blocks.shape):
+            raise ValueError("full_kv_num_blocks must have kv_num_blocks' shape "
+                             f"{tuple(self.kv_num_blocks.shape)}, got {tuple(conv[2].shape)}")
         for idx_t in (conv[1], conv[3]):
             if idx_t is not None and tuple(idx_t.shape[:-1]) != tuple(self.kv_num_blocks.shape):
                 raise ValueError("index tensors must be (..., ROWS, MAX_BLOCKS)")

@@ -81,7 +81,7 @@ def load_library_bwd(path: str):
     lib.tri_oracle_bwd.restype = c_int
     lib.tri_oracle_bwd.argtypes = (
         [i64] * 6 + [ptr] * 4 + [c_int] + [ptr] * 6 + [i64] * 4 + [c_int] + [i64] * 3
-        + [dbl] + [ptr] * 5 + [c_int]
+        + [dbl] + [ptr] * 5 + [i64, ptr, c_int]
     )
     return lib
 
@@ -221,10 +221,14 @@ def oracle_fwd(q, k, v, bias=None, *, mask=None, kv_lengths=None,
 
 def oracle_bwd(q, k, v, bias=None, *, dout, mask=None, kv_lengths=None,
                block: Optional[OracleBlockMask] = None, scale: Optional[float] = None,
-               threads: int = 0, lib=None):
+               threads: int = 0, lib=None, q_rows=None):
     """Return (dQ, dK, dV, dBias) in fp64: the gradient of O = forward(q, k,
     v, bias) against the incoming gradient ``dout`` (B,N,H,Q,D).  dBias is
-    (B,1,H,Q,K), or None without a bias.  Arguments as for oracle_fwd."""
+    (B,1,H,Q,K), or None without a bias.  Arguments as for oracle_fwd.
+
+    q_rows: optional distinct query indices; only those rows of every
+    (b,n,h) are evaluated, so dQ and dBias are exact on them (zero on the
+    other rows) and dK, dV hold only their contributions."""
     lib = lib or _load_bwd()
     qn, kn, vn = _np(q, np.float64), _np(k, np.float64), _np(v, np.float64)
     B, N, H, Q, D = qn.shape
@@ -243,9 +247,15 @@ def oracle_bwd(q, k, v, bias=None, *, dout, mask=None, kv_lengths=None,
     dv = np.empty_like(vn)
     db = np.empty((B, 1, H, Q, K), dtype=np.float64) if bn is not None else None
     s = math.nan if scale is None else float(scale)
+    qsel = None
+    if q_rows is not None:
+        qsel = np.ascontiguousarray(np.asarray(q_rows, dtype=np.int64).reshape(-1))
+        if len(set(qsel.tolist())) != qsel.size:
+            raise ValueError("q_rows must be distinct")
     rc = lib.tri_oracle_bwd(B, N, H, Q, K, D, _ptr(qn), _ptr(kn), _ptr(vn), _ptr(bn), kind,
                             _ptr(dense), _ptr(lens), *blk_args, s, _ptr(gn), _ptr(dq),
-                            _ptr(dk), _ptr(dv), _ptr(db), int(threads))
+                            _ptr(dk), _ptr(dv), _ptr(db), 0 if qsel is None else qsel.size,
+                            _ptr(qsel), int(threads))
     if rc != 0:
         raise RuntimeError(f"tri_oracle_bwd failed with status {rc}")
     return dq, dk, dv, db

@@ -40,6 +40,12 @@
  * dbias (B,1,H,Q,K) or NULL (not computed).  Work is split over (b,h)
  * pairs, each of which owns its slice of every output.
  *
+ * Optional row subset: with qsel non-NULL only the query rows listed in
+ * qsel[0..n_qsel) (each in [0,Q), no repeats) are evaluated, for every
+ * (b,n,h).  dq and dbias are then exact on those rows and zero elsewhere;
+ * dk and dv hold only those rows' contributions.  This lets a test check
+ * the bias gradient (a sum over every n) on a few rows of a large case.
+ *
  * Returns 0 on success, a negative value on a bad argument or allocation
  * failure.
  */
@@ -66,6 +72,8 @@ typedef struct {
     int64_t stride_b, stride_n, stride_h;
     double scale;
     double *dq, *dk, *dv, *dbias;
+    int64_t n_qsel;
+    const int64_t *qsel; /* NULL: every query row */
 } bwd_args;
 
 typedef struct {
@@ -133,7 +141,10 @@ static void bwd_pair(const bwd_args *a, int64_t bh, double *z, double *dp, unsig
         double *dkb = a->dk + bnh * K * D, *dvb = a->dv + bnh * K * D;
         memset(dkb, 0, (size_t)(K * D) * sizeof(double));
         memset(dvb, 0, (size_t)(K * D) * sizeof(double));
-        for (int64_t qi = 0; qi < Q; ++qi) {
+        if (a->qsel) memset(a->dq + bnh * Q * D, 0, (size_t)(Q * D) * sizeof(double));
+        const int64_t n_q = a->qsel ? a->n_qsel : Q;
+        for (int64_t qj = 0; qj < n_q; ++qj) {
+            const int64_t qi = a->qsel ? a->qsel[qj] : qj;
             const int64_t row = bnh * Q + qi;
             const double *qr = a->q + row * D, *go = a->dout + row * D;
             double *dqr = a->dq + row * D;
@@ -217,9 +228,15 @@ int tri_oracle_bwd(int64_t B, int64_t N, int64_t H, int64_t Q, int64_t K, int64_
                    int64_t q_block, int64_t kv_block, int64_t max_blocks,
                    int64_t full_max_blocks, int mask_mod, int64_t stride_b, int64_t stride_n,
                    int64_t stride_h, double scale, const double *dout, double *dq, double *dk,
-                   double *dv, double *dbias, int n_threads)
+                   double *dv, double *dbias, int64_t n_qsel, const int64_t *qsel,
+                   int n_threads)
 {
     if (B < 0 || N < 0 || H < 0 || Q < 0 || K < 1 || D < 1) return -1;
+    if (qsel) {
+        if (n_qsel < 0) return -1;
+        for (int64_t j = 0; j < n_qsel; ++j)
+            if (qsel[j] < 0 || qsel[j] >= Q) return -1;
+    }
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return -1;
     if (mask_kind == BWD_MASK_DENSE && !dense) return -1;
     if (mask_kind == BWD_MASK_KV_LENGTHS && !kv_lengths) return -1;
@@ -246,6 +263,7 @@ int tri_oracle_bwd(int64_t B, int64_t N, int64_t H, int64_t Q, int64_t K, int64_
     a.stride_b = stride_b; a.stride_n = stride_n; a.stride_h = stride_h;
     a.scale = isnan(scale) ? 1.0 / sqrt((double)D) : scale;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dbias = bias ? dbias : NULL;
+    a.n_qsel = n_qsel; a.qsel = qsel;
     if (dbias && !bias) memset(dbias, 0, (size_t)(B * H * Q * K) * sizeof(double));
 
     if (n_threads <= 0) {

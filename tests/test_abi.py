@@ -210,6 +210,29 @@ def test_blockmask_constructor_errors():
                                      mask_mod=lambda b, h, q, k: q >= k)
 
 
+def test_blockmask_rejects_mis_shaped_full_counts():
+    """The kernels read every list with kv_num_blocks' instance strides, so a
+    full_kv_num_blocks with other leading dims (e.g. broadcast (ROWS,) while
+    kv_num_blocks is per (b, n, h)) is rejected on the host, before any
+    launch."""
+    import torch
+
+    B, N, H, rows, width = 2, 3, 2, 4, 4
+    num = torch.ones(B, N, H, rows, dtype=torch.int32)
+    idx = torch.zeros(B, N, H, rows, width, dtype=torch.int32)
+    good = mat.BlockMask.from_kv_blocks(num, idx, num.clone(), idx.clone(), BLOCK_SIZE=16)
+    good._descriptor(B, N, H, 64, 64, torch.device("cpu"))
+    bad = mat.BlockMask.from_kv_blocks(num, idx, torch.ones(rows, dtype=torch.int32),
+                                       idx.clone(), BLOCK_SIZE=16)
+    with pytest.raises(ValueError, match="full_kv_num_blocks"):
+        bad._descriptor(B, N, H, 64, 64, torch.device("cpu"))
+    bad_idx = mat.BlockMask.from_kv_blocks(num, idx, num.clone(),
+                                           torch.zeros(rows, width, dtype=torch.int32),
+                                           BLOCK_SIZE=16)
+    with pytest.raises(ValueError):
+        bad_idx._descriptor(B, N, H, 64, 64, torch.device("cpu"))
+
+
 def test_blockmask_numel_and_sparsity():
     import torch
 

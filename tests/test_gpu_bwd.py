@@ -195,3 +195,32 @@ def test_dbias_routes_agree_headline_size():
     (a, b) = _both_routes(c, seed=61)
     assert torch.equal(a[3], b[3]), "dbias routes differ"
     assert float(a[3].abs().max()) > 0
+
+
+def test_dbias_headline_size_against_oracle():
+    """dBias at the headline size (B1 N768 H4 Q=K=768 D64, bf16, kv_lengths
+    U{384..768}) against the fp64 backward oracle on 12 query rows of every
+    head, each summed over all 768 n: the oracle evaluates only those rows
+    (each row's gradient terms are independent of the others)."""
+    c = wl.make_workload("bf16_lens_d64")
+    say(f"dbias vs oracle {c.name}")
+    g = torch.Generator().manual_seed(67)
+    dout = torch.randn(c.q.shape, generator=g).to(c.q.dtype)
+    gc = c.to("cuda")
+    out, lse, mx = mat.triangle_attention(gc.q, gc.k, gc.v, gc.bias, scale=gc.scale,
+                                          return_aux=True, kv_lengths=gc.kv_lengths)
+    _, _, _, db = mat.triangle_attention_backward(gc.q, gc.k, gc.v, gc.bias, out, dout.cuda(),
+                                                  lse, mx, scale=gc.scale,
+                                                  kv_lengths=gc.kv_lengths)
+    torch.cuda.synchronize()
+    qs = sorted(set(torch.randperm(768, generator=g)[:10].tolist()) | {0, 767})
+    ref = orc.oracle_bwd(c.q, c.k, c.v, c.bias, dout=dout, kv_lengths=c.kv_lengths,
+                         scale=c.scale, q_rows=qs)[3]
+    got = db.cpu().double().numpy()[:, :, :, qs]
+    want = ref[:, :, :, qs]
+    err = np.abs(got - want)
+    scale_row = np.abs(want).max(axis=-1, keepdims=True)
+    worst = float((err / scale_row).max())
+    say(f"dbias headline: max abs err {float(err.max()):.3g}, max |ref| "
+        f"{float(np.abs(want).max()):.3g}, worst err / row max {worst:.3g}")
+    assert worst <= 2e-2, f"dbias error {worst} of the row's largest value"

@@ -64,11 +64,23 @@ def test_run_to_run_determinism(key):
     assert _eq(run_gpu(c), run_gpu(c))
 
 
-@pytest.mark.parametrize("dt,D,kind", [("bf16", 64, "kv_lengths"), ("f16", 128, "dense"),
-                                       ("bf16", 24, "none"), ("f32", 16, "dense")])
-def test_every_output_element_is_written(dt, D, kind):
-    say(f"NaN-prefilled outputs {dt} D={D} {kind}")
-    c = wl.make_case(2, 2, 2, 131, 77, D, dt, kind, seed=9).to("cuda")
+@pytest.mark.parametrize("dt,D,kind,shape,extra", [
+    ("bf16", 64, "kv_lengths", (2, 2, 2, 131, 77), {}),
+    ("f16", 128, "dense", (2, 2, 2, 131, 77), {}),
+    ("bf16", 24, "none", (2, 2, 2, 131, 77), {}),
+    ("f32", 16, "dense", (2, 2, 2, 131, 77), {}),
+    # many query tiles per row, ragged last tile, odd N
+    ("bf16", 64, "kv_lengths", (1, 3, 2, 1000, 700), {"len_range": (0, 700)}),
+    ("bf16", 32, "dense", (1, 5, 2, 1000, 300), {}),
+    # block-sparse: 8 query tiles of a causal 128 x 64 BlockMask, and a
+    # random one with duplicates and out-of-range ids
+    ("bf16", 64, "block", (1, 2, 2, 1024, 1024),
+     {"q_block": 128, "kv_block": 64, "mask_mod": "causal"}),
+    ("f16", 128, "block", (2, 1, 2, 640, 600), {"q_block": 128, "kv_block": 128}),
+])
+def test_every_output_element_is_written(dt, D, kind, shape, extra):
+    say(f"NaN-prefilled outputs {dt} D={D} {kind} {shape}")
+    c = wl.make_case(*shape, D, dt, kind, seed=9, **extra).to("cuda")
     out = torch.full_like(c.q, float("nan"))
     lse = torch.full(c.q.shape[:4], float("nan"), device="cuda")
     mx = torch.full(c.q.shape[:4], float("nan"), device="cuda")
@@ -83,6 +95,8 @@ def test_every_output_element_is_written(dt, D, kind):
         desc = nat.TriAttnMask()
         desc.kind = nat.TRIATTN_MASK_KV_LENGTHS
         desc.kv_lengths = ln.data_ptr()
+    elif c.block is not None:
+        desc, keep = block_mask_of(c)._descriptor(*c.shape[:5], torch.device("cuda"))
     B, N, H, Q, K, D = c.shape
     st = mat.tri_attn_fwd(nat.TriAttnShape(B, N, H, Q, K, D), nat.DTYPE_CODES[c.q.dtype],
                           c.q, c.k, c.v, c.bias, desc, math.nan, out, lse, mx, None)
@@ -248,3 +262,33 @@ def test_slices_past_32_bit_offsets():
                   - L.astype(np.float32)).max() <= TOL[torch.bfloat16]["lse"]
     assert np.abs(mx.cpu().double().numpy().reshape(M.shape)
                   - M.astype(np.float32)).max() <= TOL[torch.bfloat16]["mx"]
+
+
+def test_valid_logits_below_the_replacement_value():
+    """The kernels carry masked logits as -inf, which equals the -1e9
+    replacement whenever a valid logit exceeds -1e9 + 700.  This pins what
+    they do in the case the two differ: a row whose every valid logit is far
+    below -1e9 (bias -3e9).  The valid keys still take all the weight (here
+    uniformly: in fp32, -3e9 + s.q.k rounds to -3e9), so O is the mean of V
+    over the valid keys and max is -3e9, while the -1e9 replacement of the
+    equation would average V over the masked keys instead."""
+    say("valid logits below -1e9")
+    B, N, H, Q, K, D = 1, 2, 2, 64, 96, 64
+    c = wl.make_case(B, N, H, Q, K, D, "bf16", "dense", seed=31)
+    c.bias[0, 0, 1, 5, :] = -3.0e9
+    c.bias[0, 0, 0, 40, :] = -3.0e9
+    out, lse, mx = run_gpu(c)
+    valid = c.mask.view(B, N, K)
+    for h, qrow in ((1, 5), (0, 40)):
+        for n in range(N):
+            vk = c.v[0, n, h].double()[valid[0, n]]
+            want = vk.mean(dim=0)
+            got = out[0, n, h, qrow].double()
+            assert (got - want).abs().max() <= TOL[c.dtype]["o"], (h, qrow, n)
+            assert float(mx[0, n, h, qrow]) == -3.0e9
+            assert abs(float(lse[0, n, h, qrow]) + 3.0e9) <= 256.0
+    # every other row is the equation's result
+    rows = [i for i in range(B * N * H * Q)
+            if (i // Q) % H != 1 or i % Q != 5]
+    rows = [i for i in rows if (i // Q) % H != 0 or i % Q != 40]
+    assert_parity(c, gpu=(out, lse, mx), rows=np.array(rows))

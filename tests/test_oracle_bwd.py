@@ -173,3 +173,27 @@ def test_pins_reject_backward_mutant(name, old, new, tmp_path):
             failed = True
             break
     assert failed, f"mutant {name} passed every finite-difference pin"
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_query_row_subset_matches_full(kind):
+    """Evaluating only some query rows gives exactly the full result's dQ and
+    dBias on those rows (zero elsewhere): each row's gradient terms do not
+    depend on the other rows."""
+    c = _case(kind, N=3, Q=4, seed=11)
+    if kind == "dense":
+        c["mk"] = dict(mask=np.random.default_rng(2).random((1, 3, 5)) < 0.6)
+    elif kind == "kv_lengths":
+        c["mk"] = dict(kv_lengths=np.array([[3, 0, 5]], dtype=np.int32))
+    args = (c["q"], c["k"], c["v"], c["bias"])
+    full = orc.oracle_bwd(*args, dout=c["dout"], scale=c["scale"], **c["mk"])
+    sel = [3, 0]
+    part = orc.oracle_bwd(*args, dout=c["dout"], scale=c["scale"], q_rows=sel, **c["mk"])
+    others = [q for q in range(4) if q not in sel]
+    assert np.array_equal(part[0][:, :, :, sel], full[0][:, :, :, sel])
+    assert not part[0][:, :, :, others].any()
+    if c["bias"] is not None:
+        assert np.array_equal(part[3][:, :, :, sel], full[3][:, :, :, sel])
+        assert not part[3][:, :, :, others].any()
+    with pytest.raises(RuntimeError):
+        orc.oracle_bwd(*args, dout=c["dout"], scale=c["scale"], q_rows=[4], **c["mk"])
