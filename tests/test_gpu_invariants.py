@@ -96,7 +96,7 @@ def test_every_output_element_is_written(dt, D, kind, shape, extra):
         desc.kind = nat.TRIATTN_MASK_KV_LENGTHS
         desc.kv_lengths = ln.data_ptr()
     elif c.block is not None:
-        desc, keep = block_mask_of(c)._descriptor(*c.shape[:5], torch.device("cuda"))
+        desc, keep = block_mask_of(c)._descriptor(*c.shape[:5], c.q.device)
     B, N, H, Q, K, D = c.shape
     st = mat.tri_attn_fwd(nat.TriAttnShape(B, N, H, Q, K, D), nat.DTYPE_CODES[c.q.dtype],
                           c.q, c.k, c.v, c.bias, desc, math.nan, out, lse, mx, None)
