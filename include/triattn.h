@@ -175,6 +175,102 @@ triattn_status tri_attn_fwd(const tri_attn_shape* shape, int32_t dtype, const vo
                             float* max, hipStream_t stream);
 
 /*
+ * ---- Packed variable-length sequences ------------------------------------
+ *
+ * The fused-attention layouts of Transformer Engine's fused_attn.h (release
+ * 0.9.0 C API: enums NVTE_QKV_Layout and NVTE_Mask_Type, and the
+ * cu_seqlens_q / cu_seqlens_kv / max_seqlen_q / max_seqlen_kv arguments of
+ * nvte_fused_attn_fwd_kvpacked and _qkvpacked).  `batch` sequences are
+ * packed one after the other along the row axis of each tensor; every row
+ * holds all H heads.  Sequence b is rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ * of q and out and rows cu_seqlens_kv[b] .. cu_seqlens_kv[b+1]-1 of k and v,
+ * and each query row attends only to the keys of its own sequence:
+ *
+ *     z_j = s * (Q_i . K_j)   for the keys j of i's sequence the mask allows
+ *     O_i = sum_j softmax_j(z) V_j,  max_i = max_j z_j,  lse_i = log sum_j exp(z_j)
+ *
+ * (no bias: the page leaves the bias layout of packed sequences open).
+ */
+
+/* Layout of the packed tensors (NVTE_QKV_Layout; the page's three layouts
+ * read as separate q, k, v; one interleaved qkv tensor; q with an
+ * interleaved kv tensor). */
+typedef enum tri_attn_qkv_layout {
+    /* q [total_q, H, D]; k and v [total_kv, H, D] */
+    TRIATTN_QKV_SEPARATE = 0,
+    /* one tensor qkv [total, 3, H, D] passed as `q` (k and v unused; the
+     * key rows are the query rows: total_kv = total_q, cu_seqlens_kv NULL
+     * or equal to cu_seqlens_q) */
+    TRIATTN_QKV_PACKED = 1,
+    /* q [total_q, H, D]; one tensor kv [total_kv, 2, H, D] passed as `k`
+     * (v unused) */
+    TRIATTN_KV_PACKED = 2
+} tri_attn_qkv_layout;
+
+/* Key mask inside a sequence (NVTE_Mask_Type). */
+typedef enum tri_attn_varlen_mask {
+    /* every key of the query's sequence */
+    TRIATTN_VARLEN_NO_MASK = 0,
+    /* the same: packed sequences carry no padding rows, the padding is the
+     * sequence boundary itself */
+    TRIATTN_VARLEN_PADDING = 1,
+    /* key j of query row i of a sequence (both counted from the sequence's
+     * first row) only if j <= i, top-left aligned when the query and key
+     * lengths differ */
+    TRIATTN_VARLEN_CAUSAL = 2
+} tri_attn_varlen_mask;
+
+typedef struct tri_attn_varlen {
+    int32_t layout;     /* tri_attn_qkv_layout */
+    int32_t mask_type;  /* tri_attn_varlen_mask */
+    int64_t batch;      /* number of sequences (>= 0) */
+    int64_t heads;      /* H (>= 0) */
+    int64_t head_dim;   /* D (>= 1) */
+    int64_t total_q;    /* rows of q and out (>= 0) */
+    int64_t total_kv;   /* rows of k and v (>= 0; QKV_PACKED: total_q) */
+    /* batch + 1 ascending int32 row offsets each, device memory */
+    const int32_t* cu_seqlens_q;
+    const int32_t* cu_seqlens_kv;
+    /* bounds on the sequence lengths (the page: "may be >=" the longest) */
+    int64_t max_seqlen_q;
+    int64_t max_seqlen_kv;
+} tri_attn_varlen;
+
+/*
+ * Host-only validation of tri_attn_varlen_fwd's arguments (no device call).
+ * Layouts and outputs: out [total_q, H, D] of type `dtype`; lse, max
+ * [total_q, H] fp32, each nullable.  dtype and D follow the envelope of
+ * tri_attn_fwd; q, k, v, out 16-byte aligned.  `scale`: NaN = 1/sqrt(D).
+ * Nothing to do (OK, pointers may be NULL) when batch, heads, total_q or
+ * max_seqlen_q is 0.  TRIATTN_ERR_INVALID_ARG for: a NULL descriptor; a
+ * negative size, D < 1 or max_seqlen_kv < 0; an unknown layout, mask type or
+ * dtype; a NULL required pointer (q; k for SEPARATE and KV_PACKED; v for
+ * SEPARATE; out; cu_seqlens_q; cu_seqlens_kv unless QKV_PACKED); QKV_PACKED
+ * with total_kv != total_q or a cu_seqlens_kv other than NULL or
+ * cu_seqlens_q; a misaligned pointer; an infinite scale.
+ * TRIATTN_ERR_UNSUPPORTED for (dtype, D) outside the envelope or sizes past
+ * the library's index range.
+ */
+triattn_status tri_attn_varlen_check(const tri_attn_varlen* desc, int32_t dtype, const void* q,
+                                     const void* k, const void* v, float scale, const void* out,
+                                     const float* lse, const float* max);
+
+/*
+ * Enqueue the forward of packed sequences on `stream`: out, lse and max of
+ * every row of every sequence; rows of the packed tensors outside every
+ * sequence are not written.  The cu_seqlens values are device data and are
+ * not validated on the host: each sequence's bounds are clamped to
+ * [0, total] and made ascending, and a sequence longer than max_seqlen_q
+ * (max_seqlen_kv) is computed over its first max_seqlen_q query rows (key
+ * rows) only.  A query row with no key (an empty key sequence) gets O = 0,
+ * max = lse = -1e9.  Returns the tri_attn_varlen_check status if not OK
+ * (nothing launched), TRIATTN_ERR_HIP if a launch fails, else TRIATTN_OK.
+ */
+triattn_status tri_attn_varlen_fwd(const tri_attn_varlen* desc, int32_t dtype, const void* q,
+                                   const void* k, const void* v, float scale, void* out,
+                                   float* lse, float* max, hipStream_t stream);
+
+/*
  * Backward of the forward's output O (the page's backward pass; lse and max
  * carry no incoming gradient).  Per (b,n,h,q) row, with P the forward's
  * softmax weights rebuilt from lse (P_k = exp(z_k - lse)) and Delta = dO.O:

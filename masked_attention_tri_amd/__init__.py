@@ -30,20 +30,30 @@ from ._native import (  # noqa: F401
     TRIATTN_MASK_NONE,
     TRIATTN_MOD_CAUSAL,
     TRIATTN_MOD_NONE,
+    TRIATTN_KV_PACKED,
     TRIATTN_OK,
+    TRIATTN_QKV_PACKED,
+    TRIATTN_QKV_SEPARATE,
+    TRIATTN_VARLEN_CAUSAL,
+    TRIATTN_VARLEN_NO_MASK,
+    TRIATTN_VARLEN_PADDING,
     LibraryNotBuilt,
     TriAttnMask,
     TriAttnShape,
+    TriAttnVarlen,
     load_library,
     tri_attn_bwd,
     tri_attn_check,
     tri_attn_fwd,
     tri_attn_mask_to_kv_lengths,
     tri_attn_status_str,
+    tri_attn_varlen_check,
+    tri_attn_varlen_fwd,
 )
 
 __all__ = ["triangle_attention", "triangle_attention_backward", "triangle_attention_autograd",
-           "mask_to_kv_lengths",
+           "triangle_attention_varlen", "mask_to_kv_lengths", "tri_attn_varlen_fwd",
+           "tri_attn_varlen_check",
            "BlockMask", "causal_mask", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_check",
            "tri_attn_status_str",
            "tri_attn_mask_to_kv_lengths", "load_library"]
@@ -390,4 +400,89 @@ def triangle_attention_autograd(q, k, v, bias=None, mask=None, scale: Optional[f
     k, v and bias (its gradient is summed over n and cast to bias's dtype);
     lse and max are not differentiable."""
     out, lse, mx = _TriangleAttentionFn.apply(q, k, v, bias, mask, scale, kv_lengths, block_mask)
+    return (out, lse, mx) if return_aux else out
+
+
+_VARLEN_LAYOUTS = {"separate": TRIATTN_QKV_SEPARATE, "qkv_packed": TRIATTN_QKV_PACKED,
+                   "kv_packed": TRIATTN_KV_PACKED}
+_VARLEN_MASKS = {"no_mask": TRIATTN_VARLEN_NO_MASK, "padding": TRIATTN_VARLEN_PADDING,
+                 "causal": TRIATTN_VARLEN_CAUSAL}
+
+
+def triangle_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q: int,
+                              max_seqlen_kv: int, *, layout: str = "separate",
+                              mask_type: str = "padding", scale: Optional[float] = None,
+                              return_aux: bool = False, stream=None):
+    """Attention over packed variable-length sequences, in the layouts of
+    Transformer Engine's fused_attn.h (NVTE_QKV_Layout, NVTE_Mask_Type,
+    cu_seqlens / max_seqlen arguments): each query row attends to the keys
+    of its own sequence only.
+
+    layout "separate": q [Tq, H, D], k and v [Tkv, H, D];
+    "qkv_packed": q is one tensor [T, 3, H, D] (k, v, cu_seqlens_kv None);
+    "kv_packed": q [Tq, H, D] and k is one tensor [Tkv, 2, H, D] (v None).
+    cu_seqlens_q / _kv: int32 [batch + 1] row offsets.  mask_type "no_mask"
+    and "padding" (the same for packed rows) or "causal" (key j of query i,
+    both counted within the sequence, only if j <= i).  Returns out
+    [Tq, H, D], or (out, lse, max) with fp32 [Tq, H] aux; rows outside every
+    sequence are left unwritten.  No bias; every step runs in the library.
+    """
+    if layout not in _VARLEN_LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(_VARLEN_LAYOUTS)}")
+    if mask_type not in _VARLEN_MASKS:
+        raise ValueError(f"mask_type must be one of {sorted(_VARLEN_MASKS)}")
+    if not q.is_cuda:
+        raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    if q.dtype not in _native.DTYPE_CODES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    dev = q.device
+    if layout == "qkv_packed":
+        if q.dim() != 4 or q.shape[1] != 3:
+            raise ValueError("qkv_packed: q must be [T, 3, H, D]")
+        total_q, _, H, D = q.shape
+        total_kv = total_q
+        tensors = [q.contiguous()]
+        kk = vv = None
+        cu_kv = None
+    else:
+        if q.dim() != 3:
+            raise ValueError("q must be [Tq, H, D]")
+        total_q, H, D = q.shape
+        if layout == "kv_packed":
+            if k is None or k.dim() != 4 or tuple(k.shape[1:]) != (2, H, D):
+                raise ValueError("kv_packed: k must be [Tkv, 2, H, D]")
+            kk, vv = k.contiguous(), None
+        else:
+            if k is None or v is None or k.dim() != 3 or tuple(k.shape[1:]) != (H, D) \
+                    or k.shape != v.shape:
+                raise ValueError("separate: k and v must be [Tkv, H, D]")
+            kk, vv = k.contiguous(), v.contiguous()
+        total_kv = kk.shape[0]
+        tensors = [q.contiguous()]
+        if cu_seqlens_kv is None:
+            raise ValueError("cu_seqlens_kv is required for this layout")
+        cu_kv = cu_seqlens_kv.to(device=dev, dtype=torch.int32).contiguous()
+    for t in (kk, vv):
+        if t is not None and t.dtype != q.dtype:
+            raise ValueError("q, k and v must share one dtype")
+    cu_q = cu_seqlens_q.to(device=dev, dtype=torch.int32).contiguous()
+    if cu_q.dim() != 1 or (cu_kv is not None and cu_kv.shape != cu_q.shape):
+        raise ValueError("cu_seqlens must be 1-D [batch + 1] and of equal length")
+    batch = cu_q.numel() - 1
+    qq = tensors[0]
+    out = torch.empty(total_q, H, D, device=dev, dtype=q.dtype)
+    lse = torch.empty(total_q, H, device=dev, dtype=torch.float32)
+    mx = torch.empty(total_q, H, device=dev, dtype=torch.float32)
+    d = TriAttnVarlen()
+    d.layout = _VARLEN_LAYOUTS[layout]
+    d.mask_type = _VARLEN_MASKS[mask_type]
+    d.batch, d.heads, d.head_dim = max(batch, 0), H, D
+    d.total_q, d.total_kv = total_q, total_kv
+    d.cu_seqlens_q = cu_q.data_ptr()
+    d.cu_seqlens_kv = cu_kv.data_ptr() if cu_kv is not None else None
+    d.max_seqlen_q, d.max_seqlen_kv = int(max_seqlen_q), int(max_seqlen_kv)
+    s = math.nan if scale is None else float(scale)
+    st = tri_attn_varlen_fwd(d, _native.DTYPE_CODES[q.dtype], qq, kk, vv, s, out, lse, mx, stream)
+    if st != TRIATTN_OK:
+        raise RuntimeError(f"tri_attn_varlen_fwd: {tri_attn_status_str(st)}")
     return (out, lse, mx) if return_aux else out

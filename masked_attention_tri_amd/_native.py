@@ -32,8 +32,16 @@ TRIATTN_MASK_BLOCK = 3
 TRIATTN_MOD_NONE = 0
 TRIATTN_MOD_CAUSAL = 1
 
-EXPORTED = ("tri_attn_check", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_mask_to_kv_lengths",
-            "tri_attn_status_str")
+EXPORTED = ("tri_attn_check", "tri_attn_fwd", "tri_attn_varlen_check", "tri_attn_varlen_fwd",
+            "tri_attn_bwd", "tri_attn_mask_to_kv_lengths", "tri_attn_status_str")
+
+TRIATTN_QKV_SEPARATE = 0
+TRIATTN_QKV_PACKED = 1
+TRIATTN_KV_PACKED = 2
+
+TRIATTN_VARLEN_NO_MASK = 0
+TRIATTN_VARLEN_PADDING = 1
+TRIATTN_VARLEN_CAUSAL = 2
 
 DTYPE_CODES = {torch.float32: TRIATTN_F32, torch.float16: TRIATTN_F16,
                torch.bfloat16: TRIATTN_BF16}
@@ -63,6 +71,22 @@ class TriAttnMask(ctypes.Structure):
     ]
 
 
+class TriAttnVarlen(ctypes.Structure):
+    _fields_ = [
+        ("layout", ctypes.c_int32),
+        ("mask_type", ctypes.c_int32),
+        ("batch", ctypes.c_int64),
+        ("heads", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("total_q", ctypes.c_int64),
+        ("total_kv", ctypes.c_int64),
+        ("cu_seqlens_q", ctypes.c_void_p),
+        ("cu_seqlens_kv", ctypes.c_void_p),
+        ("max_seqlen_q", ctypes.c_int64),
+        ("max_seqlen_kv", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -86,6 +110,11 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_check.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P]
     lib.tri_attn_fwd.restype = I32
     lib.tri_attn_fwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P]
+    varlen_p = ctypes.POINTER(TriAttnVarlen)
+    lib.tri_attn_varlen_check.restype = I32
+    lib.tri_attn_varlen_check.argtypes = [varlen_p, I32, P, P, P, F32, P, P, P]
+    lib.tri_attn_varlen_fwd.restype = I32
+    lib.tri_attn_varlen_fwd.argtypes = [varlen_p, I32, P, P, P, F32, P, P, P, P]
     lib.tri_attn_bwd.restype = I32
     lib.tri_attn_bwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P, P, P, P,
                                   ctypes.c_size_t, P]
@@ -131,6 +160,30 @@ def tri_attn_fwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: fl
         ctypes.byref(shape), int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
         ctypes.byref(mask) if mask is not None else None, ctypes.c_float(scale), _ptr(out),
         _ptr(lse), _ptr(mx), ctypes.c_void_p(handle)))
+
+
+def _addr(x):
+    return ctypes.c_void_p(x) if isinstance(x, int) else _ptr(x)
+
+
+def tri_attn_varlen_check(desc: TriAttnVarlen, dtype: int, q, k, v, scale: float, out, lse,
+                          mx) -> int:
+    """Host-only validation of a packed-sequence forward (tensors, raw
+    addresses or None)."""
+    return int(load_library().tri_attn_varlen_check(
+        ctypes.byref(desc), int(dtype), _addr(q), _addr(k), _addr(v), ctypes.c_float(scale),
+        _addr(out), _addr(lse), _addr(mx)))
+
+
+def tri_attn_varlen_fwd(desc: TriAttnVarlen, dtype: int, q, k, v, scale: float, out, lse, mx,
+                        stream) -> int:
+    """Enqueue the packed-sequence forward on `stream` (as tri_attn_fwd)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return int(load_library().tri_attn_varlen_fwd(
+        ctypes.byref(desc), int(dtype), _addr(q), _addr(k), _addr(v), ctypes.c_float(scale),
+        _addr(out), _addr(lse), _addr(mx), ctypes.c_void_p(handle)))
 
 
 def tri_attn_mask_to_kv_lengths(mask, rows: int, K: int, kv_lengths, nonprefix_rows,

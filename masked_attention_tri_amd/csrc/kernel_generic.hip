@@ -61,17 +61,37 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
     const int wave = threadIdx.x >> 6;
     const int64_t total = p.B * p.N * p.H * p.Q;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-    const bool active = row < total;
+    bool active = row < total;
     const int64_t r = active ? row : 0;
     const int64_t qi = r % p.Q;
     const int64_t h = (r / p.Q) % p.H;
     const int64_t n = (r / (p.Q * p.H)) % p.N;
     const int64_t b = r / (p.Q * p.H * p.N);
-    const int64_t D = p.D, K = p.K;
+    const int64_t D = p.D;
+    int64_t K = p.K;
     const int64_t bnh = (b * p.N + n) * p.H + h;
-    const T* qrow = static_cast<const T*>(p.q) + r * D;
-    const T* kbase = static_cast<const T*>(p.k) + bnh * K * D;
-    const T* vbase = static_cast<const T*>(p.v) + bnh * K * D;
+    // Rows of q / out and of k / v, and the lse / max index: the (b, n, h)
+    // slices, or for packed sequences (row, head) slabs of the packed tensors.
+    const bool varlen = p.mask_kind == kMaskVarlen;
+    const T* qrow;
+    const T* kbase;
+    const T* vbase;
+    int64_t kv_rs = D;
+    int64_t out_row = r;
+    if (varlen) {
+        const SeqRows sr = seq_rows(p, b);
+        active = active && qi < sr.nq;
+        K = sr.nk;
+        kv_rs = p.kv_rs;
+        qrow = static_cast<const T*>(p.q) + (sr.q0 + qi) * p.q_rs + h * D;
+        kbase = static_cast<const T*>(p.k) + sr.k0 * kv_rs + h * D;
+        vbase = static_cast<const T*>(p.v) + sr.k0 * kv_rs + h * D;
+        out_row = (sr.q0 + qi) * p.H + h;
+    } else {
+        qrow = static_cast<const T*>(p.q) + r * D;
+        kbase = static_cast<const T*>(p.k) + bnh * K * D;
+        vbase = static_cast<const T*>(p.v) + bnh * K * D;
+    }
     const float* brow = p.bias ? p.bias + ((b * p.H + h) * p.Q + qi) * K : nullptr;
 
     // Visited and full kv blocks of this row's BlockMask row.
@@ -105,6 +125,7 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
         const int64_t len = p.kv_lengths[b * p.N + n];
         limit = len < 0 ? 0 : (len > K ? K : len);
     }
+    if (varlen && p.causal) limit = limit < qi + 1 ? limit : qi + 1;  // keys j <= qi
     const uint8_t* mrow = p.mask_kind == TRIATTN_MASK_DENSE ? p.dense + (b * p.N + n) * K : nullptr;
 
     float m = -INFINITY;  // running max of the valid logits
@@ -132,7 +153,7 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
         }
         float z = -INFINITY;
         if (valid) {
-            const T* krow = kbase + kk * D;
+            const T* krow = kbase + kk * kv_rs;
             float dot = 0.f;
             for (int64_t d = 0; d < D; ++d) dot = fmaf(to_f32(qrow[d]), to_f32(krow[d]), dot);
             z = fmaf(dot, p.scale, brow ? brow[kk] : 0.f);
@@ -148,7 +169,7 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
         for (int j = 0; j < jmax; ++j) {
             const float pj = __shfl(pz, j);
             if (pj == 0.f) continue;  // uniform: pj is the same in every lane
-            const T* vrow = vbase + (c0 + j) * D;
+            const T* vrow = vbase + (c0 + j) * kv_rs;
 #pragma unroll
             for (int i = 0; i < kOut; ++i)
                 if (has[i]) o[i] = fmaf(pj, to_f32(vrow[lane + 64 * i]), o[i]);
@@ -163,16 +184,17 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
 #pragma unroll
         for (int i = 0; i < kOut; ++i) o[i] = 0.f;
         for (int64_t kk = 0; kk < K; ++kk) {
-            const T* vrow = vbase + kk * D;
+            const T* vrow = vbase + kk * kv_rs;
 #pragma unroll
             for (int i = 0; i < kOut; ++i)
                 if (has[i]) o[i] += to_f32(vrow[lane + 64 * i]);
         }
-        const float inv = 1.0f / static_cast<float>(K);
+        // (a packed sequence with no key at all averages nothing: 0)
+        const float inv = K > 0 ? 1.0f / static_cast<float>(K) : 0.f;
 #pragma unroll
         for (int i = 0; i < kOut; ++i) o[i] *= inv;
         mx = kMaskedLogit;
-        lse = kMaskedLogit + logf(static_cast<float>(K));
+        lse = kMaskedLogit + (K > 0 ? logf(static_cast<float>(K)) : 0.f);
     } else {
         const float inv = 1.0f / l;
 #pragma unroll
@@ -180,13 +202,13 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
         mx = m;
         lse = m + logf(l);
     }
-    T* orow = static_cast<T*>(p.out) + r * D;
+    T* orow = static_cast<T*>(p.out) + out_row * D;
 #pragma unroll
     for (int i = 0; i < kOut; ++i)
         if (has[i]) orow[lane + 64 * i] = static_cast<T>(o[i]);
     if (lane == 0) {
-        if (p.lse) p.lse[r] = lse;
-        if (p.mx) p.mx[r] = mx;
+        if (p.lse) p.lse[out_row] = lse;
+        if (p.mx) p.mx[out_row] = mx;
     }
 }
 

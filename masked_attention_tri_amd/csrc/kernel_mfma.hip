@@ -132,6 +132,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);
     constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK;
     constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
+    constexpr bool kVarlen = KIND == kMaskVarlen;
+    static_assert(!kVarlen || BIAS == kNoBias, "packed sequences carry no bias");
     // LDS: a ring of three buffers for K tiles and three for V tiles, and one
     // 32 x 32 fp32 bias block per wave (each wave refills its block as soon
     // as it has read it).  Every buffer is its own object, so the compiler
@@ -179,10 +181,23 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     const int64_t h = (lid / (n_qt * p.N)) % p.H;
     const int64_t b = lid / (n_qt * p.N * p.H);
 
-    const int K = static_cast<int>(p.K), Q = static_cast<int>(p.Q);
+    int K = static_cast<int>(p.K), Q = static_cast<int>(p.Q);
     const int64_t bnh = (b * p.N + n) * p.H + h;
-    const T* kbase = static_cast<const T*>(p.k) + bnh * p.K * D;
-    const T* vbase = static_cast<const T*>(p.v) + bnh * p.K * D;
+    // Rows: (b, n, h) slices of Q x D and K x D elements, or, for packed
+    // sequences, rows of q_rs / kv_rs elements from the sequence's first row.
+    int64_t q_first = 0, k_first = 0;
+    if constexpr (kVarlen) {
+        const SeqRows sr = seq_rows(p, b);
+        Q = static_cast<int>(sr.nq);
+        K = static_cast<int>(sr.nk);
+        q_first = sr.q0;
+        k_first = sr.k0;
+        if (qt * kQTile >= Q) return;  // the whole workgroup is past this sequence
+    }
+    const int64_t kv_rs = kVarlen ? p.kv_rs : D;  // K / V row stride (elements)
+    const uint32_t kv_row_bytes = static_cast<uint32_t>(kv_rs * sizeof(T));
+    const T* kbase = static_cast<const T*>(p.k) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * D);
+    const T* vbase = static_cast<const T*>(p.v) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * D);
     const float* bslice = BIAS != kNoBias ? p.bias + (b * p.H + h) * p.Q * p.K : nullptr;
     const int q0 = static_cast<int>(qt) * kQTile;
     const int q0w = q0 + 32 * wave;
@@ -198,6 +213,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
 
     // ---- visited key range / tile list -------------------------------
     int limit = K;  // keys >= limit are never valid
+    // causal packed sequences: no row of this tile sees a key past its last row
+    if (kVarlen && p.causal) limit = min(limit, q0 + kQTile);
     if (KIND == TRIATTN_MASK_KV_LENGTHS && p.kv_lengths) {
         const int64_t len = p.kv_lengths[b * p.N + n];
         limit = len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
@@ -248,7 +265,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     // ---- Q^T operand: registers for the whole key loop ----------------
     v8 qop[D / 16];
     {
-        const T* qp = static_cast<const T*>(p.q) + (bnh * p.Q + qload) * D + 8 * half;
+        const T* qp = static_cast<const T*>(p.q) +
+                      (kVarlen ? (q_first + qload) * p.q_rs + h * D : (bnh * p.Q + qload) * D) +
+                      8 * half;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
             v8 x = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(qp + 16 * st));
@@ -261,7 +280,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     }
 
     // ---- LDS regions and DMA address tables ------------------------------
-    const uint32_t kv_bytes = static_cast<uint32_t>(p.K * D * sizeof(T));
+    // rows past K read as zeros (the buffer range check)
+    const uint32_t kv_bytes = kVarlen ? static_cast<uint32_t>(K) * kv_row_bytes
+                                      : static_cast<uint32_t>(p.K * D * sizeof(T));
+    const uint32_t kv_tile_bytes = kKTile * kv_row_bytes;  // one tile of K or V rows in memory
     const uint32_t bias_bytes = BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * 4) : 0u;
     const u32x4 k_desc = make_desc(kbase, kv_bytes);
     const u32x4 v_desc = make_desc(vbase, kv_bytes);
@@ -284,11 +306,11 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         const bool is_v = I >= Ge::kDma;
         const int s = 64 * (I % Ge::kDma) + lane;
         const int r = s / Ge::chunks, c = s % Ge::chunks;
-        kv_src[j] = static_cast<uint32_t>(r * Ge::rowBytes +
+        kv_src[j] = static_cast<uint32_t>(r * kv_row_bytes +
                                           16 * (c ^ (is_v ? Ge::fv(r) : Ge::fk(r))));
     }
     auto dma_k = [&](int t, int x) {
-        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * Ge::tileBytes : kNoTile;
+        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * kv_tile_bytes : kNoTile;
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j) {
             const int I = wave + kWaves * j;  // wave-uniform
@@ -296,7 +318,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         }
     };
     auto dma_v = [&](int t, int x) {
-        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * Ge::tileBytes : kNoTile;
+        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * kv_tile_bytes : kNoTile;
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j) {
             const int I = wave + kWaves * j;
@@ -457,6 +479,12 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         if constexpr (kBlock) {
             if (p.mask_mod == TRIATTN_MOD_CAUSAL && !bit_set(full_bits, t / tiles_per_block) &&
                 k0 + kKTile - 1 > q0w) {
+                causal = true;
+                need_mask = true;
+            }
+        }
+        if constexpr (kVarlen) {
+            if (p.causal && k0 + kKTile - 1 > q0w) {
                 causal = true;
                 need_mask = true;
             }
@@ -657,7 +685,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int kk = ph; kk < K; kk += kPhases) {
             const v8 x = __builtin_bit_cast(
-                v8, *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(kk) * D + 8 * c));
+                v8, *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(kk) * kv_rs + 8 * c));
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] += static_cast<float>(x[e]);
         }
@@ -675,12 +703,14 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         for (int d = tid; d < D; d += kThreads) {
             float sum = 0.f;
             for (int w2 = 0; w2 < kWaves; ++w2) sum += part[w2 * D + d];
-            mean_v[d] = sum / static_cast<float>(K);
+            // (a packed sequence with no key at all averages nothing: 0)
+            mean_v[d] = K > 0 ? sum / static_cast<float>(K) : 0.f;
         }
         __syncthreads();
     }
     if (!row_ok) return;
-    T* orow = static_cast<T*>(p.out) + (bnh * p.Q + qrow) * D;
+    T* orow = static_cast<T*>(p.out) +
+              (kVarlen ? ((q_first + qrow) * p.H + h) * D : (bnh * p.Q + qrow) * D);
     const float inv = dead ? 0.f : 1.0f / l_tot;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -694,9 +724,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
             *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, o4);
         }
     if (half == 0) {
-        const int64_t ridx = bnh * p.Q + qrow;
+        const int64_t ridx = kVarlen ? (q_first + qrow) * p.H + h : bnh * p.Q + qrow;
         if (p.lse)
-            p.lse[ridx] = dead ? kMaskedLogit + logf(static_cast<float>(K))
+            p.lse[ridx] = dead ? kMaskedLogit + (K > 0 ? logf(static_cast<float>(K)) : 0.f)
                                : m_ref * zscale + logf(l_tot);
         if (p.mx) p.mx[ridx] = dead ? kMaskedLogit : m_true * zscale;
     }
@@ -729,12 +759,16 @@ hipError_t launch_bias(const Params& p, bool exact, hipStream_t stream) {
 
 template <typename T, int D, int KIND>
 hipError_t launch_kind(const Params& p, bool exact, hipStream_t stream) {
-    if (!p.bias) return launch_bias<T, D, KIND, kNoBias>(p, exact, stream);
-    // The DMA path moves 16-byte chunks of bias rows: rows must be 16-byte
-    // aligned.
-    const bool rows16 = p.K % 4 == 0 && reinterpret_cast<uintptr_t>(p.bias) % 16 == 0;
-    if (rows16) return launch_bias<T, D, KIND, kBiasLds>(p, exact, stream);
-    return launch_bias<T, D, KIND, kBiasScalar>(p, exact, stream);
+    if constexpr (KIND == kMaskVarlen) {
+        return launch_bias<T, D, KIND, kNoBias>(p, exact, stream);  // no bias
+    } else {
+        if (!p.bias) return launch_bias<T, D, KIND, kNoBias>(p, exact, stream);
+        // The DMA path moves 16-byte chunks of bias rows: rows must be 16-byte
+        // aligned.
+        const bool rows16 = p.K % 4 == 0 && reinterpret_cast<uintptr_t>(p.bias) % 16 == 0;
+        if (rows16) return launch_bias<T, D, KIND, kBiasLds>(p, exact, stream);
+        return launch_bias<T, D, KIND, kBiasScalar>(p, exact, stream);
+    }
 }
 
 template <typename T, int D>
@@ -747,6 +781,8 @@ hipError_t launch_d(const Params& p, bool exact, hipStream_t stream) {
         return launch_kind<T, D, TRIATTN_MASK_DENSE>(p, exact, stream);
     case TRIATTN_MASK_BLOCK:
         return launch_kind<T, D, TRIATTN_MASK_BLOCK>(p, exact, stream);
+    case kMaskVarlen:
+        return launch_kind<T, D, kMaskVarlen>(p, exact, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -779,7 +815,9 @@ bool mfma_supports(const Params& p, int32_t dtype) {
     const int64_t kpad = (p.K + kKTile - 1) / kKTile * kKTile;
     const int64_t qpad = (p.Q + 255) / 256 * 256;  // the largest query tile
     const int64_t lim = int64_t(1) << 31;
-    if (kpad * p.D * 2 >= lim || qpad * p.D * 2 >= lim || (qpad + 1) * kpad * 4 >= lim)
+    // packed sequences: K / V rows are kv_rs elements apart
+    const int64_t kv_row = p.mask_kind == kMaskVarlen ? p.kv_rs : p.D;
+    if (kpad * kv_row * 2 >= lim || qpad * p.D * 2 >= lim || (qpad + 1) * kpad * 4 >= lim)
         return false;
     // Other scales run as z = s * (Q.K + B/s): a negative s would flip the
     // max and a tiny one would overflow B/s; the generic kernel takes both.

@@ -146,6 +146,56 @@ Params make_params(const tri_attn_shape* s, const void* q, const void* k, const 
     return p;
 }
 
+// Validation of a packed variable-length call (see include/triattn.h).
+triattn_status varlen_check_impl(const tri_attn_varlen* d, int32_t dtype, const void* q,
+                                 const void* k, const void* v, float scale, const void* out,
+                                 const float* lse, const float* mx) {
+    if (!d) return TRIATTN_ERR_INVALID_ARG;
+    if (d->batch < 0 || d->heads < 0 || d->head_dim < 1 || d->total_q < 0 || d->total_kv < 0 ||
+        d->max_seqlen_q < 0 || d->max_seqlen_kv < 0)
+        return TRIATTN_ERR_INVALID_ARG;
+    if (d->layout != TRIATTN_QKV_SEPARATE && d->layout != TRIATTN_QKV_PACKED &&
+        d->layout != TRIATTN_KV_PACKED)
+        return TRIATTN_ERR_INVALID_ARG;
+    if (d->mask_type != TRIATTN_VARLEN_NO_MASK && d->mask_type != TRIATTN_VARLEN_PADDING &&
+        d->mask_type != TRIATTN_VARLEN_CAUSAL)
+        return TRIATTN_ERR_INVALID_ARG;
+    if (dtype != TRIATTN_F32 && dtype != TRIATTN_F16 && dtype != TRIATTN_BF16)
+        return TRIATTN_ERR_INVALID_ARG;
+    if (isinf(scale)) return TRIATTN_ERR_INVALID_ARG;
+    const bool packed = d->layout == TRIATTN_QKV_PACKED;
+    if (packed && (d->total_kv != d->total_q ||
+                   (d->cu_seqlens_kv && d->cu_seqlens_kv != d->cu_seqlens_q)))
+        return TRIATTN_ERR_INVALID_ARG;
+    const bool empty =
+        d->batch == 0 || d->heads == 0 || d->total_q == 0 || d->max_seqlen_q == 0;
+    if (!empty) {
+        if (!q || !out || !d->cu_seqlens_q) return TRIATTN_ERR_INVALID_ARG;
+        if (d->layout != TRIATTN_QKV_PACKED && !k) return TRIATTN_ERR_INVALID_ARG;
+        if (d->layout == TRIATTN_QKV_SEPARATE && !v) return TRIATTN_ERR_INVALID_ARG;
+        if (!packed && !d->cu_seqlens_kv) return TRIATTN_ERR_INVALID_ARG;
+    }
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(lse, 4) || !aligned(mx, 4) || !aligned(d->cu_seqlens_q, 4) ||
+        !aligned(d->cu_seqlens_kv, 4))
+        return TRIATTN_ERR_INVALID_ARG;
+    const int64_t D = d->head_dim;
+    if (dtype == TRIATTN_F32) {
+        if (D > 32 || D % 4 != 0) return TRIATTN_ERR_UNSUPPORTED;
+    } else {
+        if (D > 256 || D % 8 != 0) return TRIATTN_ERR_UNSUPPORTED;
+    }
+    // element counts of the packed tensors (3 heads-slabs per row at most)
+    const int64_t row = mul_or_neg(mul_or_neg(d->heads, D), 3);
+    if (row < 0 || mul_or_neg(d->total_q, row) < 0 || mul_or_neg(d->total_kv, row) < 0)
+        return TRIATTN_ERR_UNSUPPORTED;
+    const int64_t rows = mul_or_neg(mul_or_neg(d->batch, d->heads), d->max_seqlen_q);
+    if (rows < 0 || rows > (int64_t(1) << 40)) return TRIATTN_ERR_UNSUPPORTED;
+    if (d->total_q > INT32_MAX || d->total_kv > INT32_MAX || d->batch > INT32_MAX - 1)
+        return TRIATTN_ERR_UNSUPPORTED;  // cu_seqlens are int32
+    return TRIATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,6 +218,69 @@ triattn_status tri_attn_fwd(const tri_attn_shape* shape, int32_t dtype, const vo
     const hipError_t err = triattn::mfma_supports(p, dtype)
                                ? triattn::launch_mfma(p, dtype, stream)
                                : triattn::launch_generic(p, dtype, stream);
+    return err == hipSuccess ? TRIATTN_OK : TRIATTN_ERR_HIP;
+}
+
+triattn_status tri_attn_varlen_check(const tri_attn_varlen* desc, int32_t dtype, const void* q,
+                                     const void* k, const void* v, float scale, const void* out,
+                                     const float* lse, const float* max) {
+    return varlen_check_impl(desc, dtype, q, k, v, scale, out, lse, max);
+}
+
+triattn_status tri_attn_varlen_fwd(const tri_attn_varlen* d, int32_t dtype, const void* q,
+                                   const void* k, const void* v, float scale, void* out,
+                                   float* lse, float* max, hipStream_t stream) {
+    const triattn_status st = varlen_check_impl(d, dtype, q, k, v, scale, out, lse, max);
+    if (st != TRIATTN_OK) return st;
+    if (d->batch == 0 || d->heads == 0 || d->total_q == 0 || d->max_seqlen_q == 0)
+        return TRIATTN_OK;
+    const int64_t H = d->heads, D = d->head_dim;
+    const size_t esz = dtype == TRIATTN_F32 ? 4 : 2;
+    Params p{};
+    p.B = d->batch;
+    p.N = 1;
+    p.H = H;
+    p.Q = d->max_seqlen_q;
+    p.K = d->max_seqlen_kv;
+    p.D = D;
+    p.scale = isnan(scale) ? static_cast<float>(1.0 / sqrt(static_cast<double>(D))) : scale;
+    p.mask_kind = triattn::kMaskVarlen;
+    p.mask_mod = TRIATTN_MOD_NONE;
+    p.q_block = p.kv_block = p.max_blocks = p.full_max_blocks = 1;
+    p.n_q_rows = p.n_kv_blocks = 1;
+    p.cu_q = d->cu_seqlens_q;
+    p.cu_kv = d->layout == TRIATTN_QKV_PACKED ? d->cu_seqlens_q : d->cu_seqlens_kv;
+    p.total_q = d->total_q;
+    p.total_kv = d->layout == TRIATTN_QKV_PACKED ? d->total_q : d->total_kv;
+    p.causal = d->mask_type == TRIATTN_VARLEN_CAUSAL;
+    const char* qb = static_cast<const char*>(q);
+    switch (d->layout) {
+    case TRIATTN_QKV_SEPARATE:
+        p.q = q;
+        p.k = k;
+        p.v = v;
+        p.q_rs = p.kv_rs = H * D;
+        break;
+    case TRIATTN_QKV_PACKED:  // [T, 3, H, D]
+        p.q = q;
+        p.k = qb + H * D * esz;
+        p.v = qb + 2 * H * D * esz;
+        p.q_rs = p.kv_rs = 3 * H * D;
+        break;
+    default: {  // TRIATTN_KV_PACKED: q [Tq, H, D], kv [Tkv, 2, H, D]
+        const char* kb = static_cast<const char*>(k);
+        p.q = q;
+        p.k = k;
+        p.v = kb + H * D * esz;
+        p.q_rs = H * D;
+        p.kv_rs = 2 * H * D;
+    }
+    }
+    p.out = out;
+    p.lse = lse;
+    p.mx = max;
+    const hipError_t err = triattn::mfma_supports(p, dtype) ? triattn::launch_mfma(p, dtype, stream)
+                                                            : triattn::launch_generic(p, dtype, stream);
     return err == hipSuccess ? TRIATTN_OK : TRIATTN_ERR_HIP;
 }
 

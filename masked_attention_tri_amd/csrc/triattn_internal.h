@@ -33,7 +33,41 @@ struct Params {
     int64_t stride_b, stride_n, stride_h;
     int64_t n_q_rows;     // ceil(Q / q_block) (block kind)
     int64_t n_kv_blocks;  // ceil(K / kv_block) (block kind)
+    // Packed variable-length sequences (mask kind kMaskVarlen): B counts
+    // sequences, N = 1, Q and K are the largest lengths the launch covers,
+    // and sequence b is rows cu_q[b] .. cu_q[b+1]-1 of q / out and cu_kv[b]
+    // .. cu_kv[b+1]-1 of k / v.  Each packed row holds all H heads; q_rs and
+    // kv_rs are the row strides of q and of k / v in elements (out and the
+    // (row, head) lse / max are contiguous).
+    const int32_t* cu_q;
+    const int32_t* cu_kv;
+    int64_t total_q, total_kv;  // rows of the packed tensors
+    int64_t q_rs, kv_rs;
+    int32_t causal;  // varlen: key j of query row i valid only if j <= i
 };
+
+// Internal mask kind of the packed variable-length layouts (not a value of
+// the public tri_attn_mask_kind).
+constexpr int32_t kMaskVarlen = 4;
+
+// Rows of one packed sequence, read from the cu_seqlens arrays and clamped
+// so that they always lie inside the packed tensors: the boundaries are
+// clamped to [0, total] and made ascending, and the lengths to the launch's
+// maxima Q and K.
+struct SeqRows {
+    int64_t q0, nq, k0, nk;
+};
+__device__ __forceinline__ SeqRows seq_rows(const Params& p, int64_t b) {
+    auto clampi = [](int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); };
+    SeqRows r;
+    r.q0 = clampi(p.cu_q[b], 0, p.total_q);
+    const int64_t q1 = clampi(p.cu_q[b + 1], r.q0, p.total_q);
+    r.k0 = clampi(p.cu_kv[b], 0, p.total_kv);
+    const int64_t k1 = clampi(p.cu_kv[b + 1], r.k0, p.total_kv);
+    r.nq = q1 - r.q0 < p.Q ? q1 - r.q0 : p.Q;
+    r.nk = k1 - r.k0 < p.K ? k1 - r.k0 : p.K;
+    return r;
+}
 
 // The extra arguments of one backward call: the forward's output and the
 // incoming gradient (inputs), lse and max read through Params, and the

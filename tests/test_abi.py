@@ -277,3 +277,54 @@ def test_bwd_workspace_validation():
     # int64 overflow of the workspace size
     big = shape(B=1 << 20, N=1 << 20, H=1, Q=1 << 12, K=1 << 12, D=32)
     assert _bwd(big, ws=A, ws_bytes=0) == nat.TRIATTN_ERR_UNSUPPORTED
+
+
+def _varlen(**kw):
+    d = nat.TriAttnVarlen()
+    d.layout, d.mask_type = kw.get("layout", 0), kw.get("mask_type", 1)
+    d.batch, d.heads, d.head_dim = kw.get("batch", 2), kw.get("heads", 2), kw.get("D", 64)
+    d.total_q, d.total_kv = kw.get("total_q", 10), kw.get("total_kv", 12)
+    d.cu_seqlens_q = kw.get("cu_q", A)
+    d.cu_seqlens_kv = kw.get("cu_kv", A)
+    d.max_seqlen_q, d.max_seqlen_kv = kw.get("max_q", 8), kw.get("max_kv", 8)
+    return d
+
+
+def _vcheck(d, dtype=nat.TRIATTN_BF16, q=A, k=A, v=A, out=A, scale=math.nan):
+    return nat.tri_attn_varlen_check(d, dtype, q, k, v, scale, out, None, None)
+
+
+def test_varlen_check_accepts_every_layout():
+    assert _vcheck(_varlen()) == nat.TRIATTN_OK
+    assert _vcheck(_varlen(layout=nat.TRIATTN_QKV_PACKED, total_kv=10, cu_kv=None),
+                   k=None, v=None) == nat.TRIATTN_OK
+    assert _vcheck(_varlen(layout=nat.TRIATTN_KV_PACKED), v=None) == nat.TRIATTN_OK
+    assert _vcheck(_varlen(mask_type=nat.TRIATTN_VARLEN_CAUSAL), dtype=nat.TRIATTN_F32,
+                   ) == nat.TRIATTN_ERR_UNSUPPORTED  # D = 64 is past the fp32 envelope
+    assert _vcheck(_varlen(D=32), dtype=nat.TRIATTN_F32) == nat.TRIATTN_OK
+    # no work: pointers may be NULL
+    for kw in ({"batch": 0}, {"heads": 0}, {"total_q": 0}, {"max_q": 0}):
+        assert _vcheck(_varlen(cu_q=None, cu_kv=None, **kw), q=None, k=None, v=None,
+                       out=None) == nat.TRIATTN_OK
+
+
+@pytest.mark.parametrize("kw,ptrs", [
+    ({"layout": 3}, {}), ({"mask_type": 7}, {}), ({"batch": -1}, {}), ({"D": 0}, {}),
+    ({"max_kv": -1}, {}), ({"total_kv": -2}, {}), ({"cu_q": None}, {}), ({"cu_kv": None}, {}),
+    ({}, {"q": None}), ({}, {"k": None}), ({}, {"v": None}), ({}, {"out": None}),
+    ({}, {"q": A + 8}), ({"cu_q": A + 2}, {}),
+    ({"layout": 2}, {"k": None}),
+    ({"layout": 1, "total_kv": 11, "cu_kv": None}, {}),   # packed qkv: one row count
+    ({"layout": 1, "total_kv": 10, "cu_kv": A + 64}, {}),  # packed qkv: one offset array
+    ({}, {"scale": math.inf}),
+])
+def test_varlen_check_invalid_args(kw, ptrs):
+    assert _vcheck(_varlen(**kw), **ptrs) == nat.TRIATTN_ERR_INVALID_ARG
+
+
+def test_varlen_check_envelope_and_range():
+    assert _vcheck(_varlen(D=68)) == nat.TRIATTN_ERR_UNSUPPORTED
+    assert _vcheck(_varlen(D=264)) == nat.TRIATTN_ERR_UNSUPPORTED
+    assert _vcheck(_varlen(total_q=1 << 31)) == nat.TRIATTN_ERR_UNSUPPORTED  # int32 offsets
+    assert _vcheck(_varlen(batch=1 << 20, heads=1 << 12, max_q=1 << 12)) == \
+        nat.TRIATTN_ERR_UNSUPPORTED
