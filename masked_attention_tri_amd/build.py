@@ -13,8 +13,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtriattn.so")
-SOURCES = ["triattn_api.hip", "kernel_generic.hip", "kernel_mfma.hip", "kernel_util.hip",
-           "kernel_bwd.hip"]
+SOURCES = ["triattn_api.hip", "kernel_generic.hip", "kernel_mfma.hip", "kernel_mfma_d32.hip",
+           "kernel_mfma_d64.hip", "kernel_mfma_d128.hip", "kernel_mfma_d256.hip",
+           "kernel_util.hip", "kernel_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -35,22 +36,44 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every HIP source into one shared library; return its path."""
-    out_tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-o", out_tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature;
     # that line is expected noise.
     noise = "is not a recognized feature for this target"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
+    return res.returncode, msgs
+
+
+def build(verbose: bool = False, extra_flags=None, jobs: int = 0) -> str:
+    """Compile every HIP source into one shared library; return its path.
+
+    The sources compile to objects in parallel (up to `jobs` at once, default
+    min(8, CPUs)), then link; every call recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"] + list(extra_flags or [])
+    cmds = [[HIPCC, *compile_flags, "-c", "-o", os.path.join(objdir, src + ".o"),
+             os.path.join(CSRC, src)] for src in SOURCES]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        results = list(pool.map(_run, cmds))
+    for (rc, msgs), src in zip(results, SOURCES):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(msgs))
+        if verbose and msgs:
+            print("\n".join(msgs))
+    out_tmp = LIB + ".tmp"
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp,
+            *[os.path.join(objdir, src + ".o") for src in SOURCES]]
+    rc, msgs = _run(link)
+    if rc != 0:
+        raise RuntimeError("link failed:\n" + "\n".join(msgs))
     os.replace(out_tmp, LIB)
     return LIB
 

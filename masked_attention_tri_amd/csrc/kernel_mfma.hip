@@ -1,810 +1,19 @@
-// MFMA forward kernel for bf16 / fp16 inputs, D in {32, 64, 128}.
-//
-// Computes the triangle_attention page's equation: per (b, n, h) row,
-// O_q = sum_k softmax_k(s Q_q.K_k + B_qk, masked keys excluded) V_k, with the
-// lse / max auxiliaries, as a single pass over key tiles (an online,
-// max-shifted softmax; the page fixes the result, not the schedule).
-//
-// Work decomposition: one workgroup of 4 wavefronts owns 128 query rows of
-// one (b, n, h); wave w owns rows 32w .. 32w+31.  Keys go in tiles of 32,
-// which keeps the LDS footprint (and register state) small enough for four
-// workgroups per CU.
-//
-// Both contractions run on v_mfma_f32_32x32x16_{bf16,f16}:
-//   S^T = K . Q^T + C   A = K rows from LDS (16-byte reads), B = Q^T held in
-//                   registers for the whole key loop.  The accumulator puts
-//                   one query per lane and 16 keys per lane in registers, so
-//                   the softmax row reductions are in-lane plus one
-//                   v_permlane32_swap with the partner lane (lane ^ 32).
-//                   C is the fp32 bias tile itself, so the bias add costs no
-//                   vector instruction.
-//   O^T = V^T . P^T B = P^T taken directly from the S^T registers (converted
-//                   to bf16/fp16), A = V^T read from the row-major V tile with
-//                   ds_read_b64_tr_b16, which hands each lane four keys of
-//                   one column.  The query stays in the lane, so the running
-//                   rescale of O is a per-lane scalar.
-//
-// Data movement: every tile arrives by LDS DMA (buffer_load ... lds), never
-// through registers.  K and V tiles are shared by the workgroup in rings of
-// three buffers, loaded two tiles ahead.  The fp32 bias is the largest
-// stream (it is re-read for every n):
-// the accumulator layout would make each lane fetch 16 bytes from its own
-// query row, 32 rows per instruction, which saturates the L1 address path.
-// Instead each wave DMAs its 32 x 32 bias block with whole rows per lane
-// group (8 cache lines per instruction) into its own LDS region, reads it
-// back in the accumulator layout, and immediately refills the region with
-// the next tile's block.  LDS rows are unpadded; 16-byte chunks are stored
-// XOR-swizzled by row so that the operand reads are bank-conflict free.
-//
-// Buffer descriptors bound every access to its (b, n, h) slice.  The range
-// check covers the per-lane offset (not the scalar one), so all variable
-// offsets go in the per-lane offset: reads past a slice return 0 and touch
-// no memory, and ragged tiles need no clamping (those keys are masked).
-//
-// Scale: z = s*(Q.K) + B.  When s is 0 or a power of two, s*Q is exact in the
-// input format, so Q is scaled once at load and S = (sQ).K + B is z itself.
-// Otherwise C holds B/s and z = s*S.  Either way the exponent is one FMA:
-// p = exp2(S*c - m*c) with c = s_eff*log2(e).
-//
-// Softmax bookkeeping per query row: the exact running max (the "max"
-// output) and a reference max used in the exponent.  The reference is only
-// raised, and O and the sum rescaled, when a tile's max exceeds it by more
-// than ln(256); so p <= 256 and the rescale is rare.  The sum is taken over
-// the fp32 p, before they are rounded for the P.V contraction.
-//
-// Masks: kv_lengths and block lists cut whole tiles (tiles past the length,
-// blocks not listed); element masks are applied only on tiles that need
-// them (the ragged last tile, dense-mask tiles, causal partial blocks); full
-// blocks skip the mask.  Masked logits are -inf internally; a row left with
-// no valid key gets the page's uniform-weight result (mean of V over all K
-// keys, max -1e9, lse -1e9 + ln K).
-//
-// Grid: one workgroup per (b, n, h, query tile), remapped so that each of the
-// 8 XCDs walks a contiguous range of (b, h, n, q-tile) order: the q-tiles of
-// one (n, h) share K/V in that XCD's L2 and a head's fp32 bias (shared by
-// every n) stays resident there.  Within one (b, n, h) the q-tiles alternate
-// between the two ends, which balances causal block masks across CUs.
+// Dispatch of the MFMA forward kernel (mfma_fwd.h): which calls it serves,
+// and the head dimension's instantiation to launch (kernel_mfma_d*.hip, one
+// translation unit per D so that they compile in parallel).
 #include <math.h>
 
 #include "mfma_common.h"
 
 namespace triattn {
-namespace {
 
-using namespace tile;
-
-constexpr int kQTileBlock = 128;  // query rows per workgroup with block masks
-
-// Bias paths: none; staged through LDS by DMA; per-lane 4-byte loads (rows
-// not 16-byte aligned).
-enum BiasMode { kNoBias = 0, kBiasLds = 1, kBiasScalar = 2 };
-
-__device__ __forceinline__ bool bit_set(const uint32_t* bits, int64_t i) {
-    return (bits[i >> 5] >> (i & 31)) & 1u;
-}
-
-// First set bit at or after `from`, or -1.
-__device__ int64_t next_set(const uint32_t* bits, int64_t from, int64_t n) {
-    int64_t j = from;
-    while (j < n) {
-        const uint32_t w = bits[j >> 5] >> (j & 31);
-        if (w) {
-            const int64_t r = j + __builtin_ctz(w);
-            return r < n ? r : -1;
-        }
-        j = (j | 31) + 1;
-    }
-    return -1;
-}
-
-__device__ void mark_list(uint32_t* bits, const int32_t* counts, const int32_t* ids,
-                          int64_t list_row, int64_t width, int64_t n_blocks, int tid,
-                          int n_threads) {
-    int64_t count = counts[list_row];
-    count = count < 0 ? 0 : (count > width ? width : count);
-    const int32_t* row = ids + list_row * width;
-    for (int64_t j = tid; j < count; j += n_threads) {
-        const int64_t id = row[j];
-        if (id >= 0 && id < n_blocks) atomicOr(&bits[id >> 5], 1u << (id & 31));
-    }
-}
-
-// Waves per SIMD the register budget must allow: four (128 VGPRs) for
-// D <= 64, two for D = 128 (whose O accumulator alone takes 64 VGPRs).
-template <int D>
-constexpr int min_waves_per_simd() {
-    return D <= 64 ? 4 : 2;
-}
-
-template <typename T, int D, int KIND, int BIAS, bool EXACT, int W>
-__global__ __launch_bounds__(64 * W)
-__attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kernel(Params p) {
-    using M = Mma<T>;
-    using v8 = typename M::v8;
-    using Ge = Geo<D>;
-    constexpr int kWaves = W;
-    constexpr int kThreads = 64 * W;
-    constexpr int kQTile = 32 * W;  // query rows per workgroup
-    // The K and V DMA instructions of a tile are dealt evenly to the waves,
-    // so every wave has the same number in flight.
-    constexpr int kDmaPerWave = 2 * Ge::kDma / W;
-    static_assert(kDmaPerWave * W == 2 * Ge::kDma, "K/V DMAs split evenly over the waves");
-    constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);
-    constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK;
-    constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
-    constexpr bool kVarlen = KIND == kMaskVarlen;
-    static_assert(!kVarlen || BIAS == kNoBias, "packed sequences carry no bias");
-    // LDS: a ring of three buffers for K tiles and three for V tiles, and one
-    // 32 x 32 fp32 bias block per wave (each wave refills its block as soon
-    // as it has read it).  Every buffer is its own object, so the compiler
-    // knows that a DMA into one buffer does not write the others and does
-    // not wait for it before reading them.
-    constexpr int kBiasBuf = BIAS == kBiasLds ? kWaves * kBiasWaveBytes : 16;
-    __shared__ __attribute__((aligned(1024))) char k_lds0[Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char k_lds1[Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char k_lds2[Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char v_lds0[Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char v_lds1[Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char v_lds2[Ge::tileBytes];
-    __shared__ __attribute__((aligned(1024))) char b_lds[kBiasBuf];
-    __shared__ uint32_t listed_bits[kBlock ? kWords : 1];
-    __shared__ uint32_t full_bits[kBlock ? kWords : 1];
-    // after the key loop, the first K buffer holds the mean of V
-    float* const mean_v = reinterpret_cast<float*>(k_lds0);
-    static_assert(D * 4 <= Ge::tileBytes, "mean of V fits a K buffer");
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
-    const int col = lane & 31;  // this lane's query within the wave
-    const int half = lane >> 5;
-
-    // ---- workgroup -> (b, h, n, q tile), XCD-contiguous order ---------------
-    const int64_t n_qt = (p.Q + kQTile - 1) / kQTile;
-    const int64_t n_wg = gridDim.x;
-    const int64_t w = blockIdx.x;
-    const int64_t xcd = w % kXcds, slot = w / kXcds;
-    const int64_t per = n_wg / kXcds, rem = n_wg % kXcds;
-    const int64_t lid =
-        xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
-    // Query tiles of one (b, n, h) are taken in the order 0, T-1, 1, T-2, ...
-    // and every other (b, n, h) in the reverse of that.  Work per tile is the
-    // same for dense masks and lengths, but with a causal block mask tile i
-    // visits i + 1 blocks; when the whole grid is resident at once (512
-    // workgroups at two per CU), this puts heavy and light tiles side by side
-    // on a CU, whichever way the dispatcher fills its slots (consecutive
-    // workgroups, or workgroups one round apart).
-    const int64_t qr = lid % n_qt;
-    const int64_t qt0 = (qr & 1) ? n_qt - 1 - qr / 2 : qr / 2;
-    const int64_t qt = ((lid / n_qt) & 1) ? n_qt - 1 - qt0 : qt0;
-    const int64_t n = (lid / n_qt) % p.N;
-    const int64_t h = (lid / (n_qt * p.N)) % p.H;
-    const int64_t b = lid / (n_qt * p.N * p.H);
-
-    int K = static_cast<int>(p.K), Q = static_cast<int>(p.Q);
-    const int64_t bnh = (b * p.N + n) * p.H + h;
-    // Rows: (b, n, h) slices of Q x D and K x D elements, or, for packed
-    // sequences, rows of q_rs / kv_rs elements from the sequence's first row.
-    int64_t q_first = 0, k_first = 0;
-    if constexpr (kVarlen) {
-        const SeqRows sr = seq_rows(p, b);
-        Q = static_cast<int>(sr.nq);
-        K = static_cast<int>(sr.nk);
-        q_first = sr.q0;
-        k_first = sr.k0;
-        if (qt * kQTile >= Q) return;  // the whole workgroup is past this sequence
-    }
-    const int64_t kv_rs = kVarlen ? p.kv_rs : D;  // K / V row stride (elements)
-    const uint32_t kv_row_bytes = static_cast<uint32_t>(kv_rs * sizeof(T));
-    const T* kbase = static_cast<const T*>(p.k) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * D);
-    const T* vbase = static_cast<const T*>(p.v) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * D);
-    const float* bslice = BIAS != kNoBias ? p.bias + (b * p.H + h) * p.Q * p.K : nullptr;
-    const int q0 = static_cast<int>(qt) * kQTile;
-    const int q0w = q0 + 32 * wave;
-    const int qrow = q0w + col;  // this lane's query
-    const bool row_ok = qrow < Q;
-    const int qload = row_ok ? qrow : Q - 1;
-
-    // Scale handling (see the header comment).
-    const float zscale = EXACT ? 1.0f : p.scale;        // z = zscale * S
-    const float c_exp = zscale * kLog2e;                 // exponent slope in S units
-    const float lazy_s = kLazyLog / zscale;              // rescale threshold in S units
-    const float inv_s = EXACT ? 1.0f : 1.0f / p.scale;   // bias -> S units
-
-    // ---- visited key range / tile list -------------------------------
-    int limit = K;  // keys >= limit are never valid
-    // causal packed sequences: no row of this tile sees a key past its last row
-    if (kVarlen && p.causal) limit = min(limit, q0 + kQTile);
-    if (KIND == TRIATTN_MASK_KV_LENGTHS && p.kv_lengths) {
-        const int64_t len = p.kv_lengths[b * p.N + n];
-        limit = len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
-    }
-    const int n_tiles = (limit + kKTile - 1) / kKTile;
-    const int n_tiles_all = (K + kKTile - 1) / kKTile;
-    int tiles_per_block = 1;
-    // (if constexpr keeps the block bitmaps out of the other kinds' LDS)
-    if constexpr (kBlock) {
-        tiles_per_block = static_cast<int>(p.kv_block / kKTile);
-        const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
-        for (int i = tid; i < words; i += kThreads) {
-            listed_bits[i] = 0u;
-            full_bits[i] = 0u;
-        }
-        __syncthreads();
-        const int64_t inst = b * p.stride_b + n * p.stride_n + h * p.stride_h;
-        const int64_t list_row = inst * p.n_q_rows + q0 / p.q_block;
-        mark_list(listed_bits, p.kv_num_blocks, p.kv_indices, list_row, p.max_blocks,
-                  p.n_kv_blocks, tid, kThreads);
-        if (p.full_kv_num_blocks) {
-            mark_list(full_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid, kThreads);
-            mark_list(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid, kThreads);
-        }
-        __syncthreads();
-    }
-    auto first_tile = [&]() -> int {
-        if constexpr (!kBlock) {
-            return n_tiles > 0 ? 0 : -1;
-        } else {
-            const int64_t blk = next_set(listed_bits, 0, p.n_kv_blocks);
-            return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
-        }
-    };
-    auto next_tile = [&](int t) -> int {
-        if (t < 0) return -1;
-        if constexpr (!kBlock) {
-            return t + 1 < n_tiles ? t + 1 : -1;
-        } else {
-            if ((t + 1) % tiles_per_block != 0 && t + 1 < n_tiles_all) return t + 1;
-            const int64_t blk = next_set(listed_bits, t / tiles_per_block + 1, p.n_kv_blocks);
-            return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
-        }
-    };
-
-    // ---- Q^T operand: registers for the whole key loop ----------------
-    v8 qop[D / 16];
-    {
-        const T* qp = static_cast<const T*>(p.q) +
-                      (kVarlen ? (q_first + qload) * p.q_rs + h * D : (bnh * p.Q + qload) * D) +
-                      8 * half;
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            v8 x = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(qp + 16 * st));
-            if (EXACT) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = static_cast<T>(static_cast<float>(x[j]) * p.scale);
-            }
-            qop[st] = x;
-        }
-    }
-
-    // ---- LDS regions and DMA address tables ------------------------------
-    // rows past K read as zeros (the buffer range check)
-    const uint32_t kv_bytes = kVarlen ? static_cast<uint32_t>(K) * kv_row_bytes
-                                      : static_cast<uint32_t>(p.K * D * sizeof(T));
-    const uint32_t kv_tile_bytes = kKTile * kv_row_bytes;  // one tile of K or V rows in memory
-    const uint32_t bias_bytes = BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * 4) : 0u;
-    const u32x4 k_desc = make_desc(kbase, kv_bytes);
-    const u32x4 v_desc = make_desc(vbase, kv_bytes);
-    const u32x4 bias_desc = make_desc(bslice, bias_bytes);
-    const __amdgpu_buffer_rsrc_t bias_rsrc = make_rsrc(bslice, bias_bytes);
-    auto kbuf = [&](int x) { return (lds_char*)(x == 0 ? k_lds0 : x == 1 ? k_lds1 : k_lds2); };
-    auto vbuf = [&](int x) { return (lds_char*)(x == 0 ? v_lds0 : x == 1 ? v_lds1 : v_lds2); };
-    lds_char* const bias_lds = (lds_char*)b_lds + wave * kBiasWaveBytes;  // this wave's block
-
-    // K/V DMA of one tile: instruction I (I < kDma: K, else V) is issued by
-    // wave I % kWaves; lane l of it fills LDS slot s = 64 (I % kDma) + l of
-    // that tile, i.e. row s / chunks, stored chunk s % chunks, which holds
-    // source chunk (s % chunks) ^ f(row).  Every wave issues its
-    // instructions for every position, with kNoTile when there is no tile,
-    // so the count of DMAs in flight per position is fixed.
-    uint32_t kv_src[kDmaPerWave];
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-        const int I = wave + kWaves * j;
-        const bool is_v = I >= Ge::kDma;
-        const int s = 64 * (I % Ge::kDma) + lane;
-        const int r = s / Ge::chunks, c = s % Ge::chunks;
-        kv_src[j] = static_cast<uint32_t>(r * kv_row_bytes +
-                                          16 * (c ^ (is_v ? Ge::fv(r) : Ge::fk(r))));
-    }
-    auto dma_k = [&](int t, int x) {
-        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * kv_tile_bytes : kNoTile;
-#pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j) {
-            const int I = wave + kWaves * j;  // wave-uniform
-            if (I < Ge::kDma) dma16(k_desc, kbuf(x) + 1024 * I, kv_src[j] + toff);
-        }
-    };
-    auto dma_v = [&](int t, int x) {
-        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * kv_tile_bytes : kNoTile;
-#pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j) {
-            const int I = wave + kWaves * j;
-            if (I >= Ge::kDma) dma16(v_desc, vbuf(x) + 1024 * (I - Ge::kDma), kv_src[j] + toff);
-        }
-    };
-    // Bias DMA: the wave's block is kBiasDma instructions of 8 rows x 128
-    // bytes; lane l of instruction j fills row r = 8j + l/8, stored chunk
-    // l%8, holding source chunk (l%8) ^ fb(r) = (l%8) ^ (l/16) ^ 4(j%2).
-    // Rows past Q read past the slice and land as zeros; keys past K read
-    // the next row (masked).
-    const uint32_t b_row = static_cast<uint32_t>(q0w + (lane >> 3)) * static_cast<uint32_t>(K) * 4u;
-    const uint32_t b_src_even = b_row + 16u * static_cast<uint32_t>((lane & 7) ^ (lane >> 4));
-    const uint32_t b_src_odd = b_row + 16u * static_cast<uint32_t>((lane & 7) ^ (lane >> 4) ^ 4);
-    auto dma_bias = [&](int t) {
-        if (BIAS != kBiasLds) return;
-        const uint32_t toff = static_cast<uint32_t>(t) * kBiasRowBytes;
-#pragma unroll
-        for (int j = 0; j < kBiasDma; ++j) {
-            const uint32_t rows = static_cast<uint32_t>(8 * j) * static_cast<uint32_t>(K) * 4u;
-            dma16(bias_desc, bias_lds + 1024 * j, ((j & 1) ? b_src_odd : b_src_even) + rows + toff);
-        }
-    };
-    // Bias read into the accumulator layout: register 4g+e is key
-    // 8g + 4half + e, i.e. source chunk 2g + half of row col.
-    auto read_bias = [&](f32x16& dst) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int chunk = (2 * g + half) ^ fb(col);
-            const f32x4 bv = __builtin_bit_cast(
-                f32x4,
-                *reinterpret_cast<const lds_u32x4*>(bias_lds + col * kBiasRowBytes + 16 * chunk));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[4 * g + e] = bv[e];
-        }
-    };
-    // Bias for K % 4 != 0 (rows not 16-byte aligned): plain per-lane loads.
-    const uint32_t bias_lane_scalar =
-        static_cast<uint32_t>(qload) * static_cast<uint32_t>(K) * 4u + 16u * half;
-
-    auto load_bias_scalar = [&](int t, f32x16& dst) {
-        const uint32_t base = bias_lane_scalar + static_cast<uint32_t>(t) * kKTile * 4u;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dst[4 * g + e] = bload32(bias_rsrc, base + 4u * (8 * g + e));
-    };
-
-    // Per-lane LDS offsets of the operand reads (within a tile).
-    // K: row col, source chunk 2st + half, stored at chunk (2st + half) ^
-    // fk(col) = 2st ^ (half ^ fk(col)); the row, the chunk and its high
-    // bits occupy disjoint bits of the offset, so the offset of k-step st is
-    // k_base ^ 32st.
-    const int k_base = col * Ge::rowBytes + 16 * (half ^ Ge::fk(col));
-    // V (transposing read): lane s names row 16t + 8u + 4half + (s%16)/4 and
-    // column 32db + 16((s/16)%2) + 4(s%4), i.e. byte 8(s%2) of source chunk
-    // 4db + 2((s/16)%2) + (s%4)/2; lane l then receives V[key][32db + l%32]
-    // for the 4 keys of its slots 4u..4u+3.  The swizzle of row r depends on
-    // r % 8 only, which t and u do not change: they add (16t + 8u) rows.
-    // As for K, the column block db only flips bits of the stored chunk:
-    // the offset for db is v_base ^ 64db.
-    const int v_base = [&] {
-        const int r = 4 * half + ((lane & 15) >> 2);
-        const int chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-        return r * Ge::rowBytes + 16 * (chunk ^ Ge::fv(r)) + 8 * (lane & 1);
-    }();
-    // Dense key mask as bits: lane i of dense_word holds bit j = key
-    // 32(64c + i) + j valid, for the chunk c = dense_chunk of 64 tiles.  The
-    // loop reads a tile's word with one readlane, so it issues no memory
-    // operation for the mask; a chunk is rebuilt from the byte mask (32
-    // coalesced byte loads and ballots per 64 tiles) when the key loop
-    // reaches it.  The loads of a rebuild are waited for at once.
-    const uint8_t* dense_row = kDense ? p.dense + (b * p.N + n) * p.K : nullptr;
-    uint32_t dense_word = 0;
-    int dense_chunk = -1;
-    auto load_dense_chunk = [&](int c) {
-        const int t0 = 64 * c;
-        const int nt = min(64, n_tiles_all - t0);
-        uint32_t w = 0;
-        for (int i0 = 0; i0 < nt; i0 += 16) {
-            bool v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // the 64 lanes cover tiles t0 + i0 + 2j and t0 + i0 + 2j + 1
-                const int key = (t0 + i0 + 2 * j) * kKTile + lane;
-                v[j] = key < K && dense_row[key] != 0;
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint64_t bits = __ballot(v[j]);
-                w = lane == i0 + 2 * j ? static_cast<uint32_t>(bits) : w;
-                w = lane == i0 + 2 * j + 1 ? static_cast<uint32_t>(bits >> 32) : w;
-            }
-        }
-        dense_word = w;
-        dense_chunk = c;
-    };
-
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    float m_true = -INFINITY;  // exact running max of this row, S units
-    float m_ref = -INFINITY;   // reference max of the exponent, S units
-    float m_thr = -INFINITY;   // m_ref + the lazy-rescale margin
-    float m_exp = 0.f;         // m_ref * c_exp (0 while m_ref is -inf)
-    float l_run = 0.f;         // this lane's half of the running sum
-
-    // At D = 64 the QK MFMAs of one tile are interleaved with the
-    // exponentials of the previous one (softmax_pv below); at D = 32 and 128
-    // that measured slower than issuing them as one group.  The per-lane
-    // bias loads keep the grouped order: interleaved, their registers spill.
-    constexpr bool kInterleave = D == 64 && BIAS != kBiasScalar;
-
-    // S^T = K . Q^T + bias for tile t from K buffer x and this wave's bias
-    // block.  qk_load reads the bias into s and the K operands into kop;
-    // the key loop issues the MFMAs later, between the exponentials of the
-    // previous tile (qk does both at once, for the first tile).
-    v8 kop[D / 16];
-    auto qk_load = [&](f32x16& s, int t, int x) {
-        s = f32x16{};
-        if (BIAS == kBiasLds) read_bias(s);
-        if (BIAS == kBiasScalar) load_bias_scalar(t, s);
-        if (BIAS != kNoBias && !EXACT) s *= inv_s;
-        const lds_char* kt = kbuf(x);
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st)
-            kop[st] = __builtin_bit_cast(v8, *reinterpret_cast<const lds_u32x4*>(kt + (k_base ^ (32 * st))));
-    };
-    auto qk = [&](f32x16& s, int t, int x) {
-        qk_load(s, t, x);
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) s = M::run(kop[st], qop[st], s);
-    };
-
-    // Softmax of tile t (logits in s) and O^T += V^T . P^T from V buffer x.
-    // Between the row max and the exponentials it calls dma() (this
-    // position's DMAs, issued once the bias reads have long returned).  With
-    // kInterleave the MFMAs of the next tile's logits (operands already in
-    // kop and s_nxt) are interleaved with the exponentials, one MFMA per few
-    // vector instructions, so that the matrix core runs them while the wave
-    // keeps issuing the softmax instead of stalling on their dependent chain.
-    auto softmax_pv = [&](f32x16& s, int t, int x, f32x16& s_nxt, auto dma) {
-        const int k0 = t * kKTile;
-        // ---- element mask (only on tiles that need one) -------------------
-        // Register r holds key k0 + 8(r/4) + r%4 in lanes 0-31 and that key
-        // + 4 in lanes 32-63, so the length and dense-mask tests are uniform
-        // per wave half: they become one 64-bit lane mask per register,
-        // built with scalar instructions and applied by one select.
-        bool need_mask = k0 + kKTile > limit;
-        bool causal = false;
-        uint32_t dense_bits = ~0u;
-        if (kDense) {
-            // bit i = key k0 + i valid (both wave halves hold the same 32 keys)
-            if ((t >> 6) != dense_chunk) load_dense_chunk(t >> 6);
-            dense_bits = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dense_word), t & 63));
-            need_mask = dense_bits != ~0u;
-        }
-        if constexpr (kBlock) {
-            if (p.mask_mod == TRIATTN_MOD_CAUSAL && !bit_set(full_bits, t / tiles_per_block) &&
-                k0 + kKTile - 1 > q0w) {
-                causal = true;
-                need_mask = true;
-            }
-        }
-        if constexpr (kVarlen) {
-            if (p.causal && k0 + kKTile - 1 > q0w) {
-                causal = true;
-                need_mask = true;
-            }
-        }
-        if (need_mask) {
-            // bit i of w: key k0 + i passes the length and dense tests
-            const int room = limit - k0;
-            uint32_t w = room >= kKTile ? ~0u : room <= 0 ? 0u : (1u << room) - 1u;
-            if (kDense) w &= dense_bits;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ka = 8 * (r / 4) + (r % 4);  // key offset in lanes 0-31
-                // lanes 0-31 take bit ka, lanes 32-63 bit ka + 4, each spread
-                // over its 32 lanes by sign-extending the one-bit field
-                const uint32_t lo = static_cast<uint32_t>(static_cast<int32_t>(w << (31 - ka)) >> 31);
-                const uint32_t hi = static_cast<uint32_t>(static_cast<int32_t>(w << (27 - ka)) >> 31);
-                bool ok = __builtin_amdgcn_inverse_ballot_w64(lo | (static_cast<uint64_t>(hi) << 32));
-                if (causal) ok = ok && qrow >= k0 + ka + 4 * half;
-                s[r] = ok ? s[r] : -INFINITY;
-            }
-        }
-
-        // ---- row max; lazily raised reference ------------------------------
-        // a tree of three-input maxima (8 instructions for 16 values)
-        const float m0 = vmax(vmax(s[0], s[1]), s[2]);
-        const float m1 = vmax(vmax(s[3], s[4]), s[5]);
-        const float m2 = vmax(vmax(s[6], s[7]), s[8]);
-        const float m3 = vmax(vmax(s[9], s[10]), s[11]);
-        const float m4 = vmax(vmax(s[12], s[13]), s[14]);
-        float mloc = vmax(vmax(vmax(m0, m1), m2), vmax(vmax(m3, m4), s[15]));
-        mloc = max_halves(mloc);
-        m_true = vmax(m_true, mloc);
-        const bool raise = mloc > m_thr;  // false while mloc == -inf
-        if (__ballot(raise)) {
-            // lanes that do not raise keep alpha = 1 exactly (their m_ref may
-            // still be -inf); a raising lane with m_ref = -inf gets alpha = 0
-            const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mloc) * c_exp) : 1.0f;
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-            if (raise) {
-                m_ref = mloc;
-                m_thr = mloc + lazy_s;
-                m_exp = mloc * c_exp;
-            }
-        }
-        const float mb = m_exp;
-        dma();
-
-        // ---- probabilities, their fp32 sum, P^T operands (rounded) ---------
-        // The sum must use the unrounded p: rounding each p to bf16 moves
-        // lse by up to ~2^-9, past its tolerance on short rows.
-        v8 pop[2];
-        float psum = 0.f;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-            for (int j = 0; j < 8; j += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * tt + j], c_exp, -mb));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * tt + j + 1], c_exp, -mb));
-                psum += p0 + p1;
-                pop[tt][j] = static_cast<T>(p0);
-                pop[tt][j + 1] = static_cast<T>(p1);
-            }
-        l_run += psum;
-        // ---- S^T of the next tile, interleaved with the code above ----------
-        if constexpr (kInterleave) {
-#pragma unroll
-            for (int st = 0; st < D / 16; ++st) s_nxt = M::run(kop[st], qop[st], s_nxt);
-            // scheduling pattern: (1 MFMA, 7 VALU) per k-step
-#pragma unroll
-            for (int i = 0; i < D / 16; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-            }
-        }
-
-        // ---- O^T += V^T . P^T ----------------------------------------------
-        const lds_char* vt = vbuf(x);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(vt + (v_base ^ (64 * db)) + 16 * tt * Ge::rowBytes));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_i16x4*)(vt + (v_base ^ (64 * db)) + (16 * tt + 8) * Ge::rowBytes));
-                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo);
-                const u32x2 hi2 = __builtin_bit_cast(u32x2, hi);
-                const v8 a = __builtin_bit_cast(v8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
-                oacc[db] = M::run(a, pop[tt], oacc[db]);
-            }
-    };
-
-    // ---- key loop ---------------------------------------------------------
-    // Position j of the tile sequence t_0, t_1, ... keeps K(t_j) and V(t_j)
-    // in ring buffers j % 3.  At position j the logits of cur = t_j are in
-    // registers; the loop computes the logits of nxt = t_{j+1} (K buffer
-    // (j+1) % 3, bias block) and the softmax and P.V of t_j (V buffer j % 3),
-    // so the QK contraction of one tile overlaps the softmax of the previous
-    // one.  With kInterleave it reads the operands of the logits of t_{j+1},
-    // takes the row max of t_j, issues the DMAs and then runs the
-    // exponentials of t_j with the QK MFMAs of t_{j+1} between them; when
-    // there is no t_{j+1} those reads and MFMAs still run, on stale buffers
-    // that no DMA is writing, and their result is never used: that keeps the
-    // exponentials and the MFMAs in one scheduling region.  Otherwise the
-    // QK MFMAs go first and the DMAs follow them.  K/V DMAs run two positions ahead (K of t_{j+3}, V of
-    // t_{j+2}); the bias block is refilled with t_{j+2} right after the
-    // logits of t_{j+1} have read it.  Each position first waits for all of
-    // this wave's DMAs but the K/V ones of the previous position.
-    constexpr int kKvInFlight = kDmaPerWave;  // K/V DMAs a wave issues per position
-    f32x16 sa, sb;
-    int cur = first_tile();
-    int nxt = next_tile(cur);
-    int nxt2 = next_tile(nxt);
-    if (cur >= 0) {
-        // prologue: K(t0), bias(t0) | K(t1), V(t0) | logits of t0 | bias(t1) |
-        // K(t2), V(t1)
-        if constexpr (kDense) load_dense_chunk(cur >> 6);  // before any DMA is in flight
-        dma_k(cur, 0);
-        if (BIAS == kBiasLds) dma_bias(cur);
-        dma_k(nxt, 1);
-        dma_v(cur, 0);
-        wait_vmem();
-        __syncthreads();
-        qk(sa, cur, 0);
-        if (BIAS == kBiasLds && nxt >= 0) {
-            wait_lds();  // the bias reads are done before the block is refilled
-            dma_bias(nxt);
-        }
-        dma_k(nxt2, 2);
-        dma_v(nxt, 1);
-    }
-    auto step = [&](auto X, f32x16& s_cur, f32x16& s_nxt) {
-        constexpr int x = decltype(X)::value;  // j % 3
-        const int nxt3 = __builtin_amdgcn_readfirstlane(next_tile(nxt2));
-        // Everything but the last position's K/V DMAs has landed: K(nxt),
-        // V(cur) and the bias block of nxt, for every wave once all have
-        // passed the barrier, which also means every wave is done with the
-        // buffers refilled below.
-        __builtin_amdgcn_s_waitcnt(kVmcntWait<kKvInFlight>());
-        __syncthreads();
-        auto dma = [&]() {  // this position's DMAs
-            if (BIAS == kBiasLds && nxt2 >= 0) {
-                wait_lds();
-                dma_bias(nxt2);
-            }
-            dma_k(nxt3, x);           // K(t_j) was last read one position ago
-            dma_v(nxt2, (x + 2) % 3);  // V(t_{j-1}) likewise
-        };
-        if constexpr (kInterleave) {
-            qk_load(s_nxt, nxt, (x + 1) % 3);
-            softmax_pv(s_cur, cur, x, s_nxt, dma);
-        } else {
-            if (nxt >= 0) qk(s_nxt, nxt, (x + 1) % 3);
-            dma();
-            softmax_pv(s_cur, cur, x, s_nxt, [] {});
-        }
-        cur = nxt;
-        nxt = nxt2;
-        nxt2 = nxt3;
-    };
-    while (cur >= 0) {
-        step(Par<0>{}, sa, sb);
-        if (cur < 0) break;
-        step(Par<1>{}, sb, sa);
-        if (cur < 0) break;
-        step(Par<2>{}, sa, sb);
-        if (cur < 0) break;
-        step(Par<0>{}, sb, sa);
-        if (cur < 0) break;
-        step(Par<1>{}, sa, sb);
-        if (cur < 0) break;
-        step(Par<2>{}, sb, sa);
-    }
-
-    // ---- epilogue ---------------------------------------------------------
-    const float l_tot = sum_halves(l_run);
-    const bool dead = m_true == -INFINITY;
-    // Does any row of the workgroup lack a valid key?  The flag lives in a K
-    // buffer: after this wave's DMAs have landed and every wave has left the
-    // loop, the ring is free.
-    wait_vmem();
-    __syncthreads();
-    int* const any_dead = reinterpret_cast<int*>(k_lds1);
-    if (tid == 0) *any_dead = 0;
-    __syncthreads();
-    if (__ballot(dead && row_ok) && lane == 0) *any_dead = 1;
-    __syncthreads();
-    if (*any_dead) {
-        // Some row saw no valid key: its weights are uniform over all K keys.
-        // Thread (key phase ph, 16-byte chunk c) sums rows ph, ph + P, ...;
-        // lanes holding the same chunk are then summed by shuffles, and the
-        // per-wave partial sums in LDS.
-        constexpr int kChunks = D / 8;
-        constexpr int kPhases = kThreads / kChunks;
-        const int c = tid % kChunks, ph = tid / kChunks;
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int kk = ph; kk < K; kk += kPhases) {
-            const v8 x = __builtin_bit_cast(
-                v8, *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(kk) * kv_rs + 8 * c));
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += static_cast<float>(x[e]);
-        }
-#pragma unroll
-        for (int off = kChunks; off < 64; off <<= 1)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
-        float* const part = reinterpret_cast<float*>(k_lds2);  // kWaves x D partial sums
-        static_assert(kWaves * D * 4 <= Ge::tileBytes, "partial sums fit a K buffer");
-        if (lane < kChunks) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part[wave * D + 8 * lane + e] = acc[e];
-        }
-        __syncthreads();
-        for (int d = tid; d < D; d += kThreads) {
-            float sum = 0.f;
-            for (int w2 = 0; w2 < kWaves; ++w2) sum += part[w2 * D + d];
-            // (a packed sequence with no key at all averages nothing: 0)
-            mean_v[d] = K > 0 ? sum / static_cast<float>(K) : 0.f;
-        }
-        __syncthreads();
-    }
-    if (!row_ok) return;
-    T* orow = static_cast<T*>(p.out) +
-              (kVarlen ? ((q_first + qrow) * p.H + h) * D : (bnh * p.Q + qrow) * D);
-    const float inv = dead ? 0.f : 1.0f / l_tot;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int d0 = 32 * db + 8 * g + 4 * half;
-            T o4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o4[e] = static_cast<T>(dead ? mean_v[d0 + e] : oacc[db][4 * g + e] * inv);
-            *reinterpret_cast<u32x2*>(orow + d0) = __builtin_bit_cast(u32x2, o4);
-        }
-    if (half == 0) {
-        const int64_t ridx = kVarlen ? (q_first + qrow) * p.H + h : bnh * p.Q + qrow;
-        if (p.lse)
-            p.lse[ridx] = dead ? kMaskedLogit + (K > 0 ? logf(static_cast<float>(K)) : 0.f)
-                               : m_ref * zscale + logf(l_tot);
-        if (p.mx) p.mx[ridx] = dead ? kMaskedLogit : m_true * zscale;
-    }
-}
-
-// Waves per workgroup.  The kernel also runs with 8 (256 query rows sharing
-// each K/V tile, half the K/V bytes per wave); on the kv_lengths workload at
-// D = 64 that measured no faster than 4, which wastes fewer rows when Q is
-// not a multiple of 256, so 4 is used.
-template <int D, int KIND>
-constexpr int waves_of() {
-    return 4;
-}
-
-template <typename T, int D, int KIND, int BIAS>
-hipError_t launch_bias(const Params& p, bool exact, hipStream_t stream) {
-    constexpr int W = waves_of<D, KIND>();
-    const int64_t n_qt = (p.Q + 32 * W - 1) / (32 * W);
-    const int64_t groups = p.B * p.N * p.H * n_qt;
-    if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid(static_cast<unsigned>(groups));
-    if (exact)
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, W>), grid, dim3(64 * W), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false, W>), grid, dim3(64 * W), 0,
-                           stream, p);
-    return hipGetLastError();
-}
-
-template <typename T, int D, int KIND>
-hipError_t launch_kind(const Params& p, bool exact, hipStream_t stream) {
-    if constexpr (KIND == kMaskVarlen) {
-        return launch_bias<T, D, KIND, kNoBias>(p, exact, stream);  // no bias
-    } else {
-        if (!p.bias) return launch_bias<T, D, KIND, kNoBias>(p, exact, stream);
-        // The DMA path moves 16-byte chunks of bias rows: rows must be 16-byte
-        // aligned.
-        const bool rows16 = p.K % 4 == 0 && reinterpret_cast<uintptr_t>(p.bias) % 16 == 0;
-        if (rows16) return launch_bias<T, D, KIND, kBiasLds>(p, exact, stream);
-        return launch_bias<T, D, KIND, kBiasScalar>(p, exact, stream);
-    }
-}
-
-template <typename T, int D>
-hipError_t launch_d(const Params& p, bool exact, hipStream_t stream) {
-    switch (p.mask_kind) {
-    case TRIATTN_MASK_NONE:  // a kv_lengths mask with no lengths: limit = K
-    case TRIATTN_MASK_KV_LENGTHS:
-        return launch_kind<T, D, TRIATTN_MASK_KV_LENGTHS>(p, exact, stream);
-    case TRIATTN_MASK_DENSE:
-        return launch_kind<T, D, TRIATTN_MASK_DENSE>(p, exact, stream);
-    case TRIATTN_MASK_BLOCK:
-        return launch_kind<T, D, TRIATTN_MASK_BLOCK>(p, exact, stream);
-    case kMaskVarlen:
-        return launch_kind<T, D, kMaskVarlen>(p, exact, stream);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <typename T>
-hipError_t launch_t(const Params& p, bool exact, hipStream_t stream) {
-    switch (p.D) {
-    case 32:
-        return launch_d<T, 32>(p, exact, stream);
-    case 64:
-        return launch_d<T, 64>(p, exact, stream);
-    case 128:
-        return launch_d<T, 128>(p, exact, stream);
-    }
-    return hipErrorInvalidValue;
-}
-
-}  // namespace
+using tile::kKTile;
+using tile::kQTileBlock;
+using tile::scale_is_exact;
 
 bool mfma_supports(const Params& p, int32_t dtype) {
     if (dtype != TRIATTN_BF16 && dtype != TRIATTN_F16) return false;
-    if (p.D != 32 && p.D != 64 && p.D != 128) return false;
+    if (p.D != 32 && p.D != 64 && p.D != 128 && p.D != 256) return false;
     if (p.mask_kind == TRIATTN_MASK_BLOCK) {
         // one block row per workgroup, whole tiles per kv block
         if (p.q_block % kQTileBlock != 0 || p.kv_block % kKTile != 0) return false;
@@ -827,8 +36,17 @@ bool mfma_supports(const Params& p, int32_t dtype) {
 
 hipError_t launch_mfma(const Params& p, int32_t dtype, hipStream_t stream) {
     const bool exact = scale_is_exact(p.scale);
-    if (dtype == TRIATTN_BF16) return launch_t<__bf16>(p, exact, stream);
-    return launch_t<_Float16>(p, exact, stream);
+    switch (p.D) {
+    case 32:
+        return launch_mfma_d32(p, dtype, exact, stream);
+    case 64:
+        return launch_mfma_d64(p, dtype, exact, stream);
+    case 128:
+        return launch_mfma_d128(p, dtype, exact, stream);
+    case 256:
+        return launch_mfma_d256(p, dtype, exact, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace triattn

@@ -22,9 +22,8 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// A workgroup has W waves (4 or 8) and owns 32 W query rows; block masks use
-// W = 4 (128-row blocks hold whole workgroups).
 constexpr int kKTile = 32;           // keys per K/V tile
+constexpr int kQTileBlock = 128;  // query rows per workgroup with block masks
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog = 5.545177444479562f;  // ln(256): largest p before a rescale
@@ -61,7 +60,10 @@ struct Geo {
     static_assert(kDma * 1024 == tileBytes, "whole DMA instructions per tile");
     // K is read 16 bytes per lane down consecutive rows (8 or 16 lanes per
     // LDS cycle at one chunk): consecutive rows must land on distinct banks.
+    // (At D = 128 and 256 a row is a whole number of 256-byte bank cycles,
+    // so both take the same swizzles.)
     static __device__ __forceinline__ int fk(int r) {
+        static_assert(D == 32 || D == 64 || D == 128 || D == 256, "swizzles defined");
         if (D == 32) return ((r >> 1) ^ (r >> 3)) & 3;
         if (D == 64) return (r + (r >> 3)) & 7;
         return r & 15;

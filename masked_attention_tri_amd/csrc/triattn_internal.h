@@ -98,6 +98,12 @@ constexpr int64_t kMaxKvBlocks = 8192;
 hipError_t launch_generic(const Params& p, int32_t dtype, hipStream_t stream);
 hipError_t launch_mfma(const Params& p, int32_t dtype, hipStream_t stream);
 bool mfma_supports(const Params& p, int32_t dtype);
+// The MFMA kernel's instantiations, one per head dimension (exact: the scale
+// is folded into Q exactly).
+hipError_t launch_mfma_d32(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
+hipError_t launch_mfma_d64(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
+hipError_t launch_mfma_d128(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
+hipError_t launch_mfma_d256(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
 hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, hipStream_t stream);
 hipError_t launch_mask_to_kv_lengths(const uint8_t* mask, int64_t rows, int64_t K,
                                      int32_t* kv_lengths, int32_t* nonprefix_rows,

@@ -77,6 +77,7 @@ def test_run_to_run_determinism(key):
     ("bf16", 64, "block", (1, 2, 2, 1024, 1024),
      {"q_block": 128, "kv_block": 64, "mask_mod": "causal"}),
     ("f16", 128, "block", (2, 1, 2, 640, 600), {"q_block": 128, "kv_block": 128}),
+    ("bf16", 256, "kv_lengths", (1, 3, 2, 300, 200), {"len_range": (0, 200)}),
 ])
 def test_every_output_element_is_written(dt, D, kind, shape, extra):
     say(f"NaN-prefilled outputs {dt} D={D} {kind} {shape}")

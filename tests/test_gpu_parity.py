@@ -89,6 +89,12 @@ MFMA_CASES = [
     # dense masks past 64 key tiles: the mask bits are rebuilt per 64 tiles
     (1, 1, 2, 64, 4200, 64, "bf16", "dense", {}),
     (1, 2, 1, 96, 2090, 32, "bf16", "dense", {"p_valid": 0.9}),
+    # D = 256 (one wave per SIMD): several query tiles, ragged keys, every mask kind
+    (1, 2, 2, 300, 333, 256, "bf16", "kv_lengths", {"len_range": (0, 333)}),
+    (1, 2, 2, 130, 257, 256, "f16", "dense", {}),
+    (1, 1, 2, 384, 384, 256, "bf16", "block", {"q_block": 128, "kv_block": 64,
+                                                "mask_mod": "causal"}),
+    (2, 1, 2, 64, 100, 256, "bf16", "none", {"bias": False, "scale": 0.3}),
 ]
 
 GENERIC_CASES = [
