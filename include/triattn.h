@@ -175,6 +175,29 @@ triattn_status tri_attn_fwd(const tri_attn_shape* shape, int32_t dtype, const vo
                             float* max, hipStream_t stream);
 
 /*
+ * tri_attn_fwd with the bias in a chosen element type.  The
+ * triangle_attention page's Parameters ("bias") say that its newest kernels
+ * cast the bias to the q/k/v dtype (bf16/fp16) for best performance; this
+ * entry point takes such a bias as it is, instead of requiring fp32.
+ *
+ * `bias_dtype`: TRIATTN_F32 (then `bias` is (B,1,H,Q,K) fp32 and the call
+ * is exactly tri_attn_fwd) or equal to `dtype` when that is TRIATTN_F16 or
+ * TRIATTN_BF16 (then `bias` is (B,1,H,Q,K) of that type, 2-byte aligned;
+ * K % 8 == 0 and 16-byte alignment keep it on the MFMA kernel).  Each bias
+ * value is widened exactly to fp32 and the computation is the one of
+ * tri_attn_fwd with that fp32 bias: the only difference from passing the
+ * fp32 original is the bias's own rounding to 16 bits (on the order of 1e-3
+ * in lse for a unit-variance bias, past the 1e-3 lse tolerance kept for fp32
+ * biases).  The backward (tri_attn_bwd) takes the same values as fp32.
+ * Other arguments, results and errors as tri_attn_fwd, plus
+ * TRIATTN_ERR_INVALID_ARG for any other bias_dtype or a misaligned bias.
+ */
+triattn_status tri_attn_fwd_bias_dtype(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                                       const void* k, const void* v, const void* bias,
+                                       int32_t bias_dtype, const tri_attn_mask* mask, float scale,
+                                       void* out, float* lse, float* max, hipStream_t stream);
+
+/*
  * ---- Packed variable-length sequences ------------------------------------
  *
  * The fused-attention layouts of Transformer Engine's fused_attn.h (release

@@ -45,6 +45,7 @@ from ._native import (  # noqa: F401
     tri_attn_bwd,
     tri_attn_check,
     tri_attn_fwd,
+    tri_attn_fwd_bias_dtype,
     tri_attn_mask_to_kv_lengths,
     tri_attn_status_str,
     tri_attn_varlen_check,
@@ -54,7 +55,8 @@ from ._native import (  # noqa: F401
 __all__ = ["triangle_attention", "triangle_attention_backward", "triangle_attention_autograd",
            "triangle_attention_varlen", "mask_to_kv_lengths", "tri_attn_varlen_fwd",
            "tri_attn_varlen_check",
-           "BlockMask", "causal_mask", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_check",
+           "BlockMask", "causal_mask", "tri_attn_fwd", "tri_attn_fwd_bias_dtype", "tri_attn_bwd",
+           "tri_attn_check",
            "tri_attn_status_str",
            "tri_attn_mask_to_kv_lengths", "load_library"]
 
@@ -208,9 +210,10 @@ def _as5(x, name):
     return x
 
 
-def _prepare(q, k, v, bias, mask, kv_lengths, block_mask):
+def _prepare(q, k, v, bias, mask, kv_lengths, block_mask, bias_in_input_dtype=False):
     """Shape and dtype checks, 5-D views, contiguous copies, and the mask
-    descriptor (with the tensors it points at, which must stay alive)."""
+    descriptor (with the tensors it points at, which must stay alive).  The
+    bias is cast to fp32, or to q's 16-bit dtype with bias_in_input_dtype."""
     if mask is not None and kv_lengths is not None:
         raise ValueError("pass either mask or kv_lengths, not both")
     if block_mask is not None and (mask is not None or kv_lengths is not None):
@@ -233,7 +236,8 @@ def _prepare(q, k, v, bias, mask, kv_lengths, block_mask):
     if bias5 is not None:
         if tuple(bias5.shape) != (B, 1, H, Q, K):
             raise ValueError(f"bias must be (B,1,H,Q,K) = {(B, 1, H, Q, K)}")
-        bias5 = bias5.to(device=dev, dtype=torch.float32).contiguous()
+        bias_t = q5.dtype if bias_in_input_dtype else torch.float32
+        bias5 = bias5.to(device=dev, dtype=bias_t).contiguous()
 
     desc = None
     keep = []
@@ -262,7 +266,8 @@ def _prepare(q, k, v, bias, mask, kv_lengths, block_mask):
 
 def triangle_attention(q, k, v, bias=None, mask=None, scale: Optional[float] = None,
                        return_aux: bool = False, *, kv_lengths=None,
-                       block_mask: Optional[BlockMask] = None, stream=None):
+                       block_mask: Optional[BlockMask] = None, stream=None,
+                       bias_in_input_dtype: bool = False):
     """Attention_q = sum_k softmax_k(s Q_q.K_k + B_qk if key k is valid else
     -1e9) V_k over (B, N, H, Q, D) tensors.
 
@@ -272,9 +277,15 @@ def triangle_attention(q, k, v, bias=None, mask=None, scale: Optional[float] = N
     means 1/sqrt(D).  Returns O (q's dtype), or (O, lse, max) with fp32 lse
     and max of shape (B,N,H,Q,1) when return_aux.  Runs on `stream` (torch's
     current stream by default) and does not synchronise.
+
+    bias_in_input_dtype: cast the bias to q's dtype (bf16/fp16) instead of
+    fp32, as the triangle_attention page's newest kernels do for speed; the
+    result is that of the fp32 path on the rounded bias.
     """
+    if bias_in_input_dtype and q.dtype == torch.float32:
+        raise ValueError("bias_in_input_dtype needs bf16 or fp16 inputs")
     four_d, q5, k5, v5, bias5, desc, keep = _prepare(q, k, v, bias, mask, kv_lengths,
-                                                     block_mask)
+                                                     block_mask, bias_in_input_dtype)
     B, N, H, Q, D = q5.shape
     K = k5.shape[3]
     dev = q5.device
@@ -283,8 +294,10 @@ def triangle_attention(q, k, v, bias=None, mask=None, scale: Optional[float] = N
     mx = torch.empty(B, N, H, Q, 1, device=dev, dtype=torch.float32)
     shape = TriAttnShape(B, N, H, Q, K, D)
     s = math.nan if scale is None else float(scale)
-    st = tri_attn_fwd(shape, _native.DTYPE_CODES[q5.dtype], q5, k5, v5, bias5, desc, s, out,
-                      lse, mx, stream)
+    dt = _native.DTYPE_CODES[q5.dtype]
+    bias_dt = dt if bias_in_input_dtype and bias5 is not None else TRIATTN_F32
+    st = tri_attn_fwd_bias_dtype(shape, dt, q5, k5, v5, bias5, bias_dt, desc, s, out, lse, mx,
+                                 stream)
     if st != TRIATTN_OK:
         raise RuntimeError(f"tri_attn_fwd: {tri_attn_status_str(st)}")
     if four_d:
@@ -372,10 +385,13 @@ class _TriangleAttentionFn(torch.autograd.Function):
     """Forward through tri_attn_fwd, backward through tri_attn_bwd."""
 
     @staticmethod
-    def forward(ctx, q, k, v, bias, mask, scale, kv_lengths, block_mask):
+    def forward(ctx, q, k, v, bias, mask, scale, kv_lengths, block_mask, bias_in_input_dtype):
         out, lse, mx = triangle_attention(q, k, v, bias, mask, scale, return_aux=True,
-                                          kv_lengths=kv_lengths, block_mask=block_mask)
-        ctx.save_for_backward(q, k, v, bias, out, lse, mx)
+                                          kv_lengths=kv_lengths, block_mask=block_mask,
+                                          bias_in_input_dtype=bias_in_input_dtype)
+        # the backward recomputes the softmax from the bias the forward used
+        used_bias = bias.to(q.dtype) if bias is not None and bias_in_input_dtype else bias
+        ctx.save_for_backward(q, k, v, used_bias, out, lse, mx)
         ctx.mask, ctx.scale, ctx.kv_lengths, ctx.block_mask = mask, scale, kv_lengths, block_mask
         ctx.bias_dtype = None if bias is None else bias.dtype
         ctx.mark_non_differentiable(lse, mx)
@@ -389,17 +405,19 @@ class _TriangleAttentionFn(torch.autograd.Function):
             kv_lengths=ctx.kv_lengths, block_mask=ctx.block_mask)
         if dbias is not None:
             dbias = dbias.to(ctx.bias_dtype)
-        return dq, dk, dv, dbias, None, None, None, None
+        return dq, dk, dv, dbias, None, None, None, None, None
 
 
 def triangle_attention_autograd(q, k, v, bias=None, mask=None, scale: Optional[float] = None,
                                 return_aux: bool = False, *, kv_lengths=None,
-                                block_mask: Optional[BlockMask] = None):
+                                block_mask: Optional[BlockMask] = None,
+                                bias_in_input_dtype: bool = False):
     """triangle_attention with gradients: O (or (O, lse, max)) recorded for
     torch.autograd, whose backward runs tri_attn_bwd.  Gradients flow to q,
     k, v and bias (its gradient is summed over n and cast to bias's dtype);
     lse and max are not differentiable."""
-    out, lse, mx = _TriangleAttentionFn.apply(q, k, v, bias, mask, scale, kv_lengths, block_mask)
+    out, lse, mx = _TriangleAttentionFn.apply(q, k, v, bias, mask, scale, kv_lengths, block_mask,
+                                              bias_in_input_dtype)
     return (out, lse, mx) if return_aux else out
 
 

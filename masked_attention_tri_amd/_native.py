@@ -32,7 +32,8 @@ TRIATTN_MASK_BLOCK = 3
 TRIATTN_MOD_NONE = 0
 TRIATTN_MOD_CAUSAL = 1
 
-EXPORTED = ("tri_attn_check", "tri_attn_fwd", "tri_attn_varlen_check", "tri_attn_varlen_fwd",
+EXPORTED = ("tri_attn_check", "tri_attn_fwd", "tri_attn_fwd_bias_dtype", "tri_attn_varlen_check",
+            "tri_attn_varlen_fwd",
             "tri_attn_bwd", "tri_attn_mask_to_kv_lengths", "tri_attn_status_str")
 
 TRIATTN_QKV_SEPARATE = 0
@@ -110,6 +111,8 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_check.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P]
     lib.tri_attn_fwd.restype = I32
     lib.tri_attn_fwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P]
+    lib.tri_attn_fwd_bias_dtype.restype = I32
+    lib.tri_attn_fwd_bias_dtype.argtypes = [shape_p, I32, P, P, P, P, I32, mask_p, F32, P, P, P, P]
     varlen_p = ctypes.POINTER(TriAttnVarlen)
     lib.tri_attn_varlen_check.restype = I32
     lib.tri_attn_varlen_check.argtypes = [varlen_p, I32, P, P, P, F32, P, P, P]
@@ -158,6 +161,19 @@ def tri_attn_fwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: fl
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     return int(load_library().tri_attn_fwd(
         ctypes.byref(shape), int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+        ctypes.byref(mask) if mask is not None else None, ctypes.c_float(scale), _ptr(out),
+        _ptr(lse), _ptr(mx), ctypes.c_void_p(handle)))
+
+
+def tri_attn_fwd_bias_dtype(shape: TriAttnShape, dtype: int, q, k, v, bias, bias_dtype: int,
+                            mask, scale: float, out, lse, mx, stream) -> int:
+    """tri_attn_fwd with the bias of element type `bias_dtype` (TRIATTN_F32,
+    or q's 16-bit type)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return int(load_library().tri_attn_fwd_bias_dtype(
+        ctypes.byref(shape), int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), int(bias_dtype),
         ctypes.byref(mask) if mask is not None else None, ctypes.c_float(scale), _ptr(out),
         _ptr(lse), _ptr(mx), ctypes.c_void_p(handle)))
 

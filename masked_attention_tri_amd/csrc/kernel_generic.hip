@@ -93,6 +93,8 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
         vbase = static_cast<const T*>(p.v) + bnh * K * D;
     }
     const float* brow = p.bias ? p.bias + ((b * p.H + h) * p.Q + qi) * K : nullptr;
+    const T* brow16 =  // a bias in the input type
+        p.bias16 ? static_cast<const T*>(p.bias16) + ((b * p.H + h) * p.Q + qi) * K : nullptr;
 
     // Visited and full kv blocks of this row's BlockMask row.
     const bool block_kind = p.mask_kind == TRIATTN_MASK_BLOCK;
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
             const T* krow = kbase + kk * kv_rs;
             float dot = 0.f;
             for (int64_t d = 0; d < D; ++d) dot = fmaf(to_f32(qrow[d]), to_f32(krow[d]), dot);
-            z = fmaf(dot, p.scale, brow ? brow[kk] : 0.f);
+            z = fmaf(dot, p.scale, brow ? brow[kk] : (brow16 ? to_f32(brow16[kk]) : 0.f));
         }
         const float m_new = fmaxf(m, wave_max(z));
         const float m_use = m_new == -INFINITY ? 0.f : m_new;

@@ -14,6 +14,9 @@ using tile::scale_is_exact;
 bool mfma_supports(const Params& p, int32_t dtype) {
     if (dtype != TRIATTN_BF16 && dtype != TRIATTN_F16) return false;
     if (p.D != 32 && p.D != 64 && p.D != 128 && p.D != 256) return false;
+    // a 16-bit bias goes by DMA: its rows must be 16-byte aligned
+    if (p.bias16 && (p.K % 8 != 0 || reinterpret_cast<uintptr_t>(p.bias16) % 16 != 0))
+        return false;
     if (p.mask_kind == TRIATTN_MASK_BLOCK) {
         // one block row per workgroup, whole tiles per kv block
         if (p.q_block % kQTileBlock != 0 || p.kv_block % kKTile != 0) return false;

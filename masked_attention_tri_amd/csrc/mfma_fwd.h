@@ -81,7 +81,17 @@ using namespace tile;
 
 // Bias paths: none; staged through LDS by DMA; per-lane 4-byte loads (rows
 // not 16-byte aligned).
-enum BiasMode { kNoBias = 0, kBiasLds = 1, kBiasScalar = 2 };
+enum BiasMode { kNoBias = 0, kBiasLds = 1, kBiasScalar = 2, kBiasLdsHalf = 3 };
+
+// The bias in the inputs' 16-bit type (the page's newest kernels cast it so):
+// a wave's 32 x 32 block is 32 rows of 64 bytes, DMA'd in two instructions
+// of 16 rows.  Read back 8 bytes per lane (four keys) in the accumulator
+// layout, 16-byte chunk g of row r stored at g ^ fbh(r): rows r, r+4, r+8,
+// r+12 (the same banks) get distinct chunks, as do r and r+16.
+constexpr int kBiasHalfRowBytes = kKTile * 2;
+constexpr int kBiasHalfWaveBytes = 32 * kBiasHalfRowBytes;  // 2 KiB
+constexpr int kBiasHalfDma = kBiasHalfWaveBytes / 1024;
+__device__ __forceinline__ int fbh(int r) { return ((r >> 2) ^ (r >> 4)) & 3; }
 
 __device__ __forceinline__ bool bit_set(const uint32_t* bits, int64_t i) {
     return (bits[i >> 5] >> (i & 31)) & 1u;
@@ -143,7 +153,11 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     // as it has read it).  Every buffer is its own object, so the compiler
     // knows that a DMA into one buffer does not write the others and does
     // not wait for it before reading them.
-    constexpr int kBiasBuf = BIAS == kBiasLds ? kWaves * kBiasWaveBytes : 16;
+    constexpr bool kBiasByDma = BIAS == kBiasLds || BIAS == kBiasLdsHalf;
+    constexpr int kBiasBuf = BIAS == kBiasLds       ? kWaves * kBiasWaveBytes
+                             : BIAS == kBiasLdsHalf ? kWaves * kBiasHalfWaveBytes
+                                                    : 16;
+    constexpr uint32_t kBiasElem = BIAS == kBiasLdsHalf ? 2u : 4u;  // bytes per bias element
     __shared__ __attribute__((aligned(1024))) char k_lds0[Ge::tileBytes];
     __shared__ __attribute__((aligned(1024))) char k_lds1[Ge::tileBytes];
     __shared__ __attribute__((aligned(1024))) char k_lds2[Ge::tileBytes];
@@ -202,7 +216,11 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     const uint32_t kv_row_bytes = static_cast<uint32_t>(kv_rs * sizeof(T));
     const T* kbase = static_cast<const T*>(p.k) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * D);
     const T* vbase = static_cast<const T*>(p.v) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * D);
-    const float* bslice = BIAS != kNoBias ? p.bias + (b * p.H + h) * p.Q * p.K : nullptr;
+    const char* bslice =
+        BIAS == kNoBias ? nullptr
+                        : static_cast<const char*>(BIAS == kBiasLdsHalf ? p.bias16
+                                                                        : static_cast<const void*>(p.bias)) +
+                              (b * p.H + h) * p.Q * p.K * kBiasElem;
     const int q0 = static_cast<int>(qt) * kQTile;
     const int q0w = q0 + 32 * wave;
     const int qrow = q0w + col;  // this lane's query
@@ -288,14 +306,15 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     const uint32_t kv_bytes = kVarlen ? static_cast<uint32_t>(K) * kv_row_bytes
                                       : static_cast<uint32_t>(p.K * D * sizeof(T));
     const uint32_t kv_tile_bytes = kKTile * kv_row_bytes;  // one tile of K or V rows in memory
-    const uint32_t bias_bytes = BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * 4) : 0u;
+    const uint32_t bias_bytes = BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * kBiasElem) : 0u;
     const u32x4 k_desc = make_desc(kbase, kv_bytes);
     const u32x4 v_desc = make_desc(vbase, kv_bytes);
     const u32x4 bias_desc = make_desc(bslice, bias_bytes);
     const __amdgpu_buffer_rsrc_t bias_rsrc = make_rsrc(bslice, bias_bytes);
     auto kbuf = [&](int x) { return (lds_char*)(x == 0 ? k_lds0 : x == 1 ? k_lds1 : k_lds2); };
     auto vbuf = [&](int x) { return (lds_char*)(x == 0 ? v_lds0 : x == 1 ? v_lds1 : v_lds2); };
-    lds_char* const bias_lds = (lds_char*)b_lds + wave * kBiasWaveBytes;  // this wave's block
+    lds_char* const bias_lds =  // this wave's block
+        (lds_char*)b_lds + wave * (BIAS == kBiasLdsHalf ? kBiasHalfWaveBytes : kBiasWaveBytes);
 
     // K/V DMA of one tile: instruction I (I < kDma: K, else V) is issued by
     // wave I % kWaves; lane l of it fills LDS slot s = 64 (I % kDma) + l of
@@ -337,7 +356,20 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     const uint32_t b_row = static_cast<uint32_t>(q0w + (lane >> 3)) * static_cast<uint32_t>(K) * 4u;
     const uint32_t b_src_even = b_row + 16u * static_cast<uint32_t>((lane & 7) ^ (lane >> 4));
     const uint32_t b_src_odd = b_row + 16u * static_cast<uint32_t>((lane & 7) ^ (lane >> 4) ^ 4);
+    // 16-bit bias: lane l of instruction j fills row 16j + l/4, stored chunk
+    // l%4, from source chunk (l%4) ^ fbh(row) = (l%4) ^ ((l/16 ^ j) % 4).
+    const uint32_t bh_row = static_cast<uint32_t>(q0w + (lane >> 2)) * static_cast<uint32_t>(K) * 2u;
     auto dma_bias = [&](int t) {
+        if (BIAS == kBiasLdsHalf) {
+            const uint32_t toff = static_cast<uint32_t>(t) * kBiasHalfRowBytes;
+#pragma unroll
+            for (int j = 0; j < kBiasHalfDma; ++j) {
+                const uint32_t rows = static_cast<uint32_t>(16 * j) * static_cast<uint32_t>(K) * 2u;
+                const uint32_t chunk = static_cast<uint32_t>((lane & 3) ^ (((lane >> 4) ^ j) & 3));
+                dma16(bias_desc, bias_lds + 1024 * j, bh_row + rows + 16u * chunk + toff);
+            }
+            return;
+        }
         if (BIAS != kBiasLds) return;
         const uint32_t toff = static_cast<uint32_t>(t) * kBiasRowBytes;
 #pragma unroll
@@ -357,6 +389,30 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
                 *reinterpret_cast<const lds_u32x4*>(bias_lds + col * kBiasRowBytes + 16 * chunk));
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[4 * g + e] = bv[e];
+        }
+    };
+    // 16-bit bias block into the accumulator layout: register 4g+e is key
+    // 8g + 4half + e, i.e. bytes 8half..8half+7 of chunk g of row col.
+    auto read_bias_half = [&](f32x16& dst) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int chunk = g ^ fbh(col);
+            const u32x2 w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+                bias_lds + col * kBiasHalfRowBytes + 16 * chunk + 8 * half);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
+                    // a bf16 is the high half of the fp32 with the same value
+                    dst[4 * g + 2 * e] = __uint_as_float(w[e] << 16);
+                    dst[4 * g + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                } else {
+                    const uint32_t u = w[e];
+                    const auto lo = static_cast<unsigned short>(u & 0xffffu);
+                    const auto hi = static_cast<unsigned short>(u >> 16);
+                    dst[4 * g + 2 * e] = static_cast<float>(__builtin_bit_cast(_Float16, lo));
+                    dst[4 * g + 2 * e + 1] = static_cast<float>(__builtin_bit_cast(_Float16, hi));
+                }
+            }
         }
     };
     // Bias for K % 4 != 0 (rows not 16-byte aligned): plain per-lane loads.
@@ -444,6 +500,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     auto qk_load = [&](f32x16& s, int t, int x) {
         s = f32x16{};
         if (BIAS == kBiasLds) read_bias(s);
+        if (BIAS == kBiasLdsHalf) read_bias_half(s);
         if (BIAS == kBiasScalar) load_bias_scalar(t, s);
         if (BIAS != kNoBias && !EXACT) s *= inv_s;
         const lds_char* kt = kbuf(x);
@@ -609,13 +666,13 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         // K(t2), V(t1)
         if constexpr (kDense) load_dense_chunk(cur >> 6);  // before any DMA is in flight
         dma_k(cur, 0);
-        if (BIAS == kBiasLds) dma_bias(cur);
+        if (kBiasByDma) dma_bias(cur);
         dma_k(nxt, 1);
         dma_v(cur, 0);
         wait_vmem();
         __syncthreads();
         qk(sa, cur, 0);
-        if (BIAS == kBiasLds && nxt >= 0) {
+        if (kBiasByDma && nxt >= 0) {
             wait_lds();  // the bias reads are done before the block is refilled
             dma_bias(nxt);
         }
@@ -632,7 +689,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
         __builtin_amdgcn_s_waitcnt(kVmcntWait<kKvInFlight>());
         __syncthreads();
         auto dma = [&]() {  // this position's DMAs
-            if (BIAS == kBiasLds && nxt2 >= 0) {
+            if (kBiasByDma && nxt2 >= 0) {
                 wait_lds();
                 dma_bias(nxt2);
             }
@@ -766,6 +823,8 @@ hipError_t launch_kind(const Params& p, bool exact, hipStream_t stream) {
     if constexpr (KIND == kMaskVarlen) {
         return launch_bias<T, D, KIND, kNoBias>(p, exact, stream);  // no bias
     } else {
+        // 16-bit bias (rows 16-byte aligned: checked by mfma_supports)
+        if (p.bias16) return launch_bias<T, D, KIND, kBiasLdsHalf>(p, exact, stream);
         if (!p.bias) return launch_bias<T, D, KIND, kNoBias>(p, exact, stream);
         // The DMA path moves 16-byte chunks of bias rows: rows must be 16-byte
         // aligned.

@@ -211,10 +211,27 @@ triattn_status tri_attn_fwd(const tri_attn_shape* shape, int32_t dtype, const vo
                             const void* k, const void* v, const float* bias,
                             const tri_attn_mask* mask, float scale, void* out, float* lse,
                             float* max, hipStream_t stream) {
-    const triattn_status st = check_impl(shape, dtype, q, k, v, bias, mask, scale, out, lse, max);
+    return tri_attn_fwd_bias_dtype(shape, dtype, q, k, v, bias, TRIATTN_F32, mask, scale, out,
+                                   lse, max, stream);
+}
+
+triattn_status tri_attn_fwd_bias_dtype(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                                       const void* k, const void* v, const void* bias,
+                                       int32_t bias_dtype, const tri_attn_mask* mask, float scale,
+                                       void* out, float* lse, float* max, hipStream_t stream) {
+    // fp32, or the 16-bit type of q, k and v
+    const bool half_bias = bias_dtype != TRIATTN_F32;
+    if (half_bias && (bias_dtype != dtype || (dtype != TRIATTN_F16 && dtype != TRIATTN_BF16)))
+        return TRIATTN_ERR_INVALID_ARG;
+    const triattn_status st =
+        check_impl(shape, dtype, q, k, v, half_bias ? nullptr : static_cast<const float*>(bias),
+                   mask, scale, out, lse, max);
     if (st != TRIATTN_OK) return st;
+    if (half_bias && !aligned(bias, 2)) return TRIATTN_ERR_INVALID_ARG;
     if (shape->B == 0 || shape->N == 0 || shape->H == 0 || shape->Q == 0) return TRIATTN_OK;
-    const Params p = make_params(shape, q, k, v, bias, mask, scale, out, lse, max);
+    Params p = make_params(shape, q, k, v, half_bias ? nullptr : static_cast<const float*>(bias),
+                           mask, scale, out, lse, max);
+    if (half_bias) p.bias16 = bias;
     const hipError_t err = triattn::mfma_supports(p, dtype)
                                ? triattn::launch_mfma(p, dtype, stream)
                                : triattn::launch_generic(p, dtype, stream);

@@ -15,7 +15,8 @@ struct Params {
     const void* q;
     const void* k;
     const void* v;
-    const float* bias;  // (B,1,H,Q,K) or nullptr
+    const float* bias;    // (B,1,H,Q,K) fp32, or nullptr
+    const void* bias16;   // (B,1,H,Q,K) in the input type (then bias is nullptr), or nullptr
     void* out;
     float* lse;  // may be nullptr
     float* mx;   // may be nullptr

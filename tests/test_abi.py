@@ -328,3 +328,29 @@ def test_varlen_check_envelope_and_range():
     assert _vcheck(_varlen(total_q=1 << 31)) == nat.TRIATTN_ERR_UNSUPPORTED  # int32 offsets
     assert _vcheck(_varlen(batch=1 << 20, heads=1 << 12, max_q=1 << 12)) == \
         nat.TRIATTN_ERR_UNSUPPORTED
+
+
+def test_fwd_bias_dtype_validation():
+    """The bias may be fp32 or the inputs' own 16-bit type, nothing else;
+    a failing check launches nothing (no device call here)."""
+    lib = nat.load_library()
+    shp = shape(D=64)
+
+    def call(dtype, bias_dtype, bias=A):
+        return lib.tri_attn_fwd_bias_dtype(ctypes.byref(shp), dtype, A, A, A, bias, bias_dtype,
+                                           None, ctypes.c_float(math.inf), A, None, None, None)
+
+    # an infinite scale makes every otherwise-valid call stop at the check,
+    # so these return without touching the device
+    assert call(nat.TRIATTN_BF16, nat.TRIATTN_BF16) == nat.TRIATTN_ERR_INVALID_ARG
+    for dt, bdt in ((nat.TRIATTN_BF16, nat.TRIATTN_F16), (nat.TRIATTN_F16, nat.TRIATTN_BF16),
+                    (nat.TRIATTN_F32, nat.TRIATTN_F32 + 7), (nat.TRIATTN_BF16, 9)):
+        assert call(dt, bdt) == nat.TRIATTN_ERR_INVALID_ARG
+    # fp32 inputs have no 16-bit bias
+    assert lib.tri_attn_fwd_bias_dtype(ctypes.byref(shape(D=32)), nat.TRIATTN_F32, A, A, A, A,
+                                       nat.TRIATTN_F16, None, ctypes.c_float(math.nan), A, None,
+                                       None, None) == nat.TRIATTN_ERR_INVALID_ARG
+    # a 16-bit bias must be 2-byte aligned (checked after the common checks)
+    assert lib.tri_attn_fwd_bias_dtype(ctypes.byref(shape(B=0)), nat.TRIATTN_BF16, A, A, A, A + 1,
+                                       nat.TRIATTN_BF16, None, ctypes.c_float(math.nan), A, None,
+                                       None, None) == nat.TRIATTN_ERR_INVALID_ARG

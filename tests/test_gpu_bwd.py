@@ -126,6 +126,29 @@ def test_autograd_wrapper(four_d):
         assert err <= bound, f"{name}: {err} > {bound}"
 
 
+def test_autograd_with_bias_in_input_dtype():
+    """With the bias cast to the input type, autograd's gradients are those
+    of the fp32 path given the rounded bias, bit for bit (the forward widens
+    each 16-bit bias value exactly and the backward receives the same
+    values); dbias comes back in the bias's own dtype."""
+    c = wl.make_case(1, 3, 2, 64, 96, 64, "bf16", "kv_lengths", seed=43)
+    say(f"autograd half bias {c.name}")
+    g = torch.Generator().manual_seed(41)
+    dout = torch.randn(c.q.shape, generator=g).to(c.q.dtype).cuda()
+    grads = []
+    for half in (True, False):
+        q, k, v = (x.cuda().requires_grad_() for x in (c.q, c.k, c.v))
+        b = (c.bias if half else c.bias.to(c.dtype).float()).cuda().requires_grad_()
+        out = mat.triangle_attention_autograd(q, k, v, b, kv_lengths=c.kv_lengths.cuda(),
+                                              scale=c.scale, bias_in_input_dtype=half)
+        out.backward(dout)
+        torch.cuda.synchronize()
+        grads.append([out.detach()] + [t.grad for t in (q, k, v, b)])
+    for name, a, r in zip(("out", "dq", "dk", "dv", "dbias"), *grads):
+        assert torch.equal(a, r), name
+    assert grads[0][4].dtype == torch.float32
+
+
 def test_backward_headline_size_sampled():
     """The headline workload at full size (B1 N768 H4 Q=K=768 D64, bf16,
     kv_lengths): the GPU backward of every slice, with dQ, dK and dV of the

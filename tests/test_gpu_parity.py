@@ -9,9 +9,10 @@ import numpy as np
 import pytest
 import torch
 
+import masked_attention_tri_amd as mat
 from masked_attention_tri_amd import workloads as wl
 from tests import helpers as hp
-from tests.gpu_common import assert_parity, run_gpu, say
+from tests.gpu_common import assert_parity, block_mask_of, errors, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -156,3 +157,74 @@ def test_p1_example_shapes_and_lengths():
     gpu = run_gpu(c)
     assert list(gpu[0].shape) == g["output_shape"]
     assert_parity(c, gpu=gpu)  # rows n >= 96 have no valid key
+
+
+# ---- the bias in the inputs' 16-bit type ------------------------------------
+
+HALF_BIAS_CASES = [
+    (1, 3, 2, 200, 192, 64, "bf16", "kv_lengths", {}),
+    (1, 2, 2, 130, 96, 32, "f16", "dense", {"bias_sigma": 2.0}),
+    (1, 2, 2, 256, 256, 128, "bf16", "block", {"q_block": 128, "kv_block": 64,
+                                                "mask_mod": "causal"}),
+    (1, 2, 2, 100, 160, 256, "f16", "none", {"scale": 0.3}),
+    (2, 2, 2, 100, 100, 64, "bf16", "none", {}),      # K % 8 != 0: the generic kernel
+    (1, 2, 2, 70, 88, 40, "bf16", "kv_lengths", {}),  # no MFMA kernel at D = 40
+]
+
+
+@pytest.mark.parametrize("spec", HALF_BIAS_CASES, ids=[_case_id(c) for c in HALF_BIAS_CASES])
+def test_half_bias_matches_oracle_on_the_rounded_bias(spec):
+    """bias_in_input_dtype: the result is that of the equation with the bias
+    rounded to the input type (the oracle fed exactly those values), at the
+    usual tolerances.  Against the fp32 bias the only extra error is that
+    rounding, reported here (it is what the 16-bit mode trades)."""
+    B, N, H, Q, K, D, dt, kind, extra = spec
+    c = wl.make_case(B, N, H, Q, K, D, dt, kind, seed=17, **extra)
+    say(f"half bias {c.name}")
+    g = c.to("cuda")
+    got = mat.triangle_attention(g.q, g.k, g.v, g.bias, mask=g.mask, scale=g.scale,
+                                 return_aux=True, kv_lengths=g.kv_lengths,
+                                 block_mask=block_mask_of(g), bias_in_input_dtype=True)
+    torch.cuda.synchronize()
+    got = tuple(x.cpu() for x in got)
+    rounded = wl.Case(c.name + " (rounded bias)", c.dtype, c.q, c.k, c.v,
+                      c.bias.to(c.dtype).float(), mask=c.mask, kv_lengths=c.kv_lengths,
+                      block=c.block, scale=c.scale)
+    assert_parity(rounded, gpu=got)
+    # each 16-bit value is widened exactly, then the arithmetic is the fp32
+    # path's: the same bits as the fp32 path given the rounded bias, when
+    # both run on the same kernel (a 16-bit bias needs K % 8 == 0 for the
+    # MFMA kernel's DMA, an fp32 one K % 4 == 0)
+    if D not in (32, 64, 128, 256) or K % 8 == 0:
+        ref = run_gpu(rounded)
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), "differs from the fp32 path"
+    eo, el, em = errors(c, got)
+    say(f"half bias {c.name}: against the fp32 bias err O {eo:.3g} lse {el:.3g} max {em:.3g}")
+
+
+def test_fp32_bias_dtype_is_tri_attn_fwd():
+    """tri_attn_fwd_bias_dtype with TRIATTN_F32 is tri_attn_fwd, bit for bit."""
+    say("bias dtype fp32 == tri_attn_fwd")
+    import masked_attention_tri_amd._native as nat
+
+    c = wl.make_case(1, 2, 2, 96, 128, 64, "bf16", "kv_lengths", seed=3).to("cuda")
+    B, N, H, Q, K, D = c.shape
+    desc = nat.TriAttnMask()
+    desc.kind = nat.TRIATTN_MASK_KV_LENGTHS
+    desc.kv_lengths = c.kv_lengths.data_ptr()
+    shp = nat.TriAttnShape(B, N, H, Q, K, D)
+    res = []
+    for typed in (False, True):
+        out = torch.empty_like(c.q)
+        lse = torch.empty(B, N, H, Q, device="cuda")
+        mx = torch.empty(B, N, H, Q, device="cuda")
+        if typed:
+            st = mat.tri_attn_fwd_bias_dtype(shp, nat.TRIATTN_BF16, c.q, c.k, c.v, c.bias,
+                                             nat.TRIATTN_F32, desc, math.nan, out, lse, mx, None)
+        else:
+            st = mat.tri_attn_fwd(shp, nat.TRIATTN_BF16, c.q, c.k, c.v, c.bias, desc, math.nan,
+                                  out, lse, mx, None)
+        torch.cuda.synchronize()
+        assert st == mat.TRIATTN_OK
+        res.append((out, lse, mx))
+    assert all(torch.equal(a, b) for a, b in zip(*res))
