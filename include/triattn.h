@@ -335,6 +335,30 @@ triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const vo
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * tri_attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, and the same results, bit for
+ * bit, as tri_attn_bwd given a workspace.  The dz scratch of the dBias sum
+ * is a fixed array of this library, TRIATTN_BWD_NOALLOC_MAX_PAIRS floats
+ * (32 MiB) per GPU that loads it, held until the process ends; the call
+ * allocates and frees nothing.  With dbias != NULL it needs
+ * B*N*H*Q*K <= TRIATTN_BWD_NOALLOC_MAX_PAIRS and returns
+ * TRIATTN_ERR_UNSUPPORTED (nothing launched) for larger problems; without
+ * dbias there is no limit.  All calls on one GPU share the array: calls
+ * that overlap in time on one GPU race and must not be issued.  The calling
+ * thread's current device must be the stream's.  Errors otherwise as
+ * tri_attn_bwd (TRIATTN_ERR_HIP also if the array's address cannot be
+ * obtained).
+ */
+#define TRIATTN_BWD_NOALLOC_MAX_PAIRS (8 * 1024 * 1024)
+triattn_status tri_attn_bwd_noalloc(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                                    const void* k, const void* v, const float* bias,
+                                    const tri_attn_mask* mask, float scale, const void* out,
+                                    const void* dout, const float* lse, const float* max,
+                                    void* dq, void* dk, void* dv, float* dbias,
+                                    hipStream_t stream);
+
+/*
  * Count the valid prefix of each dense key-mask row: the page's
  * mask_to_kv_lengths helper, which turns a right-padded (B,N,1,1,K) bool mask
  * into (B,N,1,1,1) int32 lengths.  `mask`: rows*K bytes (nonzero = valid);

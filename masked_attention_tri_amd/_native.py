@@ -34,7 +34,11 @@ TRIATTN_MOD_CAUSAL = 1
 
 EXPORTED = ("tri_attn_check", "tri_attn_fwd", "tri_attn_fwd_bias_dtype", "tri_attn_varlen_check",
             "tri_attn_varlen_fwd",
-            "tri_attn_bwd", "tri_attn_mask_to_kv_lengths", "tri_attn_status_str")
+            "tri_attn_bwd", "tri_attn_bwd_noalloc", "tri_attn_mask_to_kv_lengths",
+            "tri_attn_status_str")
+
+# dz pairs (B*N*H*Q*K) the no-allocation backward holds when dbias is asked for
+TRIATTN_BWD_NOALLOC_MAX_PAIRS = 8 * 1024 * 1024
 
 TRIATTN_QKV_SEPARATE = 0
 TRIATTN_QKV_PACKED = 1
@@ -121,6 +125,9 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_bwd.restype = I32
     lib.tri_attn_bwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P, P, P, P,
                                   ctypes.c_size_t, P]
+    lib.tri_attn_bwd_noalloc.restype = I32
+    lib.tri_attn_bwd_noalloc.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P,
+                                         P, P, P]
     lib.tri_attn_mask_to_kv_lengths.restype = I32
     lib.tri_attn_mask_to_kv_lengths.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P]
     lib.tri_attn_status_str.restype = ctypes.c_char_p
@@ -225,4 +232,18 @@ def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: fl
         _ptr(dout), _ptr(lse), _ptr(mx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
         _ptr(workspace),
         ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size()),
+        ctypes.c_void_p(handle)))
+
+
+def tri_attn_bwd_noalloc(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: float, out,
+                         dout, lse, mx, dq, dk, dv, dbias, stream) -> int:
+    """tri_attn_bwd with the library's own dz scratch: no workspace argument
+    and no allocation (see include/triattn.h)."""
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return int(load_library().tri_attn_bwd_noalloc(
+        ctypes.byref(shape), int(dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+        ctypes.byref(mask) if mask is not None else None, ctypes.c_float(scale), _ptr(out),
+        _ptr(dout), _ptr(lse), _ptr(mx), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias),
         ctypes.c_void_p(handle)))

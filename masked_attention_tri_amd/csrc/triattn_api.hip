@@ -198,6 +198,37 @@ triattn_status varlen_check_impl(const tri_attn_varlen* d, int32_t dtype, const 
 
 }  // namespace
 
+namespace triattn {
+
+triattn_status bwd_validate(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                            const void* k, const void* v, const float* bias,
+                            const tri_attn_mask* mask, float scale, const void* out,
+                            const void* dout, const float* lse, const float* max, const void* dq,
+                            const void* dk, const void* dv, const float* dbias,
+                            const float* workspace, size_t workspace_bytes) {
+    // The forward's arguments (out is read, not written, here).
+    triattn_status st = check_impl(shape, dtype, q, k, v, bias, mask, scale, out, lse, max);
+    if (st != TRIATTN_OK) return st;
+    const bool empty = shape->B == 0 || shape->N == 0 || shape->H == 0 || shape->Q == 0;
+    if (!empty && (!dout || !lse || !max || !dq || !dk || !dv)) return TRIATTN_ERR_INVALID_ARG;
+    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+        !aligned(dbias, 4) || !aligned(workspace, 16))
+        return TRIATTN_ERR_INVALID_ARG;
+    if (dbias && workspace) {
+        // 4 B N H Q K bytes: dz of every (b, n, h, q, k) pair
+        const int64_t need = mul_or_neg(
+            mul_or_neg(mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H),
+                                  shape->Q),
+                       shape->K),
+            4);
+        if (need < 0) return TRIATTN_ERR_UNSUPPORTED;
+        if (workspace_bytes < static_cast<uint64_t>(need)) return TRIATTN_ERR_INVALID_ARG;
+    }
+    return TRIATTN_OK;
+}
+
+}  // namespace triattn
+
 extern "C" {
 
 triattn_status tri_attn_check(const tri_attn_shape* shape, int32_t dtype, const void* q,
@@ -307,25 +338,11 @@ triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const vo
                             const void* dout, const float* lse, const float* max, void* dq,
                             void* dk, void* dv, float* dbias, float* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
-    // The forward's arguments (out is read, not written, here).
-    triattn_status st = check_impl(shape, dtype, q, k, v, bias, mask, scale, out, lse, max);
+    const triattn_status st =
+        triattn::bwd_validate(shape, dtype, q, k, v, bias, mask, scale, out, dout, lse, max, dq,
+                              dk, dv, dbias, workspace, workspace_bytes);
     if (st != TRIATTN_OK) return st;
-    const bool empty = shape->B == 0 || shape->N == 0 || shape->H == 0 || shape->Q == 0;
-    if (!empty && (!dout || !lse || !max || !dq || !dk || !dv)) return TRIATTN_ERR_INVALID_ARG;
-    if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-        !aligned(dbias, 4) || !aligned(workspace, 16))
-        return TRIATTN_ERR_INVALID_ARG;
-    if (dbias && workspace) {
-        // 4 B N H Q K bytes: dz of every (b, n, h, q, k) pair
-        const int64_t need = mul_or_neg(
-            mul_or_neg(mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H),
-                                  shape->Q),
-                       shape->K),
-            4);
-        if (need < 0) return TRIATTN_ERR_UNSUPPORTED;
-        if (workspace_bytes < static_cast<uint64_t>(need)) return TRIATTN_ERR_INVALID_ARG;
-    }
-    if (empty) return TRIATTN_OK;
+    if (shape->B == 0 || shape->N == 0 || shape->H == 0 || shape->Q == 0) return TRIATTN_OK;
     const Params p = make_params(shape, q, k, v, bias, mask, scale, nullptr, nullptr, nullptr);
     triattn::BwdParams g{};
     g.out = out;

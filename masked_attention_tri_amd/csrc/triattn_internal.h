@@ -106,6 +106,14 @@ hipError_t launch_mfma_d64(const Params& p, int32_t dtype, bool exact, hipStream
 hipError_t launch_mfma_d128(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
 hipError_t launch_mfma_d256(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
 hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, hipStream_t stream);
+// Host-only validation of tri_attn_bwd's arguments (the checks it returns
+// before launching anything).
+triattn_status bwd_validate(const tri_attn_shape* shape, int32_t dtype, const void* q,
+                            const void* k, const void* v, const float* bias,
+                            const tri_attn_mask* mask, float scale, const void* out,
+                            const void* dout, const float* lse, const float* max, const void* dq,
+                            const void* dk, const void* dv, const float* dbias,
+                            const float* workspace, size_t workspace_bytes);
 hipError_t launch_mask_to_kv_lengths(const uint8_t* mask, int64_t rows, int64_t K,
                                      int32_t* kv_lengths, int32_t* nonprefix_rows,
                                      hipStream_t stream);

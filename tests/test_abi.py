@@ -354,3 +354,20 @@ def test_fwd_bias_dtype_validation():
     assert lib.tri_attn_fwd_bias_dtype(ctypes.byref(shape(B=0)), nat.TRIATTN_BF16, A, A, A, A + 1,
                                        nat.TRIATTN_BF16, None, ctypes.c_float(math.nan), A, None,
                                        None, None) == nat.TRIATTN_ERR_INVALID_ARG
+
+
+def test_bwd_noalloc_rejects_problems_past_its_scratch():
+    """With a bias gradient the no-allocation backward holds dz for at most
+    TRIATTN_BWD_NOALLOC_MAX_PAIRS (query, key) pairs: a larger problem is
+    refused before any device call; argument errors come first."""
+    lib = nat.load_library()
+
+    def call(shp, dbias=A, scale=math.nan):
+        return lib.tri_attn_bwd_noalloc(ctypes.byref(shp), nat.TRIATTN_BF16, A, A, A, A, None,
+                                        ctypes.c_float(scale), A, A, A, A, A, A, A, dbias, None)
+
+    big = shape(B=1, N=64, H=4, Q=256, K=129, D=64)  # 64*4*256*129 > 8 Mi pairs
+    assert 64 * 4 * 256 * 129 > nat.TRIATTN_BWD_NOALLOC_MAX_PAIRS
+    assert call(big) == nat.TRIATTN_ERR_UNSUPPORTED
+    assert call(big, scale=math.inf) == nat.TRIATTN_ERR_INVALID_ARG
+    assert call(shape(B=1, N=0, H=4, Q=256, K=129, D=64)) == nat.TRIATTN_OK  # no work
