@@ -30,7 +30,7 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 flop/clk)
 METRIC = "fwd TFLOP/s + % bf16 MFMA peak, triangle attn N=Q=K=768 H=4 D=64"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "masked_attention_tri_amd", "csrc", "kernel_mfma.hip")
+KERNEL_SRC = os.path.join(ROOT, "masked_attention_tri_amd", "csrc", "mfma_fwd.h")
 
 
 def parse():
@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bias-dtype", choices=("fp32", "input"), default="fp32",
+                    help="pass the bias as fp32 (the metric) or in the inputs' 16-bit type "
+                         "(the opt-in mode of tri_attn_fwd_bias_dtype)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for counter scaling)")
     args = ap.parse_args()
@@ -81,8 +84,9 @@ def warm_up(args, step):
     return n
 
 
-def work_counts(case):
-    """Nominal and algorithmic flops, algorithmic HBM bytes of one step."""
+def work_counts(case, bias_elem=4):
+    """Nominal and algorithmic flops, algorithmic HBM bytes of one step
+    (bias_elem: bytes per bias element)."""
     import torch
 
     B, N, H, Q, K, D = case.shape
@@ -116,7 +120,7 @@ def work_counts(case):
         alg = nominal
     qo = 2 * B * N * H * Q * D * esz
     kv = 2 * key_rows * D * esz
-    bias = B * H * Q * K * 4 if case.bias is not None else 0
+    bias = B * H * Q * K * bias_elem if case.bias is not None else 0
     aux = 2 * B * N * H * Q * 4
     mask = (B * N * 4) if case.kv_lengths is not None else (B * N * K if case.mask is not None else 0)
     return nominal, alg, qo + kv + bias + aux + mask
@@ -330,9 +334,17 @@ def main():
     scale = math.nan if g.scale is None else g.scale
     stream = torch.cuda.current_stream(dev)
 
+    half_bias = args.bias_dtype == "input" and g.bias is not None
+    if half_bias:
+        if g.q.dtype == torch.float32:
+            sys.exit("--bias-dtype input needs a bf16 or fp16 workload")
+        bias_arg, bias_dt = g.bias.to(g.q.dtype).contiguous(), dtype
+    else:
+        bias_arg, bias_dt = g.bias, nat.TRIATTN_F32
+
     def step():
-        st = mat.tri_attn_fwd(shape, dtype, g.q, g.k, g.v, g.bias, desc, scale, out, lse, mx,
-                              stream)
+        st = mat.tri_attn_fwd_bias_dtype(shape, dtype, g.q, g.k, g.v, bias_arg, bias_dt, desc,
+                                         scale, out, lse, mx, stream)
         if st != nat.TRIATTN_OK:
             raise RuntimeError(mat.tri_attn_status_str(st))
 
@@ -376,11 +388,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    nominal, alg, alg_bytes = work_counts(case)
+    nominal, alg, alg_bytes = work_counts(case, 2 if half_bias else 4)
     sec = ms * 1e-3
     value = nominal / sec / 1e12
     alg_tflops = alg / sec / 1e12
-    tr = traffic_entry(key)
+    tr = traffic_entry(key) if not half_bias else None
     traffic = None if tr is None else tr["bytes_per_launch"]
     res = {
         "metric": METRIC,
@@ -404,8 +416,9 @@ def main():
         "pct_bf16_peak_algorithmic": round(100.0 * alg_tflops / PEAK_BF16_TFLOPS, 3),
         "hbm_GBps_algorithmic": round(alg_bytes / sec / 1e9, 1),
         "config": {
-            "workload": case.name,
+            "workload": case.name + (" (bias in the input type)" if half_bias else ""),
             "key": key,
+            "bias_dtype": "input" if half_bias else "fp32",
             "B": B, "N": N, "H": H, "Q": Q, "K": K, "D": D,
             "nominal_flop": nominal,
             "algorithmic_flop": alg,

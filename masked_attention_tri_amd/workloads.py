@@ -118,6 +118,10 @@ WORKLOADS = {
                       "bf16", 1, 768, 4, 768, 64),
     "bf16_causal_blocks_d128": ("bf16 causal BlockMask 128 no-bias B2 N1 H8 Q=K=4096 D128",
                                 1005, "bf16", 2, 1, 8, 4096, 128),
+    # not one of the five: the widest head dimension of the envelope, in the
+    # headline's form
+    "bf16_lens_d256": ("bf16 kv_lengths U{256..512 step 8} B1 N256 H4 Q=K=512 D256", 1006,
+                       "bf16", 1, 256, 4, 512, 256),
 }
 HEADLINE = "bf16_lens_d64"
 
@@ -149,6 +153,10 @@ def make_workload(key: str) -> Case:
         bias = _bias(gen, B, H, S, S, 1.0)
         lens = (8 * torch.randint(48, 97, (B, N, 1, 1, 1), generator=gen)).to(torch.int32)
         return Case(name, dtype, q, k, v, bias, kv_lengths=lens, scale=1.0 / 8.0, meta=meta)
+    if key == "bf16_lens_d256":
+        bias = _bias(gen, B, H, S, S, 1.0)
+        lens = (8 * torch.randint(32, 65, (B, N, 1, 1, 1), generator=gen)).to(torch.int32)
+        return Case(name, dtype, q, k, v, bias, kv_lengths=lens, scale=1.0 / 16.0, meta=meta)
     if key == "bf16_causal_blocks_d128":
         block = causal_block_lists(gen, S // 128)
         return Case(name, dtype, q, k, v, None, block=block, scale=None, meta=meta)

@@ -64,6 +64,14 @@ def test_bf16_causal_blocks_d128_all_rows():
     assert_parity(c, gpu=run_gpu(c))
 
 
+def test_bf16_lens_d256_all_rows():
+    """Every row of the D = 256 workload (B1 N256 H4 Q=K=512 D256, kv_lengths
+    U{256..512 step 8}) against the oracle."""
+    say("bf16 kv_lengths N256 D256 workload (full size, all rows)")
+    c = wl.make_workload("bf16_lens_d256")
+    assert_parity(c, gpu=run_gpu(c))
+
+
 # ---- random shapes through both kernels ------------------------------------
 
 MFMA_CASES = [
