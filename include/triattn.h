@@ -310,19 +310,19 @@ triattn_status tri_attn_varlen_fwd(const tri_attn_varlen* desc, int32_t dtype, c
  * (B,N,H,K,D), all of type `dtype` and 16-byte aligned; dbias (B,1,H,Q,K)
  * fp32, or NULL to skip it.  All device memory; enqueued on `stream`.
  *
- * Workspace (used only when dbias is not NULL): NULL, or device memory of
- * at least 4*B*N*H*Q*K bytes, 16-byte aligned, caller-owned, whose contents
- * on entry do not matter and on return are unspecified.  With it, the dQ
- * pass stores every dz and dbias is their sum over n, read back at HBM
- * bandwidth; without it, dbias is recomputed per block by a latency-bound
- * walk over n (no extra memory).  Both routes add the same values in the
- * same order (n ascending) and give the same bits.  Calls that share one
- * workspace must not overlap.
+ * Workspace (required when there is a query row): device memory of at least
+ * tri_attn_bwd_workspace_size(shape) = 12*B*N*H*Q bytes, 16-byte aligned,
+ * caller-owned, whose contents on entry do not matter and on return are
+ * unspecified.  The first pass stores per-row data there (Delta = dO.O and
+ * lse of every row, and how many rows of each 32-row tile have no valid
+ * key) for the passes that follow.  Calls that share one workspace must not
+ * overlap.
  *
  * Errors: those of tri_attn_check for the forward's arguments, and
- * TRIATTN_ERR_INVALID_ARG for a NULL dout / lse / max / dq / dk / dv when
- * there is a query row, a misaligned pointer, or a workspace smaller than
- * the size above (TRIATTN_ERR_UNSUPPORTED if that size overflows int64);
+ * TRIATTN_ERR_INVALID_ARG for a NULL dout / lse / max / dq / dk / dv /
+ * workspace when there is a query row, a misaligned pointer, or a workspace
+ * smaller than the size above (TRIATTN_ERR_UNSUPPORTED if that size
+ * overflows int64);
  * nothing is launched then.  TRIATTN_ERR_HIP if a launch fails.  With no
  * query row the call does nothing.  Products of bf16/fp16 tiles run on
  * MFMA with fp32 accumulation, fp32 inputs on fp32 FMAs.
@@ -335,22 +335,26 @@ triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const vo
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Bytes of workspace tri_attn_bwd needs for `shape`: 12*B*N*H*Q (0 for a
+ * NULL shape, a negative size or a product past int64).  Host only.
+ */
+size_t tri_attn_bwd_workspace_size(const tri_attn_shape* shape);
+
+/*
  * tri_attn_bwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments without the workspace, and the same results, bit for
- * bit, as tri_attn_bwd given a workspace.  The dz scratch of the dBias sum
- * is a fixed array of this library, TRIATTN_BWD_NOALLOC_MAX_PAIRS floats
- * (32 MiB) per GPU that loads it, held until the process ends; the call
- * allocates and frees nothing.  With dbias != NULL it needs
- * B*N*H*Q*K <= TRIATTN_BWD_NOALLOC_MAX_PAIRS and returns
- * TRIATTN_ERR_UNSUPPORTED (nothing launched) for larger problems; without
- * dbias there is no limit.  All calls on one GPU share the array: calls
- * that overlap in time on one GPU race and must not be issued.  The calling
- * thread's current device must be the stream's.  Errors otherwise as
- * tri_attn_bwd (TRIATTN_ERR_HIP also if the array's address cannot be
- * obtained).
+ * bit, as tri_attn_bwd.  Its workspace is a fixed array of this library,
+ * 12 * TRIATTN_BWD_NOALLOC_MAX_ROWS bytes (48 MiB) per GPU that loads it,
+ * held until the process ends; the call allocates and frees nothing.  It
+ * needs B*N*H*Q <= TRIATTN_BWD_NOALLOC_MAX_ROWS and returns
+ * TRIATTN_ERR_UNSUPPORTED (nothing launched) for larger problems.  All calls
+ * on one GPU share the array: calls that overlap in time on one GPU race and
+ * must not be issued.  The calling thread's current device must be the
+ * stream's.  Errors otherwise as tri_attn_bwd (TRIATTN_ERR_HIP also if the
+ * array's address cannot be obtained).
  */
-#define TRIATTN_BWD_NOALLOC_MAX_PAIRS (8 * 1024 * 1024)
+#define TRIATTN_BWD_NOALLOC_MAX_ROWS (4 * 1024 * 1024)
 triattn_status tri_attn_bwd_noalloc(const tri_attn_shape* shape, int32_t dtype, const void* q,
                                     const void* k, const void* v, const float* bias,
                                     const tri_attn_mask* mask, float scale, const void* out,

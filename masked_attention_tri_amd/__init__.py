@@ -43,6 +43,7 @@ from ._native import (  # noqa: F401
     TriAttnVarlen,
     load_library,
     tri_attn_bwd,
+    tri_attn_bwd_workspace_size,
     tri_attn_check,
     tri_attn_fwd,
     tri_attn_fwd_bias_dtype,
@@ -56,6 +57,7 @@ __all__ = ["triangle_attention", "triangle_attention_backward", "triangle_attent
            "triangle_attention_varlen", "mask_to_kv_lengths", "tri_attn_varlen_fwd",
            "tri_attn_varlen_check",
            "BlockMask", "causal_mask", "tri_attn_fwd", "tri_attn_fwd_bias_dtype", "tri_attn_bwd",
+           "tri_attn_bwd_workspace_size",
            "tri_attn_check",
            "tri_attn_status_str",
            "tri_attn_mask_to_kv_lengths", "load_library"]
@@ -330,24 +332,16 @@ def mask_to_kv_lengths(mask):
     return lens.squeeze(0) if four_d else lens
 
 
-# Largest dz workspace triangle_attention_backward allocates by itself.
-_DBIAS_WORKSPACE_AUTO_BYTES = 16 << 30
-
-
 def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
                                 scale: Optional[float] = None, *, kv_lengths=None,
-                                block_mask: Optional[BlockMask] = None, stream=None,
-                                dbias_workspace: Optional[bool] = None):
+                                block_mask: Optional[BlockMask] = None, stream=None):
     """Gradients of O = triangle_attention(q, k, v, bias, mask, scale, ...)
     for the incoming gradient dout: returns (dq, dk, dv, dbias), dq/dk/dv in
     q's dtype and dbias fp32 of shape (B,1,H,Q,K) (None when bias is None).
     out, lse and mx are the forward's (O, lse, max) for the same arguments
-    (from return_aux=True).  Every step runs in the library's HIP kernels.
-
-    dbias_workspace: give the library a 4*B*N*H*Q*K-byte workspace so that
-    dbias is summed from stored dz at HBM bandwidth (True) or recomputed
-    without extra memory (False); None picks True up to 16 GiB.  Both give
-    the same bits.
+    (from return_aux=True).  Every step runs in the library's HIP kernels;
+    the library's workspace (12 bytes per (b, n, h, q) row) is allocated
+    here.
     """
     four_d, q5, k5, v5, bias5, desc, keep = _prepare(q, k, v, bias, mask, kv_lengths,
                                                      block_mask)
@@ -366,12 +360,10 @@ def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
     dbias = (torch.empty(B, 1, H, Q, K, device=q5.device, dtype=torch.float32)
              if bias5 is not None else None)
     s = math.nan if scale is None else float(scale)
-    ws_elems = B * N * H * Q * K
-    if dbias_workspace is None:
-        dbias_workspace = 4 * ws_elems <= _DBIAS_WORKSPACE_AUTO_BYTES
-    ws = (torch.empty(ws_elems, device=q5.device, dtype=torch.float32)
-          if dbias is not None and dbias_workspace and ws_elems > 0 else None)
-    st = tri_attn_bwd(TriAttnShape(B, N, H, Q, K, D), _native.DTYPE_CODES[q5.dtype], q5, k5, v5,
+    shape = TriAttnShape(B, N, H, Q, K, D)
+    ws_bytes = tri_attn_bwd_workspace_size(shape)
+    ws = torch.empty((ws_bytes + 3) // 4, device=q5.device, dtype=torch.float32) if ws_bytes else None
+    st = tri_attn_bwd(shape, _native.DTYPE_CODES[q5.dtype], q5, k5, v5,
                       bias5, desc, s, o5, g5, lse5, mx5, dq, dk, dv, dbias, stream, workspace=ws)
     if st != TRIATTN_OK:
         raise RuntimeError(f"tri_attn_bwd: {tri_attn_status_str(st)}")

@@ -34,11 +34,11 @@ TRIATTN_MOD_CAUSAL = 1
 
 EXPORTED = ("tri_attn_check", "tri_attn_fwd", "tri_attn_fwd_bias_dtype", "tri_attn_varlen_check",
             "tri_attn_varlen_fwd",
-            "tri_attn_bwd", "tri_attn_bwd_noalloc", "tri_attn_mask_to_kv_lengths",
-            "tri_attn_status_str")
+            "tri_attn_bwd", "tri_attn_bwd_workspace_size", "tri_attn_bwd_noalloc",
+            "tri_attn_mask_to_kv_lengths", "tri_attn_status_str")
 
-# dz pairs (B*N*H*Q*K) the no-allocation backward holds when dbias is asked for
-TRIATTN_BWD_NOALLOC_MAX_PAIRS = 8 * 1024 * 1024
+# rows (B*N*H*Q) whose per-row data the no-allocation backward holds
+TRIATTN_BWD_NOALLOC_MAX_ROWS = 4 * 1024 * 1024
 
 TRIATTN_QKV_SEPARATE = 0
 TRIATTN_QKV_PACKED = 1
@@ -125,6 +125,8 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_bwd.restype = I32
     lib.tri_attn_bwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P, P, P, P,
                                   ctypes.c_size_t, P]
+    lib.tri_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.tri_attn_bwd_workspace_size.argtypes = [shape_p]
     lib.tri_attn_bwd_noalloc.restype = I32
     lib.tri_attn_bwd_noalloc.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P,
                                          P, P, P]
@@ -222,7 +224,9 @@ def tri_attn_mask_to_kv_lengths(mask, rows: int, K: int, kv_lengths, nonprefix_r
 def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: float, out, dout,
                  lse, mx, dq, dk, dv, dbias, stream, workspace=None) -> int:
     """Enqueue the backward pass on `stream` (as tri_attn_fwd); `workspace`
-    is a tensor of at least 4*B*N*H*Q*K bytes or None."""
+    is a device tensor of at least tri_attn_bwd_workspace_size(shape) bytes
+    (None is passed as NULL, which the library refuses unless there is no
+    query row)."""
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -235,9 +239,14 @@ def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: fl
         ctypes.c_void_p(handle)))
 
 
+def tri_attn_bwd_workspace_size(shape: TriAttnShape) -> int:
+    """Bytes of workspace tri_attn_bwd needs for `shape` (12*B*N*H*Q)."""
+    return int(load_library().tri_attn_bwd_workspace_size(ctypes.byref(shape)))
+
+
 def tri_attn_bwd_noalloc(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: float, out,
                          dout, lse, mx, dq, dk, dv, dbias, stream) -> int:
-    """tri_attn_bwd with the library's own dz scratch: no workspace argument
+    """tri_attn_bwd with the library's own workspace: no workspace argument
     and no allocation (see include/triattn.h)."""
     if stream is None:
         stream = torch.cuda.current_stream(q.device)

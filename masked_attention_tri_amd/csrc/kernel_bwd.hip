@@ -14,20 +14,15 @@
 // every key and it passes nothing to Q, K or the bias.  The bias is shared by
 // every n, so dB sums over n.
 //
-// Three launches per call, no atomics, every sum in a fixed order:
-//   dQ    dq_mfma_kernel (bf16/fp16, D in {32, 64, 128}): 128 query rows
-//         per workgroup, Q and dO in registers, looping over 32-key tiles;
-//         otherwise dq_kernel: 32 rows, fp32 tiles staged in LDS (see Tiles
-//         below).  dQ = s dz K.
-//   dK dV dkdv_mfma_kernel (bf16/fp16, D in {32, 64}): 128 keys per
-//         workgroup, K and V in registers, looping over 32-row query tiles;
-//         otherwise dkdv_kernel: 32 keys, LDS-staged.  dV = P^T dO,
-//         dK = s dz^T Q.
-//   dB    with a dz workspace, the dQ kernel also stores every dz (fp32,
-//         (B,N,H,Q,K)) and dbias_sum4_kernel / dbias_sum_kernel sum it over
-//         n (HBM-bound); without one, dbias_kernel recomputes dz per
-//         (b, h, 32 query rows, 128 keys) walking n (latency-bound).  Both
-//         add the same values in the same order and give the same bits.
+// These are the general kernels: fp32 inputs, head dimensions without an MFMA
+// backward (mfma_bwd.h), and the dBias of block-sparse masks.  Three
+// launches, no atomics, every sum in a fixed order:
+//   dQ    dq_kernel: 32 query rows per workgroup, fp32 tiles staged in LDS
+//         (see Tiles below), looping over key tiles.  dQ = s dz K.
+//   dK dV dkdv_kernel: 32 keys per workgroup, looping over query tiles.
+//         dV = P^T dO, dK = s dz^T Q.
+//   dB    dbias_kernel: dz recomputed per (b, h, 32 query rows, 128 keys)
+//         walking n in order.
 // The contractions run on MFMA for bf16/fp16 (P and dz rounded to the input
 // type as operands) and as fp32 FMAs from LDS for fp32.
 #include <math.h>
@@ -351,15 +346,6 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
         stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
         __syncthreads();
         pair_tile<T>(p, t, b, n, h, q0, k0);
-        if (g.dz && q0 + r < p.Q) {
-            // this thread's own pairs (row r, keys part + 8 j), as pair_tile stored them
-            float* zr = g.dz + (bnh * p.Q + q0 + r) * p.K;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t kk = k0 + part + 8 * j;
-                if (kk < p.K) zr[kk] = t.dzs[r * (kT + 1) + part + 8 * j];
-            }
-        }
         __syncthreads();
         if constexpr (kMfma) {
             // dQ(q, d) += sum_k dz(q, k) K(k, d)
@@ -404,211 +390,6 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
         const int64_t d = part + 8 * i;
         if (d < D) dqr[d] = static_cast<T>(acc[i] * p.scale);
     }
-}
-
-// dQ for bf16/fp16 at D in {32, 64, 128}: one workgroup of 4 waves per
-// (b, n, h, 128 query rows), wave w owning rows 32 w .. 32 w + 31.  Each
-// lane keeps one query row of Q and dO as MFMA operands in registers (lane
-// l: row l % 32, coordinates 16 st + 8 (l / 32) + e), so z^T = K Q^T and
-// dP^T = V dO^T of a 32-key tile leave lane l with one query and 16 keys
-// (register r: key 8 (r / 4) + 4 (l / 32) + r % 4), P and dz are formed in
-// registers, and dQ^T += K^T dz^T takes dz straight from them: the
-// contraction over keys may run in any order as long as both operands use
-// the same one, so the A operand (K^T, from a transposed LDS copy) lists
-// the keys in the lanes' own order.  K and V tiles are double-buffered in
-// LDS and the next tile is loaded into registers while this one is used:
-// one barrier per tile.  Delta, lse and the no-valid-key flag come from
-// stage_rows, and z, dP, P and dz from the same MFMAs and expressions as
-// pair_tile, so the dz stored for dBias has the same bits as the one the
-// dBias walk recomputes.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void dq_mfma_kernel(Params p, BwdParams g) {
-    using M = Mma<T>;
-    using v8 = typename M::v8;
-    typedef T v4 __attribute__((ext_vector_type(4)));
-    constexpr int kRows = 128;                 // query rows per workgroup
-    constexpr int LDK = D + 8;                 // K, V tile row stride (elements)
-    constexpr int LDT = kT + 4;                // transposed K tile row stride (see dkdv_mfma_kernel)
-    constexpr int kChunks = kT * D / 8;        // 16-byte chunks per K (or V) tile
-    constexpr int kPerThr = (kChunks + kThreads - 1) / kThreads;
-    constexpr int kSt = D / 16, kJb = D / 32;
-    __shared__ __align__(16) T ks[2][kT * LDK];
-    __shared__ __align__(16) T vs[2][kT * LDK];
-    __shared__ __align__(16) T kts[2][D * LDT];
-    __shared__ float delta[kRows], lse[kRows], dead[kRows];
-
-    const int64_t n_qt = (p.Q + kRows - 1) / kRows;
-    const int64_t bnh = blockIdx.x / n_qt, q0 = (blockIdx.x % n_qt) * kRows;
-    const int64_t h = bnh % p.H, n = (bnh / p.H) % p.N, b = bnh / (p.H * p.N);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int row = lane & 31, hf = lane >> 5;
-    const int ql = 32 * wave + row;            // this lane's query within the workgroup
-    const int64_t qi = q0 + ql;
-
-    {
-        Tiles t{};
-        for (int i = 0; i < kRows / kT; ++i) {
-            t.delta = delta + kT * i;
-            t.lse = lse + kT * i;
-            t.dead = dead + kT * i;
-            stage_rows<T>(p, g, t, bnh, q0 + kT * i);
-        }
-    }
-    const T* qb = static_cast<const T*>(p.q) + bnh * p.Q * D;
-    const T* gb = static_cast<const T*>(g.dout) + bnh * p.Q * D;
-    const T* kb = static_cast<const T*>(p.k) + bnh * p.K * D;
-    const T* vb = static_cast<const T*>(p.v) + bnh * p.K * D;
-    v8 qop[kSt], gop[kSt];
-#pragma unroll
-    for (int st = 0; st < kSt; ++st) {
-        qop[st] = v8{};
-        gop[st] = v8{};
-        if (qi < p.Q) {
-            qop[st] = *reinterpret_cast<const v8*>(qb + qi * D + 16 * st + 8 * hf);
-            gop[st] = *reinterpret_cast<const v8*>(gb + qi * D + 16 * st + 8 * hf);
-        }
-    }
-    f32x16 acc[kJb];
-#pragma unroll
-    for (int jb = 0; jb < kJb; ++jb) acc[jb] = f32x16{};
-
-    v8 kr[kPerThr], vr[kPerThr];
-    auto load = [&](int64_t k0) {
-#pragma unroll
-        for (int i = 0; i < kPerThr; ++i) {
-            const int c = tid + kThreads * i;
-            const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-            kr[i] = v8{};
-            vr[i] = v8{};
-            if (c < kChunks && k0 + r < p.K) {
-                kr[i] = *reinterpret_cast<const v8*>(kb + (k0 + r) * D + col);
-                vr[i] = *reinterpret_cast<const v8*>(vb + (k0 + r) * D + col);
-            }
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < kPerThr; ++i) {
-            const int c = tid + kThreads * i;
-            if (c >= kChunks) continue;
-            const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-            *reinterpret_cast<v8*>(&ks[buf][r * LDK + col]) = kr[i];
-            *reinterpret_cast<v8*>(&vs[buf][r * LDK + col]) = vr[i];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kts[buf][(col + e) * LDT + r] = kr[i][e];
-        }
-    };
-
-    const int64_t lim = key_limit(p, b, n);    // no valid key at or past it
-    const int64_t n_tiles = (lim + kT - 1) / kT;
-    if (n_tiles > 0) {
-        load(0);
-        store(0);
-        if (n_tiles > 1) load(kT);
-    }
-    __syncthreads();  // rows staged, first tile in LDS
-    const float d_q = delta[ql], l2_q = lse[ql] * kLog2e, s2 = p.scale * kLog2e;
-    const bool dead_q = dead[ql] != 0.f, live = qi < p.Q && !dead_q;
-    const bool simple = p.mask_kind == TRIATTN_MASK_NONE || p.mask_kind == TRIATTN_MASK_KV_LENGTHS;
-    const float* brow = p.bias ? p.bias + ((b * p.H + h) * p.Q + qi) * p.K : nullptr;
-    float* zrow = g.dz ? g.dz + (bnh * p.Q + qi) * p.K : nullptr;
-    const bool bias4 = brow && (p.K & 3) == 0 && (reinterpret_cast<uintptr_t>(p.bias) & 15) == 0;
-
-    for (int64_t t = 0; t < n_tiles; ++t) {
-        const int buf = static_cast<int>(t & 1);
-        const int64_t k0 = t * kT;
-        // this lane's 16 bias values, issued before the MFMAs
-        float bv[16];
-        if (bias4) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int64_t kk = k0 + 8 * c + 4 * hf;  // 4 consecutive keys from here
-                const float4 v = live && kk < p.K ? *reinterpret_cast<const float4*>(brow + kk)
-                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-                bv[4 * c] = v.x;
-                bv[4 * c + 1] = v.y;
-                bv[4 * c + 2] = v.z;
-                bv[4 * c + 3] = v.w;
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t kk = k0 + 8 * (r / 4) + 4 * hf + (r % 4);
-                bv[r] = brow && live && kk < p.K ? brow[kk] : 0.f;
-            }
-        }
-        f32x16 z{}, dp{};
-#pragma unroll
-        for (int st = 0; st < kSt; ++st) {
-            const v8 ka = *reinterpret_cast<const v8*>(&ks[buf][row * LDK + 16 * st + 8 * hf]);
-            z = M::run(ka, qop[st], z);
-        }
-#pragma unroll
-        for (int st = 0; st < kSt; ++st) {
-            const v8 va = *reinterpret_cast<const v8*>(&vs[buf][row * LDK + 16 * st + 8 * hf]);
-            dp = M::run(va, gop[st], dp);
-        }
-        float dz[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int64_t kk = k0 + 8 * (r / 4) + 4 * hf + (r % 4);
-            float v = 0.f;
-            const bool ok = live && kk < p.K &&
-                            (simple ? kk < lim : key_valid(p, b, n, h, qi, kk));
-            if (ok) {
-                const float pr = softmax_p(z[r], s2, bv[r], l2_q);
-                v = pr * (dp[r] - d_q);
-            }
-            dz[r] = v;
-        }
-        if (zrow && qi < p.Q) {
-            if ((p.K & 3) == 0) {
-                // registers 4 c .. 4 c + 3 are 4 consecutive keys from a multiple of 4
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int64_t kk = k0 + 8 * c + 4 * hf;
-                    if (kk < p.K)
-                        *reinterpret_cast<float4*>(zrow + kk) =
-                            make_float4(dz[4 * c], dz[4 * c + 1], dz[4 * c + 2], dz[4 * c + 3]);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t kk = k0 + 8 * (r / 4) + 4 * hf + (r % 4);
-                    if (kk < p.K) zrow[kk] = dz[r];
-                }
-            }
-        }
-        v8 dzop[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dzop[st][e] = static_cast<T>(dz[8 * st + e]);
-#pragma unroll
-        for (int jb = 0; jb < kJb; ++jb) {
-            const int d = 32 * jb + row;
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                // keys 16 st + 4 hf + 0..3 and 16 st + 8 + 4 hf + 0..3: this lane's dz order
-                const v4 lo = *reinterpret_cast<const v4*>(&kts[buf][d * LDT + 16 * st + 4 * hf]);
-                const v4 hi = *reinterpret_cast<const v4*>(&kts[buf][d * LDT + 16 * st + 8 + 4 * hf]);
-                const v8 ka = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[jb] = M::run(ka, dzop[st], acc[jb]);
-            }
-        }
-        if (t + 1 < n_tiles) {
-            store(buf ^ 1);
-            if (t + 2 < n_tiles) load((t + 2) * kT);
-        }
-        __syncthreads();
-    }
-    if (qi >= p.Q) return;
-    T* dqr = static_cast<T*>(g.dq) + (bnh * p.Q + qi) * D;
-#pragma unroll
-    for (int jb = 0; jb < kJb; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-            dqr[32 * jb + 8 * (r / 4) + 4 * hf + (r % 4)] = static_cast<T>(acc[jb][r] * p.scale);
 }
 
 // dK and dV: one workgroup per (b, n, h, 32 keys); loops over query tiles.
@@ -756,250 +537,10 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
     }
 }
 
-// dK and dV for bf16/fp16 at D in {32, 64}: one workgroup of 4 waves per
-// (b, n, h, 128 keys), wave w owning keys 32 w .. 32 w + 31.  The mirror of
-// dq_mfma_kernel: each lane keeps one key row of K and V as MFMA operands in
-// registers, so z = Q K^T and dP = dO V^T of a 32-query tile leave lane l
-// with one key and 16 queries (register r: query 8 (r / 4) + 4 (l / 32) +
-// r % 4); dV^T += dO^T P and dK^T += Q^T dz then take P and dz from the
-// registers, with the A operands (dO^T, Q^T) read from transposed LDS copies
-// in the lanes' own query order.  Q and dO tiles are double-buffered and the
-// next tile is loaded into registers while this one is used (one barrier
-// per tile); Delta = dO.O of the tile's rows is reduced from those same
-// registers (with O loaded beside dO), lse and the no-valid-key flag beside
-// them.
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void dkdv_mfma_kernel(Params p, BwdParams g) {
-    using M = Mma<T>;
-    using v8 = typename M::v8;
-    typedef T v4 __attribute__((ext_vector_type(4)));
-    constexpr int kKeys = 128;                 // keys per workgroup
-    constexpr int LDK = D + 8;                 // Q, dO tile row stride (elements)
-    // transposed tile row stride: 72 bytes keeps the 8-byte operand reads
-    // aligned and spreads the 2-byte transposed stores of one instruction
-    // (8 column blocks x 8 rows) over twice as many banks as 80 bytes would
-    constexpr int LDT = kT + 4;
-    constexpr int kCpr = D / 8;                // 16-byte chunks per row
-    constexpr int kChunks = kT * kCpr;         // per tile
-    static_assert(kChunks <= kThreads, "one chunk per thread");
-    constexpr int kSt = D / 16, kJb = D / 32;
-    __shared__ __align__(16) T qs[2][kT * LDK];
-    __shared__ __align__(16) T gs[2][kT * LDK];
-    __shared__ __align__(16) T qts[2][D * LDT];
-    __shared__ __align__(16) T gts[2][D * LDT];
-    // per query row of the tile: Delta, lse log2 e, 1 when the row has no valid key
-    __shared__ __align__(16) float delta[2][kT], lse2[2][kT], dead[2][kT];
-
-    const int64_t n_kt = (p.K + kKeys - 1) / kKeys;
-    const int64_t bnh = blockIdx.x / n_kt, kw0 = (blockIdx.x % n_kt) * kKeys;
-    const int64_t h = bnh % p.H, n = (bnh / p.H) % p.N, b = bnh / (p.H * p.N);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int row = lane & 31, hf = lane >> 5;
-    const int64_t kk = kw0 + 32 * wave + row;  // this lane's key
-
-    const T* qb = static_cast<const T*>(p.q) + bnh * p.Q * D;
-    const T* gb = static_cast<const T*>(g.dout) + bnh * p.Q * D;
-    const T* ob = static_cast<const T*>(g.out) + bnh * p.Q * D;
-    v8 kop[kSt], vop[kSt];
-#pragma unroll
-    for (int st = 0; st < kSt; ++st) {
-        kop[st] = v8{};
-        vop[st] = v8{};
-        if (kk < p.K) {
-            const int64_t off = (bnh * p.K + kk) * D + 16 * st + 8 * hf;
-            kop[st] = *reinterpret_cast<const v8*>(static_cast<const T*>(p.k) + off);
-            vop[st] = *reinterpret_cast<const v8*>(static_cast<const T*>(p.v) + off);
-        }
-    }
-    f32x16 ak[kJb], av[kJb];
-#pragma unroll
-    for (int jb = 0; jb < kJb; ++jb) {
-        ak[jb] = f32x16{};
-        av[jb] = f32x16{};
-    }
-
-    // thread tid < kChunks holds chunk tid: row tid / kCpr, columns 8 (tid % kCpr) ..
-    const int cr = tid / kCpr, cc = (tid % kCpr) * 8;
-    v8 qr{}, gr{}, orr{};
-    float lr = 0.f, mr = 0.f;
-    auto load = [&](int64_t q0) {
-        qr = v8{};
-        gr = v8{};
-        orr = v8{};
-        if (tid < kChunks && q0 + cr < p.Q) {
-            const int64_t off = (q0 + cr) * D + cc;
-            qr = *reinterpret_cast<const v8*>(qb + off);
-            gr = *reinterpret_cast<const v8*>(gb + off);
-            orr = *reinterpret_cast<const v8*>(ob + off);
-        }
-        if (tid < kT && q0 + tid < p.Q) {
-            lr = g.lse[bnh * p.Q + q0 + tid];
-            mr = g.mx[bnh * p.Q + q0 + tid];
-        }
-    };
-    auto store = [&](int buf, int64_t q0) {
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            part = fmaf(static_cast<float>(gr[e]), static_cast<float>(orr[e]), part);
-#pragma unroll
-        for (int s = 1; s < kCpr; s <<= 1) part += __shfl_xor(part, s);
-        if (tid < kChunks) {
-            *reinterpret_cast<v8*>(&qs[buf][cr * LDK + cc]) = qr;
-            *reinterpret_cast<v8*>(&gs[buf][cr * LDK + cc]) = gr;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                qts[buf][(cc + e) * LDT + cr] = qr[e];
-                gts[buf][(cc + e) * LDT + cr] = gr[e];
-            }
-            if (cc == 0) delta[buf][cr] = part;
-        }
-        if (tid < kT) {
-            const bool in = q0 + tid < p.Q;
-            lse2[buf][tid] = in ? lr * kLog2e : 0.f;
-            dead[buf][tid] = in && mr == kMaskedLogit ? 1.f : 0.f;
-        }
-    };
-
-    const int64_t lim = key_limit(p, b, n);    // no valid key at or past it
-    // keys of this workgroup all past a nonzero limit get nothing (rows with
-    // no valid key, the only other source, exist only when lim is 0 here)
-    const int64_t n_tiles = (lim > 0 && kw0 >= lim) ? 0 : (p.Q + kT - 1) / kT;
-    if (n_tiles > 0) {
-        load(0);
-        store(0, 0);
-        if (n_tiles > 1) load(kT);
-    }
-    __syncthreads();
-    const bool simple = p.mask_kind == TRIATTN_MASK_NONE || p.mask_kind == TRIATTN_MASK_KV_LENGTHS;
-    const float inv_k = 1.0f / static_cast<float>(p.K), s2 = p.scale * kLog2e;
-    const float* bcol = p.bias ? p.bias + (b * p.H + h) * p.Q * p.K + kk : nullptr;
-
-    for (int64_t t = 0; t < n_tiles; ++t) {
-        const int buf = static_cast<int>(t & 1);
-        const int64_t q0 = t * kT;
-        f32x16 z{}, dp{};
-#pragma unroll
-        for (int st = 0; st < kSt; ++st) {
-            const v8 qa = *reinterpret_cast<const v8*>(&qs[buf][row * LDK + 16 * st + 8 * hf]);
-            z = M::run(qa, kop[st], z);
-        }
-#pragma unroll
-        for (int st = 0; st < kSt; ++st) {
-            const v8 ga = *reinterpret_cast<const v8*>(&gs[buf][row * LDK + 16 * st + 8 * hf]);
-            dp = M::run(ga, vop[st], dp);
-        }
-        v8 pop[2], zop[2];
-        auto at = [](const float4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            // registers 4 c .. 4 c + 3 hold queries 8 c + 4 hf + 0..3: one 16-byte read each
-            const float4 rl = *reinterpret_cast<const float4*>(&lse2[buf][8 * c + 4 * hf]);
-            const float4 rd = *reinterpret_cast<const float4*>(&delta[buf][8 * c + 4 * hf]);
-            const float4 rx = *reinterpret_cast<const float4*>(&dead[buf][8 * c + 4 * hf]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * c + i, ql = 8 * c + 4 * hf + i;
-                const int64_t qi = q0 + ql;
-                float pr = 0.f, dz = 0.f;
-                if (qi < p.Q && kk < p.K) {
-                    if (at(rx, i) != 0.f) {
-                        pr = inv_k;
-                    } else if (simple ? kk < lim : key_valid(p, b, n, h, qi, kk)) {
-                        const float bias = bcol ? bcol[qi * p.K] : 0.f;
-                        pr = softmax_p(z[r], s2, bias, at(rl, i));
-                        dz = pr * (dp[r] - at(rd, i));
-                    }
-                }
-                pop[r / 8][r % 8] = static_cast<T>(pr);
-                zop[r / 8][r % 8] = static_cast<T>(dz);
-            }
-        }
-#pragma unroll
-        for (int jb = 0; jb < kJb; ++jb) {
-            const int d = 32 * jb + row;
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                // queries 16 st + 4 hf + 0..3 and 16 st + 8 + 4 hf + 0..3: this lane's order
-                const int c0 = d * LDT + 16 * st + 4 * hf;
-                const v4 glo = *reinterpret_cast<const v4*>(&gts[buf][c0]);
-                const v4 ghi = *reinterpret_cast<const v4*>(&gts[buf][c0 + 8]);
-                av[jb] = M::run(__builtin_shufflevector(glo, ghi, 0, 1, 2, 3, 4, 5, 6, 7), pop[st],
-                                av[jb]);
-                const v4 qlo = *reinterpret_cast<const v4*>(&qts[buf][c0]);
-                const v4 qhi = *reinterpret_cast<const v4*>(&qts[buf][c0 + 8]);
-                ak[jb] = M::run(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7), zop[st],
-                                ak[jb]);
-            }
-        }
-        if (t + 1 < n_tiles) {
-            store(buf ^ 1, q0 + kT);
-            if (t + 2 < n_tiles) load(q0 + 2 * kT);
-        }
-        __syncthreads();
-    }
-    if (kk >= p.K) return;
-    T* dkr = static_cast<T*>(g.dk) + (bnh * p.K + kk) * D;
-    T* dvr = static_cast<T*>(g.dv) + (bnh * p.K + kk) * D;
-#pragma unroll
-    for (int jb = 0; jb < kJb; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int d = 32 * jb + 8 * (r / 4) + 4 * hf + (r % 4);
-            dkr[d] = static_cast<T>(ak[jb][r] * p.scale);
-            dvr[d] = static_cast<T>(av[jb][r]);
-        }
-}
-
-// dBias from the dz workspace: one thread per (b, h, q, k), summing over n
-// in order (dz is 0 at and past a row's key limit, where dq_kernel stored
-// nothing).  Consecutive threads take consecutive keys: every load of the
-// sum is one coalesced row segment.
-__global__ __launch_bounds__(256) void dbias_sum_kernel(Params p, BwdParams g) {
-    const int64_t total = p.B * p.H * p.Q * p.K;
-    const int64_t plane = p.H * p.Q * p.K;  // stride of n in the workspace
-    for (int64_t e = blockIdx.x * int64_t(256) + threadIdx.x; e < total;
-         e += int64_t(gridDim.x) * 256) {
-        const int64_t kk = e % p.K, bhq = e / p.K;
-        const int64_t b = bhq / (p.H * p.Q), hq = bhq % (p.H * p.Q);
-        const float* src = g.dz + b * p.N * plane + hq * p.K + kk;
-        float acc = 0.f;
-#pragma unroll 8
-        for (int64_t n = 0; n < p.N; ++n)
-            if (kk < key_limit(p, b, n)) acc += src[n * plane];
-        g.dbias[e] = acc;
-    }
-}
-
-// The same sum, 4 consecutive keys per thread with 16-byte loads and stores
-// (K a multiple of 4, dbias 16-byte aligned).  A group of 4 keys is read
-// when its first key is below the limit; its other keys then lie in a key
-// tile that dq_kernel visited, where it stored 0 for every invalid key.
-__global__ __launch_bounds__(256) void dbias_sum4_kernel(Params p, BwdParams g) {
-    const int64_t total = p.B * p.H * p.Q * p.K;
-    const int64_t plane = p.H * p.Q * p.K;
-    for (int64_t e = 4 * (blockIdx.x * int64_t(256) + threadIdx.x); e < total;
-         e += 4 * int64_t(gridDim.x) * 256) {
-        const int64_t kk = e % p.K, bhq = e / p.K;
-        const int64_t b = bhq / (p.H * p.Q), hq = bhq % (p.H * p.Q);
-        const float* src = g.dz + b * p.N * plane + hq * p.K + kk;
-        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-        for (int64_t n = 0; n < p.N; ++n) {
-            if (kk < key_limit(p, b, n)) {
-                const float4 v = *reinterpret_cast<const float4*>(src + n * plane);
-                acc.x += v.x;
-                acc.y += v.y;
-                acc.z += v.z;
-                acc.w += v.w;
-            }
-        }
-        *reinterpret_cast<float4*>(g.dbias + e) = acc;
-    }
-}
-
+// The general kernels; with dbias_only, just dBias (the MFMA backward's
+// block-sparse case).
 template <typename T, int NC>
-hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
+hipError_t launch_nc(const Params& p, const BwdParams& g, bool dbias_only, hipStream_t stream) {
     const int64_t n_qt = (p.Q + kT - 1) / kT, n_kt = (p.K + kT - 1) / kT;
     const int64_t n_kc = (p.K + kT * kChunk - 1) / (kT * kChunk);
     const int64_t gq = p.B * p.N * p.H * n_qt, gk = p.B * p.N * p.H * n_kt,
@@ -1021,71 +562,45 @@ hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
                                     hipFuncAttributeMaxDynamicSharedMemorySize, b);
         if (e != hipSuccess) return e;
     }
-    if (gq > 0) {
-        bool done = false;
-        if constexpr (!std::is_same<T, float>::value) {
-            const dim3 gm(static_cast<unsigned>(p.B * p.N * p.H * ((p.Q + 127) / 128)));
-            done = true;
-            if (p.D == 32)
-                hipLaunchKernelGGL((dq_mfma_kernel<T, 32>), gm, block, 0, stream, p, g);
-            else if (p.D == 64)
-                hipLaunchKernelGGL((dq_mfma_kernel<T, 64>), gm, block, 0, stream, p, g);
-            else if (p.D == 128)
-                hipLaunchKernelGGL((dq_mfma_kernel<T, 128>), gm, block, 0, stream, p, g);
-            else
-                done = false;
-        }
-        if (!done)
-            hipLaunchKernelGGL((dq_kernel<T, NC>), dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
-    }
-    if (gk > 0) {
-        bool done = false;
-        if constexpr (!std::is_same<T, float>::value) {
-            const dim3 gm(static_cast<unsigned>(p.B * p.N * p.H * ((p.K + 127) / 128)));
-            done = true;
-            if (p.D == 32)
-                hipLaunchKernelGGL((dkdv_mfma_kernel<T, 32>), gm, block, 0, stream, p, g);
-            else if (p.D == 64)
-                hipLaunchKernelGGL((dkdv_mfma_kernel<T, 64>), gm, block, 0, stream, p, g);
-            else
-                done = false;
-        }
-        if (!done)
-            hipLaunchKernelGGL((dkdv_kernel<T, NC>), dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
-    }
-    if (g.dbias && g.dz) {
-        const int64_t total = p.B * p.H * p.Q * p.K;
-        const bool vec4 = (p.K & 3) == 0 && (reinterpret_cast<uintptr_t>(g.dbias) & 15) == 0;
-        const int64_t want = (total / (vec4 ? 4 : 1) + 255) / 256;
-        const unsigned gs = static_cast<unsigned>(want < (1 << 20) ? want : (1 << 20));
-        if (gs > 0 && vec4)
-            hipLaunchKernelGGL(dbias_sum4_kernel, dim3(gs), dim3(256), 0, stream, p, g);
-        else if (gs > 0)
-            hipLaunchKernelGGL(dbias_sum_kernel, dim3(gs), dim3(256), 0, stream, p, g);
-    } else if (g.dbias && gb > 0) {
+    if (!dbias_only && gq > 0)
+        hipLaunchKernelGGL((dq_kernel<T, NC>), dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
+    if (!dbias_only && gk > 0)
+        hipLaunchKernelGGL((dkdv_kernel<T, NC>), dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
+    if (g.dbias && gb > 0)
         hipLaunchKernelGGL((dbias_kernel<T, NC>), dim3(static_cast<unsigned>(gb)), block, shm, stream, p, g);
-    }
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_t(const Params& p, const BwdParams& g, hipStream_t stream) {
-    if (p.D <= 32) return launch_nc<T, 4>(p, g, stream);
-    if (p.D <= 64) return launch_nc<T, 8>(p, g, stream);
-    if (p.D <= 128) return launch_nc<T, 16>(p, g, stream);
-    return launch_nc<T, 32>(p, g, stream);
+hipError_t launch_t(const Params& p, const BwdParams& g, bool dbias_only, hipStream_t stream) {
+    if (p.D <= 32) return launch_nc<T, 4>(p, g, dbias_only, stream);
+    if (p.D <= 64) return launch_nc<T, 8>(p, g, dbias_only, stream);
+    if (p.D <= 128) return launch_nc<T, 16>(p, g, dbias_only, stream);
+    return launch_nc<T, 32>(p, g, dbias_only, stream);
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, hipStream_t stream) {
+hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
+                      hipStream_t stream) {
+    if (bwd_mfma_supports(p, dtype)) {
+        hipError_t e = p.D == 32   ? launch_bwd_mfma_d32(p, g, dtype, ws, stream)
+                       : p.D == 64 ? launch_bwd_mfma_d64(p, g, dtype, ws, stream)
+                                   : launch_bwd_mfma_d128(p, g, dtype, ws, stream);
+        if (e != hipSuccess) return e;
+        // dBias of a block-sparse mask: the general walk over n
+        if (p.mask_kind == TRIATTN_MASK_BLOCK && g.dbias && p.bias)
+            return dtype == TRIATTN_BF16 ? launch_t<__bf16>(p, g, true, stream)
+                                         : launch_t<_Float16>(p, g, true, stream);
+        return hipSuccess;
+    }
     switch (dtype) {
     case TRIATTN_F32:
-        return launch_t<float>(p, g, stream);
+        return launch_t<float>(p, g, false, stream);
     case TRIATTN_F16:
-        return launch_t<_Float16>(p, g, stream);
+        return launch_t<_Float16>(p, g, false, stream);
     case TRIATTN_BF16:
-        return launch_t<__bf16>(p, g, stream);
+        return launch_t<__bf16>(p, g, false, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -1,0 +1,13 @@
+// The MFMA backward kernels (mfma_bwd.h) at D = 128.
+#include "mfma_bwd.h"
+
+namespace triattn {
+
+hipError_t launch_bwd_mfma_d128(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
+                               hipStream_t stream) {
+    const bool exact = tile::scale_is_exact(p.scale);
+    if (dtype == TRIATTN_BF16) return launch_bwd_d<__bf16, 128>(p, g, exact, ws, stream);
+    return launch_bwd_d<_Float16, 128>(p, g, exact, ws, stream);
+}
+
+}  // namespace triattn

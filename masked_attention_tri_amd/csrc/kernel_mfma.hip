@@ -37,6 +37,31 @@ bool mfma_supports(const Params& p, int32_t dtype) {
     return true;
 }
 
+bool bwd_mfma_supports(const Params& p, int32_t dtype) {
+    if (dtype != TRIATTN_BF16 && dtype != TRIATTN_F16) return false;
+    if (p.D != 32 && p.D != 64 && p.D != 128) return false;
+    if (p.mask_kind != TRIATTN_MASK_NONE && p.mask_kind != TRIATTN_MASK_KV_LENGTHS &&
+        p.mask_kind != TRIATTN_MASK_DENSE && p.mask_kind != TRIATTN_MASK_BLOCK)
+        return false;
+    // the dK / dV kernel keeps one bit per 32-row query tile in a wave's
+    // 64 lanes of 32 bits
+    if (p.Q > 65536) return false;
+    if (p.mask_kind == TRIATTN_MASK_BLOCK) {
+        // dQ: one block row per 128-row workgroup; dK / dV: whole query tiles
+        // per block and one kv block per wave
+        if (p.q_block % 128 != 0 || p.kv_block % kKTile != 0) return false;
+        if (p.n_q_rows > 2048 || p.n_kv_blocks > kMaxKvBlocks) return false;
+    }
+    const int64_t kpad = (p.K + 127) / 128 * 128;
+    const int64_t qpad = (p.Q + 127) / 128 * 128;
+    const int64_t lim = int64_t(1) << 31;
+    if (kpad * p.D * 2 >= lim || qpad * p.D * 2 >= lim || (qpad + 32) * kpad * 4 >= lim ||
+        qpad * 8 >= lim)
+        return false;
+    if (!scale_is_exact(p.scale) && !(p.scale >= 0x1p-40f)) return false;
+    return true;
+}
+
 hipError_t launch_mfma(const Params& p, int32_t dtype, hipStream_t stream) {
     const bool exact = scale_is_exact(p.scale);
     switch (p.D) {

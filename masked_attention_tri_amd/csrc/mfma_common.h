@@ -112,7 +112,9 @@ __device__ __forceinline__ u32x4 make_desc(const void* base, uint32_t bytes) {
 // which defeats prefetching more than one tile ahead.  The key loop waits
 // for them explicitly (vmcnt) and fences with barriers instead.
 __device__ __forceinline__ void dma16(const u32x4& r, lds_char* dst, uint32_t voff) {
-    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
+    // (dst is wave-uniform by construction; readfirstlane tells the compiler)
+    const uint32_t lds = static_cast<uint32_t>(
+        __builtin_amdgcn_readfirstlane(static_cast<int>(reinterpret_cast<uintptr_t>(dst))));
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :
                  : "s"(lds), "v"(voff), "s"(r)
@@ -156,6 +158,37 @@ struct Par {
 // An offset past every buffer's range: a DMA with it reads nothing (the
 // buffer range check returns zeros) and only fills a dead LDS buffer.
 constexpr uint32_t kNoTile = 0x80000000u;
+
+// Block bitmaps in LDS: one bit per kv (or query) block.
+__device__ __forceinline__ bool bit_set(const uint32_t* bits, int64_t i) {
+    return (bits[i >> 5] >> (i & 31)) & 1u;
+}
+
+// First set bit at or after `from`, or -1.
+__device__ inline int64_t next_set(const uint32_t* bits, int64_t from, int64_t n) {
+    int64_t j = from;
+    while (j < n) {
+        const uint32_t w = bits[j >> 5] >> (j & 31);
+        if (w) {
+            const int64_t r = j + __builtin_ctz(w);
+            return r < n ? r : -1;
+        }
+        j = (j | 31) + 1;
+    }
+    return -1;
+}
+
+__device__ inline void mark_list(uint32_t* bits, const int32_t* counts, const int32_t* ids,
+                          int64_t list_row, int64_t width, int64_t n_blocks, int tid,
+                          int n_threads) {
+    int64_t count = counts[list_row];
+    count = count < 0 ? 0 : (count > width ? width : count);
+    const int32_t* row = ids + list_row * width;
+    for (int64_t j = tid; j < count; j += n_threads) {
+        const int64_t id = row[j];
+        if (id >= 0 && id < n_blocks) atomicOr(&bits[id >> 5], 1u << (id & 31));
+    }
+}
 
 // s*x is exact for every normal x of the input format when s is 0 or a power
 // of two with |s| <= 1 (so s*x cannot overflow).  An fp16 product that falls

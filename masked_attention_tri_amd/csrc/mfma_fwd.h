@@ -93,36 +93,6 @@ constexpr int kBiasHalfWaveBytes = 32 * kBiasHalfRowBytes;  // 2 KiB
 constexpr int kBiasHalfDma = kBiasHalfWaveBytes / 1024;
 __device__ __forceinline__ int fbh(int r) { return ((r >> 2) ^ (r >> 4)) & 3; }
 
-__device__ __forceinline__ bool bit_set(const uint32_t* bits, int64_t i) {
-    return (bits[i >> 5] >> (i & 31)) & 1u;
-}
-
-// First set bit at or after `from`, or -1.
-__device__ int64_t next_set(const uint32_t* bits, int64_t from, int64_t n) {
-    int64_t j = from;
-    while (j < n) {
-        const uint32_t w = bits[j >> 5] >> (j & 31);
-        if (w) {
-            const int64_t r = j + __builtin_ctz(w);
-            return r < n ? r : -1;
-        }
-        j = (j | 31) + 1;
-    }
-    return -1;
-}
-
-__device__ void mark_list(uint32_t* bits, const int32_t* counts, const int32_t* ids,
-                          int64_t list_row, int64_t width, int64_t n_blocks, int tid,
-                          int n_threads) {
-    int64_t count = counts[list_row];
-    count = count < 0 ? 0 : (count > width ? width : count);
-    const int32_t* row = ids + list_row * width;
-    for (int64_t j = tid; j < count; j += n_threads) {
-        const int64_t id = row[j];
-        if (id >= 0 && id < n_blocks) atomicOr(&bits[id >> 5], 1u << (id & 31));
-    }
-}
-
 // Waves per SIMD the register budget must allow: four (128 VGPRs) for
 // D <= 64, two for D = 128 (whose O accumulator alone takes 64 VGPRs).
 template <int D>

@@ -1,16 +1,18 @@
 // tri_attn_bwd_noalloc: the backward for callers that cannot allocate (code
 // under HIP graph capture, tight serving loops, harnesses that forbid
-// hipMalloc).  It is tri_attn_bwd with its dz workspace taken from a fixed
-// device array of this library instead of from the caller: nothing is
-// allocated or freed, and nothing but the kernels of tri_attn_bwd runs.
+// hipMalloc).  It is tri_attn_bwd with its workspace (the per-row data)
+// taken from a fixed device array of this library instead of from the
+// caller: nothing is allocated or freed, and nothing but the kernels of
+// tri_attn_bwd runs.
 //
 // The array (`scratch`) lives in every GPU that loads the library until the
 // process ends.  Its address differs per device, so it is resolved with
 // hipGetSymbolAddress on the first call on each device (that device
 // current) and cached; host code never passes the symbol itself to a
 // kernel.  Calls on one GPU share the array: calls that overlap in time on
-// one GPU race (each stores dz there and sums it back).  Nothing in it needs
-// clearing: a call's dQ pass writes every dz entry its dBias sum reads.
+// one GPU race (each stores its per-row data there and reads it back).
+// Nothing in it needs clearing: a call's first pass writes every entry its
+// later passes read.
 #include <atomic>
 #include <mutex>
 
@@ -18,8 +20,8 @@
 
 namespace {
 
-// 32 MiB of fp32: dz for B*N*H*Q*K <= TRIATTN_BWD_NOALLOC_MAX_PAIRS.
-constexpr int64_t kScratchFloats = TRIATTN_BWD_NOALLOC_MAX_PAIRS;
+// 48 MiB: 12 bytes (3 floats) of per-row data for B*N*H*Q <= TRIATTN_BWD_NOALLOC_MAX_ROWS.
+constexpr int64_t kScratchFloats = 3 * int64_t(TRIATTN_BWD_NOALLOC_MAX_ROWS);
 static __device__ __align__(256) float scratch[kScratchFloats];
 
 constexpr int kMaxDevices = 64;
@@ -60,30 +62,25 @@ triattn_status tri_attn_bwd_noalloc(const tri_attn_shape* shape, int32_t dtype, 
                                     const void* dout, const float* lse, const float* max,
                                     void* dq, void* dk, void* dv, float* dbias,
                                     hipStream_t stream) {
-    // Everything tri_attn_bwd validates (with no workspace: the arguments
-    // alone), then the scratch's capacity; nothing touches the device first.
+    // Everything tri_attn_bwd validates but the workspace, then the
+    // scratch's capacity; nothing touches the device first.
     const triattn_status st =
         triattn::bwd_validate(shape, dtype, q, k, v, bias, mask, scale, out, dout, lse, max, dq,
-                              dk, dv, dbias, nullptr, 0);
+                              dk, dv, dbias, nullptr, 0, false);
     if (st != TRIATTN_OK) return st;
     if (shape->B == 0 || shape->N == 0 || shape->H == 0 || shape->Q == 0) return TRIATTN_OK;
-    if (dbias) {  // dz of every (b, n, h, q, k) pair must fit the scratch
-        int64_t pairs = 1;
-        for (const int64_t x : {shape->B, shape->N, shape->H, shape->Q, shape->K}) {
-            if (pairs > kScratchFloats / x) return TRIATTN_ERR_UNSUPPORTED;
-            pairs *= x;
-        }
-        if (pairs > kScratchFloats) return TRIATTN_ERR_UNSUPPORTED;
+    // the per-row data of B*N*H*Q rows must fit the scratch
+    int64_t rows = 1;
+    for (const int64_t x : {shape->B, shape->N, shape->H, shape->Q}) {
+        if (rows > TRIATTN_BWD_NOALLOC_MAX_ROWS / x) return TRIATTN_ERR_UNSUPPORTED;
+        rows *= x;
     }
-    float* ws = nullptr;
-    if (dbias) {
-        hipError_t err = hipSuccess;
-        ws = device_scratch(&err);
-        if (!ws) return TRIATTN_ERR_HIP;
-    }
+    if (rows > TRIATTN_BWD_NOALLOC_MAX_ROWS) return TRIATTN_ERR_UNSUPPORTED;
+    hipError_t err = hipSuccess;
+    float* ws = device_scratch(&err);
+    if (!ws) return TRIATTN_ERR_HIP;
     return tri_attn_bwd(shape, dtype, q, k, v, bias, mask, scale, out, dout, lse, max, dq, dk,
-                        dv, dbias, ws,
-                        ws ? static_cast<size_t>(kScratchFloats) * sizeof(float) : 0, stream);
+                        dv, dbias, ws, static_cast<size_t>(kScratchFloats) * sizeof(float), stream);
 }
 
 }  // extern "C"

@@ -205,7 +205,8 @@ triattn_status bwd_validate(const tri_attn_shape* shape, int32_t dtype, const vo
                             const tri_attn_mask* mask, float scale, const void* out,
                             const void* dout, const float* lse, const float* max, const void* dq,
                             const void* dk, const void* dv, const float* dbias,
-                            const float* workspace, size_t workspace_bytes) {
+                            const float* workspace, size_t workspace_bytes,
+                            bool check_workspace) {
     // The forward's arguments (out is read, not written, here).
     triattn_status st = check_impl(shape, dtype, q, k, v, bias, mask, scale, out, lse, max);
     if (st != TRIATTN_OK) return st;
@@ -214,15 +215,13 @@ triattn_status bwd_validate(const tri_attn_shape* shape, int32_t dtype, const vo
     if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
         !aligned(dbias, 4) || !aligned(workspace, 16))
         return TRIATTN_ERR_INVALID_ARG;
-    if (dbias && workspace) {
-        // 4 B N H Q K bytes: dz of every (b, n, h, q, k) pair
+    if (!empty && check_workspace) {
+        // 12 B N H Q bytes of per-row data
         const int64_t need = mul_or_neg(
-            mul_or_neg(mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H),
-                                  shape->Q),
-                       shape->K),
-            4);
+            mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H), shape->Q), 12);
         if (need < 0) return TRIATTN_ERR_UNSUPPORTED;
-        if (workspace_bytes < static_cast<uint64_t>(need)) return TRIATTN_ERR_INVALID_ARG;
+        if (!workspace || workspace_bytes < static_cast<uint64_t>(need))
+            return TRIATTN_ERR_INVALID_ARG;
     }
     return TRIATTN_OK;
 }
@@ -353,9 +352,15 @@ triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const vo
     g.dk = dk;
     g.dv = dv;
     g.dbias = dbias;
-    g.dz = dbias ? workspace : nullptr;
-    const hipError_t err = triattn::launch_bwd(p, g, dtype, stream);
+    const hipError_t err = triattn::launch_bwd(p, g, dtype, workspace, stream);
     return err == hipSuccess ? TRIATTN_OK : TRIATTN_ERR_HIP;
+}
+
+size_t tri_attn_bwd_workspace_size(const tri_attn_shape* shape) {
+    if (!shape || shape->B < 0 || shape->N < 0 || shape->H < 0 || shape->Q < 0) return 0;
+    const int64_t need = mul_or_neg(
+        mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H), shape->Q), 12);
+    return need < 0 ? 0 : static_cast<size_t>(need);
 }
 
 triattn_status tri_attn_mask_to_kv_lengths(const uint8_t* mask, int64_t rows, int64_t K,

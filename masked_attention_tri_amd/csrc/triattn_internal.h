@@ -82,7 +82,6 @@ struct BwdParams {
     void* dk;
     void* dv;
     float* dbias;
-    float* dz;  // (B,N,H,Q,K) fp32 dz from dq_kernel for the dBias sum, or null
 };
 
 // Masked logits are carried as -inf inside the kernels: when a row has at
@@ -105,15 +104,28 @@ hipError_t launch_mfma_d32(const Params& p, int32_t dtype, bool exact, hipStream
 hipError_t launch_mfma_d64(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
 hipError_t launch_mfma_d128(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
 hipError_t launch_mfma_d256(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
-hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, hipStream_t stream);
+// The backward: per-row data in `ws` (12 B N H Q bytes), then dK / dV, dQ
+// and dBias.
+hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
+                      hipStream_t stream);
+// Calls the MFMA backward kernels (bf16 / fp16, D in {32, 64, 128}) serve,
+// and their instantiations per head dimension.
+bool bwd_mfma_supports(const Params& p, int32_t dtype);
+hipError_t launch_bwd_mfma_d32(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
+                               hipStream_t stream);
+hipError_t launch_bwd_mfma_d64(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
+                               hipStream_t stream);
+hipError_t launch_bwd_mfma_d128(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
+                               hipStream_t stream);
 // Host-only validation of tri_attn_bwd's arguments (the checks it returns
-// before launching anything).
+// before launching anything; the workspace's only with check_workspace).
 triattn_status bwd_validate(const tri_attn_shape* shape, int32_t dtype, const void* q,
                             const void* k, const void* v, const float* bias,
                             const tri_attn_mask* mask, float scale, const void* out,
                             const void* dout, const float* lse, const float* max, const void* dq,
                             const void* dk, const void* dv, const float* dbias,
-                            const float* workspace, size_t workspace_bytes);
+                            const float* workspace, size_t workspace_bytes,
+                            bool check_workspace = true);
 hipError_t launch_mask_to_kv_lengths(const uint8_t* mask, int64_t rows, int64_t K,
                                      int32_t* kv_lengths, int32_t* nonprefix_rows,
                                      hipStream_t stream);

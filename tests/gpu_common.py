@@ -31,6 +31,14 @@ def block_mask_of(case):
                                         mask_mod=b.mask_mod)
 
 
+def mask_descriptor(case):
+    """(TriAttnMask descriptor, objects it points into) of a device Case,
+    built by the package's own argument preparation."""
+    prep = mat._prepare(case.q, case.k, case.v, case.bias, case.mask, case.kv_lengths,
+                        block_mask_of(case))
+    return prep[5], prep
+
+
 def run_gpu(case, stream=None, scale="case"):
     """(O, lse, max) from the library, copied to the CPU."""
     c = case.to("cuda")

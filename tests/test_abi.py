@@ -266,17 +266,23 @@ def _bwd(shp, dbias=A, ws=None, ws_bytes=0):
 
 
 def test_bwd_workspace_validation():
-    """The dz workspace must hold 4 B N H Q K bytes and be 16-byte aligned;
-    a failing check launches nothing (these calls make no device call)."""
+    """The workspace must hold 12 B N H Q bytes (tri_attn_bwd_workspace_size)
+    and be 16-byte aligned, with or without a bias gradient; a failing check
+    launches nothing (these calls make no device call)."""
     shp = shape(B=1, N=2, H=2, Q=8, K=8, D=32)
-    need = 4 * 1 * 2 * 2 * 8 * 8
+    need = 12 * 1 * 2 * 2 * 8
+    assert nat.tri_attn_bwd_workspace_size(shp) == need
     assert _bwd(shp, ws=A, ws_bytes=need - 1) == nat.TRIATTN_ERR_INVALID_ARG
+    assert _bwd(shp, dbias=None, ws=A, ws_bytes=need - 1) == nat.TRIATTN_ERR_INVALID_ARG
+    assert _bwd(shp, ws=None, ws_bytes=need) == nat.TRIATTN_ERR_INVALID_ARG
     assert _bwd(shp, ws=A + 4, ws_bytes=need) == nat.TRIATTN_ERR_INVALID_ARG
     # no query row: nothing to do, whatever the workspace
-    assert _bwd(shape(Q=0), ws=A, ws_bytes=0) == nat.TRIATTN_OK
+    assert _bwd(shape(Q=0), ws=None, ws_bytes=0) == nat.TRIATTN_OK
     # int64 overflow of the workspace size
-    big = shape(B=1 << 20, N=1 << 20, H=1, Q=1 << 12, K=1 << 12, D=32)
+    big = shape(B=1 << 20, N=1 << 20, H=1 << 12, Q=1 << 12, K=8, D=32)
     assert _bwd(big, ws=A, ws_bytes=0) == nat.TRIATTN_ERR_UNSUPPORTED
+    assert nat.tri_attn_bwd_workspace_size(big) == 0
+    assert nat.tri_attn_bwd_workspace_size(shape(B=-1)) == 0
 
 
 def _varlen(**kw):
@@ -357,17 +363,19 @@ def test_fwd_bias_dtype_validation():
 
 
 def test_bwd_noalloc_rejects_problems_past_its_scratch():
-    """With a bias gradient the no-allocation backward holds dz for at most
-    TRIATTN_BWD_NOALLOC_MAX_PAIRS (query, key) pairs: a larger problem is
-    refused before any device call; argument errors come first."""
+    """The no-allocation backward holds the per-row data of at most
+    TRIATTN_BWD_NOALLOC_MAX_ROWS (b, n, h, q) rows: a larger problem is
+    refused before any device call, with or without a bias gradient;
+    argument errors come first."""
     lib = nat.load_library()
 
     def call(shp, dbias=A, scale=math.nan):
         return lib.tri_attn_bwd_noalloc(ctypes.byref(shp), nat.TRIATTN_BF16, A, A, A, A, None,
                                         ctypes.c_float(scale), A, A, A, A, A, A, A, dbias, None)
 
-    big = shape(B=1, N=64, H=4, Q=256, K=129, D=64)  # 64*4*256*129 > 8 Mi pairs
-    assert 64 * 4 * 256 * 129 > nat.TRIATTN_BWD_NOALLOC_MAX_PAIRS
+    big = shape(B=1, N=1025, H=4, Q=1024, K=8, D=64)
+    assert 1025 * 4 * 1024 > nat.TRIATTN_BWD_NOALLOC_MAX_ROWS
     assert call(big) == nat.TRIATTN_ERR_UNSUPPORTED
+    assert call(big, dbias=None) == nat.TRIATTN_ERR_UNSUPPORTED
     assert call(big, scale=math.inf) == nat.TRIATTN_ERR_INVALID_ARG
     assert call(shape(B=1, N=0, H=4, Q=256, K=129, D=64)) == nat.TRIATTN_OK  # no work

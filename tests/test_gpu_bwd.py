@@ -81,8 +81,21 @@ CASES = [
     # D = 32, K not a multiple of 4 (scalar dz and dBias paths), about half
     # the rows fully masked
     (1, 3, 2, 40, 130, 32, "f16", "dense", {"p_valid": 0.005}),
-    # non-causal block mask at D = 64 through the validity predicate
+    # non-causal block mask at D = 64 with 32-row blocks: the general kernels
     (1, 2, 2, 96, 96, 64, "bf16", "block", {"q_block": 32, "kv_block": 32}),
+    # MFMA kernels: causal block lists (partial diagonal blocks, unlisted and
+    # full blocks) with a bias
+    (1, 2, 2, 256, 256, 64, "bf16", "block", {"q_block": 128, "kv_block": 64, "mask_mod": "causal"}),
+    # D = 128, sparse lists: query blocks with no listed block (rows without a
+    # valid key), several kv blocks per 128-key workgroup
+    (1, 2, 2, 384, 200, 128, "f16", "block", {"q_block": 128, "kv_block": 32,
+                                              "block_density": 0.25}),
+    (1, 2, 2, 200, 160, 128, "bf16", "kv_lengths", {}),
+    (2, 3, 2, 100, 72, 32, "bf16", "dense", {}),
+    # scale that is not a power of two; K % 4 != 0 (per-lane bias loads)
+    (1, 2, 2, 96, 70, 64, "bf16", "none", {"scale": 0.3}),
+    # s = 0: z is the bias alone
+    (1, 3, 2, 64, 64, 64, "f16", "kv_lengths", {"scale": 0.0}),
 ]
 
 
@@ -177,47 +190,88 @@ def test_backward_headline_size_sampled():
         assert err <= bound, f"{name}: {err} > {bound}"
 
 
-def _both_routes(c, seed):
-    """dbias from the dz workspace and from the walk over n."""
-    g = torch.Generator().manual_seed(seed)
-    dout = torch.randn(c.q.shape, generator=g).to(c.q.dtype).cuda()
+def _run_bwd(c, dout, ws_fill):
+    """tri_attn_bwd through the C ABI with a workspace prefilled with ws_fill."""
+    import masked_attention_tri_amd._native as nat
+    from tests.gpu_common import mask_descriptor
+
     gc = c.to("cuda")
     bm = block_mask_of(gc)
     out, lse, mx = mat.triangle_attention(gc.q, gc.k, gc.v, gc.bias, mask=gc.mask,
                                           scale=gc.scale, return_aux=True,
                                           kv_lengths=gc.kv_lengths, block_mask=bm)
-    res = []
-    for ws in (True, False):
-        res.append(mat.triangle_attention_backward(
-            gc.q, gc.k, gc.v, gc.bias, out, dout, lse, mx, mask=gc.mask, scale=gc.scale,
-            kv_lengths=gc.kv_lengths, block_mask=bm, dbias_workspace=ws))
+    B, N, H, Q, K, D = c.shape
+    shape = nat.TriAttnShape(B, N, H, Q, K, D)
+    ws = torch.full(((mat.tri_attn_bwd_workspace_size(shape) + 3) // 4,), ws_fill,
+                    device="cuda", dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(gc.q), torch.empty_like(gc.k), torch.empty_like(gc.v)
+    db = torch.empty_like(gc.bias) if gc.bias is not None else None
+    desc, keep = mask_descriptor(gc)
+    s = float("nan") if gc.scale is None else float(gc.scale)
+    st = mat.tri_attn_bwd(shape, nat.DTYPE_CODES[gc.q.dtype], gc.q, gc.k, gc.v, gc.bias, desc, s,
+                          out.reshape(gc.q.shape), dout, lse, mx, dq, dk, dv, db, None,
+                          workspace=ws)
     torch.cuda.synchronize()
-    return res
+    assert st == mat.TRIATTN_OK, mat.tri_attn_status_str(st)
+    return dq, dk, dv, db
 
 
-@pytest.mark.parametrize("spec", [s for s in CASES if s[8].get("bias", True)],
+@pytest.mark.parametrize("spec", CASES[1:4] + CASES[-7:],
                          ids=[f"B{c[0]}N{c[1]}H{c[2]}Q{c[3]}K{c[4]}D{c[5]}-{c[6]}-{c[7]}"
-                              for c in CASES if c[8].get("bias", True)])
-def test_dbias_routes_agree_bitwise(spec):
-    """dbias summed from the stored dz (workspace) and recomputed by the walk
-    over n add the same fp32 values in the same order: equal bits, and the
-    other gradients do not depend on the route."""
+                              for c in CASES[1:4] + CASES[-7:]])
+def test_backward_independent_of_workspace_contents(spec):
+    """The workspace's contents on entry do not matter (every entry a later
+    pass reads is written by the first), and the backward is deterministic:
+    a NaN-filled and a zeroed workspace give the same bits."""
     B, N, H, Q, K, D, dt, kind, extra = spec
     c = wl.make_case(B, N, H, Q, K, D, dt, kind, seed=19, **extra)
-    say(f"dbias routes {c.name}")
-    (a, b) = _both_routes(c, seed=59)
+    say(f"workspace contents {c.name}")
+    g = torch.Generator().manual_seed(59)
+    dout = torch.randn(c.q.shape, generator=g).to(c.q.dtype).cuda()
+    a = _run_bwd(c, dout, float("nan"))
+    b = _run_bwd(c, dout, 0.0)
     for name, x, y in zip(("dq", "dk", "dv", "dbias"), a, b):
-        assert torch.equal(x, y), f"{c.name} {name}: routes differ"
+        if x is None:
+            continue
+        assert torch.equal(x, y), f"{c.name} {name}: depends on the workspace's contents"
 
 
-def test_dbias_routes_agree_headline_size():
-    """The same equality at the headline size (B1 N768 H4 Q=K=768 D64, bf16,
-    kv_lengths U{384..768}): every n contributes to each dbias element."""
-    c = wl.make_workload("bf16_lens_d64")
-    say(f"dbias routes {c.name}")
-    (a, b) = _both_routes(c, seed=61)
-    assert torch.equal(a[3], b[3]), "dbias routes differ"
-    assert float(a[3].abs().max()) > 0
+def test_block_causal_backward_config_shape():
+    """The causal BlockMask workload at full size (B2 N1 H8 Q=K=4096 D128,
+    128 x 128 blocks, bf16, no bias) through the MFMA backward: dQ of 24
+    rows of every (b, h) (both ends of several 128-row tiles) against the
+    oracle evaluated on those rows only, and dK, dV of two whole slices
+    (b, h) = (0, 0) and (1, 7) against the oracle run on those slices."""
+    c = wl.make_workload("bf16_causal_blocks_d128")
+    say(f"backward block causal {c.name}")
+    g = torch.Generator().manual_seed(71)
+    dout = torch.randn(c.q.shape, generator=g).to(c.q.dtype)
+    gc = c.to("cuda")
+    bm = block_mask_of(gc)
+    out, lse, mx = mat.triangle_attention(gc.q, gc.k, gc.v, None, return_aux=True,
+                                          block_mask=bm)
+    dq, dk, dv, _ = mat.triangle_attention_backward(gc.q, gc.k, gc.v, None, out, dout.cuda(),
+                                                    lse, mx, block_mask=bm)
+    torch.cuda.synchronize()
+    blk = hp.oracle_block(c)
+    qs = sorted({0, 1, 127, 128, 255, 1023, 1024, 2047, 2048, 2049, 3071, 3072, 4095}
+                | set(torch.randperm(4096, generator=g)[:11].tolist()))
+    ref = orc.oracle_bwd(c.q, c.k, c.v, None, dout=dout, block=blk, q_rows=qs)
+    got = dq.cpu().double().numpy()[:, :, :, qs]
+    want = ref[0][:, :, :, qs]
+    err = float(np.abs(got - want).max())
+    bound = 2e-2 * (1 + float(np.abs(want).max()))
+    say(f"block causal dq ({len(qs)} rows x 16 slices): err {err:.3g} bound {bound:.3g}")
+    assert err <= bound
+    for b, h in ((0, 0), (1, 7)):
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        r = orc.oracle_bwd(c.q[sl], c.k[sl], c.v[sl], None, dout=dout[sl], block=blk)
+        for name, t, want in (("dq", dq, r[0]), ("dk", dk, r[1]), ("dv", dv, r[2])):
+            got = t[sl].cpu().double().numpy()
+            err = float(np.abs(got - want).max())
+            bound = 2e-2 * (1 + float(np.abs(want).max()))
+            say(f"block causal ({b},{h}) {name}: err {err:.3g} bound {bound:.3g}")
+            assert err <= bound, f"({b},{h}) {name}: {err} > {bound}"
 
 
 def test_dbias_headline_size_against_oracle():

@@ -1,8 +1,8 @@
 """The no-allocation backward (tri_attn_bwd_noalloc) through the C ABI,
 against tri_attn_bwd given a caller-owned workspace: both run the same
 kernels on the same values, so every gradient must have the same bits.  Two
-calls in a row, the second smaller, check that the library's shared dz
-scratch carries nothing over from one call to the next."""
+calls in a row, the second smaller, check that the library's shared scratch
+(the per-row data) carries nothing over from one call to the next."""
 import math
 
 import pytest
@@ -41,7 +41,7 @@ def _backward(c, dout, noalloc):
     if noalloc:
         st = nat.tri_attn_bwd_noalloc(*args, None)
     else:
-        ws = torch.empty(B * N * H * Q * K, device="cuda")
+        ws = torch.empty((nat.tri_attn_bwd_workspace_size(shp) + 3) // 4, device="cuda")
         st = nat.tri_attn_bwd(*args, None, workspace=ws)
     torch.cuda.synchronize()
     assert st == mat.TRIATTN_OK, mat.tri_attn_status_str(st)
@@ -50,7 +50,7 @@ def _backward(c, dout, noalloc):
 
 @pytest.mark.parametrize("spec", [
     (1, 4, 2, 160, 160, 64, "bf16", "kv_lengths", {"len_range": (0, 160)}),
-    # the second call is smaller: dz of the first must not leak into it
+    # the second call is smaller: the first's row data must not leak into it
     (1, 2, 2, 96, 96, 32, "f16", "dense", {}),
 ])
 def test_noalloc_backward_equals_workspace_backward(spec):
