@@ -219,9 +219,9 @@ def bench_backward(args, case, g, key, shape, dtype, desc, scale, out, lse, mx, 
     dout = torch.randn(g.q.shape, generator=gen).to(g.q.dtype).to(g.q.device)
     dq, dk, dv = torch.empty_like(g.q), torch.empty_like(g.k), torch.empty_like(g.v)
     dbias = torch.empty_like(g.bias) if g.bias is not None else None
-    # the library's workspace (per-row data, 12 B N H Q bytes), allocated once
-    ws = torch.empty((mat.tri_attn_bwd_workspace_size(shape) + 3) // 4, device=g.q.device,
-                     dtype=torch.float32)
+    # the library's workspace (per-row data and dBias partial sums), allocated once
+    ws = torch.empty((mat.tri_attn_bwd_workspace_size(shape, dbias is not None) + 3) // 4,
+                     device=g.q.device, dtype=torch.float32)
 
     def step():
         st = mat.tri_attn_bwd(shape, dtype, g.q, g.k, g.v, g.bias, desc, scale, out, dout, lse,

@@ -340,8 +340,8 @@ def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
     q's dtype and dbias fp32 of shape (B,1,H,Q,K) (None when bias is None).
     out, lse and mx are the forward's (O, lse, max) for the same arguments
     (from return_aux=True).  Every step runs in the library's HIP kernels;
-    the library's workspace (12 bytes per (b, n, h, q) row) is allocated
-    here.
+    the library's workspace (12 bytes per (b, n, h, q) row, and with a bias
+    the planes of dBias partial sums it asks for) is allocated here.
     """
     four_d, q5, k5, v5, bias5, desc, keep = _prepare(q, k, v, bias, mask, kv_lengths,
                                                      block_mask)
@@ -361,7 +361,7 @@ def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
              if bias5 is not None else None)
     s = math.nan if scale is None else float(scale)
     shape = TriAttnShape(B, N, H, Q, K, D)
-    ws_bytes = tri_attn_bwd_workspace_size(shape)
+    ws_bytes = tri_attn_bwd_workspace_size(shape, dbias is not None)
     ws = torch.empty((ws_bytes + 3) // 4, device=q5.device, dtype=torch.float32) if ws_bytes else None
     st = tri_attn_bwd(shape, _native.DTYPE_CODES[q5.dtype], q5, k5, v5,
                       bias5, desc, s, o5, g5, lse5, mx5, dq, dk, dv, dbias, stream, workspace=ws)

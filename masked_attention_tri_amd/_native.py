@@ -126,7 +126,7 @@ def load_library(path: str = LIB_PATH):
     lib.tri_attn_bwd.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P, P, P, P,
                                   ctypes.c_size_t, P]
     lib.tri_attn_bwd_workspace_size.restype = ctypes.c_size_t
-    lib.tri_attn_bwd_workspace_size.argtypes = [shape_p]
+    lib.tri_attn_bwd_workspace_size.argtypes = [shape_p, I32]
     lib.tri_attn_bwd_noalloc.restype = I32
     lib.tri_attn_bwd_noalloc.argtypes = [shape_p, I32, P, P, P, P, mask_p, F32, P, P, P, P, P, P,
                                          P, P, P]
@@ -224,9 +224,9 @@ def tri_attn_mask_to_kv_lengths(mask, rows: int, K: int, kv_lengths, nonprefix_r
 def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: float, out, dout,
                  lse, mx, dq, dk, dv, dbias, stream, workspace=None) -> int:
     """Enqueue the backward pass on `stream` (as tri_attn_fwd); `workspace`
-    is a device tensor of at least tri_attn_bwd_workspace_size(shape) bytes
-    (None is passed as NULL, which the library refuses unless there is no
-    query row)."""
+    is a device tensor of at least 12*B*N*H*Q bytes, up to
+    tri_attn_bwd_workspace_size(shape, dbias is not None) (None is passed as
+    NULL, which the library refuses unless there is no query row)."""
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
@@ -239,9 +239,10 @@ def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: fl
         ctypes.c_void_p(handle)))
 
 
-def tri_attn_bwd_workspace_size(shape: TriAttnShape) -> int:
-    """Bytes of workspace tri_attn_bwd needs for `shape` (12*B*N*H*Q)."""
-    return int(load_library().tri_attn_bwd_workspace_size(ctypes.byref(shape)))
+def tri_attn_bwd_workspace_size(shape: TriAttnShape, with_dbias: bool = True) -> int:
+    """Bytes of workspace tri_attn_bwd uses at most for `shape` (12*B*N*H*Q,
+    plus the dBias split's partial sums when with_dbias)."""
+    return int(load_library().tri_attn_bwd_workspace_size(ctypes.byref(shape), int(bool(with_dbias))))
 
 
 def tri_attn_bwd_noalloc(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: float, out,

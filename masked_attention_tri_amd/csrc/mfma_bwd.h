@@ -23,9 +23,11 @@
 //   bwd_dkdv_kernel   one workgroup per (b, n, h, 128 keys); K and V rows in
 //                     registers; 32-row query tiles of Q, dO and the row data
 //                     by LDS DMA.
-//   bwd_dbias_kernel  one workgroup per (b, h, 64 queries, 64 keys), walking
-//                     n: the bias block stays in registers, Q, dO, K and V of
-//                     each n arrive by LDS DMA, dB accumulates in registers.
+//   bwd_dbias_kernel  one workgroup per (b, h, 128 queries (64 at D = 128),
+//                     64 keys, range of n), walking n: the bias block stays in
+//                     registers, Q, dO, K and V of each n arrive by LDS DMA,
+//                     dB accumulates in registers; the ranges' sums are added
+//                     in order by bwd_dbias_combine_kernel.
 //   bwd_dq_kernel     one workgroup per (b, n, h, 128 queries), the forward's
 //                     layout: Q and dO rows in registers, 32-key tiles of K, V
 //                     and the bias by LDS DMA.
@@ -933,45 +935,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
 }
 
 // ---- dBias ---------------------------------------------------------------
-// dB_qk = sum over n, in order, of dz_qk.  One workgroup of 4 waves per (b,
-// h, 64 query rows, 64 keys); wave w takes rows 32 (w % 2) .. + 31 and keys
-// 32 (w / 2) .. + 31 in the dQ kernel's layout (lane l: row 32 (w % 2) + l %
-// 32, 16 keys in registers), and keeps the 32 x 32 bias block (divided by s
-// when that is not exact) as the C operand and the sums in registers.  Per
-// n, the 64 rows of Q and dO, the 64 rows of K and V and the row data arrive
-// by LDS DMA one n ahead (two buffers):
-//   z^T = K Q^T + C,  dP^T = V dO^T   A = K, V rows, B = Q, dO rows
-// P = exp2(z c - lse log2 e), dz = P (dP - Delta), dB += dz.  n whose length
-// leaves no key of the workgroup valid are skipped; the ragged tile and the
-// dense mask select per element; rows with no valid key contribute nothing.
+// dB_qk = sum over n, in order, of dz_qk.  One workgroup of QW x KW waves per
+// (b, h, 32 QW query rows, 32 KW keys, range of n); wave w takes rows
+// 32 (w % QW) .. + 31 and keys 32 (w / QW) .. + 31 in the dQ kernel's layout
+// (lane l: row 32 (w % QW) + l % 32, 16 keys in registers), and keeps its
+// 32 x 32 bias block (divided by s) as the C operand and its sums in
+// registers.  Per n, the workgroup's rows of Q and dO, its keys of K and V and
+// the row data arrive by LDS DMA, `slots - 1` n ahead in a ring:
+//   z^T = K Q^T + C,  dP^T = V dO^T - Delta   A = K, V rows, B = Q, dO rows
+// (-Delta is the initial accumulator of dP^T), P = exp2(z c - lse log2 e),
+// dB += P dP^T.  n whose length leaves no key of the workgroup valid are
+// skipped; the ragged tile and the dense mask select per element; rows with
+// no valid key contribute nothing.  With more than one range of n (splits),
+// each range's sums go to its own plane of the workspace and
+// bwd_dbias_combine_kernel adds the planes in range order.
+template <int D>
+struct DbGeo {
+    static constexpr int QW = D <= 64 ? 4 : 2;  // waves along the query rows
+    static constexpr int KW = 2;                // waves along the keys
+    static constexpr int waves = QW * KW;
+    static constexpr int slots = D <= 64 ? 3 : 2;
+    static constexpr int rowsQ = 32 * QW, rowsK = 32 * KW;
+    static constexpr int tileBytes = BGeo<D>::tileBytes;
+    // one n: QW tiles of Q, QW of dO, KW of K, KW of V
+    static constexpr int slotBytes = (2 * QW + 2 * KW) * tileBytes;
+    static constexpr int dmaPerWave = slotBytes / 1024 / waves;
+    static_assert(dmaPerWave * waves * 1024 == slotBytes, "DMAs split evenly over the waves");
+    static constexpr int infoBytes = rowsQ * 8;  // row data: 128 bytes per wave
+    static_assert(infoBytes == 128 * waves, "one 8-lane DMA of row data per wave");
+};
+
 template <typename T, int D, int KIND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_dbias_kernel(
-    Params p, BwdParams g, const float* rows) {
+__global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params p, BwdParams g,
+                                                                        const float* rows,
+                                                                        float* part, int splits) {
     using M = Mma<T>;
     using v8 = typename M::v8;
     using Ge = BGeo<D>;
+    using G = DbGeo<D>;
     constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
     constexpr bool kLens = KIND == TRIATTN_MASK_KV_LENGTHS;
-    constexpr int kSlot = 8 * Ge::tileBytes;  // Q, dO, K, V: two 32-row tiles each
-    constexpr int kDmaPerWave = 8 * Ge::tileDma / 4;
-    __shared__ __attribute__((aligned(1024))) char t_lds0[kSlot];
-    __shared__ __attribute__((aligned(1024))) char t_lds1[kSlot];
-    __shared__ __attribute__((aligned(1024))) char r_lds0[512];
-    __shared__ __attribute__((aligned(1024))) char r_lds1[512];
+    constexpr int R = G::slots;
+    constexpr int kPer = G::dmaPerWave + 1;  // DMAs per wave and n (with the row data)
+    __shared__ __attribute__((aligned(1024))) char t_lds[R][G::slotBytes];
+    __shared__ __attribute__((aligned(1024))) char r_lds[R][G::infoBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
-    const int qg = wave & 1, kg = wave >> 1;
+    const int qg = wave % G::QW, kg = wave / G::QW;
 
-    const int64_t n_qt = (p.Q + 63) / 64, n_kt = (p.K + 63) / 64;
+    // ---- workgroup -> (b, h, range of n, query tile, key tile), XCD-contiguous
+    const int64_t n_qt = (p.Q + G::rowsQ - 1) / G::rowsQ, n_kt = (p.K + G::rowsK - 1) / G::rowsK;
     const int64_t lid = xcd_order(blockIdx.x, gridDim.x);
     const int64_t kt = lid % n_kt;
     const int64_t qt = (lid / n_kt) % n_qt;
-    const int64_t h = (lid / (n_kt * n_qt)) % p.H;
-    const int64_t b = lid / (n_kt * n_qt * p.H);
+    const int64_t sp = (lid / (n_kt * n_qt)) % splits;
+    const int64_t h = (lid / (n_kt * n_qt * splits)) % p.H;
+    const int64_t b = lid / (n_kt * n_qt * splits * p.H);
     const int K = static_cast<int>(p.K), Q = static_cast<int>(p.Q), N = static_cast<int>(p.N);
-    const int q0 = static_cast<int>(qt) * 64, k0 = static_cast<int>(kt) * 64;
+    const int q0 = static_cast<int>(qt) * G::rowsQ, k0 = static_cast<int>(kt) * G::rowsK;
+    const int n_begin = static_cast<int>(sp * N / splits), n_end = static_cast<int>((sp + 1) * N / splits);
     const int qrow = q0 + 32 * qg + col;  // this lane's query
     const int kw = k0 + 32 * kg;          // this wave's first key
 
@@ -992,74 +1016,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
             for (int e = 0; e < 4; ++e) cb[4 * gg + e] = bload32(b_rsrc, base + 4u * (8 * gg + e)) * inv_s;
     }
 
-    // n visited: every n, or those whose length leaves a key of the workgroup
+    // n visited: every n of the range, or those whose length leaves a key of
+    // the workgroup valid
     auto key_lim = [&](int m) -> int {
         if (!kLens || !p.kv_lengths) return K;
         const int64_t len = p.kv_lengths[b * p.N + m];
         return len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
     };
-    auto next_n = [&](int m0) -> int {  // first visited n >= m0, or -1
+    auto next_n = [&](int m0) -> int {  // first visited n >= m0 of the range, or -1
+        if (m0 < 0) return -1;
         if constexpr (!kLens) {
-            return m0 < N ? m0 : -1;
+            return m0 < n_end ? m0 : -1;
         } else {
-            for (int base = m0; base < N; base += 64) {
+            for (int base = m0; base < n_end; base += 64) {
                 const int m = base + lane;
-                const uint64_t bits = __ballot(m < N && k0 < key_lim(m));
+                const uint64_t bits = __ballot(m < n_end && k0 < key_lim(m));
                 if (bits) return base + static_cast<int>(__builtin_ctzll(bits));
             }
             return -1;
         }
     };
 
-    // DMA of one n: instruction I = wave + 4 j; tile I / tileDma of {Q rows
-    // q0.., Q rows q0+32.., dO.., dO.., K rows k0.., K.., V.., V..}, piece
-    // I % tileDma
-    uint32_t src[kDmaPerWave];
+    // DMA of one n: instruction I = wave + waves j; tile I / tileDma of the
+    // slot (Q tiles, dO tiles, K tiles, V tiles), piece I % tileDma
+    uint32_t src[G::dmaPerWave];
 #pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) src[j] = Ge::dma_src((wave + 4 * j) % Ge::tileDma, lane);
-    auto tbuf = [&](int x) { return (lds_char*)(x == 0 ? t_lds0 : t_lds1); };
-    auto rbuf = [&](int x) { return (lds_char*)(x == 0 ? r_lds0 : r_lds1); };
+    for (int j = 0; j < G::dmaPerWave; ++j) src[j] = Ge::dma_src((wave + G::waves * j) % Ge::tileDma, lane);
+    const uint32_t qbytes = static_cast<uint32_t>(p.Q * D * sizeof(T));
+    const uint32_t kbytes = static_cast<uint32_t>(p.K * D * sizeof(T));
     auto dma_n = [&](int m, int x) {
         const int64_t bnh = (b * p.N + (m >= 0 ? m : 0)) * p.H + h;
-        const uint32_t qbytes = static_cast<uint32_t>(p.Q * D * sizeof(T));
-        const uint32_t kbytes = static_cast<uint32_t>(p.K * D * sizeof(T));
         const u32x4 dq = make_desc(static_cast<const T*>(p.q) + bnh * p.Q * D, qbytes);
         const u32x4 dg = make_desc(static_cast<const T*>(g.dout) + bnh * p.Q * D, qbytes);
         const u32x4 dk = make_desc(static_cast<const T*>(p.k) + bnh * p.K * D, kbytes);
         const u32x4 dv = make_desc(static_cast<const T*>(p.v) + bnh * p.K * D, kbytes);
         const u32x4 dr = make_desc(rows + 2 * bnh * p.Q, static_cast<uint32_t>(p.Q * 8));
-        const uint32_t qoff = m >= 0 ? static_cast<uint32_t>(q0) * Ge::rowBytes : kNoTile;
-        const uint32_t koff = m >= 0 ? static_cast<uint32_t>(k0) * Ge::rowBytes : kNoTile;
 #pragma unroll
-        for (int j = 0; j < kDmaPerWave; ++j) {
-            const int I = wave + 4 * j;
-            const int tile = I / Ge::tileDma;  // 0, 1: Q; 2, 3: dO; 4, 5: K; 6, 7: V
-            const uint32_t sub = static_cast<uint32_t>((tile & 1) * Ge::tileBytes);
-            lds_char* dst = tbuf(x) + 1024 * I;
-            const uint32_t o = src[j] + sub;
-            if (tile < 2)
-                dma16(dq, dst, o + qoff);
-            else if (tile < 4)
-                dma16(dg, dst, o + qoff);
-            else if (tile < 6)
-                dma16(dk, dst, o + koff);
-            else
-                dma16(dv, dst, o + koff);
+        for (int j = 0; j < G::dmaPerWave; ++j) {
+            const int I = wave + G::waves * j;
+            const int tile = I / Ge::tileDma;
+            lds_char* dst = (lds_char*)t_lds[x] + 1024 * I;
+            if (tile < G::QW) {
+                const uint32_t o = static_cast<uint32_t>(q0 + 32 * tile) * Ge::rowBytes + src[j];
+                dma16(dq, dst, m >= 0 ? o : kNoTile);
+            } else if (tile < 2 * G::QW) {
+                const uint32_t o = static_cast<uint32_t>(q0 + 32 * (tile - G::QW)) * Ge::rowBytes + src[j];
+                dma16(dg, dst, m >= 0 ? o : kNoTile);
+            } else if (tile < 2 * G::QW + G::KW) {
+                const uint32_t o = static_cast<uint32_t>(k0 + 32 * (tile - 2 * G::QW)) * Ge::rowBytes + src[j];
+                dma16(dk, dst, m >= 0 ? o : kNoTile);
+            } else {
+                const uint32_t o = static_cast<uint32_t>(k0 + 32 * (tile - 2 * G::QW - G::KW)) * Ge::rowBytes + src[j];
+                dma16(dv, dst, m >= 0 ? o : kNoTile);
+            }
         }
-        // row data of rows q0 .. q0 + 63: 8 lanes (128 bytes) per wave
+        // row data of rows q0 + 16 w .. + 15 (8 lanes of 16 bytes)
         const uint32_t roff = m >= 0 ? static_cast<uint32_t>(q0 * 8 + 128 * wave + 16 * lane) : kNoTile;
-        if (lane < 8) dma16(dr, rbuf(x) + 128 * wave, roff);
+        if (lane < 8) dma16(dr, (lds_char*)r_lds[x] + 128 * wave, roff);
     };
 
     const int rrd = Ge::row_base(col, half);
-    // this wave's tiles within a slot
-    const int q_tile = qg * Ge::tileBytes, g_tile = (2 + qg) * Ge::tileBytes;
-    const int k_tile = (4 + kg) * Ge::tileBytes, v_tile = (6 + kg) * Ge::tileBytes;
+    const int q_tile = qg * Ge::tileBytes, g_tile = (G::QW + qg) * Ge::tileBytes;
+    const int k_tile = (2 * G::QW + kg) * Ge::tileBytes, v_tile = (2 * G::QW + G::KW + kg) * Ge::tileBytes;
 
     f32x16 acc{};
     auto compute = [&](int m, int x) {
-        const lds_char* t = tbuf(x);
-        f32x16 z = cb, dp{};
+        const lds_char* t = (const lds_char*)t_lds[x];
+        const f32x4 ri = __builtin_bit_cast(
+            f32x4, *reinterpret_cast<const lds_u32x4*>((const lds_char*)r_lds[x] + (32 * qg + (col & ~1)) * 8));
+        const float delta = (col & 1) ? ri[2] : ri[0];
+        float nl2 = (col & 1) ? ri[3] : ri[1];
+        nl2 = nl2 != nl2 ? -INFINITY : nl2;  // no valid key: no contribution
+        f32x16 z = cb, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = -delta;
         if (!zero_s) {
 #pragma unroll
             for (int st = 0; st < D / 16; ++st)
@@ -1068,11 +1098,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
 #pragma unroll
         for (int st = 0; st < D / 16; ++st)
             dp = M::run(row_operand<v8>(t + v_tile, rrd, st), row_operand<v8>(t + g_tile, rrd, st), dp);
-        const f32x4 ri = __builtin_bit_cast(
-            f32x4, *reinterpret_cast<const lds_u32x4*>(rbuf(x) + (32 * qg + (col & ~1)) * 8));
-        const float delta = (col & 1) ? ri[2] : ri[0];
-        float nl2 = (col & 1) ? ri[3] : ri[1];
-        nl2 = nl2 != nl2 ? -INFINITY : nl2;  // no valid key: no contribution
         // keys valid for this n (the ragged tile of a length, the dense mask)
         const int lim = key_lim(m);
         uint32_t w = lim - kw >= 32 ? ~0u : lim - kw <= 0 ? 0u : (1u << (lim - kw)) - 1u;
@@ -1091,34 +1116,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
             }
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(fmaf(z[r], c_exp, nl2));
-            acc[r] += pr * (dp[r] - delta);
-        }
+        for (int r = 0; r < 16; ++r) acc[r] = fmaf(__builtin_amdgcn_exp2f(fmaf(z[r], c_exp, nl2)), dp[r], acc[r]);
     };
 
-    int cur = next_n(0);
-    if (cur >= 0) {
-        dma_n(cur, 0);
+    // ring position j holds n_j in slot j % R, loaded R - 1 positions ahead
+    int ns[R];
+    ns[0] = next_n(n_begin);
+#pragma unroll
+    for (int i = 1; i < R; ++i) ns[i] = next_n(ns[i - 1] >= 0 ? ns[i - 1] + 1 : -1);
+    if (ns[0] >= 0) {
+#pragma unroll
+        for (int i = 0; i < R - 1; ++i) dma_n(ns[i], i);
         int x = 0;
-        while (cur >= 0) {
-            const int nxt = next_n(cur + 1);
-            wait_vmem();
-            __syncthreads();  // slot x landed for every wave; slot x ^ 1 is free
-            dma_n(nxt, x ^ 1);
-            compute(cur, x);
-            cur = nxt;
-            x ^= 1;
+        while (ns[0] >= 0) {
+            // every DMA but the last R - 2 positions' has landed
+            __builtin_amdgcn_s_waitcnt(kVmcntWait<kPer * (R - 2)>());
+            __syncthreads();  // slot x landed for every wave; slot x - 1 is free
+            dma_n(ns[R - 1], (x + R - 1) % R);
+            compute(ns[0], x);
+#pragma unroll
+            for (int i = 0; i < R - 1; ++i) ns[i] = ns[i + 1];
+            ns[R - 1] = next_n(ns[R - 2] >= 0 ? ns[R - 2] + 1 : -1);
+            x = (x + 1) % R;
         }
         wait_vmem();
     }
 
     if (qrow >= Q) return;
-    float* dbr = g.dbias + ((b * p.H + h) * p.Q + qrow) * p.K;
+    float* dst = (splits > 1 ? part + sp * p.B * p.H * p.Q * p.K : g.dbias) + ((b * p.H + h) * p.Q + qrow) * p.K;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int kk = kw + 8 * (r / 4) + 4 * half + (r % 4);
-        if (kk < K) dbr[kk] = acc[r];
+        if (kk < K) dst[kk] = acc[r];
+    }
+}
+
+// dBias = the sum of the splits' planes, in split order.
+__global__ __launch_bounds__(256) void bwd_dbias_combine_kernel(float* dbias, const float* part,
+                                                                int64_t count, int splits) {
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < count; i += static_cast<int64_t>(gridDim.x) * 256) {
+        float s = part[i];
+        for (int j = 1; j < splits; ++j) s += part[j * count + i];
+        dbias[i] = s;
     }
 }
 
@@ -1144,9 +1183,10 @@ hipError_t launch_bwd_bias(const Params& p, const BwdParams& g, bool exact, floa
 
 template <typename T, int D, int KIND>
 hipError_t launch_bwd_kind(const Params& p, const BwdParams& g, bool exact, float* ws,
-                           hipStream_t stream) {
+                           size_t ws_bytes, hipStream_t stream) {
+    const int64_t n_rows = p.B * p.N * p.H * p.Q;
     float* rows = ws;
-    uint32_t* tdead = reinterpret_cast<uint32_t*>(ws + 2 * p.B * p.N * p.H * p.Q);
+    uint32_t* tdead = reinterpret_cast<uint32_t*>(ws + 2 * n_rows);
     const int64_t tiles = p.B * p.N * p.H * ((p.Q + 31) / 32);
     const unsigned gr = static_cast<unsigned>(tiles < (1 << 20) ? tiles : (1 << 20));
     hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3(gr), dim3(4 * D), 0, stream, p, g, rows, tdead);
@@ -1160,9 +1200,26 @@ hipError_t launch_bwd_kind(const Params& p, const BwdParams& g, bool exact, floa
     if (e != hipSuccess) return e;
     if constexpr (KIND != TRIATTN_MASK_BLOCK) {
         if (g.dbias && p.bias) {
-            const int64_t gb = p.B * p.H * ((p.Q + 63) / 64) * ((p.K + 63) / 64);
+            using G = DbGeo<D>;
+            // splits beyond the first need a plane of partial sums each, after
+            // the row data (12 bytes per row)
+            const int64_t plane = p.B * p.H * p.Q * p.K;
+            const size_t used = static_cast<size_t>(12 * n_rows);
+            const size_t room = ws_bytes > used ? ws_bytes - used : 0;
+            int splits = dbias_splits(p.B, p.N, p.H, p.Q, p.K, D);
+            while (splits > 1 && room < static_cast<size_t>(4 * splits * plane)) --splits;
+            float* part = ws + 3 * n_rows;
+            const int64_t gb = p.B * p.H * ((p.Q + G::rowsQ - 1) / G::rowsQ) *
+                               ((p.K + G::rowsK - 1) / G::rowsK) * splits;
             if (gb > 0x7fffffff) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL((bwd_dbias_kernel<T, D, KIND>), dim3(static_cast<unsigned>(gb)), dim3(256), 0, stream, p, g, rows);
+            hipLaunchKernelGGL((bwd_dbias_kernel<T, D, KIND>), dim3(static_cast<unsigned>(gb)),
+                               dim3(64 * G::waves), 0, stream, p, g, rows, part, splits);
+            if (splits > 1) {
+                const int64_t want = (plane + 255) / 256;
+                const unsigned gc = static_cast<unsigned>(want < 8192 ? want : 8192);
+                hipLaunchKernelGGL(bwd_dbias_combine_kernel, dim3(gc), dim3(256), 0, stream,
+                                   g.dbias, part, plane, splits);
+            }
         }
     }
     return hipGetLastError();
@@ -1170,15 +1227,15 @@ hipError_t launch_bwd_kind(const Params& p, const BwdParams& g, bool exact, floa
 
 template <typename T, int D>
 hipError_t launch_bwd_d(const Params& p, const BwdParams& g, bool exact, float* ws,
-                        hipStream_t stream) {
+                        size_t ws_bytes, hipStream_t stream) {
     switch (p.mask_kind) {
     case TRIATTN_MASK_NONE:
     case TRIATTN_MASK_KV_LENGTHS:
-        return launch_bwd_kind<T, D, TRIATTN_MASK_KV_LENGTHS>(p, g, exact, ws, stream);
+        return launch_bwd_kind<T, D, TRIATTN_MASK_KV_LENGTHS>(p, g, exact, ws, ws_bytes, stream);
     case TRIATTN_MASK_DENSE:
-        return launch_bwd_kind<T, D, TRIATTN_MASK_DENSE>(p, g, exact, ws, stream);
+        return launch_bwd_kind<T, D, TRIATTN_MASK_DENSE>(p, g, exact, ws, ws_bytes, stream);
     case TRIATTN_MASK_BLOCK:
-        return launch_bwd_kind<T, D, TRIATTN_MASK_BLOCK>(p, g, exact, ws, stream);
+        return launch_bwd_kind<T, D, TRIATTN_MASK_BLOCK>(p, g, exact, ws, ws_bytes, stream);
     }
     return hipErrorInvalidValue;
 }

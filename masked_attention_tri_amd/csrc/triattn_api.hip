@@ -216,7 +216,7 @@ triattn_status bwd_validate(const tri_attn_shape* shape, int32_t dtype, const vo
         !aligned(dbias, 4) || !aligned(workspace, 16))
         return TRIATTN_ERR_INVALID_ARG;
     if (!empty && check_workspace) {
-        // 12 B N H Q bytes of per-row data
+        // 12 B N H Q bytes of per-row data (more only speeds dBias up)
         const int64_t need = mul_or_neg(
             mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H), shape->Q), 12);
         if (need < 0) return TRIATTN_ERR_UNSUPPORTED;
@@ -352,15 +352,28 @@ triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const vo
     g.dk = dk;
     g.dv = dv;
     g.dbias = dbias;
-    const hipError_t err = triattn::launch_bwd(p, g, dtype, workspace, stream);
+    const hipError_t err = triattn::launch_bwd(p, g, dtype, workspace, workspace_bytes, stream);
     return err == hipSuccess ? TRIATTN_OK : TRIATTN_ERR_HIP;
 }
 
-size_t tri_attn_bwd_workspace_size(const tri_attn_shape* shape) {
-    if (!shape || shape->B < 0 || shape->N < 0 || shape->H < 0 || shape->Q < 0) return 0;
-    const int64_t need = mul_or_neg(
+size_t tri_attn_bwd_workspace_size(const tri_attn_shape* shape, int32_t with_dbias) {
+    if (!shape || shape->B < 0 || shape->N < 0 || shape->H < 0 || shape->Q < 0 || shape->K < 0)
+        return 0;
+    int64_t need = mul_or_neg(
         mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H), shape->Q), 12);
-    return need < 0 ? 0 : static_cast<size_t>(need);
+    if (need < 0) return 0;
+    if (with_dbias) {
+        const int s = triattn::dbias_splits(shape->B, shape->N, shape->H, shape->Q, shape->K,
+                                            shape->D);
+        if (s > 1) {
+            const int64_t planes = mul_or_neg(
+                mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->H), shape->Q), shape->K),
+                4 * s);
+            if (planes < 0 || need > INT64_MAX - planes) return 0;
+            need += planes;
+        }
+    }
+    return static_cast<size_t>(need);
 }
 
 triattn_status tri_attn_mask_to_kv_lengths(const uint8_t* mask, int64_t rows, int64_t K,

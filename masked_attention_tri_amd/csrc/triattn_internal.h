@@ -94,6 +94,30 @@ constexpr float kMaskedLogit = -1.0e9f;
 // one visited bit and one full bit per block in LDS.
 constexpr int64_t kMaxKvBlocks = 8192;
 
+// Ranges of n the MFMA dBias kernel splits its sum into for a shape: its
+// workgroups cover (32 QW) x 64 (query, key) tiles (QW = 4 for D <= 64, else
+// 2) and there are 256 CUs; the split that fills whole rounds of
+// workgroups best (ties: fewer splits), at most 8 and at least 16 n each.
+// Each split beyond the first needs a B H Q K fp32 plane of workspace.
+inline int dbias_splits(int64_t B, int64_t N, int64_t H, int64_t Q, int64_t K, int64_t D) {
+    if (D != 32 && D != 64 && D != 128) return 1;
+    const int64_t rows_q = D <= 64 ? 128 : 64;
+    const int64_t tiles = B * H * ((Q + rows_q - 1) / rows_q) * ((K + 63) / 64);
+    const int64_t slots = D == 32 ? 512 : 256;  // resident workgroups
+    int best = 1;
+    double best_eff = 0.0;
+    for (int s = 1; s <= 8 && (s == 1 || N / s >= 16); ++s) {
+        const double wg = static_cast<double>(tiles * s);
+        const double rounds = static_cast<double>((tiles * s + slots - 1) / slots);
+        const double eff = wg / (rounds * static_cast<double>(slots));
+        if (eff > best_eff + 1e-9) {
+            best_eff = eff;
+            best = s;
+        }
+    }
+    return best;
+}
+
 // Launchers (enqueue only; return the launch error, if any).
 hipError_t launch_generic(const Params& p, int32_t dtype, hipStream_t stream);
 hipError_t launch_mfma(const Params& p, int32_t dtype, hipStream_t stream);
@@ -104,19 +128,19 @@ hipError_t launch_mfma_d32(const Params& p, int32_t dtype, bool exact, hipStream
 hipError_t launch_mfma_d64(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
 hipError_t launch_mfma_d128(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
 hipError_t launch_mfma_d256(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
-// The backward: per-row data in `ws` (12 B N H Q bytes), then dK / dV, dQ
-// and dBias.
+// The backward: per-row data in `ws` (12 B N H Q bytes; the rest, if any,
+// holds dBias partial sums), then dK / dV, dQ and dBias.
 hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
-                      hipStream_t stream);
+                      size_t ws_bytes, hipStream_t stream);
 // Calls the MFMA backward kernels (bf16 / fp16, D in {32, 64, 128}) serve,
 // and their instantiations per head dimension.
 bool bwd_mfma_supports(const Params& p, int32_t dtype);
 hipError_t launch_bwd_mfma_d32(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
-                               hipStream_t stream);
+                               size_t ws_bytes, hipStream_t stream);
 hipError_t launch_bwd_mfma_d64(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
-                               hipStream_t stream);
+                               size_t ws_bytes, hipStream_t stream);
 hipError_t launch_bwd_mfma_d128(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
-                               hipStream_t stream);
+                               size_t ws_bytes, hipStream_t stream);
 // Host-only validation of tri_attn_bwd's arguments (the checks it returns
 // before launching anything; the workspace's only with check_workspace).
 triattn_status bwd_validate(const tri_attn_shape* shape, int32_t dtype, const void* q,

@@ -283,6 +283,12 @@ def test_bwd_workspace_validation():
     assert _bwd(big, ws=A, ws_bytes=0) == nat.TRIATTN_ERR_UNSUPPORTED
     assert nat.tri_attn_bwd_workspace_size(big) == 0
     assert nat.tri_attn_bwd_workspace_size(shape(B=-1)) == 0
+    # with a bias gradient, whole B H Q K fp32 planes of partial sums on top
+    head = shape(B=1, N=768, H=4, Q=768, K=768, D=64)
+    rows = 12 * 768 * 4 * 768
+    assert nat.tri_attn_bwd_workspace_size(head, False) == rows
+    extra = nat.tri_attn_bwd_workspace_size(head, True) - rows
+    assert extra > 0 and extra % (4 * 4 * 768 * 768) == 0
 
 
 def _varlen(**kw):

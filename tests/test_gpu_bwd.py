@@ -202,7 +202,7 @@ def _run_bwd(c, dout, ws_fill):
                                           kv_lengths=gc.kv_lengths, block_mask=bm)
     B, N, H, Q, K, D = c.shape
     shape = nat.TriAttnShape(B, N, H, Q, K, D)
-    ws = torch.full(((mat.tri_attn_bwd_workspace_size(shape) + 3) // 4,), ws_fill,
+    ws = torch.full(((mat.tri_attn_bwd_workspace_size(shape, True) + 3) // 4,), ws_fill,
                     device="cuda", dtype=torch.float32)
     dq, dk, dv = torch.empty_like(gc.q), torch.empty_like(gc.k), torch.empty_like(gc.v)
     db = torch.empty_like(gc.bias) if gc.bias is not None else None
@@ -234,6 +234,45 @@ def test_backward_independent_of_workspace_contents(spec):
         if x is None:
             continue
         assert torch.equal(x, y), f"{c.name} {name}: depends on the workspace's contents"
+
+
+def test_dbias_split_matches_unsplit_headline():
+    """At the headline size dBias sums over 768 n in ranges added in order
+    (the workspace holds one plane of partial sums per extra range); with
+    only the minimal workspace (the row data) the sum runs in one range.
+    dq, dk and dv do not depend on it (same bits); dbias agrees to fp32
+    rounding."""
+    import masked_attention_tri_amd._native as nat
+
+    c = wl.make_workload("bf16_lens_d64")
+    say(f"dbias split {c.name}")
+    B, N, H, Q, K, D = c.shape
+    shape = nat.TriAttnShape(B, N, H, Q, K, D)
+    full = mat.tri_attn_bwd_workspace_size(shape, True)
+    least = mat.tri_attn_bwd_workspace_size(shape, False)
+    assert full > least
+    g = torch.Generator().manual_seed(73)
+    dout = torch.randn(c.q.shape, generator=g).to(c.q.dtype).cuda()
+    gc = c.to("cuda")
+    out, lse, mx = mat.triangle_attention(gc.q, gc.k, gc.v, gc.bias, scale=gc.scale,
+                                          return_aux=True, kv_lengths=gc.kv_lengths)
+    desc, keep = __import__("tests.gpu_common", fromlist=["mask_descriptor"]).mask_descriptor(gc)
+    res = []
+    for size in (full, least):
+        ws = torch.empty((size + 3) // 4, device="cuda")
+        grads = [torch.empty_like(gc.q), torch.empty_like(gc.k), torch.empty_like(gc.v),
+                 torch.empty_like(gc.bias)]
+        st = mat.tri_attn_bwd(shape, nat.DTYPE_CODES[gc.q.dtype], gc.q, gc.k, gc.v, gc.bias, desc,
+                              float(gc.scale), out, dout, lse, mx, *grads, None, workspace=ws)
+        torch.cuda.synchronize()
+        assert st == mat.TRIATTN_OK
+        res.append(grads)
+    for name, a, b in zip(("dq", "dk", "dv"), res[0][:3], res[1][:3]):
+        assert torch.equal(a, b), name
+    d = (res[0][3] - res[1][3]).abs().max().item()
+    ref = res[1][3].abs().max().item()
+    say(f"dbias split vs one range: max diff {d:.3g}, max |dbias| {ref:.3g}")
+    assert d <= 1e-5 * ref
 
 
 def test_block_causal_backward_config_shape():

@@ -213,7 +213,7 @@ def test_graph_capture_replays_match_eager():
         torch.empty(B, N, H, Q, device="cuda")
     dq, dk, dv = torch.empty_like(c.q), torch.empty_like(c.k), torch.empty_like(c.v)
     db = torch.empty_like(c.bias)
-    ws = torch.empty((mat.tri_attn_bwd_workspace_size(shape) + 3) // 4, device="cuda")
+    ws = torch.empty((mat.tri_attn_bwd_workspace_size(shape, True) + 3) // 4, device="cuda")
 
     def run(stream):
         assert mat.tri_attn_fwd(shape, dt, c.q, c.k, c.v, c.bias, desc, math.nan, out, lse, mx,

@@ -41,7 +41,7 @@ def _backward(c, dout, noalloc):
     if noalloc:
         st = nat.tri_attn_bwd_noalloc(*args, None)
     else:
-        ws = torch.empty((nat.tri_attn_bwd_workspace_size(shp) + 3) // 4, device="cuda")
+        ws = torch.empty((nat.tri_attn_bwd_workspace_size(shp, True) + 3) // 4, device="cuda")
         st = nat.tri_attn_bwd(*args, None, workspace=ws)
     torch.cuda.synchronize()
     assert st == mat.TRIATTN_OK, mat.tri_attn_status_str(st)
