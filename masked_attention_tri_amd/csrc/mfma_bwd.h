@@ -979,6 +979,12 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
     constexpr int kPer = G::dmaPerWave + 1;  // DMAs per wave and n (with the row data)
     __shared__ __attribute__((aligned(1024))) char t_lds[R][G::slotBytes];
     __shared__ __attribute__((aligned(1024))) char r_lds[R][G::infoBytes];
+    // Bit i of valid_w[m - c0]: key k0 + i valid for n = m, for a chunk of n
+    // starting at c0.  Built before the ring starts, so that the loop issues
+    // no memory load besides the DMAs (a wait for such a load would also wait
+    // for the DMAs issued before it).
+    constexpr int kChunkN = 512;
+    __shared__ uint64_t valid_w[kChunkN];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1016,21 +1022,37 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
             for (int e = 0; e < 4; ++e) cb[4 * gg + e] = bload32(b_rsrc, base + 4u * (8 * gg + e)) * inv_s;
     }
 
-    // n visited: every n of the range, or those whose length leaves a key of
-    // the workgroup valid
-    auto key_lim = [&](int m) -> int {
-        if (!kLens || !p.kv_lengths) return K;
-        const int64_t len = p.kv_lengths[b * p.N + m];
-        return len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
+    // key validity words of n = c0 .. c1 - 1 (the workgroup's 64 keys)
+    int c0 = n_begin, c1 = n_begin;
+    auto fill_valid = [&]() {
+        for (int i = tid; i < c1 - c0; i += 64 * G::waves) {
+            const int m = c0 + i;
+            uint64_t word = ~0ull;
+            if constexpr (kLens) {
+                if (p.kv_lengths) {
+                    const int64_t len = p.kv_lengths[b * p.N + m];
+                    const int lim = len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
+                    const int rel = lim - k0;
+                    word = rel >= 64 ? ~0ull : rel <= 0 ? 0ull : (1ull << rel) - 1ull;
+                }
+            } else if constexpr (kDense) {
+                const uint8_t* drow = p.dense + (b * p.N + m) * p.K;
+                word = 0ull;
+                for (int j = 0; j < 64 && k0 + j < K; ++j)
+                    if (drow[k0 + j] != 0) word |= 1ull << j;
+            }
+            valid_w[i] = word;
+        }
     };
-    auto next_n = [&](int m0) -> int {  // first visited n >= m0 of the range, or -1
+    // first n >= m0 of the chunk with a valid key, or -1
+    auto next_n = [&](int m0) -> int {
         if (m0 < 0) return -1;
-        if constexpr (!kLens) {
-            return m0 < n_end ? m0 : -1;
+        if constexpr (!kLens && !kDense) {
+            return m0 < c1 ? m0 : -1;
         } else {
-            for (int base = m0; base < n_end; base += 64) {
+            for (int base = m0; base < c1; base += 64) {
                 const int m = base + lane;
-                const uint64_t bits = __ballot(m < n_end && k0 < key_lim(m));
+                const uint64_t bits = __ballot(m < c1 && valid_w[m - c0] != 0ull);
                 if (bits) return base + static_cast<int>(__builtin_ctzll(bits));
             }
             return -1;
@@ -1099,12 +1121,7 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
         for (int st = 0; st < D / 16; ++st)
             dp = M::run(row_operand<v8>(t + v_tile, rrd, st), row_operand<v8>(t + g_tile, rrd, st), dp);
         // keys valid for this n (the ragged tile of a length, the dense mask)
-        const int lim = key_lim(m);
-        uint32_t w = lim - kw >= 32 ? ~0u : lim - kw <= 0 ? 0u : (1u << (lim - kw)) - 1u;
-        if constexpr (kDense) {
-            const int kk = kw + col;
-            w &= static_cast<uint32_t>(__ballot(kk < K && p.dense[(b * p.N + m) * p.K + kk] != 0));
-        }
+        const uint32_t w = static_cast<uint32_t>(valid_w[m - c0] >> (32 * kg));
         if (w != ~0u) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -1119,12 +1136,18 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
         for (int r = 0; r < 16; ++r) acc[r] = fmaf(__builtin_amdgcn_exp2f(fmaf(z[r], c_exp, nl2)), dp[r], acc[r]);
     };
 
-    // ring position j holds n_j in slot j % R, loaded R - 1 positions ahead
-    int ns[R];
-    ns[0] = next_n(n_begin);
+    // chunks of the range; in each, ring position j holds n_j in slot j % R,
+    // loaded R - 1 positions ahead
+    for (c0 = n_begin; c0 < n_end; c0 = c1) {
+        c1 = min(c0 + kChunkN, n_end);
+        __syncthreads();  // the previous chunk's words are no longer read
+        fill_valid();
+        __syncthreads();
+        int ns[R];
+        ns[0] = next_n(c0);
 #pragma unroll
-    for (int i = 1; i < R; ++i) ns[i] = next_n(ns[i - 1] >= 0 ? ns[i - 1] + 1 : -1);
-    if (ns[0] >= 0) {
+        for (int i = 1; i < R; ++i) ns[i] = next_n(ns[i - 1] >= 0 ? ns[i - 1] + 1 : -1);
+        if (ns[0] < 0) continue;
 #pragma unroll
         for (int i = 0; i < R - 1; ++i) dma_n(ns[i], i);
         int x = 0;
