@@ -207,8 +207,8 @@ enum BwdBias { kBNone = 0, kBLds = 1, kBScalar = 2 };
 // 32 w + 31, lane l key 32 w + l % 32, whose K and V rows it holds as MFMA B
 // operands.  Per 32-row query tile (shared by the workgroup, LDS DMA two
 // tiles ahead in rings of three):
-//   z  = Q K^T + C     A = Q rows, C = the bias block (rows = queries)
-//   dP = dO V^T        A = dO rows
+//   z  = Q K^T + C          A = Q rows, C = the bias block (rows = queries)
+//   dP = dO V^T - Delta     A = dO rows, -Delta the initial accumulator
 // leave lane l with its key and 16 queries (register r: query 8 (r / 4) +
 // 4 (l / 32) + r % 4); P and dz are formed there and
 //   dV^T += dO^T P,  dK^T += Q^T dz     A = dO^T, Q^T by transposed reads
@@ -476,7 +476,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
         const bool plain = listed && !causal && !dead_t && wave_clean && q0 + 32 <= Q;
         const lds_char* qt = qbuf(x);
         const lds_char* gt = gbuf(x);
-        f32x16 z, dp{};
+        // -Delta (the initial accumulator of dP) and -lse log2 e of the 16
+        // rows: 4 consecutive rows per c
+        const lds_char* rt = rbuf(x);
+        f32x16 z, dp;
+        float nl[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const f32x4 a0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(rt + (8 * c + 4 * half) * 8);
+            const f32x4 a1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(rt + (8 * c + 4 * half) * 8 + 16);
+            dp[4 * c] = -a0[0];
+            nl[4 * c] = a0[1];
+            dp[4 * c + 1] = -a0[2];
+            nl[4 * c + 1] = a0[3];
+            dp[4 * c + 2] = -a1[0];
+            nl[4 * c + 2] = a1[1];
+            dp[4 * c + 3] = -a1[2];
+            nl[4 * c + 3] = a1[3];
+        }
         if constexpr (BIAS == kBLds) {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
@@ -499,29 +516,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) dp = M::run(row_operand<v8>(gt, rrd, st), vop[st], dp);
         dma();
-        // Delta and -lse log2 e of the 16 rows: 4 consecutive rows per c
-        const lds_char* rt = rbuf(x);
-        float dl[16], nl[16];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const f32x4 a0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(rt + (8 * c + 4 * half) * 8);
-            const f32x4 a1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(rt + (8 * c + 4 * half) * 8 + 16);
-            dl[4 * c] = a0[0];
-            nl[4 * c] = a0[1];
-            dl[4 * c + 1] = a0[2];
-            nl[4 * c + 1] = a0[3];
-            dl[4 * c + 2] = a1[0];
-            nl[4 * c + 2] = a1[1];
-            dl[4 * c + 3] = a1[2];
-            nl[4 * c + 3] = a1[3];
-        }
         v8 pop[2], zop[2];
         if (plain) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float pr = __builtin_amdgcn_exp2f(fmaf(z[r], c_exp, nl[r]));
                 pop[r / 8][r % 8] = static_cast<T>(pr);
-                zop[r / 8][r % 8] = static_cast<T>(pr * (dp[r] - dl[r]));
+                zop[r / 8][r % 8] = static_cast<T>(pr * dp[r]);
             }
         } else {
 #pragma unroll
@@ -531,7 +532,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
                 if (causal) ok = ok && qr >= key;
                 const bool dead = nl[r] != nl[r];
                 float pr = ok ? __builtin_amdgcn_exp2f(fmaf(z[r], c_exp, nl[r])) : 0.f;
-                const float dz = ok && !dead ? pr * (dp[r] - dl[r]) : 0.f;
+                const float dz = ok && !dead ? pr * dp[r] : 0.f;
                 pr = dead ? inv_k : pr;
                 pop[r / 8][r % 8] = static_cast<T>(pr);
                 zop[r / 8][r % 8] = static_cast<T>(dz);
@@ -610,8 +611,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
 // valid key, so that its P and dz vanish).  Per 32-key tile (K and V by LDS
 // DMA two tiles ahead in rings of three, the wave's 32 x 32 fp32 bias block
 // by DMA into its own LDS region):
-//   z^T  = K Q^T + C    A = K rows, C = the bias block (rows = queries)
-//   dP^T = V dO^T       A = V rows
+//   z^T  = K Q^T + C          A = K rows, C = the bias block (rows = queries)
+//   dP^T = V dO^T - Delta     A = V rows, -Delta the initial accumulator
 // leave lane l with its row and 16 keys; P and dz are formed there and
 //   dQ^T += K^T dz^T    A = K^T by transposed reads of the same K tile
 // takes dz as the B operand.  Masks as in the forward kernel: tiles past
@@ -823,7 +824,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
         const int k0 = t * kKTile;
         const lds_char* kt = kbuf(x);
         const lds_char* vt = vbuf(x);
-        f32x16 z, dp{};
+        f32x16 z, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = -delta;
         if constexpr (BIAS == kBLds) {
 #pragma unroll
             for (int gg = 0; gg < 4; ++gg) {
@@ -880,7 +883,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const float pr = __builtin_amdgcn_exp2f(fmaf(z[r], c_exp, nl2));
-            dzop[r / 8][r % 8] = static_cast<T>(pr * (dp[r] - delta));
+            dzop[r / 8][r % 8] = static_cast<T>(pr * dp[r]);
         }
 #pragma unroll
         for (int jb = 0; jb < D / 32; ++jb)
