@@ -94,15 +94,22 @@ constexpr int kBiasHalfDma = kBiasHalfWaveBytes / 1024;
 __device__ __forceinline__ int fbh(int r) { return ((r >> 2) ^ (r >> 4)) & 3; }
 
 // Waves per SIMD the register budget must allow: four (128 VGPRs) for
-// D <= 64, two for D = 128 (whose O accumulator alone takes 64 VGPRs).
-template <int D>
+// D <= 64, two for D = 128 (whose O accumulator alone takes 64 VGPRs).  At
+// D = 64 a bias with a block-sparse mask, with a dense mask, or with a scale
+// that is not a power of two needs more than 128 VGPRs (the block
+// bookkeeping, the mask words, the bias / s products), and those kernels run
+// three waves instead of spilling.
+template <int D, int KIND, int BIAS, bool EXACT>
 constexpr int min_waves_per_simd() {
+    if (D == 64 && BIAS != 0 &&
+        (KIND == TRIATTN_MASK_BLOCK || KIND == TRIATTN_MASK_DENSE || !EXACT))
+        return 3;
     return D <= 64 ? 4 : D <= 128 ? 2 : 1;
 }
 
 template <typename T, int D, int KIND, int BIAS, bool EXACT, int W>
 __global__ __launch_bounds__(64 * W)
-__attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kernel(Params p) {
+__attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>()))) void mfma_fwd_kernel(Params p) {
     using M = Mma<T>;
     using v8 = typename M::v8;
     using Ge = Geo<D>;
@@ -459,8 +466,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D>()))) void mfma_fwd_kern
     // At D = 64 the QK MFMAs of one tile are interleaved with the
     // exponentials of the previous one (softmax_pv below); at D = 32 and 128
     // that measured slower than issuing them as one group.  The per-lane
-    // bias loads keep the grouped order: interleaved, their registers spill.
-    constexpr bool kInterleave = D == 64 && BIAS != kBiasScalar;
+    // bias loads keep the grouped order: interleaved, their registers spill;
+    // so do the block-sparse kernels with a bias (interleaved, the 16-bit
+    // bias one spilled past 128 VGPRs).
+    constexpr bool kInterleave = D == 64 && BIAS != kBiasScalar && !(kBlock && BIAS != kNoBias);
 
     // S^T = K . Q^T + bias for tile t from K buffer x and this wave's bias
     // block.  qk_load reads the bias into s and the K operands into kop;

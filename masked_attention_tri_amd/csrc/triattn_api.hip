@@ -70,7 +70,7 @@ triattn_status check_impl(const tri_attn_shape* shape, int32_t dtype, const void
             if (!aligned(mask->kv_num_blocks, 4) || !aligned(mask->kv_indices, 4) ||
                 !aligned(mask->full_kv_num_blocks, 4) || !aligned(mask->full_kv_indices, 4))
                 return TRIATTN_ERR_INVALID_ARG;
-            if ((K + mask->kv_block - 1) / mask->kv_block > triattn::kMaxKvBlocks)
+            if ((K - 1) / mask->kv_block + 1 > triattn::kMaxKvBlocks)  // K >= 1
                 return TRIATTN_ERR_UNSUPPORTED;
             break;
         default:
@@ -139,8 +139,9 @@ Params make_params(const tri_attn_shape* s, const void* q, const void* k, const 
             p.stride_b = mask->stride_b;
             p.stride_n = mask->stride_n;
             p.stride_h = mask->stride_h;
-            p.n_q_rows = (s->Q + mask->q_block - 1) / mask->q_block;
-            p.n_kv_blocks = (s->K + mask->kv_block - 1) / mask->kv_block;
+            // ceil(Q / q_block), ceil(K / kv_block) without overflow (any block size >= 1)
+            p.n_q_rows = s->Q == 0 ? 0 : (s->Q - 1) / mask->q_block + 1;
+            p.n_kv_blocks = (s->K - 1) / mask->kv_block + 1;
         }
     }
     return p;

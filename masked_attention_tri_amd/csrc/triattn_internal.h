@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "triattn.h"
@@ -101,15 +102,21 @@ constexpr int64_t kMaxKvBlocks = 8192;
 // Each split beyond the first needs a B H Q K fp32 plane of workspace.
 inline int dbias_splits(int64_t B, int64_t N, int64_t H, int64_t Q, int64_t K, int64_t D) {
     if (D != 32 && D != 64 && D != 128) return 1;
+    // (sizes past these the kernels never take; no product below overflows)
+    const int64_t lim = int64_t(1) << 31;
+    if (B < 1 || H < 1 || Q < 1 || K < 1 || N < 1 || B > lim || H > lim || Q > lim || K > lim ||
+        B * H > lim)
+        return 1;
     const int64_t rows_q = D <= 64 ? 128 : 64;
-    const int64_t tiles = B * H * ((Q + rows_q - 1) / rows_q) * ((K + 63) / 64);
-    const int64_t slots = D == 32 ? 512 : 256;  // resident workgroups
+    const double tiles = static_cast<double>(B * H) * static_cast<double>((Q - 1) / rows_q + 1) *
+                         static_cast<double>((K - 1) / 64 + 1);
+    const double slots = D == 32 ? 512.0 : 256.0;  // resident workgroups
     int best = 1;
     double best_eff = 0.0;
     for (int s = 1; s <= 8 && (s == 1 || N / s >= 16); ++s) {
-        const double wg = static_cast<double>(tiles * s);
-        const double rounds = static_cast<double>((tiles * s + slots - 1) / slots);
-        const double eff = wg / (rounds * static_cast<double>(slots));
+        const double wg = tiles * s;
+        const double rounds = ceil(wg / slots);
+        const double eff = wg / (rounds * slots);
         if (eff > best_eff + 1e-9) {
             best_eff = eff;
             best = s;
