@@ -311,10 +311,12 @@ triattn_status tri_attn_varlen_fwd(const tri_attn_varlen* desc, int32_t dtype, c
  * fp32, or NULL to skip it.  All device memory; enqueued on `stream`.
  *
  * Workspace (required when there is a query row): device memory of at least
- * 12*B*N*H*Q bytes, 16-byte aligned, caller-owned, whose contents on entry
- * do not matter and on return are unspecified.  The first pass stores
- * per-row data there (Delta = dO.O and lse of every row, and how many rows
- * of each 32-row tile have no valid key) for the passes that follow.  With
+ * tri_attn_bwd_workspace_size(shape, 0) bytes (260 per (b, n, h) slice and
+ * 32-row tile, rounded up to 16), 16-byte aligned, caller-owned, whose
+ * contents on entry do not matter and on return are unspecified.  The first
+ * pass stores per-row data there (Delta = dO.O and lse of every row, and how
+ * many rows of each 32-row tile have no valid key) for the passes that
+ * follow.  With
  * dbias, more workspace lets the dBias pass split its sum over n into
  * ranges summed by separate workgroups and then added in range order
  * (deterministic for a given workspace size; the split changes only the
@@ -339,10 +341,12 @@ triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const vo
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Bytes of workspace tri_attn_bwd uses at most for `shape`: 12*B*N*H*Q,
- * plus, when with_dbias is nonzero, the planes of partial sums of the
- * preferred dBias split (a whole number of B*H*Q*K fp32 planes).  0 for a
- * NULL shape, a negative size or a size past int64.  Host only.
+ * Bytes of workspace tri_attn_bwd uses at most for `shape`: the per-row data
+ * (260 bytes per (b, n, h) slice and 32-row tile, rounded up to 16; the
+ * minimum tri_attn_bwd accepts), plus, when with_dbias is nonzero, the
+ * planes of partial sums of the preferred dBias split (a whole number of
+ * B*H*Q*K fp32 planes).  0 for a NULL shape, a negative size or a size past
+ * int64.  Host only.
  */
 size_t tri_attn_bwd_workspace_size(const tri_attn_shape* shape, int32_t with_dbias);
 
@@ -350,17 +354,18 @@ size_t tri_attn_bwd_workspace_size(const tri_attn_shape* shape, int32_t with_dbi
  * tri_attn_bwd for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same arguments without the workspace, and the same results, bit for
- * bit, as tri_attn_bwd given a workspace of 12 * TRIATTN_BWD_NOALLOC_MAX_ROWS
- * bytes.  That workspace is a fixed array of this library (48 MiB) per GPU
- * that loads it, held until the process ends; the call allocates and frees
- * nothing.  It needs B*N*H*Q <= TRIATTN_BWD_NOALLOC_MAX_ROWS and returns
- * TRIATTN_ERR_UNSUPPORTED (nothing launched) for larger problems.  All calls
- * on one GPU share the array: calls that overlap in time on one GPU race and
- * must not be issued.  The calling thread's current device must be the
- * stream's.  Errors otherwise as tri_attn_bwd (TRIATTN_ERR_HIP also if the
- * array's address cannot be obtained).
+ * bit, as tri_attn_bwd given a workspace of TRIATTN_BWD_NOALLOC_BYTES bytes.
+ * That workspace is a fixed array of this library (48 MiB) per GPU that
+ * loads it, held until the process ends; the call allocates and frees
+ * nothing.  It needs tri_attn_bwd_workspace_size(shape, 0) <=
+ * TRIATTN_BWD_NOALLOC_BYTES (about 6 Mi rows when Q is a multiple of 32)
+ * and returns TRIATTN_ERR_UNSUPPORTED (nothing launched) for larger
+ * problems.  All calls on one GPU share the array: calls that overlap in
+ * time on one GPU race and must not be issued.  The calling thread's
+ * current device must be the stream's.  Errors otherwise as tri_attn_bwd
+ * (TRIATTN_ERR_HIP also if the array's address cannot be obtained).
  */
-#define TRIATTN_BWD_NOALLOC_MAX_ROWS (4 * 1024 * 1024)
+#define TRIATTN_BWD_NOALLOC_BYTES (48 * 1024 * 1024)
 triattn_status tri_attn_bwd_noalloc(const tri_attn_shape* shape, int32_t dtype, const void* q,
                                     const void* k, const void* v, const float* bias,
                                     const tri_attn_mask* mask, float scale, const void* out,

@@ -340,7 +340,7 @@ def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
     q's dtype and dbias fp32 of shape (B,1,H,Q,K) (None when bias is None).
     out, lse and mx are the forward's (O, lse, max) for the same arguments
     (from return_aux=True).  Every step runs in the library's HIP kernels;
-    the library's workspace (12 bytes per (b, n, h, q) row, and with a bias
+    the library's workspace (its per-row data, and with a bias
     the planes of dBias partial sums it asks for) is allocated here.
     """
     four_d, q5, k5, v5, bias5, desc, keep = _prepare(q, k, v, bias, mask, kv_lengths,

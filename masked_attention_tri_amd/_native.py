@@ -37,8 +37,8 @@ EXPORTED = ("tri_attn_check", "tri_attn_fwd", "tri_attn_fwd_bias_dtype", "tri_at
             "tri_attn_bwd", "tri_attn_bwd_workspace_size", "tri_attn_bwd_noalloc",
             "tri_attn_mask_to_kv_lengths", "tri_attn_status_str")
 
-# rows (B*N*H*Q) whose per-row data the no-allocation backward holds
-TRIATTN_BWD_NOALLOC_MAX_ROWS = 4 * 1024 * 1024
+# bytes of the no-allocation backward's own workspace
+TRIATTN_BWD_NOALLOC_BYTES = 48 * 1024 * 1024
 
 TRIATTN_QKV_SEPARATE = 0
 TRIATTN_QKV_PACKED = 1
@@ -224,7 +224,7 @@ def tri_attn_mask_to_kv_lengths(mask, rows: int, K: int, kv_lengths, nonprefix_r
 def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: float, out, dout,
                  lse, mx, dq, dk, dv, dbias, stream, workspace=None) -> int:
     """Enqueue the backward pass on `stream` (as tri_attn_fwd); `workspace`
-    is a device tensor of at least 12*B*N*H*Q bytes, up to
+    is a device tensor of at least tri_attn_bwd_workspace_size(shape, False) bytes, up to
     tri_attn_bwd_workspace_size(shape, dbias is not None) (None is passed as
     NULL, which the library refuses unless there is no query row)."""
     if stream is None:
@@ -240,8 +240,8 @@ def tri_attn_bwd(shape: TriAttnShape, dtype: int, q, k, v, bias, mask, scale: fl
 
 
 def tri_attn_bwd_workspace_size(shape: TriAttnShape, with_dbias: bool = True) -> int:
-    """Bytes of workspace tri_attn_bwd uses at most for `shape` (12*B*N*H*Q,
-    plus the dBias split's partial sums when with_dbias)."""
+    """Bytes of workspace tri_attn_bwd uses at most for `shape` (the per-row
+    data, plus the dBias split's partial sums when with_dbias)."""
     return int(load_library().tri_attn_bwd_workspace_size(ctypes.byref(shape), int(bool(with_dbias))))
 
 

@@ -19,7 +19,7 @@
 //
 //   bwd_rows_kernel   Delta and -lse log2 e of every row, and per 32-row tile
 //                     the number of rows with no valid key, into the
-//                     workspace (12 bytes per row).
+//                     workspace (260 bytes per 32-row tile).
 //   bwd_dkdv_kernel   one workgroup per (b, n, h, 128 keys); K and V rows in
 //                     registers; 32-row query tiles of Q, dO and the row data
 //                     by LDS DMA.
@@ -127,12 +127,14 @@ __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float 
 }
 
 // ---- per-row data -----------------------------------------------------------
-// For row i = ((b N + n) H + h) Q + q: rows[2 i] = Delta_i = dO_i . O_i (fp32
-// products of the stored values), rows[2 i + 1] = -lse_i log2 e, or NaN when
-// the forward's max of the row is the -1e9 replacement (no valid key).
-// tile_dead[(b N + n) H nT + t] = rows of 32-row tile t with no valid key.
-// One workgroup of 32 (D / 8) threads per tile: thread (r, c) takes the
-// 16-byte chunk c of row r; shuffles sum the D / 8 partial products.
+// Per (b, n, h) slice and 32-row tile t, 64 floats at rows + (slice nT + t) 64:
+// -Delta of the tile's 32 rows (Delta_q = dO_q . O_q, fp32 products of the
+// stored values), then -lse_q log2 e (NaN when the forward's max of row q is
+// the -1e9 replacement: no valid key); rows past Q hold 0 and -inf.  Then,
+// after all tiles, tile_dead[slice nT + t] = rows of tile t with no valid key.
+// Workspace bytes: 260 per (slice, tile) (bwd_rows_bytes).  One workgroup of
+// 32 (D / 8) threads per tile: thread (r, c) takes the 16-byte chunk c of row
+// r; shuffles sum the D / 8 partial products.
 template <typename T, int D>
 __global__ __launch_bounds__(4 * D) void bwd_rows_kernel(Params p, BwdParams g, float* rows,
                                                          uint32_t* tile_dead) {
@@ -155,11 +157,15 @@ __global__ __launch_bounds__(4 * D) void bwd_rows_kernel(Params p, BwdParams g, 
 #pragma unroll
         for (int s = 1; s < kC; s <<= 1) acc += __shfl_xor(acc, s);
         bool dead = false;
-        if (in && c == 0) {
-            const int64_t i = bnh * p.Q + q;
-            dead = g.mx[i] == kMaskedLogit;
-            const float nl2 = dead ? __builtin_nanf("") : -g.lse[i] * kLog2e;
-            *reinterpret_cast<float2*>(rows + 2 * i) = make_float2(acc, nl2);
+        if (c == 0) {
+            float nl2 = -INFINITY;
+            if (in) {
+                const int64_t i = bnh * p.Q + q;
+                dead = g.mx[i] == kMaskedLogit;
+                nl2 = dead ? __builtin_nanf("") : -g.lse[i] * kLog2e;
+            }
+            rows[w * 64 + r] = -acc;
+            rows[w * 64 + 32 + r] = nl2;
         }
         const int cnt = __syncthreads_count(dead);
         if (tid == 0) tile_dead[w] = static_cast<uint32_t>(cnt);
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
     const uint32_t slice_bytes = static_cast<uint32_t>(p.Q * D * sizeof(T));
     const u32x4 q_desc = make_desc(static_cast<const T*>(p.q) + bnh * p.Q * D, slice_bytes);
     const u32x4 g_desc = make_desc(static_cast<const T*>(g.dout) + bnh * p.Q * D, slice_bytes);
-    const u32x4 r_desc = make_desc(rows + 2 * bnh * p.Q, static_cast<uint32_t>(p.Q * 8));
+    const u32x4 r_desc = make_desc(rows + bnh * nT * 64, static_cast<uint32_t>(nT * 256));
     auto qbuf = [&](int x) { return (lds_char*)(x == 0 ? q_lds0 : x == 1 ? q_lds1 : q_lds2); };
     auto gbuf = [&](int x) { return (lds_char*)(x == 0 ? g_lds0 : x == 1 ? g_lds1 : g_lds2); };
     auto rbuf = [&](int x) { return (lds_char*)(x == 0 ? r_lds0 : x == 1 ? r_lds1 : r_lds2); };
@@ -412,8 +418,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
             else
                 dma16(g_desc, gbuf(x) + 1024 * (I - Ge::tileDma), ring_src[j] + toff);
         }
-        // rows 8 w .. 8 w + 7 of the tile's row data (8 bytes each)
-        const uint32_t roff = t >= 0 ? static_cast<uint32_t>((32 * t + 8 * wave) * 8 + 16 * lane) : kNoTile;
+        // bytes 64 w .. 64 w + 63 of the tile's 256 bytes of row data
+        const uint32_t roff = t >= 0 ? static_cast<uint32_t>(256 * t + 64 * wave + 16 * lane) : kNoTile;
         if (lane < 4) dma16(r_desc, rbuf(x) + 64 * wave, roff);
     };
     // bias block: instruction j, lane l fills stored row 8 j + l / 8 (source
@@ -477,22 +483,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
         const lds_char* qt = qbuf(x);
         const lds_char* gt = gbuf(x);
         // -Delta (the initial accumulator of dP) and -lse log2 e of the 16
-        // rows: 4 consecutive rows per c
+        // rows: 4 consecutive rows per c, one 16-byte read each
         const lds_char* rt = rbuf(x);
         f32x16 z, dp;
         float nl[16];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const f32x4 a0 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(rt + (8 * c + 4 * half) * 8);
-            const f32x4 a1 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(rt + (8 * c + 4 * half) * 8 + 16);
-            dp[4 * c] = -a0[0];
-            nl[4 * c] = a0[1];
-            dp[4 * c + 1] = -a0[2];
-            nl[4 * c + 1] = a0[3];
-            dp[4 * c + 2] = -a1[0];
-            nl[4 * c + 2] = a1[1];
-            dp[4 * c + 3] = -a1[2];
-            nl[4 * c + 3] = a1[3];
+            const f32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(rt + (8 * c + 4 * half) * 4);
+            const f32x4 l = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(rt + 128 + (8 * c + 4 * half) * 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dp[4 * c + i] = a[i];
+                nl[4 * c + i] = l[i];
+            }
         }
         if constexpr (BIAS == kBLds) {
 #pragma unroll
@@ -964,7 +967,7 @@ struct DbGeo {
     static constexpr int slotBytes = (2 * QW + 2 * KW) * tileBytes;
     static constexpr int dmaPerWave = slotBytes / 1024 / waves;
     static_assert(dmaPerWave * waves * 1024 == slotBytes, "DMAs split evenly over the waves");
-    static constexpr int infoBytes = rowsQ * 8;  // row data: 128 bytes per wave
+    static constexpr int infoBytes = rowsQ * 8;  // row data (QW tiles of 256 bytes): 128 per wave
     static_assert(infoBytes == 128 * waves, "one 8-lane DMA of row data per wave");
 };
 
@@ -1007,6 +1010,7 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
     const int n_begin = static_cast<int>(sp * N / splits), n_end = static_cast<int>((sp + 1) * N / splits);
     const int qrow = q0 + 32 * qg + col;  // this lane's query
     const int kw = k0 + 32 * kg;          // this wave's first key
+    const int64_t n_t32 = (p.Q + 31) / 32;  // 32-row tiles of the row data per slice
 
     // scale: z = s (Q.K + B / s); s = 0 leaves z = B
     const bool zero_s = p.scale == 0.0f;
@@ -1075,7 +1079,7 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
         const u32x4 dg = make_desc(static_cast<const T*>(g.dout) + bnh * p.Q * D, qbytes);
         const u32x4 dk = make_desc(static_cast<const T*>(p.k) + bnh * p.K * D, kbytes);
         const u32x4 dv = make_desc(static_cast<const T*>(p.v) + bnh * p.K * D, kbytes);
-        const u32x4 dr = make_desc(rows + 2 * bnh * p.Q, static_cast<uint32_t>(p.Q * 8));
+        const u32x4 dr = make_desc(rows + bnh * n_t32 * 64, static_cast<uint32_t>(n_t32 * 256));
 #pragma unroll
         for (int j = 0; j < G::dmaPerWave; ++j) {
             const int I = wave + G::waves * j;
@@ -1095,8 +1099,8 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
                 dma16(dv, dst, m >= 0 ? o : kNoTile);
             }
         }
-        // row data of rows q0 + 16 w .. + 15 (8 lanes of 16 bytes)
-        const uint32_t roff = m >= 0 ? static_cast<uint32_t>(q0 * 8 + 128 * wave + 16 * lane) : kNoTile;
+        // 128 bytes per wave of the row data of tiles q0 / 32 ..
+        const uint32_t roff = m >= 0 ? static_cast<uint32_t>((q0 / 32) * 256 + 128 * wave + 16 * lane) : kNoTile;
         if (lane < 8) dma16(dr, (lds_char*)r_lds[x] + 128 * wave, roff);
     };
 
@@ -1107,14 +1111,13 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
     f32x16 acc{};
     auto compute = [&](int m, int x) {
         const lds_char* t = (const lds_char*)t_lds[x];
-        const f32x4 ri = __builtin_bit_cast(
-            f32x4, *reinterpret_cast<const lds_u32x4*>((const lds_char*)r_lds[x] + (32 * qg + (col & ~1)) * 8));
-        const float delta = (col & 1) ? ri[2] : ri[0];
-        float nl2 = (col & 1) ? ri[3] : ri[1];
+        const lds_char* ri = (const lds_char*)r_lds[x] + 256 * qg + 4 * col;  // tile qg, row col
+        const float ndelta = *reinterpret_cast<const __attribute__((address_space(3))) float*>(ri);
+        float nl2 = *reinterpret_cast<const __attribute__((address_space(3))) float*>(ri + 128);
         nl2 = nl2 != nl2 ? -INFINITY : nl2;  // no valid key: no contribution
         f32x16 z = cb, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = -delta;
+        for (int r = 0; r < 16; ++r) dp[r] = ndelta;
         if (!zero_s) {
 #pragma unroll
             for (int st = 0; st < D / 16; ++st)
@@ -1210,10 +1213,9 @@ hipError_t launch_bwd_bias(const Params& p, const BwdParams& g, bool exact, floa
 template <typename T, int D, int KIND>
 hipError_t launch_bwd_kind(const Params& p, const BwdParams& g, bool exact, float* ws,
                            size_t ws_bytes, hipStream_t stream) {
-    const int64_t n_rows = p.B * p.N * p.H * p.Q;
-    float* rows = ws;
-    uint32_t* tdead = reinterpret_cast<uint32_t*>(ws + 2 * n_rows);
     const int64_t tiles = p.B * p.N * p.H * ((p.Q + 31) / 32);
+    float* rows = ws;
+    uint32_t* tdead = reinterpret_cast<uint32_t*>(ws + 64 * tiles);
     const unsigned gr = static_cast<unsigned>(tiles < (1 << 20) ? tiles : (1 << 20));
     hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3(gr), dim3(4 * D), 0, stream, p, g, rows, tdead);
     hipError_t e;
@@ -1228,13 +1230,13 @@ hipError_t launch_bwd_kind(const Params& p, const BwdParams& g, bool exact, floa
         if (g.dbias && p.bias) {
             using G = DbGeo<D>;
             // splits beyond the first need a plane of partial sums each, after
-            // the row data (12 bytes per row)
+            // the row data
             const int64_t plane = p.B * p.H * p.Q * p.K;
-            const size_t used = static_cast<size_t>(12 * n_rows);
+            const size_t used = static_cast<size_t>(bwd_rows_bytes(p.B * p.N * p.H, p.Q));
             const size_t room = ws_bytes > used ? ws_bytes - used : 0;
             int splits = dbias_splits(p.B, p.N, p.H, p.Q, p.K, D);
             while (splits > 1 && room < static_cast<size_t>(4 * splits * plane)) --splits;
-            float* part = ws + 3 * n_rows;
+            float* part = ws + used / 4;
             const int64_t gb = p.B * p.H * ((p.Q + G::rowsQ - 1) / G::rowsQ) *
                                ((p.K + G::rowsK - 1) / G::rowsK) * splits;
             if (gb > 0x7fffffff) return hipErrorInvalidConfiguration;

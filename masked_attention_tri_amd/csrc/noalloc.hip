@@ -20,8 +20,8 @@
 
 namespace {
 
-// 48 MiB: 12 bytes (3 floats) of per-row data for B*N*H*Q <= TRIATTN_BWD_NOALLOC_MAX_ROWS.
-constexpr int64_t kScratchFloats = 3 * int64_t(TRIATTN_BWD_NOALLOC_MAX_ROWS);
+// The workspace: TRIATTN_BWD_NOALLOC_BYTES (48 MiB).
+constexpr int64_t kScratchFloats = TRIATTN_BWD_NOALLOC_BYTES / 4;
 static __device__ __align__(256) float scratch[kScratchFloats];
 
 constexpr int kMaxDevices = 64;
@@ -69,13 +69,10 @@ triattn_status tri_attn_bwd_noalloc(const tri_attn_shape* shape, int32_t dtype, 
                               dk, dv, dbias, nullptr, 0, false);
     if (st != TRIATTN_OK) return st;
     if (shape->B == 0 || shape->N == 0 || shape->H == 0 || shape->Q == 0) return TRIATTN_OK;
-    // the per-row data of B*N*H*Q rows must fit the scratch
-    int64_t rows = 1;
-    for (const int64_t x : {shape->B, shape->N, shape->H, shape->Q}) {
-        if (rows > TRIATTN_BWD_NOALLOC_MAX_ROWS / x) return TRIATTN_ERR_UNSUPPORTED;
-        rows *= x;
-    }
-    if (rows > TRIATTN_BWD_NOALLOC_MAX_ROWS) return TRIATTN_ERR_UNSUPPORTED;
+    // the per-row data must fit the scratch
+    const int64_t slices = shape->B * shape->N * shape->H;  // validated: no overflow
+    const int64_t need = triattn::bwd_rows_bytes(slices, shape->Q);
+    if (need < 0 || need > TRIATTN_BWD_NOALLOC_BYTES) return TRIATTN_ERR_UNSUPPORTED;
     hipError_t err = hipSuccess;
     float* ws = device_scratch(&err);
     if (!ws) return TRIATTN_ERR_HIP;

@@ -217,9 +217,9 @@ triattn_status bwd_validate(const tri_attn_shape* shape, int32_t dtype, const vo
         !aligned(dbias, 4) || !aligned(workspace, 16))
         return TRIATTN_ERR_INVALID_ARG;
     if (!empty && check_workspace) {
-        // 12 B N H Q bytes of per-row data (more only speeds dBias up)
-        const int64_t need = mul_or_neg(
-            mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H), shape->Q), 12);
+        // the per-row data (more only speeds dBias up)
+        const int64_t slices = mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H);
+        const int64_t need = slices < 0 ? -1 : triattn::bwd_rows_bytes(slices, shape->Q);
         if (need < 0) return TRIATTN_ERR_UNSUPPORTED;
         if (!workspace || workspace_bytes < static_cast<uint64_t>(need))
             return TRIATTN_ERR_INVALID_ARG;
@@ -360,8 +360,8 @@ triattn_status tri_attn_bwd(const tri_attn_shape* shape, int32_t dtype, const vo
 size_t tri_attn_bwd_workspace_size(const tri_attn_shape* shape, int32_t with_dbias) {
     if (!shape || shape->B < 0 || shape->N < 0 || shape->H < 0 || shape->Q < 0 || shape->K < 0)
         return 0;
-    int64_t need = mul_or_neg(
-        mul_or_neg(mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H), shape->Q), 12);
+    const int64_t slices = mul_or_neg(mul_or_neg(shape->B, shape->N), shape->H);
+    int64_t need = slices < 0 ? -1 : triattn::bwd_rows_bytes(slices, shape->Q);
     if (need < 0) return 0;
     if (with_dbias) {
         const int s = triattn::dbias_splits(shape->B, shape->N, shape->H, shape->Q, shape->K,

@@ -95,6 +95,16 @@ constexpr float kMaskedLogit = -1.0e9f;
 // one visited bit and one full bit per block in LDS.
 constexpr int64_t kMaxKvBlocks = 8192;
 
+// Bytes of the backward's per-row data for `slices` (b, n, h) slices of Q
+// rows: 260 per slice and 32-row tile (two planes of 32 floats and a count),
+// rounded up to 16 (what follows stays 16-byte aligned); -1 past int64.
+inline int64_t bwd_rows_bytes(int64_t slices, int64_t Q) {
+    if (slices < 0 || Q < 0) return -1;
+    const int64_t tiles = Q == 0 ? 0 : (Q - 1) / 32 + 1;
+    if (tiles != 0 && slices > INT64_MAX / 272 / tiles) return -1;
+    return (slices * tiles * 260 + 15) / 16 * 16;
+}
+
 // Ranges of n the MFMA dBias kernel splits its sum into for a shape: its
 // workgroups cover (32 QW) x 64 (query, key) tiles (QW = 4 for D <= 64, else
 // 2) and there are 256 CUs; the split that fills whole rounds of
@@ -135,7 +145,7 @@ hipError_t launch_mfma_d32(const Params& p, int32_t dtype, bool exact, hipStream
 hipError_t launch_mfma_d64(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
 hipError_t launch_mfma_d128(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
 hipError_t launch_mfma_d256(const Params& p, int32_t dtype, bool exact, hipStream_t stream);
-// The backward: per-row data in `ws` (12 B N H Q bytes; the rest, if any,
+// The backward: per-row data in `ws` (bwd_rows_bytes; the rest, if any,
 // holds dBias partial sums), then dK / dV, dQ and dBias.
 hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
                       size_t ws_bytes, hipStream_t stream);

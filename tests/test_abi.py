@@ -266,11 +266,12 @@ def _bwd(shp, dbias=A, ws=None, ws_bytes=0):
 
 
 def test_bwd_workspace_validation():
-    """The workspace must hold 12 B N H Q bytes (tri_attn_bwd_workspace_size)
+    """The workspace must hold the per-row data (260 bytes per (b, n, h)
+    slice and 32-row tile, rounded up to 16: tri_attn_bwd_workspace_size)
     and be 16-byte aligned, with or without a bias gradient; a failing check
     launches nothing (these calls make no device call)."""
     shp = shape(B=1, N=2, H=2, Q=8, K=8, D=32)
-    need = 12 * 1 * 2 * 2 * 8
+    need = 260 * 1 * 2 * 2 * 1
     assert nat.tri_attn_bwd_workspace_size(shp) == need
     assert _bwd(shp, ws=A, ws_bytes=need - 1) == nat.TRIATTN_ERR_INVALID_ARG
     assert _bwd(shp, dbias=None, ws=A, ws_bytes=need - 1) == nat.TRIATTN_ERR_INVALID_ARG
@@ -285,7 +286,7 @@ def test_bwd_workspace_validation():
     assert nat.tri_attn_bwd_workspace_size(shape(B=-1)) == 0
     # with a bias gradient, whole B H Q K fp32 planes of partial sums on top
     head = shape(B=1, N=768, H=4, Q=768, K=768, D=64)
-    rows = 12 * 768 * 4 * 768
+    rows = 260 * 768 * 4 * 24
     assert nat.tri_attn_bwd_workspace_size(head, False) == rows
     extra = nat.tri_attn_bwd_workspace_size(head, True) - rows
     assert extra > 0 and extra % (4 * 4 * 768 * 768) == 0
@@ -369,19 +370,20 @@ def test_fwd_bias_dtype_validation():
 
 
 def test_bwd_noalloc_rejects_problems_past_its_scratch():
-    """The no-allocation backward holds the per-row data of at most
-    TRIATTN_BWD_NOALLOC_MAX_ROWS (b, n, h, q) rows: a larger problem is
-    refused before any device call, with or without a bias gradient;
-    argument errors come first."""
+    """The no-allocation backward holds the per-row data in its own
+    TRIATTN_BWD_NOALLOC_BYTES: a larger problem is refused before any device
+    call, with or without a bias gradient; argument errors come first."""
     lib = nat.load_library()
 
     def call(shp, dbias=A, scale=math.nan):
         return lib.tri_attn_bwd_noalloc(ctypes.byref(shp), nat.TRIATTN_BF16, A, A, A, A, None,
                                         ctypes.c_float(scale), A, A, A, A, A, A, A, dbias, None)
 
-    big = shape(B=1, N=1025, H=4, Q=1024, K=8, D=64)
-    assert 1025 * 4 * 1024 > nat.TRIATTN_BWD_NOALLOC_MAX_ROWS
+    big = shape(B=1, N=1025, H=8, Q=1024, K=8, D=64)
+    assert nat.tri_attn_bwd_workspace_size(big, False) > nat.TRIATTN_BWD_NOALLOC_BYTES
     assert call(big) == nat.TRIATTN_ERR_UNSUPPORTED
     assert call(big, dbias=None) == nat.TRIATTN_ERR_UNSUPPORTED
     assert call(big, scale=math.inf) == nat.TRIATTN_ERR_INVALID_ARG
+    fits = shape(B=1, N=768, H=4, Q=768, K=768, D=64)
+    assert nat.tri_attn_bwd_workspace_size(fits, False) <= nat.TRIATTN_BWD_NOALLOC_BYTES
     assert call(shape(B=1, N=0, H=4, Q=256, K=129, D=64)) == nat.TRIATTN_OK  # no work
