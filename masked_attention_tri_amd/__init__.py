@@ -212,6 +212,14 @@ def _as5(x, name):
     return x
 
 
+def _dense16(t):
+    """t contiguous and 16-byte aligned (the library's requirement for the
+    tensors it reads in 16-byte pieces): a view at an unaligned offset is
+    copied into a fresh allocation."""
+    t = t.contiguous()
+    return t if t.data_ptr() % 16 == 0 else t.clone()
+
+
 def _prepare(q, k, v, bias, mask, kv_lengths, block_mask, bias_in_input_dtype=False):
     """Shape and dtype checks, 5-D views, contiguous copies, and the mask
     descriptor (with the tensors it points at, which must stay alive).  The
@@ -229,12 +237,14 @@ def _prepare(q, k, v, bias, mask, kv_lengths, block_mask, bias_in_input_dtype=Fa
         raise ValueError("q, k and v must share one dtype")
     if not q5.is_cuda:
         raise ValueError("inputs must be on a GPU device (there is no CPU path)")
+    if k5.device != q5.device or v5.device != q5.device:
+        raise ValueError("q, k and v must be on one device")
     B, N, H, Q, D = q5.shape
     K = k5.shape[3]
     if tuple(k5.shape) != (B, N, H, K, D) or tuple(v5.shape) != (B, N, H, K, D):
         raise ValueError(f"k and v must be (B,N,H,K,D) = {(B, N, H, K, D)}")
     dev = q5.device
-    q5, k5, v5 = q5.contiguous(), k5.contiguous(), v5.contiguous()
+    q5, k5, v5 = _dense16(q5), _dense16(k5), _dense16(v5)
     if bias5 is not None:
         if tuple(bias5.shape) != (B, 1, H, Q, K):
             raise ValueError(f"bias must be (B,1,H,Q,K) = {(B, 1, H, Q, K)}")
@@ -347,7 +357,9 @@ def triangle_attention_backward(q, k, v, bias, out, dout, lse, mx, mask=None,
                                                      block_mask)
     B, N, H, Q, D = q5.shape
     K = k5.shape[3]
-    o5, g5 = _as5(out, "out").contiguous(), _as5(dout, "dout").contiguous()
+    o5, g5 = _dense16(_as5(out, "out")), _dense16(_as5(dout, "dout"))
+    if any(t.device != q5.device for t in (o5, g5, lse, mx)):
+        raise ValueError("out, dout, lse and max must be on q's device")
     if tuple(o5.shape) != (B, N, H, Q, D) or tuple(g5.shape) != (B, N, H, Q, D):
         raise ValueError(f"out and dout must be (B,N,H,Q,D) = {(B, N, H, Q, D)}")
     if o5.dtype != q5.dtype or g5.dtype != q5.dtype:
@@ -451,7 +463,7 @@ def triangle_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q
             raise ValueError("qkv_packed: q must be [T, 3, H, D]")
         total_q, _, H, D = q.shape
         total_kv = total_q
-        tensors = [q.contiguous()]
+        tensors = [_dense16(q)]
         kk = vv = None
         cu_kv = None
     else:
@@ -461,20 +473,22 @@ def triangle_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q
         if layout == "kv_packed":
             if k is None or k.dim() != 4 or tuple(k.shape[1:]) != (2, H, D):
                 raise ValueError("kv_packed: k must be [Tkv, 2, H, D]")
-            kk, vv = k.contiguous(), None
+            kk, vv = _dense16(k), None
         else:
             if k is None or v is None or k.dim() != 3 or tuple(k.shape[1:]) != (H, D) \
                     or k.shape != v.shape:
                 raise ValueError("separate: k and v must be [Tkv, H, D]")
-            kk, vv = k.contiguous(), v.contiguous()
+            kk, vv = _dense16(k), _dense16(v)
         total_kv = kk.shape[0]
-        tensors = [q.contiguous()]
+        tensors = [_dense16(q)]
         if cu_seqlens_kv is None:
             raise ValueError("cu_seqlens_kv is required for this layout")
         cu_kv = cu_seqlens_kv.to(device=dev, dtype=torch.int32).contiguous()
     for t in (kk, vv):
         if t is not None and t.dtype != q.dtype:
             raise ValueError("q, k and v must share one dtype")
+        if t is not None and t.device != dev:
+            raise ValueError("q, k and v must be on one device")
     cu_q = cu_seqlens_q.to(device=dev, dtype=torch.int32).contiguous()
     if cu_q.dim() != 1 or (cu_kv is not None and cu_kv.shape != cu_q.shape):
         raise ValueError("cu_seqlens must be 1-D [batch + 1] and of equal length")

@@ -119,12 +119,55 @@ def test_optional_aux_outputs_and_invalid_args_write_nothing():
     ref = run_gpu(c.to("cpu"), scale=None)
     assert torch.equal(out.cpu(), ref[0])
     poison = torch.full_like(c.q, 7.0)
-    bad = nat.TriAttnShape(B, N, H, Q, K, 72)  # D % 8 != 0 for bf16... 72 % 8 == 0, use 68
-    bad.D = 68
+    bad = nat.TriAttnShape(B, N, H, Q, K, 68)  # D % 8 != 0: no 16-bit kernel takes it
     assert mat.tri_attn_fwd(bad, nat.TRIATTN_BF16, c.q, c.k, c.v, c.bias, None, math.nan,
                             poison, None, None, None) == mat.TRIATTN_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.all(poison == 7.0)
+
+
+def test_inputs_on_another_device_are_rejected():
+    """Every tensor the binding hands to the library must live on q's
+    device: a host tensor among them is an error, never a host pointer
+    passed to a kernel."""
+    say("inputs split across devices")
+    c = wl.make_case(1, 2, 2, 32, 32, 32, "bf16", "kv_lengths", seed=12).to("cuda")
+    with pytest.raises(ValueError, match="one device"):
+        mat.triangle_attention(c.q, c.k.cpu(), c.v, c.bias, kv_lengths=c.kv_lengths)
+    with pytest.raises(ValueError, match="one device"):
+        mat.triangle_attention(c.q, c.k, c.v.cpu(), c.bias, kv_lengths=c.kv_lengths)
+    out, lse, mx = mat.triangle_attention(c.q, c.k, c.v, c.bias, kv_lengths=c.kv_lengths,
+                                          return_aux=True)
+    with pytest.raises(ValueError, match="q's device"):
+        mat.triangle_attention_backward(c.q, c.k, c.v, c.bias, out, out.cpu(), lse, mx,
+                                        kv_lengths=c.kv_lengths)
+    with pytest.raises(ValueError, match="q's device"):
+        mat.triangle_attention_backward(c.q, c.k, c.v, c.bias, out, out, lse.cpu(), mx,
+                                        kv_lengths=c.kv_lengths)
+    q = torch.randn(40, 2, 32, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(40, 2, 32, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 15, 40], dtype=torch.int32)
+    with pytest.raises(ValueError, match="one device"):
+        mat.triangle_attention_varlen(q, k, k.cuda(), cu, cu, 25, 25)
+    torch.cuda.synchronize()
+
+
+def test_unaligned_views_are_copied_not_rejected():
+    """Contiguous views at an offset that is not a multiple of 16 bytes give
+    the same result as aligned copies of the same values."""
+    say("unaligned input views")
+    c = wl.make_case(1, 2, 2, 32, 32, 32, "bf16", "kv_lengths", seed=13).to("cuda")
+    want = mat.triangle_attention(c.q, c.k, c.v, c.bias, kv_lengths=c.kv_lengths)
+    def shifted(t):  # same values, 2 bytes past a 16-byte boundary
+        buf = torch.empty(t.numel() + 8, device=t.device, dtype=t.dtype)
+        view = buf[1:1 + t.numel()].view(t.shape)
+        view.copy_(t)
+        assert view.data_ptr() % 16 != 0
+        return view
+    got = mat.triangle_attention(shifted(c.q), shifted(c.k), shifted(c.v), c.bias,
+                                 kv_lengths=c.kv_lengths)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
 
 
 def test_four_d_inputs_and_side_stream():
