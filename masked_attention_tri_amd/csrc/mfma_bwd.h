@@ -146,9 +146,14 @@ __global__ __launch_bounds__(4 * D) void bwd_rows_kernel(Params p, BwdParams g, 
     for (int64_t w = blockIdx.x; w < total; w += gridDim.x) {
         const int64_t bnh = w / n_t, q = 32 * (w % n_t) + r;
         const bool in = q < p.Q;
-        float acc = 0.f;
+        float acc = 0.f, lse = 0.f, mx = 0.f;
         if (in) {
-            const int64_t off = (bnh * p.Q + q) * D + 8 * c;
+            // the row's lse and max are loaded with its O and dO (every
+            // thread of the row: one request per row), not after the sum
+            const int64_t i = bnh * p.Q + q;
+            lse = g.lse[i];
+            mx = g.mx[i];
+            const int64_t off = i * D + 8 * c;
             const v8 go = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(static_cast<const T*>(g.dout) + off));
             const v8 o = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(static_cast<const T*>(g.out) + off));
 #pragma unroll
@@ -156,18 +161,12 @@ __global__ __launch_bounds__(4 * D) void bwd_rows_kernel(Params p, BwdParams g, 
         }
 #pragma unroll
         for (int s = 1; s < kC; s <<= 1) acc += __shfl_xor(acc, s);
-        bool dead = false;
+        const bool dead = in && mx == kMaskedLogit;
         if (c == 0) {
-            float nl2 = -INFINITY;
-            if (in) {
-                const int64_t i = bnh * p.Q + q;
-                dead = g.mx[i] == kMaskedLogit;
-                nl2 = dead ? __builtin_nanf("") : -g.lse[i] * kLog2e;
-            }
             rows[w * 64 + r] = -acc;
-            rows[w * 64 + 32 + r] = nl2;
+            rows[w * 64 + 32 + r] = !in ? -INFINITY : dead ? __builtin_nanf("") : -lse * kLog2e;
         }
-        const int cnt = __syncthreads_count(dead);
+        const int cnt = __syncthreads_count(dead && c == 0);  // one vote per row
         if (tid == 0) tile_dead[w] = static_cast<uint32_t>(cnt);
     }
 }
