@@ -957,17 +957,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
 template <int D>
 struct DbGeo {
     static constexpr int QW = D <= 64 ? 4 : 2;  // waves along the query rows
-    static constexpr int KW = 2;                // waves along the keys
+    static constexpr int KW = D <= 64 ? 4 : 2;  // waves along the keys
     static constexpr int waves = QW * KW;
-    static constexpr int slots = D <= 64 ? 3 : 2;
+    static constexpr int slots = 2;
     static constexpr int rowsQ = 32 * QW, rowsK = 32 * KW;
     static constexpr int tileBytes = BGeo<D>::tileBytes;
     // one n: QW tiles of Q, QW of dO, KW of K, KW of V
     static constexpr int slotBytes = (2 * QW + 2 * KW) * tileBytes;
     static constexpr int dmaPerWave = slotBytes / 1024 / waves;
     static_assert(dmaPerWave * waves * 1024 == slotBytes, "DMAs split evenly over the waves");
-    static constexpr int infoBytes = rowsQ * 8;  // row data (QW tiles of 256 bytes): 128 per wave
-    static_assert(infoBytes == 128 * waves, "one 8-lane DMA of row data per wave");
+    static constexpr int infoBytes = rowsQ * 8;  // row data (QW tiles of 256 bytes)
+    static constexpr int infoWaves = infoBytes / 128;  // waves issuing an 8-lane row-data DMA
+    static_assert(infoWaves >= 1 && infoWaves <= waves, "row data in 128-byte pieces");
+    static constexpr int keyWords = rowsK / 64;  // 64-bit validity words per n
 };
 
 template <typename T, int D, int KIND>
@@ -981,15 +983,16 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
     constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
     constexpr bool kLens = KIND == TRIATTN_MASK_KV_LENGTHS;
     constexpr int R = G::slots;
-    constexpr int kPer = G::dmaPerWave + 1;  // DMAs per wave and n (with the row data)
+    static_assert(R == 2, "every position waits for all DMAs (counts differ between waves)");
     __shared__ __attribute__((aligned(1024))) char t_lds[R][G::slotBytes];
     __shared__ __attribute__((aligned(1024))) char r_lds[R][G::infoBytes];
-    // Bit i of valid_w[m - c0]: key k0 + i valid for n = m, for a chunk of n
+    // Bit i of valid_w[(m - c0) keyWords + i / 64]: key k0 + i valid for n =
+    // m, for a chunk of n
     // starting at c0.  Built before the ring starts, so that the loop issues
     // no memory load besides the DMAs (a wait for such a load would also wait
     // for the DMAs issued before it).
     constexpr int kChunkN = 512;
-    __shared__ uint64_t valid_w[kChunkN];
+    __shared__ uint64_t valid_w[kChunkN * G::keyWords];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1028,27 +1031,34 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
             for (int e = 0; e < 4; ++e) cb[4 * gg + e] = bload32(b_rsrc, base + 4u * (8 * gg + e)) * inv_s;
     }
 
-    // key validity words of n = c0 .. c1 - 1 (the workgroup's 64 keys)
+    // key validity words of n = c0 .. c1 - 1 (the workgroup's rowsK keys)
     int c0 = n_begin, c1 = n_begin;
     auto fill_valid = [&]() {
-        for (int i = tid; i < c1 - c0; i += 64 * G::waves) {
-            const int m = c0 + i;
+        for (int i = tid; i < (c1 - c0) * G::keyWords; i += 64 * G::waves) {
+            const int m = c0 + i / G::keyWords;
+            const int kb = k0 + 64 * (i % G::keyWords);  // first key of the word
             uint64_t word = ~0ull;
             if constexpr (kLens) {
                 if (p.kv_lengths) {
                     const int64_t len = p.kv_lengths[b * p.N + m];
                     const int lim = len < 0 ? 0 : (len > K ? K : static_cast<int>(len));
-                    const int rel = lim - k0;
+                    const int rel = lim - kb;
                     word = rel >= 64 ? ~0ull : rel <= 0 ? 0ull : (1ull << rel) - 1ull;
                 }
             } else if constexpr (kDense) {
                 const uint8_t* drow = p.dense + (b * p.N + m) * p.K;
                 word = 0ull;
-                for (int j = 0; j < 64 && k0 + j < K; ++j)
-                    if (drow[k0 + j] != 0) word |= 1ull << j;
+                for (int j = 0; j < 64 && kb + j < K; ++j)
+                    if (drow[kb + j] != 0) word |= 1ull << j;
             }
             valid_w[i] = word;
         }
+    };
+    auto any_valid = [&](int m) {
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < G::keyWords; ++j) any = any || valid_w[(m - c0) * G::keyWords + j] != 0ull;
+        return any;
     };
     // first n >= m0 of the chunk with a valid key, or -1
     auto next_n = [&](int m0) -> int {
@@ -1058,7 +1068,7 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
         } else {
             for (int base = m0; base < c1; base += 64) {
                 const int m = base + lane;
-                const uint64_t bits = __ballot(m < c1 && valid_w[m - c0] != 0ull);
+                const uint64_t bits = __ballot(m < c1 && any_valid(m));
                 if (bits) return base + static_cast<int>(__builtin_ctzll(bits));
             }
             return -1;
@@ -1099,8 +1109,10 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
             }
         }
         // 128 bytes per wave of the row data of tiles q0 / 32 ..
-        const uint32_t roff = m >= 0 ? static_cast<uint32_t>((q0 / 32) * 256 + 128 * wave + 16 * lane) : kNoTile;
-        if (lane < 8) dma16(dr, (lds_char*)r_lds[x] + 128 * wave, roff);
+        if (wave < G::infoWaves) {
+            const uint32_t roff = m >= 0 ? static_cast<uint32_t>((q0 / 32) * 256 + 128 * wave + 16 * lane) : kNoTile;
+            if (lane < 8) dma16(dr, (lds_char*)r_lds[x] + 128 * wave, roff);
+        }
     };
 
     const int rrd = Ge::row_base(col, half);
@@ -1126,7 +1138,7 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
         for (int st = 0; st < D / 16; ++st)
             dp = M::run(row_operand<v8>(t + v_tile, rrd, st), row_operand<v8>(t + g_tile, rrd, st), dp);
         // keys valid for this n (the ragged tile of a length, the dense mask)
-        const uint32_t w = static_cast<uint32_t>(valid_w[m - c0] >> (32 * kg));
+        const uint32_t w = static_cast<uint32_t>(valid_w[(m - c0) * G::keyWords + kg / 2] >> (32 * (kg % 2)));
         if (w != ~0u) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -1157,8 +1169,8 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
         for (int i = 0; i < R - 1; ++i) dma_n(ns[i], i);
         int x = 0;
         while (ns[0] >= 0) {
-            // every DMA but the last R - 2 positions' has landed
-            __builtin_amdgcn_s_waitcnt(kVmcntWait<kPer * (R - 2)>());
+            // every DMA has landed (the ring of two is loaded one n ahead)
+            wait_vmem();
             __syncthreads();  // slot x landed for every wave; slot x - 1 is free
             dma_n(ns[R - 1], (x + R - 1) % R);
             compute(ns[0], x);

@@ -106,9 +106,9 @@ inline int64_t bwd_rows_bytes(int64_t slices, int64_t Q) {
 }
 
 // Ranges of n the MFMA dBias kernel splits its sum into for a shape: its
-// workgroups cover (32 QW) x 64 (query, key) tiles (QW = 4 for D <= 64, else
-// 2) and there are 256 CUs; the split that fills whole rounds of
-// workgroups best (ties: fewer splits), at most 8 and at least 16 n each.
+// workgroups cover 128 x 128 (query, key) tiles (64 x 64 at D = 128), one
+// resident per CU, and there are 256 CUs; the split that fills whole rounds
+// of workgroups best (ties: fewer splits), at most 8 and at least 16 n each.
 // Each split beyond the first needs a B H Q K fp32 plane of workspace.
 inline int dbias_splits(int64_t B, int64_t N, int64_t H, int64_t Q, int64_t K, int64_t D) {
     if (D != 32 && D != 64 && D != 128) return 1;
@@ -117,10 +117,10 @@ inline int dbias_splits(int64_t B, int64_t N, int64_t H, int64_t Q, int64_t K, i
     if (B < 1 || H < 1 || Q < 1 || K < 1 || N < 1 || B > lim || H > lim || Q > lim || K > lim ||
         B * H > lim)
         return 1;
-    const int64_t rows_q = D <= 64 ? 128 : 64;
+    const int64_t rows_q = D <= 64 ? 128 : 64, rows_k = D <= 64 ? 128 : 64;
     const double tiles = static_cast<double>(B * H) * static_cast<double>((Q - 1) / rows_q + 1) *
-                         static_cast<double>((K - 1) / 64 + 1);
-    const double slots = D == 32 ? 512.0 : 256.0;  // resident workgroups
+                         static_cast<double>((K - 1) / rows_k + 1);
+    const double slots = 256.0;  // resident workgroups: one per CU
     int best = 1;
     double best_eff = 0.0;
     for (int s = 1; s <= 8 && (s == 1 || N / s >= 16); ++s) {
