@@ -23,8 +23,8 @@
 //   bwd_dkdv_kernel   one workgroup per (b, n, h, 128 keys); K and V rows in
 //                     registers; 32-row query tiles of Q, dO and the row data
 //                     by LDS DMA.
-//   bwd_dbias_kernel  one workgroup per (b, h, 128 queries (64 at D = 128),
-//                     64 keys, range of n), walking n: the bias block stays in
+//   bwd_dbias_kernel  one workgroup per (b, h, 128 queries and 128 keys (64 x
+//                     64 at D = 128), range of n), walking n: the bias block stays in
 //                     registers, Q, dO, K and V of each n arrive by LDS DMA,
 //                     dB accumulates in registers; the ranges' sums are added
 //                     in order by bwd_dbias_combine_kernel.
