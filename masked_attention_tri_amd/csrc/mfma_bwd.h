@@ -1191,10 +1191,28 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
     }
 }
 
-// dBias = the sum of the splits' planes, in split order.
+// dBias = the sum of the splits' planes, in split order.  Four elements per
+// thread (16-byte loads of every plane issued together) when the plane size
+// and the pointers allow it; the tail and other shapes one at a time.
+constexpr int kMaxSplits = 8;
 __global__ __launch_bounds__(256) void bwd_dbias_combine_kernel(float* dbias, const float* part,
                                                                 int64_t count, int splits) {
-    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < count; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    const bool vec = splits <= kMaxSplits && count % 4 == 0 && reinterpret_cast<uintptr_t>(part) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(dbias) % 16 == 0;
+    const int64_t n4 = vec ? count / 4 : 0;
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+        f32x4 v[kMaxSplits];
+#pragma unroll
+        for (int j = 0; j < kMaxSplits; ++j)
+            if (j < splits) v[j] = reinterpret_cast<const f32x4*>(part + j * count)[i];
+        f32x4 s = v[0];
+#pragma unroll
+        for (int j = 1; j < kMaxSplits; ++j)
+            if (j < splits) s += v[j];
+        reinterpret_cast<f32x4*>(dbias)[i] = s;
+    }
+    for (int64_t i = 4 * n4 + blockIdx.x * 256 + threadIdx.x; i < count; i += stride) {
         float s = part[i];
         for (int j = 1; j < splits; ++j) s += part[j * count + i];
         dbias[i] = s;
@@ -1253,8 +1271,9 @@ hipError_t launch_bwd_kind(const Params& p, const BwdParams& g, bool exact, floa
             if (gb > 0x7fffffff) return hipErrorInvalidConfiguration;
             hipLaunchKernelGGL((bwd_dbias_kernel<T, D, KIND>), dim3(static_cast<unsigned>(gb)),
                                dim3(64 * G::waves), 0, stream, p, g, rows, part, splits);
+            static_assert(kMaxSplits >= 8, "dbias_splits returns at most 8");
             if (splits > 1) {
-                const int64_t want = (plane + 255) / 256;
+                const int64_t want = (plane / 4 + 255) / 256 + 1;
                 const unsigned gc = static_cast<unsigned>(want < 8192 ? want : 8192);
                 hipLaunchKernelGGL(bwd_dbias_combine_kernel, dim3(gc), dim3(256), 0, stream,
                                    g.dbias, part, plane, splits);
