@@ -13,7 +13,11 @@ using tile::scale_is_exact;
 
 bool mfma_supports(const Params& p, int32_t dtype) {
     if (dtype != TRIATTN_BF16 && dtype != TRIATTN_F16) return false;
-    if (p.D != 32 && p.D != 64 && p.D != 128 && p.D != 256) return false;
+    // Any multiple of 8 up to 256 runs on the tiles of the next width of 32,
+    // 64, 128 or 256 (zero columns); packed sequences take those widths only.
+    if (p.D % 8 != 0 || p.D < 8 || p.D > 256) return false;
+    if (p.mask_kind == kMaskVarlen && p.D != 32 && p.D != 64 && p.D != 128 && p.D != 256)
+        return false;
     // a 16-bit bias goes by DMA: its rows must be 16-byte aligned
     if (p.bias16 && (p.K % 8 != 0 || reinterpret_cast<uintptr_t>(p.bias16) % 16 != 0))
         return false;
@@ -64,16 +68,10 @@ bool bwd_mfma_supports(const Params& p, int32_t dtype) {
 
 hipError_t launch_mfma(const Params& p, int32_t dtype, hipStream_t stream) {
     const bool exact = scale_is_exact(p.scale);
-    switch (p.D) {
-    case 32:
-        return launch_mfma_d32(p, dtype, exact, stream);
-    case 64:
-        return launch_mfma_d64(p, dtype, exact, stream);
-    case 128:
-        return launch_mfma_d128(p, dtype, exact, stream);
-    case 256:
-        return launch_mfma_d256(p, dtype, exact, stream);
-    }
+    if (p.D <= 32) return launch_mfma_d32(p, dtype, exact, stream);
+    if (p.D <= 64) return launch_mfma_d64(p, dtype, exact, stream);
+    if (p.D <= 128) return launch_mfma_d128(p, dtype, exact, stream);
+    if (p.D <= 256) return launch_mfma_d256(p, dtype, exact, stream);
     return hipErrorInvalidValue;
 }
 

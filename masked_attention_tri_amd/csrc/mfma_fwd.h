@@ -107,7 +107,7 @@ constexpr int min_waves_per_simd() {
     return D <= 64 ? 4 : D <= 128 ? 2 : 1;
 }
 
-template <typename T, int D, int KIND, int BIAS, bool EXACT, int W>
+template <typename T, int D, int KIND, int BIAS, bool EXACT, int W, bool PAD>
 __global__ __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>()))) void mfma_fwd_kernel(Params p) {
     using M = Mma<T>;
@@ -189,10 +189,16 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         k_first = sr.k0;
         if (qt * kQTile >= Q) return;  // the whole workgroup is past this sequence
     }
-    const int64_t kv_rs = kVarlen ? p.kv_rs : D;  // K / V row stride (elements)
+    // Dn: the head dimension of the data, D that of the tiles (with PAD, Dn <
+    // D, a multiple of 8; without, and for packed sequences, Dn = D, so that
+    // every test of it below folds away).  Columns Dn .. D-1 of Q, K and V
+    // enter the tiles as zeros: they add nothing to Q.K, and the O columns
+    // they produce are not stored.
+    const int Dn = (PAD && !kVarlen) ? static_cast<int>(p.D) : D;
+    const int64_t kv_rs = kVarlen ? p.kv_rs : Dn;  // K / V row stride (elements)
     const uint32_t kv_row_bytes = static_cast<uint32_t>(kv_rs * sizeof(T));
-    const T* kbase = static_cast<const T*>(p.k) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * D);
-    const T* vbase = static_cast<const T*>(p.v) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * D);
+    const T* kbase = static_cast<const T*>(p.k) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * Dn);
+    const T* vbase = static_cast<const T*>(p.v) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * Dn);
     const char* bslice =
         BIAS == kNoBias ? nullptr
                         : static_cast<const char*>(BIAS == kBiasLdsHalf ? p.bias16
@@ -265,11 +271,16 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     v8 qop[D / 16];
     {
         const T* qp = static_cast<const T*>(p.q) +
-                      (kVarlen ? (q_first + qload) * p.q_rs + h * D : (bnh * p.Q + qload) * D) +
+                      (kVarlen ? (q_first + qload) * p.q_rs + h * D : (bnh * p.Q + qload) * Dn) +
                       8 * half;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            v8 x = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(qp + 16 * st));
+            // this lane's 8 columns 16 st + 8 half ..; zeros past Dn (the
+            // load is unconditional, from the row's first columns there, so
+            // that the four loads stay in flight together)
+            const bool in_row = 16 * st + 8 * half < Dn;
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(qp + (in_row ? 16 * st : -8 * half));
+            v8 x = __builtin_bit_cast(v8, in_row ? raw : u32x4{0u, 0u, 0u, 0u});
             if (EXACT) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) x[j] = static_cast<T>(static_cast<float>(x[j]) * p.scale);
@@ -281,7 +292,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     // ---- LDS regions and DMA address tables ------------------------------
     // rows past K read as zeros (the buffer range check)
     const uint32_t kv_bytes = kVarlen ? static_cast<uint32_t>(K) * kv_row_bytes
-                                      : static_cast<uint32_t>(p.K * D * sizeof(T));
+                                      : static_cast<uint32_t>(p.K * Dn * sizeof(T));
     const uint32_t kv_tile_bytes = kKTile * kv_row_bytes;  // one tile of K or V rows in memory
     const uint32_t bias_bytes = BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * kBiasElem) : 0u;
     const u32x4 k_desc = make_desc(kbase, kv_bytes);
@@ -299,6 +310,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     // source chunk (s % chunks) ^ f(row).  Every wave issues its
     // instructions for every position, with kNoTile when there is no tile,
     // so the count of DMAs in flight per position is fixed.
+    // A source chunk at or past Dn / 8 (columns the data does not have)
+    // reads at kNoTile and lands as zeros; with a tile offset added the sum
+    // stays in [2^31, 2^32), past every slice.  (For kNoTile tiles it wraps,
+    // filling a buffer that no one reads, from inside the slice.)
     uint32_t kv_src[kDmaPerWave];
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
@@ -306,8 +321,8 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         const bool is_v = I >= Ge::kDma;
         const int s = 64 * (I % Ge::kDma) + lane;
         const int r = s / Ge::chunks, c = s % Ge::chunks;
-        kv_src[j] = static_cast<uint32_t>(r * kv_row_bytes +
-                                          16 * (c ^ (is_v ? Ge::fv(r) : Ge::fk(r))));
+        const int sc = c ^ (is_v ? Ge::fv(r) : Ge::fk(r));
+        kv_src[j] = 8 * sc < Dn ? static_cast<uint32_t>(r * kv_row_bytes + 16 * sc) : kNoTile;
     }
     auto dma_k = [&](int t, int x) {
         const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * kv_tile_bytes : kNoTile;
@@ -723,7 +738,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         constexpr int kPhases = kThreads / kChunks;
         const int c = tid % kChunks, ph = tid / kChunks;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int kk = ph; kk < K; kk += kPhases) {
+        for (int kk = ph; kk < K && 8 * c < Dn; kk += kPhases) {
             const v8 x = __builtin_bit_cast(
                 v8, *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(kk) * kv_rs + 8 * c));
 #pragma unroll
@@ -750,13 +765,14 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     }
     if (!row_ok) return;
     T* orow = static_cast<T*>(p.out) +
-              (kVarlen ? ((q_first + qrow) * p.H + h) * D : (bnh * p.Q + qrow) * D);
+              (kVarlen ? ((q_first + qrow) * p.H + h) * D : (bnh * p.Q + qrow) * Dn);
     const float inv = dead ? 0.f : 1.0f / l_tot;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int d0 = 32 * db + 8 * g + 4 * half;
+            if (d0 >= Dn) continue;  // a padding column (Dn is a multiple of 8)
             T o4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -788,12 +804,25 @@ hipError_t launch_bias(const Params& p, bool exact, hipStream_t stream) {
     const int64_t groups = p.B * p.N * p.H * n_qt;
     if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(groups));
+    // head dimensions between the tile widths take the padded instantiation
+    // (packed sequences come at the tile widths only)
+    if constexpr (KIND != kMaskVarlen) {
+        if (p.D != D) {
+            if (exact)
+                hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, W, true>), grid,
+                                   dim3(64 * W), 0, stream, p);
+            else
+                hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false, W, true>), grid,
+                                   dim3(64 * W), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
     if (exact)
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, W>), grid, dim3(64 * W), 0,
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, W, false>), grid, dim3(64 * W), 0,
                            stream, p);
     else
-        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false, W>), grid, dim3(64 * W), 0,
-                           stream, p);
+        hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false, W, false>), grid, dim3(64 * W),
+                           0, stream, p);
     return hipGetLastError();
 }
 

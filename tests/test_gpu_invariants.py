@@ -78,6 +78,9 @@ def test_run_to_run_determinism(key):
      {"q_block": 128, "kv_block": 64, "mask_mod": "causal"}),
     ("f16", 128, "block", (2, 1, 2, 640, 600), {"q_block": 128, "kv_block": 128}),
     ("bf16", 256, "kv_lengths", (1, 3, 2, 300, 200), {"len_range": (0, 200)}),
+    # widths between the MFMA tiles: every one of the D columns is stored
+    ("bf16", 96, "kv_lengths", (1, 3, 2, 300, 200), {"len_range": (0, 200)}),
+    ("f16", 200, "dense", (1, 2, 2, 131, 77), {}),
 ])
 def test_every_output_element_is_written(dt, D, kind, shape, extra):
     say(f"NaN-prefilled outputs {dt} D={D} {kind} {shape}")

@@ -106,20 +106,33 @@ MFMA_CASES = [
     (2, 1, 2, 64, 100, 256, "bf16", "none", {"bias": False, "scale": 0.3}),
 ]
 
-GENERIC_CASES = [
+# head dimensions between the MFMA widths (multiples of 8): the MFMA kernel
+# at the next width of 32, 64, 128 or 256, the extra columns zero
+PADDED_D_CASES = [
     (2, 2, 3, 37, 29, 8, "bf16", "kv_lengths", {}),
     (1, 2, 2, 50, 70, 24, "f16", "dense", {}),
     (1, 2, 2, 33, 41, 40, "bf16", "none", {}),
     (1, 2, 1, 20, 130, 120, "f16", "kv_lengths", {}),
+    (1, 3, 2, 150, 200, 96, "bf16", "kv_lengths", {"len_range": (0, 200)}),
+    (1, 2, 2, 130, 131, 72, "f16", "none", {}),  # K % 4 != 0: per-lane bias loads
+    (1, 2, 2, 256, 320, 48, "bf16", "block", {"q_block": 128, "kv_block": 64,
+                                               "mask_mod": "causal"}),
+    (1, 2, 2, 100, 100, 200, "bf16", "dense", {"p_valid": 0.02}),  # rows with no valid key
+    (1, 2, 2, 90, 90, 56, "bf16", "none", {"scale": 0.3}),
+    (1, 2, 2, 40, 33, 192, "f16", "dense", {}),
+]
+
+# the generic kernel: fp32 inputs, and block masks whose query blocks are
+# not whole 128-row tiles
+GENERIC_CASES = [
     (2, 2, 2, 40, 37, 16, "bf16", "block", {"q_block": 16, "kv_block": 8, "mask_mod": "causal"}),
     (1, 2, 2, 64, 64, 64, "bf16", "block", {"q_block": 32, "kv_block": 32}),
     (2, 3, 2, 19, 23, 12, "f32", "dense", {}),
     (1, 2, 2, 40, 40, 32, "f32", "kv_lengths", {"len_range": (-2, 45)}),
     (1, 1, 2, 30, 30, 4, "f32", "block", {"q_block": 8, "kv_block": 4, "mask_mod": "causal"}),
     (1, 2, 2, 9, 1, 32, "f32", "none", {}),
-    # head dimensions past 128 (half types, up to 256)
+    # D = 256 (half types)
     (1, 2, 2, 70, 90, 256, "bf16", "kv_lengths", {}),
-    (1, 2, 2, 40, 33, 192, "f16", "dense", {}),
     (1, 2, 2, 30, 50, 256, "bf16", "dense", {"p_valid": 0.02}),
     (1, 1, 2, 64, 64, 136, "bf16", "block", {"q_block": 32, "kv_block": 16, "mask_mod": "causal"}),
 ]
@@ -131,8 +144,8 @@ def _case_id(c):
         f"{k}" for k in extra) if extra else "")
 
 
-@pytest.mark.parametrize("spec", MFMA_CASES + GENERIC_CASES,
-                         ids=[_case_id(c) for c in MFMA_CASES + GENERIC_CASES])
+@pytest.mark.parametrize("spec", MFMA_CASES + PADDED_D_CASES + GENERIC_CASES,
+                         ids=[_case_id(c) for c in MFMA_CASES + PADDED_D_CASES + GENERIC_CASES])
 @pytest.mark.parametrize("seed", [1, 2])
 def test_random_shapes(spec, seed):
     B, N, H, Q, K, D, dt, kind, extra = spec
@@ -176,7 +189,7 @@ HALF_BIAS_CASES = [
                                                 "mask_mod": "causal"}),
     (1, 2, 2, 100, 160, 256, "f16", "none", {"scale": 0.3}),
     (2, 2, 2, 100, 100, 64, "bf16", "none", {}),      # K % 8 != 0: the generic kernel
-    (1, 2, 2, 70, 88, 40, "bf16", "kv_lengths", {}),  # no MFMA kernel at D = 40
+    (1, 2, 2, 70, 88, 40, "bf16", "kv_lengths", {}),  # D = 40 on the width-64 tiles
 ]
 
 
