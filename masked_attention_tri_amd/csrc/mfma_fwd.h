@@ -1,4 +1,6 @@
-// MFMA forward kernel for bf16 / fp16 inputs, D in {32, 64, 128, 256}.
+// MFMA forward kernel for bf16 / fp16 inputs: tiles of width D in {32, 64,
+// 128, 256}, serving every head dimension that is a multiple of 8 up to 256
+// (those between the widths through the PAD instantiations, zero columns).
 //
 // Computes the triangle_attention page's equation: per (b, n, h) row,
 // O_q = sum_k softmax_k(s Q_q.K_k + B_qk, masked keys excluded) V_k, with the
