@@ -584,8 +584,8 @@ hipError_t launch_t(const Params& p, const BwdParams& g, bool dbias_only, hipStr
 hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
                       size_t ws_bytes, hipStream_t stream) {
     if (bwd_mfma_supports(p, dtype)) {
-        hipError_t e = p.D == 32   ? launch_bwd_mfma_d32(p, g, dtype, ws, ws_bytes, stream)
-                       : p.D == 64 ? launch_bwd_mfma_d64(p, g, dtype, ws, ws_bytes, stream)
+        hipError_t e = p.D <= 32   ? launch_bwd_mfma_d32(p, g, dtype, ws, ws_bytes, stream)
+                       : p.D <= 64 ? launch_bwd_mfma_d64(p, g, dtype, ws, ws_bytes, stream)
                                    : launch_bwd_mfma_d128(p, g, dtype, ws, ws_bytes, stream);
         if (e != hipSuccess) return e;
         // dBias of a block-sparse mask: the general walk over n

@@ -43,7 +43,9 @@ bool mfma_supports(const Params& p, int32_t dtype) {
 
 bool bwd_mfma_supports(const Params& p, int32_t dtype) {
     if (dtype != TRIATTN_BF16 && dtype != TRIATTN_F16) return false;
-    if (p.D != 32 && p.D != 64 && p.D != 128) return false;
+    // any multiple of 8 up to 128, on the tiles of the next width of 32, 64
+    // or 128 (zero columns)
+    if (p.D % 8 != 0 || p.D < 8 || p.D > 128) return false;
     if (p.mask_kind != TRIATTN_MASK_NONE && p.mask_kind != TRIATTN_MASK_KV_LENGTHS &&
         p.mask_kind != TRIATTN_MASK_DENSE && p.mask_kind != TRIATTN_MASK_BLOCK)
         return false;

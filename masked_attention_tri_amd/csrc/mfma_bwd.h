@@ -97,7 +97,27 @@ struct BGeo {
         const int r = s / chunks, c = s % chunks;
         return static_cast<uint32_t>(r * rowBytes + 16 * (c ^ f(r)));
     }
+    // The same for rows of dn <= D elements in memory (dn a multiple of 8):
+    // a source chunk at or past dn / 8 reads at kNoTile and lands as zeros
+    // (with a tile offset added the sum stays in [2^31, 2^32), past every
+    // slice).  With dn = D it is dma_src.
+    static __device__ __forceinline__ uint32_t dma_src(int i, int lane, int dn) {
+        const int s = 64 * i + lane;
+        const int r = s / chunks, c = s % chunks;
+        const int sc = c ^ f(r);
+        return 8 * sc < dn ? static_cast<uint32_t>(r * 2 * dn + 16 * sc) : kNoTile;
+    }
 };
+
+// Eight elements of a row at column c0 (a multiple of 8) of a row of dn
+// elements, zeros at and past dn; the load is unconditional (from the row's
+// first columns there) so that several stay in flight together.
+template <typename V, typename T>
+__device__ __forceinline__ V load8_or_zero(const T* row, int c0, int dn) {
+    const bool in_row = c0 < dn;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(row + (in_row ? c0 : 0));
+    return __builtin_bit_cast(V, in_row ? raw : u32x4{0u, 0u, 0u, 0u});
+}
 
 // The A operand of an accumulating product from a tile: rows 16 st + 4 half
 // + 0..3 and 16 st + 8 + 4 half + 0..3 of column 32 jb + lane % 32, i.e. the
@@ -135,7 +155,7 @@ __device__ __forceinline__ void store4(T* dst, float a, float b, float c, float 
 // Workspace bytes: 260 per (slice, tile) (bwd_rows_bytes).  One workgroup of
 // 32 (D / 8) threads per tile: thread (r, c) takes the 16-byte chunk c of row
 // r; shuffles sum the D / 8 partial products.
-template <typename T, int D>
+template <typename T, int D, bool PAD>
 __global__ __launch_bounds__(4 * D) void bwd_rows_kernel(Params p, BwdParams g, float* rows,
                                                          uint32_t* tile_dead) {
     using v8 = typename Mma<T>::v8;
@@ -153,9 +173,11 @@ __global__ __launch_bounds__(4 * D) void bwd_rows_kernel(Params p, BwdParams g, 
             const int64_t i = bnh * p.Q + q;
             lse = g.lse[i];
             mx = g.mx[i];
-            const int64_t off = i * D + 8 * c;
-            const v8 go = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(static_cast<const T*>(g.dout) + off));
-            const v8 o = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(static_cast<const T*>(g.out) + off));
+            // (rows of Dn elements; with PAD the columns past Dn are zeros)
+            const int Dn = PAD ? static_cast<int>(p.D) : D;
+            const int64_t off = i * Dn;
+            const v8 go = load8_or_zero<v8>(static_cast<const T*>(g.dout) + off, 8 * c, Dn);
+            const v8 o = load8_or_zero<v8>(static_cast<const T*>(g.out) + off, 8 * c, Dn);
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc = fmaf(static_cast<float>(go[e]), static_cast<float>(o[e]), acc);
         }
@@ -231,7 +253,7 @@ enum BwdBias { kBNone = 0, kBLds = 1, kBScalar = 2 };
 // element.  A tile where every element is valid and no row lacks a valid key
 // takes the plain path; otherwise each element selects.  Tiles that no wave
 // needs (unlisted and without rows lacking a valid key) are skipped.
-template <typename T, int D, int KIND, int BIAS, bool EXACT>
+template <typename T, int D, int KIND, int BIAS, bool EXACT, bool PAD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_dkdv_kernel(
     Params p, BwdParams g, const float* rows, const uint32_t* tile_dead) {
     using M = Mma<T>;
@@ -295,15 +317,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
                 (t & 31)) & 1u;
     };
 
-    T* dkb = static_cast<T*>(g.dk) + bnh * p.K * D;
-    T* dvb = static_cast<T*>(g.dv) + bnh * p.K * D;
+    // Dn: the head dimension of the data, D that of the tiles (with PAD, Dn <
+    // D and a multiple of 8: columns past Dn enter as zeros and are not stored)
+    const int Dn = PAD ? static_cast<int>(p.D) : D;
+    T* dkb = static_cast<T*>(g.dk) + bnh * p.K * Dn;
+    T* dvb = static_cast<T*>(g.dv) + bnh * p.K * Dn;
     // Keys past the length with every row having a valid key: nothing to add.
     if (!kBlock && kw0 >= lim && !slice_dead) {
         if (key < K) {
 #pragma unroll
             for (int d = 0; d < D; d += 4) {
-                *reinterpret_cast<u32x2*>(dkb + static_cast<int64_t>(key) * D + d) = u32x2{0u, 0u};
-                *reinterpret_cast<u32x2*>(dvb + static_cast<int64_t>(key) * D + d) = u32x2{0u, 0u};
+                if (d >= Dn) break;
+                *reinterpret_cast<u32x2*>(dkb + static_cast<int64_t>(key) * Dn + d) = u32x2{0u, 0u};
+                *reinterpret_cast<u32x2*>(dvb + static_cast<int64_t>(key) * Dn + d) = u32x2{0u, 0u};
             }
         }
         return;
@@ -379,26 +405,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
     // ---- K, V rows of this lane's key (B operands) --------------------------
     v8 kop[D / 16], vop[D / 16];
     {
-        const T* kr = static_cast<const T*>(p.k) + (bnh * p.K + (key < K ? key : K - 1)) * D + 8 * half;
-        const T* vr = static_cast<const T*>(p.v) + (bnh * p.K + (key < K ? key : K - 1)) * D + 8 * half;
+        const T* kr = static_cast<const T*>(p.k) + (bnh * p.K + (key < K ? key : K - 1)) * Dn;
+        const T* vr = static_cast<const T*>(p.v) + (bnh * p.K + (key < K ? key : K - 1)) * Dn;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            v8 x = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(kr + 16 * st));
+            v8 x = load8_or_zero<v8>(kr, 16 * st + 8 * half, Dn);
             if (EXACT) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) x[j] = static_cast<T>(static_cast<float>(x[j]) * p.scale);
             }
             kop[st] = x;
-            vop[st] = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(vr + 16 * st));
+            vop[st] = load8_or_zero<v8>(vr, 16 * st + 8 * half, Dn);
         }
     }
     const float c_exp = (EXACT ? 1.0f : p.scale) * kLog2e;  // exponent slope of Q.K + C
     const float inv_s = EXACT ? 1.0f : 1.0f / p.scale;      // bias -> units of Q.K
 
     // ---- DMA --------------------------------------------------------------
-    const uint32_t slice_bytes = static_cast<uint32_t>(p.Q * D * sizeof(T));
-    const u32x4 q_desc = make_desc(static_cast<const T*>(p.q) + bnh * p.Q * D, slice_bytes);
-    const u32x4 g_desc = make_desc(static_cast<const T*>(g.dout) + bnh * p.Q * D, slice_bytes);
+    const uint32_t slice_bytes = static_cast<uint32_t>(p.Q * Dn * sizeof(T));
+    const u32x4 q_desc = make_desc(static_cast<const T*>(p.q) + bnh * p.Q * Dn, slice_bytes);
+    const u32x4 g_desc = make_desc(static_cast<const T*>(g.dout) + bnh * p.Q * Dn, slice_bytes);
+    const uint32_t mem_tile = static_cast<uint32_t>(32 * 2 * Dn);  // one tile of rows in memory
     const u32x4 r_desc = make_desc(rows + bnh * nT * 64, static_cast<uint32_t>(nT * 256));
     auto qbuf = [&](int x) { return (lds_char*)(x == 0 ? q_lds0 : x == 1 ? q_lds1 : q_lds2); };
     auto gbuf = [&](int x) { return (lds_char*)(x == 0 ? g_lds0 : x == 1 ? g_lds1 : g_lds2); };
@@ -406,9 +433,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
     // instruction I = wave + 4 j of a tile: Q for I < tileDma, else dO
     uint32_t ring_src[kRingDma];
 #pragma unroll
-    for (int j = 0; j < kRingDma; ++j) ring_src[j] = Ge::dma_src((wave + 4 * j) % Ge::tileDma, lane);
+    for (int j = 0; j < kRingDma; ++j) ring_src[j] = Ge::dma_src((wave + 4 * j) % Ge::tileDma, lane, Dn);
     auto dma_ring = [&](int t, int x) {
-        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * Ge::tileBytes : kNoTile;
+        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * mem_tile : kNoTile;
 #pragma unroll
         for (int j = 0; j < kRingDma; ++j) {
             const int I = wave + 4 * j;
@@ -591,13 +618,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
 
     // ---- epilogue: lane = key, register r = column 32 jb + 8 (r / 4) + 4 half + r % 4
     if (key >= K) return;
-    T* dkr = dkb + static_cast<int64_t>(key) * D;
-    T* dvr = dvb + static_cast<int64_t>(key) * D;
+    T* dkr = dkb + static_cast<int64_t>(key) * Dn;
+    T* dvr = dvb + static_cast<int64_t>(key) * Dn;
 #pragma unroll
     for (int jb = 0; jb < D / 32; ++jb)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int d0 = 32 * jb + 8 * c + 4 * half;
+            if (d0 >= Dn) continue;  // a padding column
             store4(dkr + d0, ak[jb][4 * c] * p.scale, ak[jb][4 * c + 1] * p.scale,
                    ak[jb][4 * c + 2] * p.scale, ak[jb][4 * c + 3] * p.scale);
             store4(dvr + d0, av[jb][4 * c], av[jb][4 * c + 1], av[jb][4 * c + 2], av[jb][4 * c + 3]);
@@ -620,7 +648,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
 // takes dz as the B operand.  Masks as in the forward kernel: tiles past
 // the length or not listed are not visited, element masks only where a tile
 // needs one.
-template <typename T, int D, int KIND, int BIAS, bool EXACT>
+template <typename T, int D, int KIND, int BIAS, bool EXACT, bool PAD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_dq_kernel(
     Params p, BwdParams g) {
     using M = Mma<T>;
@@ -711,24 +739,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
     };
 
     // ---- this lane's row: Q (B operand), dO (B operand), Delta, -lse log2 e
+    // Dn: the head dimension of the data, D that of the tiles (with PAD, Dn <
+    // D and a multiple of 8: columns past Dn enter as zeros and are not stored)
+    const int Dn = PAD ? static_cast<int>(p.D) : D;
     v8 qop[D / 16], gop[D / 16];
     float delta = 0.f;
     {
-        const int64_t roff = (bnh * p.Q + qload) * D + 8 * half;
+        const int64_t roff = (bnh * p.Q + qload) * Dn;
         const T* qp = static_cast<const T*>(p.q) + roff;
         const T* gp = static_cast<const T*>(g.dout) + roff;
         const T* op = static_cast<const T*>(g.out) + roff;
         float part = 0.f;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
-            v8 x = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(qp + 16 * st));
+            const int c0 = 16 * st + 8 * half;
+            v8 x = load8_or_zero<v8>(qp, c0, Dn);
             if (EXACT) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) x[j] = static_cast<T>(static_cast<float>(x[j]) * p.scale);
             }
             qop[st] = x;
-            gop[st] = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(gp + 16 * st));
-            const v8 o = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(op + 16 * st));
+            gop[st] = load8_or_zero<v8>(gp, c0, Dn);
+            const v8 o = load8_or_zero<v8>(op, c0, Dn);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
                 part = fmaf(static_cast<float>(gop[st][j]), static_cast<float>(o[j]), part);
@@ -742,16 +774,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
     const float inv_s = EXACT ? 1.0f : 1.0f / p.scale;
 
     // ---- DMA ----------------------------------------------------------------
-    const uint32_t kv_bytes = static_cast<uint32_t>(p.K * D * sizeof(T));
-    const u32x4 k_desc = make_desc(static_cast<const T*>(p.k) + bnh * p.K * D, kv_bytes);
-    const u32x4 v_desc = make_desc(static_cast<const T*>(p.v) + bnh * p.K * D, kv_bytes);
+    const uint32_t kv_bytes = static_cast<uint32_t>(p.K * Dn * sizeof(T));
+    const u32x4 k_desc = make_desc(static_cast<const T*>(p.k) + bnh * p.K * Dn, kv_bytes);
+    const u32x4 v_desc = make_desc(static_cast<const T*>(p.v) + bnh * p.K * Dn, kv_bytes);
+    const uint32_t mem_tile = static_cast<uint32_t>(32 * 2 * Dn);  // one tile of rows in memory
     auto kbuf = [&](int x) { return (lds_char*)(x == 0 ? k_lds0 : x == 1 ? k_lds1 : k_lds2); };
     auto vbuf = [&](int x) { return (lds_char*)(x == 0 ? v_lds0 : x == 1 ? v_lds1 : v_lds2); };
     uint32_t kv_src[kKvDma];
 #pragma unroll
-    for (int j = 0; j < kKvDma; ++j) kv_src[j] = Ge::dma_src((wave + 4 * j) % Ge::tileDma, lane);
+    for (int j = 0; j < kKvDma; ++j) kv_src[j] = Ge::dma_src((wave + 4 * j) % Ge::tileDma, lane, Dn);
     auto dma_kv = [&](int t, int x) {
-        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * Ge::tileBytes : kNoTile;
+        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * mem_tile : kNoTile;
 #pragma unroll
         for (int j = 0; j < kKvDma; ++j) {
             const int I = wave + 4 * j;
@@ -930,12 +963,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
     wait_vmem();
 
     if (!row_ok) return;
-    T* dqr = static_cast<T*>(g.dq) + (bnh * p.Q + qrow) * D;
+    T* dqr = static_cast<T*>(g.dq) + (bnh * p.Q + qrow) * Dn;
 #pragma unroll
     for (int jb = 0; jb < D / 32; ++jb)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            store4(dqr + 32 * jb + 8 * c + 4 * half, acc[jb][4 * c] * p.scale, acc[jb][4 * c + 1] * p.scale,
+            if (32 * jb + 8 * c + 4 * half < Dn)  // (not a padding column)
+                store4(dqr + 32 * jb + 8 * c + 4 * half, acc[jb][4 * c] * p.scale, acc[jb][4 * c + 1] * p.scale,
                    acc[jb][4 * c + 2] * p.scale, acc[jb][4 * c + 3] * p.scale);
 }
 
@@ -972,7 +1006,7 @@ struct DbGeo {
     static constexpr int keyWords = rowsK / 64;  // 64-bit validity words per n
 };
 
-template <typename T, int D, int KIND>
+template <typename T, int D, int KIND, bool PAD>
 __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params p, BwdParams g,
                                                                         const float* rows,
                                                                         float* part, int splits) {
@@ -1077,17 +1111,20 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
 
     // DMA of one n: instruction I = wave + waves j; tile I / tileDma of the
     // slot (Q tiles, dO tiles, K tiles, V tiles), piece I % tileDma
+    // (rows of Dn elements in memory; with PAD the columns past Dn are zeros)
+    const int Dn = PAD ? static_cast<int>(p.D) : D;
+    const uint32_t mem_row = static_cast<uint32_t>(2 * Dn);
     uint32_t src[G::dmaPerWave];
 #pragma unroll
-    for (int j = 0; j < G::dmaPerWave; ++j) src[j] = Ge::dma_src((wave + G::waves * j) % Ge::tileDma, lane);
-    const uint32_t qbytes = static_cast<uint32_t>(p.Q * D * sizeof(T));
-    const uint32_t kbytes = static_cast<uint32_t>(p.K * D * sizeof(T));
+    for (int j = 0; j < G::dmaPerWave; ++j) src[j] = Ge::dma_src((wave + G::waves * j) % Ge::tileDma, lane, Dn);
+    const uint32_t qbytes = static_cast<uint32_t>(p.Q * Dn * sizeof(T));
+    const uint32_t kbytes = static_cast<uint32_t>(p.K * Dn * sizeof(T));
     auto dma_n = [&](int m, int x) {
         const int64_t bnh = (b * p.N + (m >= 0 ? m : 0)) * p.H + h;
-        const u32x4 dq = make_desc(static_cast<const T*>(p.q) + bnh * p.Q * D, qbytes);
-        const u32x4 dg = make_desc(static_cast<const T*>(g.dout) + bnh * p.Q * D, qbytes);
-        const u32x4 dk = make_desc(static_cast<const T*>(p.k) + bnh * p.K * D, kbytes);
-        const u32x4 dv = make_desc(static_cast<const T*>(p.v) + bnh * p.K * D, kbytes);
+        const u32x4 dq = make_desc(static_cast<const T*>(p.q) + bnh * p.Q * Dn, qbytes);
+        const u32x4 dg = make_desc(static_cast<const T*>(g.dout) + bnh * p.Q * Dn, qbytes);
+        const u32x4 dk = make_desc(static_cast<const T*>(p.k) + bnh * p.K * Dn, kbytes);
+        const u32x4 dv = make_desc(static_cast<const T*>(p.v) + bnh * p.K * Dn, kbytes);
         const u32x4 dr = make_desc(rows + bnh * n_t32 * 64, static_cast<uint32_t>(n_t32 * 256));
 #pragma unroll
         for (int j = 0; j < G::dmaPerWave; ++j) {
@@ -1095,16 +1132,16 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
             const int tile = I / Ge::tileDma;
             lds_char* dst = (lds_char*)t_lds[x] + 1024 * I;
             if (tile < G::QW) {
-                const uint32_t o = static_cast<uint32_t>(q0 + 32 * tile) * Ge::rowBytes + src[j];
+                const uint32_t o = static_cast<uint32_t>(q0 + 32 * tile) * mem_row + src[j];
                 dma16(dq, dst, m >= 0 ? o : kNoTile);
             } else if (tile < 2 * G::QW) {
-                const uint32_t o = static_cast<uint32_t>(q0 + 32 * (tile - G::QW)) * Ge::rowBytes + src[j];
+                const uint32_t o = static_cast<uint32_t>(q0 + 32 * (tile - G::QW)) * mem_row + src[j];
                 dma16(dg, dst, m >= 0 ? o : kNoTile);
             } else if (tile < 2 * G::QW + G::KW) {
-                const uint32_t o = static_cast<uint32_t>(k0 + 32 * (tile - 2 * G::QW)) * Ge::rowBytes + src[j];
+                const uint32_t o = static_cast<uint32_t>(k0 + 32 * (tile - 2 * G::QW)) * mem_row + src[j];
                 dma16(dk, dst, m >= 0 ? o : kNoTile);
             } else {
-                const uint32_t o = static_cast<uint32_t>(k0 + 32 * (tile - 2 * G::QW - G::KW)) * Ge::rowBytes + src[j];
+                const uint32_t o = static_cast<uint32_t>(k0 + 32 * (tile - 2 * G::QW - G::KW)) * mem_row + src[j];
                 dma16(dv, dst, m >= 0 ? o : kNoTile);
             }
         }
@@ -1229,12 +1266,21 @@ hipError_t launch_bwd_bias(const Params& p, const BwdParams& g, bool exact, floa
     const int64_t bnh = p.B * p.N * p.H;
     const int64_t gk = bnh * ((p.K + 127) / 128), gq = bnh * ((p.Q + 127) / 128);
     if (gk > 0x7fffffff || gq > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (exact) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, true>), dim3(static_cast<unsigned>(gk)), block, 0, stream, p, g, rows, tdead);
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, true>), dim3(static_cast<unsigned>(gq)), block, 0, stream, p, g);
+    // head dimensions between the tile widths take the padded instantiations
+    const dim3 gdk(static_cast<unsigned>(gk)), gdq(static_cast<unsigned>(gq));
+    const bool pad = p.D != D;
+    if (exact && !pad) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, true, false>), gdk, block, 0, stream, p, g, rows, tdead);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, true, false>), gdq, block, 0, stream, p, g);
+    } else if (!pad) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, false, false>), gdk, block, 0, stream, p, g, rows, tdead);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, false, false>), gdq, block, 0, stream, p, g);
+    } else if (exact) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, true, true>), gdk, block, 0, stream, p, g, rows, tdead);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, true, true>), gdq, block, 0, stream, p, g);
     } else {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, false>), dim3(static_cast<unsigned>(gk)), block, 0, stream, p, g, rows, tdead);
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, false>), dim3(static_cast<unsigned>(gq)), block, 0, stream, p, g);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, false, true>), gdk, block, 0, stream, p, g, rows, tdead);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, false, true>), gdq, block, 0, stream, p, g);
     }
     return hipGetLastError();
 }
@@ -1246,7 +1292,10 @@ hipError_t launch_bwd_kind(const Params& p, const BwdParams& g, bool exact, floa
     float* rows = ws;
     uint32_t* tdead = reinterpret_cast<uint32_t*>(ws + 64 * tiles);
     const unsigned gr = static_cast<unsigned>(tiles < (1 << 20) ? tiles : (1 << 20));
-    hipLaunchKernelGGL((bwd_rows_kernel<T, D>), dim3(gr), dim3(4 * D), 0, stream, p, g, rows, tdead);
+    if (p.D != D)
+        hipLaunchKernelGGL((bwd_rows_kernel<T, D, true>), dim3(gr), dim3(4 * D), 0, stream, p, g, rows, tdead);
+    else
+        hipLaunchKernelGGL((bwd_rows_kernel<T, D, false>), dim3(gr), dim3(4 * D), 0, stream, p, g, rows, tdead);
     hipError_t e;
     if (!p.bias)
         e = launch_bwd_bias<T, D, KIND, kBNone>(p, g, exact, rows, tdead, stream);
@@ -1269,8 +1318,12 @@ hipError_t launch_bwd_kind(const Params& p, const BwdParams& g, bool exact, floa
             const int64_t gb = p.B * p.H * ((p.Q + G::rowsQ - 1) / G::rowsQ) *
                                ((p.K + G::rowsK - 1) / G::rowsK) * splits;
             if (gb > 0x7fffffff) return hipErrorInvalidConfiguration;
-            hipLaunchKernelGGL((bwd_dbias_kernel<T, D, KIND>), dim3(static_cast<unsigned>(gb)),
-                               dim3(64 * G::waves), 0, stream, p, g, rows, part, splits);
+            if (p.D != D)
+                hipLaunchKernelGGL((bwd_dbias_kernel<T, D, KIND, true>), dim3(static_cast<unsigned>(gb)),
+                                   dim3(64 * G::waves), 0, stream, p, g, rows, part, splits);
+            else
+                hipLaunchKernelGGL((bwd_dbias_kernel<T, D, KIND, false>), dim3(static_cast<unsigned>(gb)),
+                                   dim3(64 * G::waves), 0, stream, p, g, rows, part, splits);
             static_assert(kMaxSplits >= 8, "dbias_splits returns at most 8");
             if (splits > 1) {
                 const int64_t want = (plane / 4 + 255) / 256 + 1;

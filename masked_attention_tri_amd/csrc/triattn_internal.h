@@ -109,9 +109,11 @@ inline int64_t bwd_rows_bytes(int64_t slices, int64_t Q) {
 // workgroups cover 128 x 128 (query, key) tiles (64 x 64 at D = 128), one
 // resident per CU, and there are 256 CUs; the split that fills whole rounds
 // of workgroups best (ties: fewer splits), at most 8 and at least 16 n each.
-// Each split beyond the first needs a B H Q K fp32 plane of workspace.
-inline int dbias_splits(int64_t B, int64_t N, int64_t H, int64_t Q, int64_t K, int64_t D) {
-    if (D != 32 && D != 64 && D != 128) return 1;
+// With more than one split, each needs a B H Q K fp32 plane of workspace.
+inline int dbias_splits(int64_t B, int64_t N, int64_t H, int64_t Q, int64_t K, int64_t Dh) {
+    // the tile width that serves head dimension Dh
+    if (Dh % 8 != 0 || Dh < 8 || Dh > 128) return 1;
+    const int64_t D = Dh <= 32 ? 32 : Dh <= 64 ? 64 : 128;
     // (sizes past these the kernels never take; no product below overflows)
     const int64_t lim = int64_t(1) << 31;
     if (B < 1 || H < 1 || Q < 1 || K < 1 || N < 1 || B > lim || H > lim || Q > lim || K > lim ||

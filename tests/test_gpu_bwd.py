@@ -96,6 +96,14 @@ CASES = [
     (1, 2, 2, 96, 70, 64, "bf16", "none", {"scale": 0.3}),
     # s = 0: z is the bias alone
     (1, 3, 2, 64, 64, 64, "f16", "kv_lengths", {"scale": 0.0}),
+    # head dimensions between the tile widths (zero columns on the next width)
+    (1, 3, 2, 130, 150, 96, "bf16", "kv_lengths", {"len_range": (0, 150)}),
+    (1, 2, 2, 100, 90, 24, "f16", "dense", {}),
+    (1, 2, 2, 256, 256, 48, "bf16", "block", {"q_block": 128, "kv_block": 64, "mask_mod": "causal"}),
+    (1, 2, 2, 70, 70, 72, "bf16", "none", {"scale": 0.3}),
+    (1, 2, 2, 64, 64, 120, "f16", "kv_lengths", {"scale": 0.0}),
+    (1, 3, 2, 40, 40, 8, "bf16", "kv_lengths", {}),
+    (1, 48, 2, 128, 128, 40, "bf16", "kv_lengths", {}),  # dBias in ranges of n
 ]
 
 
