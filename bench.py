@@ -30,7 +30,18 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 flop/clk)
 METRIC = "fwd TFLOP/s + % bf16 MFMA peak, triangle attn N=Q=K=768 H=4 D=64"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "masked_attention_tri_amd", "csrc", "mfma_fwd.h")
+# the forward kernel's sources: the kernel and its tile geometry / swizzles
+KERNEL_SRCS = [os.path.join(ROOT, "masked_attention_tri_amd", "csrc", f)
+               for f in ("mfma_fwd.h", "mfma_common.h")]
+
+
+def kernel_source_sha256():
+    """SHA-256 of the forward kernel's sources, concatenated in order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -134,8 +145,7 @@ def traffic_entry(workload):
         return None
     with open(path) as f:
         t = json.load(f)
-    src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if t.get("kernel_source_sha256") != src:
+    if t.get("kernel_source_sha256") != kernel_source_sha256():
         return None
     return t
 

@@ -58,14 +58,18 @@ struct Geo {
     // round-robin to the waves.
     static constexpr int kDma = tileBytes / 1024;
     static_assert(kDma * 1024 == tileBytes, "whole DMA instructions per tile");
-    // K is read 16 bytes per lane down consecutive rows (8 or 16 lanes per
-    // LDS cycle at one chunk): consecutive rows must land on distinct banks.
-    // (At D = 128 and 256 a row is a whole number of 256-byte bank cycles,
-    // so both take the same swizzles.)
+    // K is read 16 bytes per lane down consecutive rows at one chunk.  At
+    // D <= 128 it takes the backward kernels' tile swizzle (rows r, r+4,
+    // r+8, r+12 to distinct chunk groups, a function of r % 16): measured
+    // with the LDS bank-conflict counter, it leaves no conflict at D = 32 and
+    // 64, where the swizzles (r/2 ^ r/8) % 4 and (r + r/8) % 8 left 0.7 and
+    // 0.9 conflict cycles per LDS instruction.  At D = 256 a row is two
+    // 256-byte bank cycles and r % 16 spreads 16 rows over the chunks.
     static __device__ __forceinline__ int fk(int r) {
         static_assert(D == 32 || D == 64 || D == 128 || D == 256, "swizzles defined");
-        if (D == 32) return ((r >> 1) ^ (r >> 3)) & 3;
-        if (D == 64) return (r + (r >> 3)) & 7;
+        if (D == 32) return (r >> 2) & 3;
+        if (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+        if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
         return r & 15;
     }
     // V is read by ds_read_b64_tr_b16: each 16 lanes take 4 consecutive rows
