@@ -327,9 +327,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
         if (key < K) {
 #pragma unroll
             for (int d = 0; d < D; d += 4) {
-                if (d >= Dn) break;
-                *reinterpret_cast<u32x2*>(dkb + static_cast<int64_t>(key) * Dn + d) = u32x2{0u, 0u};
-                *reinterpret_cast<u32x2*>(dvb + static_cast<int64_t>(key) * Dn + d) = u32x2{0u, 0u};
+                if (d < Dn) {  // (not a padding column)
+                    *reinterpret_cast<u32x2*>(dkb + static_cast<int64_t>(key) * Dn + d) = u32x2{0u, 0u};
+                    *reinterpret_cast<u32x2*>(dvb + static_cast<int64_t>(key) * Dn + d) = u32x2{0u, 0u};
+                }
             }
         }
         return;
