@@ -14,10 +14,8 @@ using tile::scale_is_exact;
 bool mfma_supports(const Params& p, int32_t dtype) {
     if (dtype != TRIATTN_BF16 && dtype != TRIATTN_F16) return false;
     // Any multiple of 8 up to 256 runs on the tiles of the next width of 32,
-    // 64, 128 or 256 (zero columns); packed sequences take those widths only.
+    // 64, 128 or 256 (zero columns).
     if (p.D % 8 != 0 || p.D < 8 || p.D > 256) return false;
-    if (p.mask_kind == kMaskVarlen && p.D != 32 && p.D != 64 && p.D != 128 && p.D != 256)
-        return false;
     // a 16-bit bias goes by DMA: its rows must be 16-byte aligned
     if (p.bias16 && (p.K % 8 != 0 || reinterpret_cast<uintptr_t>(p.bias16) % 16 != 0))
         return false;

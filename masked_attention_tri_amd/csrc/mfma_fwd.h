@@ -192,15 +192,14 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         if (qt * kQTile >= Q) return;  // the whole workgroup is past this sequence
     }
     // Dn: the head dimension of the data, D that of the tiles (with PAD, Dn <
-    // D, a multiple of 8; without, and for packed sequences, Dn = D, so that
-    // every test of it below folds away).  Columns Dn .. D-1 of Q, K and V
-    // enter the tiles as zeros: they add nothing to Q.K, and the O columns
-    // they produce are not stored.
-    const int Dn = (PAD && !kVarlen) ? static_cast<int>(p.D) : D;
+    // D, a multiple of 8; without, Dn = D, so that every test of it below
+    // folds away).  Columns Dn .. D-1 of Q, K and V enter the tiles as zeros:
+    // they add nothing to Q.K, and the O columns they produce are not stored.
+    const int Dn = PAD ? static_cast<int>(p.D) : D;
     const int64_t kv_rs = kVarlen ? p.kv_rs : Dn;  // K / V row stride (elements)
     const uint32_t kv_row_bytes = static_cast<uint32_t>(kv_rs * sizeof(T));
-    const T* kbase = static_cast<const T*>(p.k) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * Dn);
-    const T* vbase = static_cast<const T*>(p.v) + (kVarlen ? k_first * kv_rs + h * D : bnh * p.K * Dn);
+    const T* kbase = static_cast<const T*>(p.k) + (kVarlen ? k_first * kv_rs + h * Dn : bnh * p.K * Dn);
+    const T* vbase = static_cast<const T*>(p.v) + (kVarlen ? k_first * kv_rs + h * Dn : bnh * p.K * Dn);
     const char* bslice =
         BIAS == kNoBias ? nullptr
                         : static_cast<const char*>(BIAS == kBiasLdsHalf ? p.bias16
@@ -273,7 +272,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     v8 qop[D / 16];
     {
         const T* qp = static_cast<const T*>(p.q) +
-                      (kVarlen ? (q_first + qload) * p.q_rs + h * D : (bnh * p.Q + qload) * Dn) +
+                      (kVarlen ? (q_first + qload) * p.q_rs + h * Dn : (bnh * p.Q + qload) * Dn) +
                       8 * half;
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) {
@@ -767,7 +766,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     }
     if (!row_ok) return;
     T* orow = static_cast<T*>(p.out) +
-              (kVarlen ? ((q_first + qrow) * p.H + h) * D : (bnh * p.Q + qrow) * Dn);
+              (kVarlen ? ((q_first + qrow) * p.H + h) * Dn : (bnh * p.Q + qrow) * Dn);
     const float inv = dead ? 0.f : 1.0f / l_tot;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -807,17 +806,14 @@ hipError_t launch_bias(const Params& p, bool exact, hipStream_t stream) {
     if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(groups));
     // head dimensions between the tile widths take the padded instantiation
-    // (packed sequences come at the tile widths only)
-    if constexpr (KIND != kMaskVarlen) {
-        if (p.D != D) {
-            if (exact)
-                hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, W, true>), grid,
-                                   dim3(64 * W), 0, stream, p);
-            else
-                hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false, W, true>), grid,
-                                   dim3(64 * W), 0, stream, p);
-            return hipGetLastError();
-        }
+    if (p.D != D) {
+        if (exact)
+            hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, W, true>), grid, dim3(64 * W),
+                               0, stream, p);
+        else
+            hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, false, W, true>), grid, dim3(64 * W),
+                               0, stream, p);
+        return hipGetLastError();
     }
     if (exact)
         hipLaunchKernelGGL((mfma_fwd_kernel<T, D, KIND, BIAS, true, W, false>), grid, dim3(64 * W), 0,

@@ -88,10 +88,12 @@ CASES = [
     ("qkv_packed", "padding", "bf16", 2, 64, [128, 77], None),
     ("kv_packed", "causal", "bf16", 2, 128, [40, 257, 3], [64, 200, 3]),
     ("kv_packed", "padding", "bf16", 3, 32, [10, 90], [300, 45]),
-    # the generic kernel: fp32, and a head dimension without an MFMA kernel
+    # fp32 (the generic kernel), and head dimensions between the tile widths
+    # (the MFMA kernel of the next width, zero columns)
     ("separate", "causal", "f32", 2, 32, [30, 17], [25, 40]),
     ("kv_packed", "padding", "bf16", 2, 40, [33, 64], [70, 12]),
     ("qkv_packed", "causal", "f16", 2, 136, [45, 20], None),
+    ("separate", "no_mask", "bf16", 2, 96, [70, 200], [90, 33]),
 ]
 
 
