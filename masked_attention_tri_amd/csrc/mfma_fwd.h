@@ -296,9 +296,16 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
                                       : static_cast<uint32_t>(p.K * Dn * sizeof(T));
     const uint32_t kv_tile_bytes = kKTile * kv_row_bytes;  // one tile of K or V rows in memory
     const uint32_t bias_bytes = BIAS != kNoBias ? static_cast<uint32_t>(p.Q * p.K * kBiasElem) : 0u;
-    const u32x4 k_desc = make_desc(kbase, kv_bytes);
-    const u32x4 v_desc = make_desc(vbase, kv_bytes);
-    const u32x4 bias_desc = make_desc(bslice, bias_bytes);
+    // A DMA of tile t goes through a descriptor whose base is moved to the
+    // tile and whose size shrinks by as much, so that the range check still
+    // ends where the slice does, and a missing tile (t < 0) gets size 0 and
+    // reads zeros.  The per-lane offsets are then the same for every tile
+    // and the per-tile arithmetic is scalar.
+    auto tile_desc = [](const void* base, uint32_t bytes, int t, uint32_t stride) {
+        t = __builtin_amdgcn_readfirstlane(t);  // wave-uniform already
+        const uint32_t off = t >= 0 ? static_cast<uint32_t>(t) * stride : 0u;
+        return make_desc(static_cast<const char*>(base) + off, t >= 0 ? bytes - off : 0u);
+    };
     const __amdgpu_buffer_rsrc_t bias_rsrc = make_rsrc(bslice, bias_bytes);
     auto kbuf = [&](int x) { return (lds_char*)(x == 0 ? k_lds0 : x == 1 ? k_lds1 : k_lds2); };
     auto vbuf = [&](int x) { return (lds_char*)(x == 0 ? v_lds0 : x == 1 ? v_lds1 : v_lds2); };
@@ -312,9 +319,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     // instructions for every position, with kNoTile when there is no tile,
     // so the count of DMAs in flight per position is fixed.
     // A source chunk at or past Dn / 8 (columns the data does not have)
-    // reads at kNoTile and lands as zeros; with a tile offset added the sum
-    // stays in [2^31, 2^32), past every slice.  (For kNoTile tiles it wraps,
-    // filling a buffer that no one reads, from inside the slice.)
+    // reads at kNoTile and lands as zeros: every slice is under 2^31 bytes.
     uint32_t kv_src[kDmaPerWave];
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
@@ -326,19 +331,19 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         kv_src[j] = 8 * sc < Dn ? static_cast<uint32_t>(r * kv_row_bytes + 16 * sc) : kNoTile;
     }
     auto dma_k = [&](int t, int x) {
-        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * kv_tile_bytes : kNoTile;
+        const u32x4 desc = tile_desc(kbase, kv_bytes, t, kv_tile_bytes);
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j) {
             const int I = wave + kWaves * j;  // wave-uniform
-            if (I < Ge::kDma) dma16(k_desc, kbuf(x) + 1024 * I, kv_src[j] + toff);
+            if (I < Ge::kDma) dma16(desc, kbuf(x) + 1024 * I, kv_src[j]);
         }
     };
     auto dma_v = [&](int t, int x) {
-        const uint32_t toff = t >= 0 ? static_cast<uint32_t>(t) * kv_tile_bytes : kNoTile;
+        const u32x4 desc = tile_desc(vbase, kv_bytes, t, kv_tile_bytes);
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j) {
             const int I = wave + kWaves * j;
-            if (I >= Ge::kDma) dma16(v_desc, vbuf(x) + 1024 * (I - Ge::kDma), kv_src[j] + toff);
+            if (I >= Ge::kDma) dma16(desc, vbuf(x) + 1024 * (I - Ge::kDma), kv_src[j]);
         }
     };
     // Bias DMA: the wave's block is kBiasDma instructions of 8 rows x 128
@@ -352,23 +357,23 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     // 16-bit bias: lane l of instruction j fills row 16j + l/4, stored chunk
     // l%4, from source chunk (l%4) ^ fbh(row) = (l%4) ^ ((l/16 ^ j) % 4).
     const uint32_t bh_row = static_cast<uint32_t>(q0w + (lane >> 2)) * static_cast<uint32_t>(K) * 2u;
-    auto dma_bias = [&](int t) {
+    auto dma_bias = [&](int t) {  // t >= 0
         if (BIAS == kBiasLdsHalf) {
-            const uint32_t toff = static_cast<uint32_t>(t) * kBiasHalfRowBytes;
+            const u32x4 desc = tile_desc(bslice, bias_bytes, t, kBiasHalfRowBytes);
 #pragma unroll
             for (int j = 0; j < kBiasHalfDma; ++j) {
                 const uint32_t rows = static_cast<uint32_t>(16 * j) * static_cast<uint32_t>(K) * 2u;
                 const uint32_t chunk = static_cast<uint32_t>((lane & 3) ^ (((lane >> 4) ^ j) & 3));
-                dma16(bias_desc, bias_lds + 1024 * j, bh_row + rows + 16u * chunk + toff);
+                dma16(desc, bias_lds + 1024 * j, bh_row + rows + 16u * chunk);
             }
             return;
         }
         if (BIAS != kBiasLds) return;
-        const uint32_t toff = static_cast<uint32_t>(t) * kBiasRowBytes;
+        const u32x4 desc = tile_desc(bslice, bias_bytes, t, kBiasRowBytes);
 #pragma unroll
         for (int j = 0; j < kBiasDma; ++j) {
             const uint32_t rows = static_cast<uint32_t>(8 * j) * static_cast<uint32_t>(K) * 4u;
-            dma16(bias_desc, bias_lds + 1024 * j, ((j & 1) ? b_src_odd : b_src_even) + rows + toff);
+            dma16(desc, bias_lds + 1024 * j, ((j & 1) ? b_src_odd : b_src_even) + rows);
         }
     };
     // Bias read into the accumulator layout: register 4g+e is key
@@ -571,10 +576,13 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         const float m3 = vmax(vmax(s[9], s[10]), s[11]);
         const float m4 = vmax(vmax(s[12], s[13]), s[14]);
         float mloc = vmax(vmax(vmax(m0, m1), m2), vmax(vmax(m3, m4), s[15]));
-        mloc = max_halves(mloc);
+        // The two lanes of a row hold 16 keys each; their maxima are combined
+        // only when one of them passes the threshold (the same in both), and
+        // m_true after the loop.
         m_true = vmax(m_true, mloc);
-        const bool raise = mloc > m_thr;  // false while mloc == -inf
-        if (__ballot(raise)) {
+        if (__ballot(mloc > m_thr)) {  // false while mloc == -inf
+            mloc = max_halves(mloc);
+            const bool raise = mloc > m_thr;
             // lanes that do not raise keep alpha = 1 exactly (their m_ref may
             // still be -inf); a raising lane with m_ref = -inf gets alpha = 0
             const float alpha = raise ? __builtin_amdgcn_exp2f((m_ref - mloc) * c_exp) : 1.0f;
@@ -594,14 +602,14 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         // The sum must use the unrounded p: rounding each p to bf16 moves
         // lse by up to ~2^-9, past its tolerance on short rows.
         v8 pop[2];
-        float psum = 0.f;
+        float psum;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * tt + j], c_exp, -mb));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * tt + j + 1], c_exp, -mb));
-                psum += p0 + p1;
+                psum = tt + j == 0 ? p0 + p1 : psum + (p0 + p1);
                 pop[tt][j] = static_cast<T>(p0);
                 pop[tt][j + 1] = static_cast<T>(p1);
             }
@@ -719,6 +727,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
 
     // ---- epilogue ---------------------------------------------------------
     const float l_tot = sum_halves(l_run);
+    m_true = max_halves(m_true);
     const bool dead = m_true == -INFINITY;
     // Does any row of the workgroup lack a valid key?  The flag lives in a K
     // buffer: after this wave's DMAs have landed and every wave has left the

@@ -77,6 +77,9 @@ def test_run_to_run_determinism(key):
     ("bf16", 64, "block", (1, 2, 2, 1024, 1024),
      {"q_block": 128, "kv_block": 64, "mask_mod": "causal"}),
     ("f16", 128, "block", (2, 1, 2, 640, 600), {"q_block": 128, "kv_block": 128}),
+    # sparse block lists (rows with none) at a padded width
+    ("bf16", 120, "block", (1, 2, 2, 300, 250),
+     {"q_block": 128, "kv_block": 32, "block_density": 0.15}),
     ("bf16", 256, "kv_lengths", (1, 3, 2, 300, 200), {"len_range": (0, 200)}),
     # widths between the MFMA tiles: every one of the D columns is stored
     ("bf16", 96, "kv_lengths", (1, 3, 2, 300, 200), {"len_range": (0, 200)}),

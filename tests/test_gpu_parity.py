@@ -122,6 +122,23 @@ PADDED_D_CASES = [
     (1, 2, 2, 40, 33, 192, "f16", "dense", {}),
 ]
 
+# block masks at D = 128 (and a width padded to it): odd and single-tile
+# visited counts, rows with no listed block, ragged Q and K, every bias
+# form, an inexact scale
+BLOCK_D128_CASES = [
+    (1, 2, 2, 256, 300, 128, "bf16", "block", {"q_block": 128, "kv_block": 32,
+                                                "block_density": 0.3}),
+    (1, 2, 2, 200, 96, 128, "f16", "block", {"q_block": 128, "kv_block": 32,
+                                              "block_density": 0.2, "with_full": False}),
+    (1, 1, 2, 256, 256, 128, "bf16", "block", {"q_block": 128, "kv_block": 128,
+                                                "bias": False, "mask_mod": "causal"}),
+    (2, 1, 2, 384, 384, 128, "bf16", "block", {"q_block": 128, "kv_block": 64,
+                                                "mask_mod": "causal", "scale": 0.3}),
+    (1, 2, 2, 256, 200, 104, "bf16", "block", {"q_block": 128, "kv_block": 64,
+                                                "mask_mod": "causal"}),
+    (1, 2, 2, 130, 131, 128, "f16", "block", {"q_block": 128, "kv_block": 32}),  # scalar bias
+]
+
 # the generic kernel: fp32 inputs, and block masks whose query blocks are
 # not whole 128-row tiles
 GENERIC_CASES = [
@@ -144,8 +161,10 @@ def _case_id(c):
         f"{k}" for k in extra) if extra else "")
 
 
-@pytest.mark.parametrize("spec", MFMA_CASES + PADDED_D_CASES + GENERIC_CASES,
-                         ids=[_case_id(c) for c in MFMA_CASES + PADDED_D_CASES + GENERIC_CASES])
+ALL_CASES = MFMA_CASES + PADDED_D_CASES + BLOCK_D128_CASES + GENERIC_CASES
+
+
+@pytest.mark.parametrize("spec", ALL_CASES, ids=[_case_id(c) for c in ALL_CASES])
 @pytest.mark.parametrize("seed", [1, 2])
 def test_random_shapes(spec, seed):
     B, N, H, Q, K, D, dt, kind, extra = spec
