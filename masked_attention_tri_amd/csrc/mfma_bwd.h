@@ -1139,8 +1139,9 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
                 const uint32_t o = static_cast<uint32_t>(q0 + 32 * (tile - G::QW)) * mem_row + src[j];
                 dma16(dg, dst, m >= 0 ? o : kNoTile);
             } else if (tile < 2 * G::QW + G::KW) {
+                // (s = 0: the K tiles are zeros, so Q.K adds exactly 0 to B)
                 const uint32_t o = static_cast<uint32_t>(k0 + 32 * (tile - 2 * G::QW)) * mem_row + src[j];
-                dma16(dk, dst, m >= 0 ? o : kNoTile);
+                dma16(dk, dst, m >= 0 && !zero_s ? o : kNoTile);
             } else {
                 const uint32_t o = static_cast<uint32_t>(k0 + 32 * (tile - 2 * G::QW - G::KW)) * mem_row + src[j];
                 dma16(dv, dst, m >= 0 ? o : kNoTile);
@@ -1164,14 +1165,14 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
         const float ndelta = *reinterpret_cast<const __attribute__((address_space(3))) float*>(ri);
         float nl2 = *reinterpret_cast<const __attribute__((address_space(3))) float*>(ri + 128);
         nl2 = nl2 != nl2 ? -INFINITY : nl2;  // no valid key: no contribution
+        // (no branch on s = 0 here: a phi of z would copy the bias block
+        // into the MFMA's registers on every n)
         f32x16 z = cb, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) dp[r] = ndelta;
-        if (!zero_s) {
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st)
-                z = M::run(row_operand<v8>(t + k_tile, rrd, st), row_operand<v8>(t + q_tile, rrd, st), z);
-        }
+        for (int st = 0; st < D / 16; ++st)
+            z = M::run(row_operand<v8>(t + k_tile, rrd, st), row_operand<v8>(t + q_tile, rrd, st), z);
 #pragma unroll
         for (int st = 0; st < D / 16; ++st)
             dp = M::run(row_operand<v8>(t + v_tile, rrd, st), row_operand<v8>(t + g_tile, rrd, st), dp);
