@@ -99,13 +99,15 @@ __device__ __forceinline__ int fbh(int r) { return ((r >> 2) ^ (r >> 4)) & 3; }
 // D <= 64, two for D = 128 (whose O accumulator alone takes 64 VGPRs).  At
 // D = 64 a bias with a block-sparse mask, with a dense mask, or with a scale
 // that is not a power of two needs more than 128 VGPRs (the block
-// bookkeeping, the mask words, the bias / s products), and those kernels run
-// three waves instead of spilling.
+// bookkeeping, the mask words, the bias / s products), and so does a dense
+// mask with such a scale (the mask operands of the logits' MFMAs): those
+// kernels run three waves instead of spilling.
 template <int D, int KIND, int BIAS, bool EXACT>
 constexpr int min_waves_per_simd() {
     if (D == 64 && BIAS != 0 &&
         (KIND == TRIATTN_MASK_BLOCK || KIND == TRIATTN_MASK_DENSE || !EXACT))
         return 3;
+    if (D == 64 && KIND == TRIATTN_MASK_DENSE && !EXACT) return 3;
     return D <= 64 ? 4 : D <= 128 ? 2 : 1;
 }
 
@@ -492,6 +494,23 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     // bias one spilled past 128 VGPRs).
     constexpr bool kInterleave = D == 64 && BIAS != kBiasScalar && !(kBlock && BIAS != kNoBias);
 
+    // A dense mask enters the logits through the matrix core, as one more
+    // k-step: its A operand holds, in element 0 of lanes 0-31 (key col of
+    // the tile), 0 for a valid key and -inf for a masked one (keys past K
+    // included), its B operand 1 in element 0 of lanes 0-31 (every query),
+    // and every other element is 0.  S^T then gains exactly 0 or -inf in
+    // each key row, with no per-element select.
+    v8 ones_op{};
+    if constexpr (kDense) ones_op[0] = half == 0 ? static_cast<T>(1.0f) : static_cast<T>(0.0f);
+    auto dense_op = [&](int t) {
+        if ((t >> 6) != dense_chunk) load_dense_chunk(t >> 6);
+        const uint32_t w = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dense_word), t & 63));
+        v8 a{};
+        a[0] = half == 0 && ((w >> col) & 1u) == 0u ? static_cast<T>(-INFINITY) : static_cast<T>(0.0f);
+        return a;
+    };
+    v8 mop{};  // the dense-mask operand of the logits being formed
+
     // S^T = K . Q^T + bias for tile t from K buffer x and this wave's bias
     // block.  qk_load reads the bias into s and the K operands into kop;
     // the key loop issues the MFMAs later, between the exponentials of the
@@ -507,11 +526,13 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
 #pragma unroll
         for (int st = 0; st < D / 16; ++st)
             kop[st] = __builtin_bit_cast(v8, *reinterpret_cast<const lds_u32x4*>(kt + (k_base ^ (32 * st))));
+        if constexpr (kDense) mop = t >= 0 ? dense_op(t) : v8{};
     };
     auto qk = [&](f32x16& s, int t, int x) {
         qk_load(s, t, x);
 #pragma unroll
         for (int st = 0; st < D / 16; ++st) s = M::run(kop[st], qop[st], s);
+        if constexpr (kDense) s = M::run(mop, ones_op, s);
     };
 
     // Softmax of tile t (logits in s) and O^T += V^T . P^T from V buffer x.
@@ -530,13 +551,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         // built with scalar instructions and applied by one select.
         bool need_mask = k0 + kKTile > limit;
         bool causal = false;
-        uint32_t dense_bits = ~0u;
-        if (kDense) {
-            // bit i = key k0 + i valid (both wave halves hold the same 32 keys)
-            if ((t >> 6) != dense_chunk) load_dense_chunk(t >> 6);
-            dense_bits = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dense_word), t & 63));
-            need_mask = dense_bits != ~0u;
-        }
+        if constexpr (kDense) need_mask = false;  // (masked in the logits' MFMAs)
         if constexpr (kBlock) {
             if (p.mask_mod == TRIATTN_MOD_CAUSAL && !bit_set(full_bits, t / tiles_per_block) &&
                 k0 + kKTile - 1 > q0w) {
@@ -554,7 +569,6 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
             // bit i of w: key k0 + i passes the length and dense tests
             const int room = limit - k0;
             uint32_t w = room >= kKTile ? ~0u : room <= 0 ? 0u : (1u << room) - 1u;
-            if (kDense) w &= dense_bits;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ka = 8 * (r / 4) + (r % 4);  // key offset in lanes 0-31
@@ -618,9 +632,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         if constexpr (kInterleave) {
 #pragma unroll
             for (int st = 0; st < D / 16; ++st) s_nxt = M::run(kop[st], qop[st], s_nxt);
+            if constexpr (kDense) s_nxt = M::run(mop, ones_op, s_nxt);
             // scheduling pattern: (1 MFMA, 7 VALU) per k-step
 #pragma unroll
-            for (int i = 0; i < D / 16; ++i) {
+            for (int i = 0; i < D / 16 + (kDense ? 1 : 0); ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
             }
