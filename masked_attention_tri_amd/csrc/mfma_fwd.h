@@ -39,9 +39,11 @@
 // XOR-swizzled by row so that the operand reads are bank-conflict free.
 //
 // Buffer descriptors bound every access to its (b, n, h) slice.  The range
-// check covers the per-lane offset (not the scalar one), so all variable
-// offsets go in the per-lane offset: reads past a slice return 0 and touch
-// no memory, and ragged tiles need no clamping (those keys are masked).
+// check covers the per-lane offset (not the scalar one), so no variable
+// offset goes in the scalar one: a tile's offset moves the descriptor's base
+// (its size shrinking by as much, to 0 for a missing tile) and the rest is
+// per lane.  Reads past a slice return 0 and touch no memory, and ragged
+// tiles need no clamping (those keys are masked).
 //
 // Scale: z = s*(Q.K) + B.  When s is 0 or a power of two, s*Q is exact in the
 // input format, so Q is scaled once at load and S = (sQ).K + B is z itself.
@@ -51,15 +53,18 @@
 // Softmax bookkeeping per query row: the exact running max (the "max"
 // output) and a reference max used in the exponent.  The reference is only
 // raised, and O and the sum rescaled, when a tile's max exceeds it by more
-// than ln(256); so p <= 256 and the rescale is rare.  The sum is taken over
-// the fp32 p, before they are rounded for the P.V contraction.
+// than ln(256); so p <= 256 and the rescale is rare.  Each of the two lanes
+// of a row keeps the max of its 16 keys; they are combined only when one
+// passes the threshold, and for the output after the loop.  The sum is
+// taken over the fp32 p, before they are rounded for the P.V contraction.
 //
 // Masks: kv_lengths and block lists cut whole tiles (tiles past the length,
 // blocks not listed); element masks are applied only on tiles that need
-// them (the ragged last tile, dense-mask tiles, causal partial blocks); full
-// blocks skip the mask.  Masked logits are -inf internally; a row left with
-// no valid key gets the page's uniform-weight result (mean of V over all K
-// keys, max -1e9, lse -1e9 + ln K).
+// them (the ragged last tile, causal partial blocks); full blocks skip the
+// mask.  A dense mask, a function of the key alone, is added to the logits
+// by one more MFMA k-step (0 or -inf per key).  Masked logits are -inf
+// internally; a row left with no valid key gets the page's uniform-weight
+// result (mean of V over all K keys, max -1e9, lse -1e9 + ln K).
 //
 // Grid: one workgroup per (b, n, h, query tile), remapped so that each of the
 // 8 XCDs walks a contiguous range of (b, h, n, q-tile) order: the q-tiles of
