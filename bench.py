@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 PEAK_HBM_GBPS = 8000.0
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector (256 CU x 2.4 GHz x 256 flop/clk)
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA (the fp32 forward's v_mfma_f32_32x32x2_f32)
 METRIC = "fwd TFLOP/s + % bf16 MFMA peak, triangle attn N=Q=K=768 H=4 D=64"
 PROFILES = os.path.join(ROOT, "profiles")
 # the forward kernel's sources: the kernel and its tile geometry / swizzles
@@ -402,6 +403,7 @@ def main():
     sec = ms * 1e-3
     value = nominal / sec / 1e12
     alg_tflops = alg / sec / 1e12
+    fwd_peak = PEAK_FP32_MFMA_TFLOPS if case.dtype == torch.float32 else PEAK_BF16_TFLOPS
     tr = traffic_entry(key) if not half_bias else None
     traffic = None if tr is None else tr["bytes_per_launch"]
     res = {
@@ -434,12 +436,14 @@ def main():
             "algorithmic_flop": alg,
             "algorithmic_bytes": alg_bytes,
         },
+        # fp32 inputs run on the fp32 matrix product, the 16-bit types on
+        # the bf16/fp16 one
         "roofline": {
             "bound": "mfma",
             "achieved": round(alg_tflops, 3),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": fwd_peak,
             "unit": "TFLOP/s",
-            "frac": round(alg_tflops / PEAK_BF16_TFLOPS, 5),
+            "frac": round(alg_tflops / fwd_peak, 5),
             "traffic": traffic,
             "hbm_frac_algorithmic": round(alg_bytes / sec / 1e9 / PEAK_HBM_GBPS, 5),
         },

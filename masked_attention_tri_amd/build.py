@@ -16,7 +16,7 @@ LIB = os.path.join(PKG, "libtriattn.so")
 SOURCES = ["triattn_api.hip", "kernel_generic.hip", "kernel_mfma.hip", "kernel_mfma_d32.hip",
            "kernel_mfma_d64.hip", "kernel_mfma_d128.hip", "kernel_mfma_d256.hip",
            "kernel_util.hip", "kernel_bwd.hip", "kernel_bwd_d32.hip", "kernel_bwd_d64.hip",
-           "kernel_bwd_d128.hip", "noalloc.hip"]
+           "kernel_bwd_d128.hip", "noalloc.hip", "kernel_fp32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -1,0 +1,217 @@
+// fp32 forward on the matrix core (v_mfma_f32_32x32x2_f32), for fp32 inputs
+// (head dimension D <= 32, a multiple of 4: the triangle_attention page's
+// envelope for fp32, Notes item 3) with no mask, kv_lengths or a dense key
+// mask; block masks and packed sequences stay on the generic kernel.
+//
+// A workgroup of 4 waves takes 128 query rows of one (b, n, h), wave w rows
+// 32w .. 32w+31, lane l the row 32w + l%32.  Keys go in tiles of 32, staged
+// in LDS by the whole workgroup.  Both products are 16 k-steps of the 32 x 32
+// x 2 MFMA, each k-step pairing two values of the summed index:
+//   S^T = K . Q^T   step s pairs d = s and d = s + 16: lane l gives K[l%32][s +
+//                   16 (l/32)] (A, from LDS) and Q[row][s + 16 (l/32)] (B,
+//                   held in 16 registers for the whole key loop);
+//   O^T = V^T . P^T step r pairs keys 8(r/4) + r%4 and that key + 4, which is
+//                   where the accumulator of S^T puts them: register r of
+//                   lane l holds key 8(r/4) + 4(l/32) + r%4 of row l%32, so
+//                   the B operand of step r is the lane's own p[r], and the A
+//                   operand is V[that key][l%32] from LDS.
+// The softmax is the max-shifted online one in fp32 with expf: per tile the
+// row max is raised and O and the sum rescaled.  Masked logits are -inf; a
+// row with no valid key gets the uniform-weight result over all K keys
+// (mean of V, max -1e9, lse -1e9 + ln K), as in the other kernels.
+#include <math.h>
+
+#include "triattn_internal.h"
+
+namespace triattn {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kW = 4;         // waves per workgroup
+constexpr int kQT = 32 * kW;  // query rows per workgroup
+constexpr int kKT = 32;       // keys per tile
+constexpr int kDT = 32;       // head dimension of the tiles (zero columns past D)
+constexpr int kRow = kDT + 1;  // LDS row stride in floats (odd)
+
+__device__ __forceinline__ f32x16 mma(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// max / sum of the two lanes of a row (lane and lane ^ 32)
+__device__ __forceinline__ float max2(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float sum2(float x) { return x + __shfl_xor(x, 32); }
+
+__global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
+    __shared__ float k_lds[kKT * kRow];
+    __shared__ float v_lds[kKT * kRow];
+    __shared__ uint32_t valid_word;  // bit i: key k0 + i of the tile valid
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int64_t n_qt = (p.Q + kQT - 1) / kQT;
+    const int64_t g = blockIdx.x / n_qt;  // (b, n, h)
+    const int64_t q0 = (blockIdx.x % n_qt) * kQT;
+    const int64_t h = g % p.H, n = (g / p.H) % p.N, b = g / (p.H * p.N);
+    const int64_t Q = p.Q, K = p.K, D = p.D;
+    const int64_t row = q0 + 32 * wave + col;  // this lane's query
+    const bool row_ok = row < Q;
+    const float* qb = static_cast<const float*>(p.q) + g * Q * D;
+    const float* kb = static_cast<const float*>(p.k) + g * K * D;
+    const float* vb = static_cast<const float*>(p.v) + g * K * D;
+    const float* brow = p.bias && row_ok ? p.bias + ((b * p.H + h) * Q + row) * K : nullptr;
+    const uint8_t* dense = p.mask_kind == TRIATTN_MASK_DENSE ? p.dense + (b * p.N + n) * K : nullptr;
+
+    int64_t limit = K;  // keys >= limit are never valid
+    if (p.mask_kind == TRIATTN_MASK_KV_LENGTHS && p.kv_lengths) {
+        const int64_t len = p.kv_lengths[b * p.N + n];
+        limit = len < 0 ? 0 : (len > K ? K : len);
+    }
+    const int64_t n_tiles = (limit + kKT - 1) / kKT;
+
+    // Q^T operand: dims 16 half .. 16 half + 15 of the row (0 past D)
+    float qv[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t d = 16 * half + 4 * j;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (row_ok && d < D) x = *reinterpret_cast<const f32x4*>(qb + row * D + d);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qv[4 * j + e] = x[e];
+    }
+
+    f32x16 o = {};
+    float m = -INFINITY;  // running max of the valid logits of the row
+    float l = 0.f;        // this lane's half of the running sum
+    // staging: thread t copies 4 floats (chunk t % 8) of key row t / 8
+    const int st_key = tid >> 3, st_c = tid & 7;
+    for (int64_t t = 0; t < n_tiles; ++t) {
+        const int64_t k0 = t * kKT;
+        __syncthreads();  // the previous tile is no longer read
+        {
+            const int64_t key = k0 + st_key;
+            const int64_t d = 4 * st_c;
+            f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
+            if (key < K && d < D) {
+                kx = *reinterpret_cast<const f32x4*>(kb + key * D + d);
+                vx = *reinterpret_cast<const f32x4*>(vb + key * D + d);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                k_lds[st_key * kRow + 4 * st_c + e] = kx[e];
+                v_lds[st_key * kRow + 4 * st_c + e] = vx[e];
+            }
+        }
+        if (wave == 0) {
+            const int64_t key = k0 + lane;
+            const bool ok = lane < kKT && key < limit && (!dense || dense[key] != 0);
+            const uint64_t bits = __ballot(ok);
+            if (lane == 0) valid_word = static_cast<uint32_t>(bits);
+        }
+        __syncthreads();
+        const uint32_t vw = valid_word;
+
+        // S^T of the tile
+        f32x16 s = {};
+#pragma unroll
+        for (int st = 0; st < 16; ++st) s = mma(k_lds[col * kRow + st + 16 * half], qv[st], s);
+
+        // logits, tile max
+        float z[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kr = 8 * (r / 4) + 4 * half + (r % 4);
+            const bool ok = (vw >> kr) & 1u;
+            const float bias = brow && ok ? brow[k0 + kr] : 0.f;
+            z[r] = ok ? fmaf(s[r], p.scale, bias) : -INFINITY;
+            tmax = fmaxf(tmax, z[r]);
+        }
+        const float m_new = fmaxf(m, max2(tmax));
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = expf(m - m_use);
+        float psum = 0.f;
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            pr[r] = expf(z[r] - m_use);  // 0 for a masked key
+            psum += pr[r];
+        }
+        l = l * alpha + psum;
+        o *= alpha;
+        m = m_new;
+
+        // O^T += V^T . P^T
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kr = 8 * (r / 4) + 4 * half + (r % 4);
+            o = mma(v_lds[kr * kRow + col], pr[r], o);
+        }
+    }
+
+    const float l_tot = sum2(l);
+    const bool dead = m == -INFINITY;
+    // a row with no valid key: the mean of V over all K keys (every lane
+    // sums the columns it stores)
+    float mean[16];
+    if (dead) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mean[r] = 0.f;
+        for (int64_t key = 0; key < K; ++key) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int64_t d = 8 * gq + 4 * half;
+                if (d < D) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(vb + key * D + d);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) mean[4 * gq + e] += x[e];
+                }
+            }
+        }
+        const float inv = K > 0 ? 1.0f / static_cast<float>(K) : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mean[r] *= inv;
+    }
+    if (!row_ok) return;
+    float* orow = static_cast<float*>(p.out) + (g * Q + row) * D;
+    const float inv_l = dead ? 0.f : 1.0f / l_tot;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+        const int64_t d = 8 * gq + 4 * half;
+        if (d < D) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = dead ? mean[4 * gq + e] : o[4 * gq + e] * inv_l;
+            *reinterpret_cast<f32x4*>(orow + d) = x;
+        }
+    }
+    if (half == 0) {
+        const int64_t ridx = g * Q + row;
+        if (p.lse) p.lse[ridx] = dead ? kMaskedLogit + (K > 0 ? logf(static_cast<float>(K)) : 0.f)
+                                      : m + logf(l_tot);
+        if (p.mx) p.mx[ridx] = dead ? kMaskedLogit : m;
+    }
+}
+
+}  // namespace
+
+bool fp32_mfma_supports(const Params& p) {
+    if (p.mask_kind != TRIATTN_MASK_NONE && p.mask_kind != TRIATTN_MASK_KV_LENGTHS &&
+        p.mask_kind != TRIATTN_MASK_DENSE)
+        return false;
+    if (p.D < 4 || p.D > kDT || p.D % 4 != 0 || p.bias16) return false;
+    // 16-byte loads of Q, K and V rows and stores of O rows
+    const uintptr_t al = reinterpret_cast<uintptr_t>(p.q) | reinterpret_cast<uintptr_t>(p.k) |
+                         reinterpret_cast<uintptr_t>(p.v) | reinterpret_cast<uintptr_t>(p.out);
+    return al % 16 == 0;
+}
+
+hipError_t launch_fp32_mfma(const Params& p, hipStream_t stream) {
+    const int64_t groups = p.B * p.N * p.H * ((p.Q + kQT - 1) / kQT);
+    if (groups > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(fp32_fwd_kernel, dim3(static_cast<unsigned>(groups)), dim3(64 * kW), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace triattn

@@ -3,8 +3,9 @@
 // Serves every (dtype, D) in the envelope of the triangle_attention page
 // (Notes item 3: D <= 32 for fp32, D <= 256 for the half types, the wider
 // bound being the one that page gives its newest forward kernels) and every
-// mask form; it is the path for fp32 inputs and for shapes the MFMA kernel
-// is not instantiated for.  Lanes split the keys
+// mask form; it is the path for shapes the MFMA kernels do not take (fp32
+// inputs with a block mask or packed sequences, and the half-type cases
+// outside the MFMA kernel's envelope).  Lanes split the keys
 // for the logits and the d coordinates for P.V; the softmax runs online over
 // chunks of 64 keys with a running max and sum (the max-shifted evaluation of
 // the page's softmax), so a row of any length needs O(D) state.
@@ -217,6 +218,7 @@ __global__ __launch_bounds__(256) void generic_fwd_kernel(Params p) {
 }  // namespace
 
 hipError_t launch_generic(const Params& p, int32_t dtype, hipStream_t stream) {
+    if (dtype == TRIATTN_F32 && fp32_mfma_supports(p)) return launch_fp32_mfma(p, stream);
     const int64_t rows = p.B * p.N * p.H * p.Q;
     const int64_t blocks = (rows + kWaves - 1) / kWaves;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;

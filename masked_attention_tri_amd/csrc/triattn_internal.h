@@ -139,6 +139,10 @@ inline int dbias_splits(int64_t B, int64_t N, int64_t H, int64_t Q, int64_t K, i
 
 // Launchers (enqueue only; return the launch error, if any).
 hipError_t launch_generic(const Params& p, int32_t dtype, hipStream_t stream);
+// fp32 inputs with no mask, kv_lengths or a dense mask: the MFMA kernel of
+// kernel_fp32.hip (launch_generic hands them to it)
+bool fp32_mfma_supports(const Params& p);
+hipError_t launch_fp32_mfma(const Params& p, hipStream_t stream);
 hipError_t launch_mfma(const Params& p, int32_t dtype, hipStream_t stream);
 bool mfma_supports(const Params& p, int32_t dtype);
 // The MFMA kernel's instantiations, one per head dimension (exact: the scale

@@ -139,15 +139,27 @@ BLOCK_D128_CASES = [
     (1, 2, 2, 130, 131, 128, "f16", "block", {"q_block": 128, "kv_block": 32}),  # scalar bias
 ]
 
-# the generic kernel: fp32 inputs, and block masks whose query blocks are
-# not whole 128-row tiles
+# fp32 inputs on the fp32 MFMA kernel (no mask, lengths, dense masks):
+# several 128-row query tiles and 32-key tiles with ragged tails, rows with
+# no valid key (length 0, a 2% dense mask), an inexact scale, no bias,
+# widths below 32
+FP32_MFMA_CASES = [
+    (1, 2, 2, 300, 250, 28, "f32", "kv_lengths", {"len_range": (0, 250)}),
+    (1, 3, 2, 150, 131, 32, "f32", "dense", {}),
+    (1, 2, 2, 140, 70, 16, "f32", "dense", {"p_valid": 0.02}),
+    (2, 2, 2, 129, 100, 8, "f32", "none", {"scale": 0.3}),
+    (1, 2, 2, 200, 96, 32, "f32", "none", {"bias": False}),
+    (2, 3, 2, 19, 23, 12, "f32", "dense", {}),
+    (1, 2, 2, 40, 40, 32, "f32", "kv_lengths", {"len_range": (-2, 45)}),
+    (1, 2, 2, 9, 1, 32, "f32", "none", {}),
+]
+
+# the generic kernel: fp32 block masks, and block masks whose query blocks
+# are not whole 128-row tiles
 GENERIC_CASES = [
     (2, 2, 2, 40, 37, 16, "bf16", "block", {"q_block": 16, "kv_block": 8, "mask_mod": "causal"}),
     (1, 2, 2, 64, 64, 64, "bf16", "block", {"q_block": 32, "kv_block": 32}),
-    (2, 3, 2, 19, 23, 12, "f32", "dense", {}),
-    (1, 2, 2, 40, 40, 32, "f32", "kv_lengths", {"len_range": (-2, 45)}),
     (1, 1, 2, 30, 30, 4, "f32", "block", {"q_block": 8, "kv_block": 4, "mask_mod": "causal"}),
-    (1, 2, 2, 9, 1, 32, "f32", "none", {}),
     # D = 256 (half types)
     (1, 2, 2, 70, 90, 256, "bf16", "kv_lengths", {}),
     (1, 2, 2, 30, 50, 256, "bf16", "dense", {"p_valid": 0.02}),
@@ -161,7 +173,7 @@ def _case_id(c):
         f"{k}" for k in extra) if extra else "")
 
 
-ALL_CASES = MFMA_CASES + PADDED_D_CASES + BLOCK_D128_CASES + GENERIC_CASES
+ALL_CASES = MFMA_CASES + PADDED_D_CASES + BLOCK_D128_CASES + FP32_MFMA_CASES + GENERIC_CASES
 
 
 @pytest.mark.parametrize("spec", ALL_CASES, ids=[_case_id(c) for c in ALL_CASES])
