@@ -1,7 +1,9 @@
 // fp32 forward on the matrix core (v_mfma_f32_32x32x2_f32), for fp32 inputs
 // (head dimension D <= 32, a multiple of 4: the triangle_attention page's
-// envelope for fp32, Notes item 3) with no mask, kv_lengths or a dense key
-// mask; block masks and packed sequences stay on the generic kernel.
+// envelope for fp32, Notes item 3) with no mask, kv_lengths, a dense key
+// mask or a BlockMask whose query blocks are whole 128-row tiles and whose
+// key blocks are whole 32-key tiles; packed sequences and other block sizes
+// stay on the generic kernel.
 //
 // A workgroup of 4 waves takes 128 query rows of one (b, n, h), wave w rows
 // 32w .. 32w+31, lane l the row 32w + l%32.  Keys go in tiles of 32, staged
@@ -19,6 +21,13 @@
 // row max is raised and O and the sum rescaled.  Masked logits are -inf; a
 // row with no valid key gets the uniform-weight result over all K keys
 // (mean of V, max -1e9, lse -1e9 + ln K), as in the other kernels.
+//
+// Block masks (the tensorplay BlockMask page): the workgroup's 128 rows lie
+// in one block row, whose listed and full blocks (kv_indices and
+// full_kv_indices, read as a union, ids out of range ignored) are marked as
+// bits in LDS; key tiles of unlisted blocks are skipped, and the causal
+// mask_mod (query >= key) applies per element only on listed blocks that are
+// not full.
 #include <math.h>
 
 #include "triattn_internal.h"
@@ -47,6 +56,8 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
     __shared__ float k_lds[kKT * kRow];
     __shared__ float v_lds[kKT * kRow];
     __shared__ uint32_t valid_word;  // bit i: key k0 + i of the tile valid
+    __shared__ uint32_t listed_bits[kMaxKvBlocks / 32];
+    __shared__ uint32_t full_bits[kMaxKvBlocks / 32];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, half = lane >> 5;
@@ -70,6 +81,34 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
     }
     const int64_t n_tiles = (limit + kKT - 1) / kKT;
 
+    // the block row of the workgroup: listed and full blocks as bits
+    const bool block_kind = p.mask_kind == TRIATTN_MASK_BLOCK;
+    if (block_kind) {  // uniform over the workgroup
+        const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
+        for (int i = tid; i < words; i += 64 * kW) {
+            listed_bits[i] = 0u;
+            full_bits[i] = 0u;
+        }
+        __syncthreads();
+        const int64_t list_row = (b * p.stride_b + n * p.stride_n + h * p.stride_h) * p.n_q_rows + q0 / p.q_block;
+        auto mark = [&](uint32_t* bits, const int32_t* counts, const int32_t* ids, int64_t width) {
+            int64_t cnt = counts[list_row];
+            cnt = cnt < 0 ? 0 : (cnt > width ? width : cnt);
+            for (int64_t j = tid; j < cnt; j += 64 * kW) {
+                const int64_t id = ids[list_row * width + j];
+                if (id >= 0 && id < p.n_kv_blocks) atomicOr(&bits[id >> 5], 1u << (id & 31));
+            }
+        };
+        mark(listed_bits, p.kv_num_blocks, p.kv_indices, p.max_blocks);
+        if (p.full_kv_num_blocks) {
+            mark(full_bits, p.full_kv_num_blocks, p.full_kv_indices, p.full_max_blocks);
+            mark(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, p.full_max_blocks);
+        }
+        __syncthreads();
+    }
+    const int64_t tiles_per_block = block_kind ? p.kv_block / kKT : 1;
+    auto bit = [](const uint32_t* bits, int64_t i) { return ((bits[i >> 5] >> (i & 31)) & 1u) != 0; };
+
     // Q^T operand: dims 16 half .. 16 half + 15 of the row (0 past D)
     float qv[16];
 #pragma unroll
@@ -88,6 +127,12 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
     const int st_key = tid >> 3, st_c = tid & 7;
     for (int64_t t = 0; t < n_tiles; ++t) {
         const int64_t k0 = t * kKT;
+        bool causal = false;  // element mask q >= key on this tile
+        if (block_kind) {
+            const int64_t blk = t / tiles_per_block;
+            if (!bit(listed_bits, blk)) continue;  // (uniform: no barrier skipped unevenly)
+            causal = p.mask_mod == TRIATTN_MOD_CAUSAL && !bit(full_bits, blk);
+        }
         __syncthreads();  // the previous tile is no longer read
         {
             const int64_t key = k0 + st_key;
@@ -123,7 +168,7 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int kr = 8 * (r / 4) + 4 * half + (r % 4);
-            const bool ok = (vw >> kr) & 1u;
+            const bool ok = ((vw >> kr) & 1u) && (!causal || row >= k0 + kr);
             const float bias = brow && ok ? brow[k0 + kr] : 0.f;
             z[r] = ok ? fmaf(s[r], p.scale, bias) : -INFINITY;
             tmax = fmaxf(tmax, z[r]);
@@ -198,7 +243,11 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
 
 bool fp32_mfma_supports(const Params& p) {
     if (p.mask_kind != TRIATTN_MASK_NONE && p.mask_kind != TRIATTN_MASK_KV_LENGTHS &&
-        p.mask_kind != TRIATTN_MASK_DENSE)
+        p.mask_kind != TRIATTN_MASK_DENSE && p.mask_kind != TRIATTN_MASK_BLOCK)
+        return false;
+    // a workgroup's 128 rows in one block row, whole 32-key tiles per block
+    if (p.mask_kind == TRIATTN_MASK_BLOCK &&
+        (p.q_block % kQT != 0 || p.kv_block % kKT != 0 || p.n_kv_blocks > kMaxKvBlocks))
         return false;
     if (p.D < 4 || p.D > kDT || p.D % 4 != 0 || p.bias16) return false;
     // 16-byte loads of Q, K and V rows and stores of O rows

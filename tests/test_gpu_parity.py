@@ -139,11 +139,15 @@ BLOCK_D128_CASES = [
     (1, 2, 2, 130, 131, 128, "f16", "block", {"q_block": 128, "kv_block": 32}),  # scalar bias
 ]
 
-# fp32 inputs on the fp32 MFMA kernel (no mask, lengths, dense masks):
-# several 128-row query tiles and 32-key tiles with ragged tails, rows with
-# no valid key (length 0, a 2% dense mask), an inexact scale, no bias,
-# widths below 32
+# fp32 inputs on the fp32 MFMA kernel (no mask, lengths, dense masks, block
+# masks of whole 128-row / 32-key tiles): several 128-row query tiles and
+# 32-key tiles with ragged tails, rows with no valid key (length 0, a 2%
+# dense mask, sparse block lists), an inexact scale, no bias, widths below 32
 FP32_MFMA_CASES = [
+    (1, 2, 2, 256, 200, 32, "f32", "block", {"q_block": 128, "kv_block": 32, "mask_mod": "causal"}),
+    (1, 2, 2, 300, 300, 16, "f32", "block", {"q_block": 128, "kv_block": 64, "block_density": 0.3}),
+    (2, 1, 2, 256, 256, 8, "f32", "block", {"q_block": 256, "kv_block": 128, "mask_mod": "causal",
+                                             "block_broadcast": True}),
     (1, 2, 2, 300, 250, 28, "f32", "kv_lengths", {"len_range": (0, 250)}),
     (1, 3, 2, 150, 131, 32, "f32", "dense", {}),
     (1, 2, 2, 140, 70, 16, "f32", "dense", {"p_valid": 0.02}),
