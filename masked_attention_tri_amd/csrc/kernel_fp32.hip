@@ -1,9 +1,10 @@
 // fp32 forward on the matrix core (v_mfma_f32_32x32x2_f32), for fp32 inputs
 // (head dimension D <= 32, a multiple of 4: the triangle_attention page's
 // envelope for fp32, Notes item 3) with no mask, kv_lengths, a dense key
-// mask or a BlockMask whose query blocks are whole 128-row tiles and whose
-// key blocks are whole 32-key tiles; packed sequences and other block sizes
-// stay on the generic kernel.
+// mask, a BlockMask whose query blocks are whole 128-row tiles and whose
+// key blocks are whole 32-key tiles, or packed sequences (the Transformer
+// Engine page's layouts, no mask or causal); other block sizes stay on the
+// generic kernel.
 //
 // A workgroup of 4 waves takes 128 query rows of one (b, n, h), wave w rows
 // 32w .. 32w+31, lane l the row 32w + l%32.  Keys go in tiles of 32, staged
@@ -65,13 +66,31 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
     const int64_t g = blockIdx.x / n_qt;  // (b, n, h)
     const int64_t q0 = (blockIdx.x % n_qt) * kQT;
     const int64_t h = g % p.H, n = (g / p.H) % p.N, b = g / (p.H * p.N);
-    const int64_t Q = p.Q, K = p.K, D = p.D;
+    const int64_t D = p.D;
+    // Rows: the (b, n, h) slices (row strides D), or for packed sequences
+    // sequence b's rows of the packed tensors (row strides q_rs / kv_rs, head
+    // h at column h D); Q and K are then that sequence's row counts.
+    const bool varlen = p.mask_kind == kMaskVarlen;
+    int64_t Q = p.Q, K = p.K, q_rs = D, kv_rs = D;
+    const float* qb = static_cast<const float*>(p.q) + g * p.Q * D;
+    const float* kb = static_cast<const float*>(p.k) + g * p.K * D;
+    const float* vb = static_cast<const float*>(p.v) + g * p.K * D;
+    int64_t q_first = 0;
+    if (varlen) {
+        const SeqRows sr = seq_rows(p, b);
+        Q = sr.nq;
+        K = sr.nk;
+        q_first = sr.q0;
+        q_rs = p.q_rs;
+        kv_rs = p.kv_rs;
+        qb = static_cast<const float*>(p.q) + sr.q0 * q_rs + h * D;
+        kb = static_cast<const float*>(p.k) + sr.k0 * kv_rs + h * D;
+        vb = static_cast<const float*>(p.v) + sr.k0 * kv_rs + h * D;
+        if (q0 >= Q) return;  // the whole workgroup is past this sequence
+    }
     const int64_t row = q0 + 32 * wave + col;  // this lane's query
     const bool row_ok = row < Q;
-    const float* qb = static_cast<const float*>(p.q) + g * Q * D;
-    const float* kb = static_cast<const float*>(p.k) + g * K * D;
-    const float* vb = static_cast<const float*>(p.v) + g * K * D;
-    const float* brow = p.bias && row_ok ? p.bias + ((b * p.H + h) * Q + row) * K : nullptr;
+    const float* brow = p.bias && !varlen && row_ok ? p.bias + ((b * p.H + h) * Q + row) * K : nullptr;
     const uint8_t* dense = p.mask_kind == TRIATTN_MASK_DENSE ? p.dense + (b * p.N + n) * K : nullptr;
 
     int64_t limit = K;  // keys >= limit are never valid
@@ -79,6 +98,10 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
         const int64_t len = p.kv_lengths[b * p.N + n];
         limit = len < 0 ? 0 : (len > K ? K : len);
     }
+    // causal packed sequences: key j <= row (no row of the workgroup sees
+    // a key past its last row)
+    const bool seq_causal = varlen && p.causal;
+    if (seq_causal) limit = limit < q0 + kQT ? limit : q0 + kQT;
     const int64_t n_tiles = (limit + kKT - 1) / kKT;
 
     // the block row of the workgroup: listed and full blocks as bits
@@ -115,7 +138,7 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
     for (int j = 0; j < 4; ++j) {
         const int64_t d = 16 * half + 4 * j;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (row_ok && d < D) x = *reinterpret_cast<const f32x4*>(qb + row * D + d);
+        if (row_ok && d < D) x = *reinterpret_cast<const f32x4*>(qb + row * q_rs + d);
 #pragma unroll
         for (int e = 0; e < 4; ++e) qv[4 * j + e] = x[e];
     }
@@ -139,8 +162,8 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
             const int64_t d = 4 * st_c;
             f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
             if (key < K && d < D) {
-                kx = *reinterpret_cast<const f32x4*>(kb + key * D + d);
-                vx = *reinterpret_cast<const f32x4*>(vb + key * D + d);
+                kx = *reinterpret_cast<const f32x4*>(kb + key * kv_rs + d);
+                vx = *reinterpret_cast<const f32x4*>(vb + key * kv_rs + d);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -168,7 +191,7 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int kr = 8 * (r / 4) + 4 * half + (r % 4);
-            const bool ok = ((vw >> kr) & 1u) && (!causal || row >= k0 + kr);
+            const bool ok = ((vw >> kr) & 1u) && (!(causal || seq_causal) || row >= k0 + kr);
             const float bias = brow && ok ? brow[k0 + kr] : 0.f;
             z[r] = ok ? fmaf(s[r], p.scale, bias) : -INFINITY;
             tmax = fmaxf(tmax, z[r]);
@@ -208,7 +231,7 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
             for (int gq = 0; gq < 4; ++gq) {
                 const int64_t d = 8 * gq + 4 * half;
                 if (d < D) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(vb + key * D + d);
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(vb + key * kv_rs + d);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) mean[4 * gq + e] += x[e];
                 }
@@ -219,7 +242,8 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
         for (int r = 0; r < 16; ++r) mean[r] *= inv;
     }
     if (!row_ok) return;
-    float* orow = static_cast<float*>(p.out) + (g * Q + row) * D;
+    const int64_t ridx = varlen ? (q_first + row) * p.H + h : g * p.Q + row;  // (row, head) index
+    float* orow = static_cast<float*>(p.out) + ridx * D;
     const float inv_l = dead ? 0.f : 1.0f / l_tot;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
@@ -232,7 +256,6 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
         }
     }
     if (half == 0) {
-        const int64_t ridx = g * Q + row;
         if (p.lse) p.lse[ridx] = dead ? kMaskedLogit + (K > 0 ? logf(static_cast<float>(K)) : 0.f)
                                       : m + logf(l_tot);
         if (p.mx) p.mx[ridx] = dead ? kMaskedLogit : m;
@@ -243,7 +266,8 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
 
 bool fp32_mfma_supports(const Params& p) {
     if (p.mask_kind != TRIATTN_MASK_NONE && p.mask_kind != TRIATTN_MASK_KV_LENGTHS &&
-        p.mask_kind != TRIATTN_MASK_DENSE && p.mask_kind != TRIATTN_MASK_BLOCK)
+        p.mask_kind != TRIATTN_MASK_DENSE && p.mask_kind != TRIATTN_MASK_BLOCK &&
+        p.mask_kind != kMaskVarlen)
         return false;
     // a workgroup's 128 rows in one block row, whole 32-key tiles per block
     if (p.mask_kind == TRIATTN_MASK_BLOCK &&

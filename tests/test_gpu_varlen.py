@@ -88,9 +88,13 @@ CASES = [
     ("qkv_packed", "padding", "bf16", 2, 64, [128, 77], None),
     ("kv_packed", "causal", "bf16", 2, 128, [40, 257, 3], [64, 200, 3]),
     ("kv_packed", "padding", "bf16", 3, 32, [10, 90], [300, 45]),
-    # fp32 (the generic kernel), and head dimensions between the tile widths
-    # (the MFMA kernel of the next width, zero columns)
+    # fp32 (the fp32 MFMA kernel): every layout, sequences past one 128-row
+    # tile, an empty one; and head dimensions between the tile widths (the
+    # MFMA kernel of the next width, zero columns)
     ("separate", "causal", "f32", 2, 32, [30, 17], [25, 40]),
+    ("qkv_packed", "causal", "f32", 2, 16, [200, 1, 0, 129], None),
+    ("kv_packed", "padding", "f32", 3, 28, [140, 60], [70, 300]),
+    ("separate", "no_mask", "f32", 2, 8, [257, 5], [33, 0]),
     ("kv_packed", "padding", "bf16", 2, 40, [33, 64], [70, 12]),
     ("qkv_packed", "causal", "f16", 2, 136, [45, 20], None),
     ("separate", "no_mask", "bf16", 2, 96, [70, 200], [90, 33]),
