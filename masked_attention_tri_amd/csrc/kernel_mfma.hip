@@ -20,8 +20,13 @@ bool mfma_supports(const Params& p, int32_t dtype) {
     if (p.bias16 && (p.K % 8 != 0 || reinterpret_cast<uintptr_t>(p.bias16) % 16 != 0))
         return false;
     if (p.mask_kind == TRIATTN_MASK_BLOCK) {
-        // one block row per workgroup, whole tiles per kv block
-        if (p.q_block % kQTileBlock != 0 || p.kv_block % kKTile != 0) return false;
+        // whole 128-row tiles per block, or 2 or 4 blocks of 64 / 32 rows
+        // per tile (each wave's 32 rows in one block; their bitmaps hold
+        // kMultiWords x 32 kv blocks)
+        if (p.kv_block % kKTile != 0) return false;
+        if (p.q_block % kQTileBlock != 0 &&
+            ((p.q_block != 64 && p.q_block != 32) || p.n_kv_blocks > tile::kMultiWords * 32))
+            return false;
     }
     // Byte offsets within one (b, n, h) or (b, h) slice, including the
     // overhang of a ragged last tile and of the last query tile, must fit

@@ -24,6 +24,12 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kKTile = 32;           // keys per K/V tile
 constexpr int kQTileBlock = 128;  // query rows per workgroup with block masks
+// Block masks with 32- or 64-row query blocks: the kv-block bitmaps of the
+// up to four block rows of a workgroup share the LDS of the one-row bitmaps
+// (2 x kMaxKvBlocks bits): the union of the rows' listed blocks, then each
+// row's listed and full blocks, kMultiWords words apiece.
+constexpr int kRowsMulti = kQTileBlock / 32;
+constexpr int kMultiWords = static_cast<int>(2 * (kMaxKvBlocks / 32) / (1 + 2 * kRowsMulti));
 constexpr int kXcds = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyLog = 5.545177444479562f;  // ln(256): largest p before a rescale

@@ -100,6 +100,19 @@ constexpr int kBiasHalfWaveBytes = 32 * kBiasHalfRowBytes;  // 2 KiB
 constexpr int kBiasHalfDma = kBiasHalfWaveBytes / 1024;
 __device__ __forceinline__ int fbh(int r) { return ((r >> 2) ^ (r >> 4)) & 3; }
 
+// Kernel variant (a template value, not a mask kind of the calls) of block
+// masks with 32- or 64-row query blocks, kept apart so that the per-tile
+// tests of the block rows cost the whole-tile kernel nothing.
+constexpr int kMaskBlockRows = 5;
+
+// a block row's bitmaps with 32- or 64-row query blocks (kMultiWords)
+__device__ __forceinline__ uint32_t* row_listed_bits(uint32_t* bits, int r) {
+    return bits + kMultiWords * (1 + r);
+}
+__device__ __forceinline__ uint32_t* row_full_bits(uint32_t* bits, int r) {
+    return bits + kMultiWords * (1 + kRowsMulti + r);
+}
+
 // Waves per SIMD the register budget must allow: four (128 VGPRs) for
 // D <= 64, two for D = 128 (whose O accumulator alone takes 64 VGPRs).  At
 // D = 64 a bias with a block-sparse mask, with a dense mask, or with a scale
@@ -110,7 +123,8 @@ __device__ __forceinline__ int fbh(int r) { return ((r >> 2) ^ (r >> 4)) & 3; }
 template <int D, int KIND, int BIAS, bool EXACT>
 constexpr int min_waves_per_simd() {
     if (D == 64 && BIAS != 0 &&
-        (KIND == TRIATTN_MASK_BLOCK || KIND == TRIATTN_MASK_DENSE || !EXACT))
+        (KIND == TRIATTN_MASK_BLOCK || KIND == kMaskBlockRows || KIND == TRIATTN_MASK_DENSE ||
+         !EXACT))
         return 3;
     if (D == 64 && KIND == TRIATTN_MASK_DENSE && !EXACT) return 3;
     return D <= 64 ? 4 : D <= 128 ? 2 : 1;
@@ -130,7 +144,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     constexpr int kDmaPerWave = 2 * Ge::kDma / W;
     static_assert(kDmaPerWave * W == 2 * Ge::kDma, "K/V DMAs split evenly over the waves");
     constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);
-    constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK;
+    constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK || KIND == kMaskBlockRows;
     constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
     constexpr bool kVarlen = KIND == kMaskVarlen;
     static_assert(!kVarlen || BIAS == kNoBias, "packed sequences carry no bias");
@@ -151,8 +165,14 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     __shared__ __attribute__((aligned(1024))) char v_lds1[Ge::tileBytes];
     __shared__ __attribute__((aligned(1024))) char v_lds2[Ge::tileBytes];
     __shared__ __attribute__((aligned(1024))) char b_lds[kBiasBuf];
-    __shared__ uint32_t listed_bits[kBlock ? kWords : 1];
-    __shared__ uint32_t full_bits[kBlock ? kWords : 1];
+    // Block masks: bitmaps of the kv blocks listed and full for the
+    // workgroup's block row.  Query blocks of 32 or 64 rows put 4 or 2
+    // block rows in the 128 rows (each wave's 32 rows lie in one): the same
+    // LDS then holds their union (the tiles visited) and a pair per block
+    // row, of kMultiWords words each.
+    __shared__ uint32_t block_bits[kBlock ? 2 * kWords : 1];
+    uint32_t* const listed_bits = block_bits;
+    uint32_t* const full_bits = block_bits + kWords;
     // after the key loop, the first K buffer holds the mean of V
     float* const mean_v = reinterpret_cast<float*>(k_lds0);
     static_assert(D * 4 <= Ge::tileBytes, "mean of V fits a K buffer");
@@ -235,24 +255,55 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     const int n_tiles = (limit + kKTile - 1) / kKTile;
     const int n_tiles_all = (K + kKTile - 1) / kKTile;
     int tiles_per_block = 1;
+    constexpr bool multi_row = KIND == kMaskBlockRows;  // 32- or 64-row query blocks
+    int wrow = 0;  // with multi_row: this wave's block row within the workgroup
     // (if constexpr keeps the block bitmaps out of the other kinds' LDS)
     if constexpr (kBlock) {
         tiles_per_block = static_cast<int>(p.kv_block / kKTile);
         const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
-        for (int i = tid; i < words; i += kThreads) {
-            listed_bits[i] = 0u;
-            full_bits[i] = 0u;
-        }
-        __syncthreads();
         const int64_t inst = b * p.stride_b + n * p.stride_n + h * p.stride_h;
-        const int64_t list_row = inst * p.n_q_rows + q0 / p.q_block;
-        mark_list(listed_bits, p.kv_num_blocks, p.kv_indices, list_row, p.max_blocks,
-                  p.n_kv_blocks, tid, kThreads);
-        if (p.full_kv_num_blocks) {
-            mark_list(full_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid, kThreads);
-            mark_list(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid, kThreads);
+        if constexpr (!multi_row) {
+            for (int i = tid; i < words; i += kThreads) {
+                listed_bits[i] = 0u;
+                full_bits[i] = 0u;
+            }
+            __syncthreads();
+            const int64_t list_row = inst * p.n_q_rows + q0 / p.q_block;
+            mark_list(listed_bits, p.kv_num_blocks, p.kv_indices, list_row, p.max_blocks,
+                      p.n_kv_blocks, tid, kThreads);
+            if (p.full_kv_num_blocks) {
+                mark_list(full_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
+                          p.full_max_blocks, p.n_kv_blocks, tid, kThreads);
+                mark_list(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
+                          p.full_max_blocks, p.n_kv_blocks, tid, kThreads);
+            }
+        } else {
+            const int qb = static_cast<int>(p.q_block);
+            const int rows = kQTileBlock / qb;  // 2 or 4
+            wrow = (32 * wave) / qb;
+            for (int i = tid; i < (1 + 2 * kRowsMulti) * kMultiWords; i += kThreads)
+                block_bits[i] = 0u;
+            __syncthreads();
+            for (int r = 0; r < rows; ++r) {
+                const int64_t qrow_blk = q0 / qb + r;
+                if (qrow_blk >= p.n_q_rows) break;  // rows past Q
+                const int64_t list_row = inst * p.n_q_rows + qrow_blk;
+                mark_list(row_listed_bits(block_bits, r), p.kv_num_blocks, p.kv_indices, list_row,
+                          p.max_blocks, p.n_kv_blocks, tid, kThreads);
+                if (p.full_kv_num_blocks) {
+                    mark_list(row_full_bits(block_bits, r), p.full_kv_num_blocks, p.full_kv_indices,
+                              list_row, p.full_max_blocks, p.n_kv_blocks, tid, kThreads);
+                    mark_list(row_listed_bits(block_bits, r), p.full_kv_num_blocks,
+                              p.full_kv_indices, list_row, p.full_max_blocks, p.n_kv_blocks, tid,
+                              kThreads);
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < words; i += kThreads) {
+                uint32_t u = 0u;
+                for (int r = 0; r < rows; ++r) u |= row_listed_bits(block_bits, r)[i];
+                listed_bits[i] = u;
+            }
         }
         __syncthreads();
     }
@@ -557,9 +608,15 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         bool need_mask = k0 + kKTile > limit;
         bool causal = false;
         if constexpr (kDense) need_mask = false;  // (masked in the logits' MFMAs)
+        bool unlisted = false;  // a tile visited for another block row of the workgroup
         if constexpr (kBlock) {
-            if (p.mask_mod == TRIATTN_MOD_CAUSAL && !bit_set(full_bits, t / tiles_per_block) &&
-                k0 + kKTile - 1 > q0w) {
+            const int blk = t / tiles_per_block;
+            if (multi_row && !bit_set(row_listed_bits(block_bits, wrow), blk)) {
+                unlisted = true;
+                need_mask = true;
+            } else if (p.mask_mod == TRIATTN_MOD_CAUSAL &&
+                       !bit_set(multi_row ? row_full_bits(block_bits, wrow) : full_bits, blk) &&
+                       k0 + kKTile - 1 > q0w) {
                 causal = true;
                 need_mask = true;
             }
@@ -574,6 +631,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
             // bit i of w: key k0 + i passes the length and dense tests
             const int room = limit - k0;
             uint32_t w = room >= kKTile ? ~0u : room <= 0 ? 0u : (1u << room) - 1u;
+            if constexpr (multi_row) {
+                if (unlisted) w = 0u;
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ka = 8 * (r / 4) + (r % 4);  // key offset in lanes 0-31
@@ -878,6 +938,7 @@ hipError_t launch_d(const Params& p, bool exact, hipStream_t stream) {
     case TRIATTN_MASK_DENSE:
         return launch_kind<T, D, TRIATTN_MASK_DENSE>(p, exact, stream);
     case TRIATTN_MASK_BLOCK:
+        if (p.q_block < kQTileBlock) return launch_kind<T, D, kMaskBlockRows>(p, exact, stream);
         return launch_kind<T, D, TRIATTN_MASK_BLOCK>(p, exact, stream);
     case kMaskVarlen:
         return launch_kind<T, D, kMaskVarlen>(p, exact, stream);

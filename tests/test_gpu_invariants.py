@@ -81,6 +81,9 @@ def test_run_to_run_determinism(key):
     ("bf16", 120, "block", (1, 2, 2, 300, 250),
      {"q_block": 128, "kv_block": 32, "block_density": 0.15}),
     ("bf16", 256, "kv_lengths", (1, 3, 2, 300, 200), {"len_range": (0, 200)}),
+    # 32-row query blocks (four block rows per workgroup), sparse lists
+    ("bf16", 64, "block", (1, 2, 2, 300, 250),
+     {"q_block": 32, "kv_block": 32, "block_density": 0.2}),
     # widths between the MFMA tiles: every one of the D columns is stored
     ("bf16", 96, "kv_lengths", (1, 3, 2, 300, 200), {"len_range": (0, 200)}),
     ("f16", 200, "dense", (1, 2, 2, 131, 77), {}),

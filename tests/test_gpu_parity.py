@@ -158,11 +158,32 @@ FP32_MFMA_CASES = [
     (1, 2, 2, 9, 1, 32, "f32", "none", {}),
 ]
 
+# half types with 32- or 64-row query blocks on the MFMA kernel (2 or 4
+# block rows per 128-row workgroup, each with its own kv lists): ragged Q
+# (a last block row partly or wholly past Q), rows with no listed block,
+# causal with full lists, broadcast lists, every width class, an inexact
+# scale, no bias
+MULTI_ROW_BLOCK_CASES = [
+    (1, 2, 2, 200, 300, 64, "bf16", "block", {"q_block": 64, "kv_block": 32, "mask_mod": "causal"}),
+    (1, 2, 2, 250, 260, 128, "f16", "block", {"q_block": 32, "kv_block": 64,
+                                               "block_density": 0.3}),
+    (2, 1, 2, 256, 256, 32, "bf16", "block", {"q_block": 32, "kv_block": 32, "mask_mod": "causal",
+                                               "block_broadcast": True}),
+    (1, 2, 2, 130, 100, 256, "bf16", "block", {"q_block": 64, "kv_block": 32,
+                                                "block_density": 0.4, "with_full": False}),
+    (1, 2, 2, 256, 200, 64, "bf16", "block", {"q_block": 32, "kv_block": 64, "mask_mod": "causal",
+                                               "scale": 0.3}),
+    (1, 2, 2, 100, 150, 40, "f16", "block", {"q_block": 64, "kv_block": 32, "mask_mod": "causal"}),
+    (1, 1, 2, 160, 128, 64, "bf16", "block", {"q_block": 32, "kv_block": 32, "bias": False,
+                                               "mask_mod": "causal"}),
+    (1, 2, 2, 64, 64, 64, "bf16", "block", {"q_block": 32, "kv_block": 32}),
+]
+
 # the generic kernel: fp32 block masks, and block masks whose query blocks
-# are not whole 128-row tiles
+# are not whole 128-row tiles or 32 / 64 rows
 GENERIC_CASES = [
     (2, 2, 2, 40, 37, 16, "bf16", "block", {"q_block": 16, "kv_block": 8, "mask_mod": "causal"}),
-    (1, 2, 2, 64, 64, 64, "bf16", "block", {"q_block": 32, "kv_block": 32}),
+    (1, 2, 2, 64, 64, 64, "bf16", "block", {"q_block": 96, "kv_block": 32}),
     (1, 1, 2, 30, 30, 4, "f32", "block", {"q_block": 8, "kv_block": 4, "mask_mod": "causal"}),
     # D = 256 (half types)
     (1, 2, 2, 70, 90, 256, "bf16", "kv_lengths", {}),
@@ -177,7 +198,8 @@ def _case_id(c):
         f"{k}" for k in extra) if extra else "")
 
 
-ALL_CASES = MFMA_CASES + PADDED_D_CASES + BLOCK_D128_CASES + FP32_MFMA_CASES + GENERIC_CASES
+ALL_CASES = (MFMA_CASES + PADDED_D_CASES + BLOCK_D128_CASES + MULTI_ROW_BLOCK_CASES +
+             FP32_MFMA_CASES + GENERIC_CASES)
 
 
 @pytest.mark.parametrize("spec", ALL_CASES, ids=[_case_id(c) for c in ALL_CASES])
