@@ -56,9 +56,14 @@ bool bwd_mfma_supports(const Params& p, int32_t dtype) {
     // 64 lanes of 32 bits
     if (p.Q > 65536) return false;
     if (p.mask_kind == TRIATTN_MASK_BLOCK) {
-        // dQ: one block row per 128-row workgroup; dK / dV: whole query tiles
-        // per block and one kv block per wave
-        if (p.q_block % 128 != 0 || p.kv_block % kKTile != 0) return false;
+        // dQ: one block row per 128-row workgroup, or 2 or 4 of 64 / 32 rows
+        // (each wave's 32 rows in one; their bitmaps hold kMultiWords x 32
+        // kv blocks); dK / dV: whole 32-row query tiles per block and one kv
+        // block per wave
+        if (p.kv_block % kKTile != 0) return false;
+        if (p.q_block % 128 != 0 &&
+            ((p.q_block != 64 && p.q_block != 32) || p.n_kv_blocks > tile::kMultiWords * 32))
+            return false;
         if (p.n_q_rows > 2048 || p.n_kv_blocks > kMaxKvBlocks) return false;
     }
     const int64_t kpad = (p.K + 127) / 128 * 128;

@@ -649,13 +649,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
 // takes dz as the B operand.  Masks as in the forward kernel: tiles past
 // the length or not listed are not visited, element masks only where a tile
 // needs one.
+// dQ kernel variant (a template value, not a mask kind of the calls) of
+// block masks with 32- or 64-row query blocks: 4 or 2 block rows per
+// 128-row workgroup, each wave's 32 rows in one.  Their bitmaps share the
+// LDS of the one-row ones: the union of the rows' listed kv blocks (the
+// tiles visited), then each row's listed and full blocks, kMultiWords
+// words apiece.
+constexpr int kBwdBlockRows = 5;
+
 template <typename T, int D, int KIND, int BIAS, bool EXACT, bool PAD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd<D>()))) void bwd_dq_kernel(
     Params p, BwdParams g) {
     using M = Mma<T>;
     using v8 = typename M::v8;
     using Ge = BGeo<D>;
-    constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK;
+    constexpr bool kBlock = KIND == TRIATTN_MASK_BLOCK || KIND == kBwdBlockRows;
+    constexpr bool kMultiRow = KIND == kBwdBlockRows;
     constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
     constexpr int kKvDma = 2 * Ge::tileDma / 4;  // K and V DMAs per wave and tile
     constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);
@@ -666,8 +675,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
     __shared__ __attribute__((aligned(1024))) char v_lds1[Ge::tileBytes];
     __shared__ __attribute__((aligned(1024))) char v_lds2[Ge::tileBytes];
     __shared__ __attribute__((aligned(1024))) char b_lds[BIAS == kBLds ? 4 * kBiasWaveBytes : 16];
-    __shared__ uint32_t listed_bits[kBlock ? kWords : 1];
-    __shared__ uint32_t full_bits[kBlock ? kWords : 1];
+    __shared__ uint32_t block_bits[kBlock ? 2 * kWords : 1];
+    uint32_t* const listed_bits = block_bits;
+    uint32_t* const full_bits = block_bits + kWords;
+    auto row_listed = [&](int r) { return block_bits + kMultiWords * (1 + r); };
+    auto row_full = [&](int r) { return block_bits + kMultiWords * (1 + kRowsMulti + r); };
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -700,23 +712,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
     const int n_tiles = (limit + kKTile - 1) / kKTile;
     const int n_tiles_all = (K + kKTile - 1) / kKTile;
     int tiles_per_block = 1;
+    int wrow = 0;  // 32- or 64-row query blocks: this wave's block row in the workgroup
     if constexpr (kBlock) {
         tiles_per_block = static_cast<int>(p.kv_block / kKTile);
         const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
-        for (int i = tid; i < words; i += 256) {
-            listed_bits[i] = 0u;
-            full_bits[i] = 0u;
-        }
-        __syncthreads();
         const int64_t inst = b * p.stride_b + n * p.stride_n + h * p.stride_h;
-        const int64_t list_row = inst * p.n_q_rows + q0 / p.q_block;
-        mark_list(listed_bits, p.kv_num_blocks, p.kv_indices, list_row, p.max_blocks, p.n_kv_blocks,
-                  tid, 256);
-        if (p.full_kv_num_blocks) {
-            mark_list(full_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid, 256);
-            mark_list(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
-                      p.full_max_blocks, p.n_kv_blocks, tid, 256);
+        if constexpr (!kMultiRow) {
+            for (int i = tid; i < words; i += 256) {
+                listed_bits[i] = 0u;
+                full_bits[i] = 0u;
+            }
+            __syncthreads();
+            const int64_t list_row = inst * p.n_q_rows + q0 / p.q_block;
+            mark_list(listed_bits, p.kv_num_blocks, p.kv_indices, list_row, p.max_blocks,
+                      p.n_kv_blocks, tid, 256);
+            if (p.full_kv_num_blocks) {
+                mark_list(full_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
+                          p.full_max_blocks, p.n_kv_blocks, tid, 256);
+                mark_list(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, list_row,
+                          p.full_max_blocks, p.n_kv_blocks, tid, 256);
+            }
+        } else {
+            const int qb = static_cast<int>(p.q_block);
+            const int rows = 128 / qb;  // 2 or 4
+            wrow = (32 * wave) / qb;
+            for (int i = tid; i < (1 + 2 * kRowsMulti) * kMultiWords; i += 256) block_bits[i] = 0u;
+            __syncthreads();
+            for (int r = 0; r < rows; ++r) {
+                const int64_t qrow_blk = q0 / qb + r;
+                if (qrow_blk >= p.n_q_rows) break;  // rows past Q
+                const int64_t list_row = inst * p.n_q_rows + qrow_blk;
+                mark_list(row_listed(r), p.kv_num_blocks, p.kv_indices, list_row, p.max_blocks,
+                          p.n_kv_blocks, tid, 256);
+                if (p.full_kv_num_blocks) {
+                    mark_list(row_full(r), p.full_kv_num_blocks, p.full_kv_indices, list_row,
+                              p.full_max_blocks, p.n_kv_blocks, tid, 256);
+                    mark_list(row_listed(r), p.full_kv_num_blocks, p.full_kv_indices, list_row,
+                              p.full_max_blocks, p.n_kv_blocks, tid, 256);
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < words; i += 256) {
+                uint32_t u = 0u;
+                for (int r = 0; r < rows; ++r) u |= row_listed(r)[i];
+                listed_bits[i] = u;
+            }
         }
         __syncthreads();
     }
@@ -894,9 +934,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
             dense_bits = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(dense_word), t & 63));
             need_mask = need_mask || dense_bits != ~0u;
         }
+        bool unlisted = false;  // a tile visited for another block row of the workgroup
         if constexpr (kBlock) {
-            if (p.mask_mod == TRIATTN_MOD_CAUSAL && !bit_set(full_bits, t / tiles_per_block) &&
-                k0 + kKTile - 1 > q0w) {
+            const int blk = t / tiles_per_block;
+            if (kMultiRow && !bit_set(row_listed(wrow), blk)) {
+                unlisted = true;
+                need_mask = true;
+            } else if (p.mask_mod == TRIATTN_MOD_CAUSAL &&
+                       !bit_set(kMultiRow ? row_full(wrow) : full_bits, blk) && k0 + kKTile - 1 > q0w) {
                 causal = true;
                 need_mask = true;
             }
@@ -905,6 +950,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(bwd_waves_p
             const int room = limit - k0;
             uint32_t w = room >= kKTile ? ~0u : room <= 0 ? 0u : (1u << room) - 1u;
             if (kDense) w &= dense_bits;
+            if constexpr (kMultiRow) {
+                if (unlisted) w = 0u;
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ka = 8 * (r / 4) + (r % 4);
@@ -1261,29 +1309,38 @@ __global__ __launch_bounds__(256) void bwd_dbias_combine_kernel(float* dbias, co
 // ---- launch -----------------------------------------------------------------
 // The workspace holds the row data: 8 B N H Q bytes of (Delta, -lse log2 e)
 // pairs, then one uint32 per 32-row tile.
+template <typename T, int D, int KIND, int BIAS, bool EXACT, bool PAD>
+void launch_bwd_pair(const Params& p, const BwdParams& g, float* rows, uint32_t* tdead, dim3 gdk,
+                     dim3 gdq, hipStream_t stream) {
+    const dim3 block(256);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, EXACT, PAD>), gdk, block, 0, stream, p, g, rows, tdead);
+    if constexpr (KIND == TRIATTN_MASK_BLOCK) {
+        if (p.q_block < 128) {  // 32- or 64-row query blocks
+            hipLaunchKernelGGL((bwd_dq_kernel<T, D, kBwdBlockRows, BIAS, EXACT, PAD>), gdq, block, 0, stream,
+                               p, g);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, EXACT, PAD>), gdq, block, 0, stream, p, g);
+}
+
 template <typename T, int D, int KIND, int BIAS>
 hipError_t launch_bwd_bias(const Params& p, const BwdParams& g, bool exact, float* rows,
                            uint32_t* tdead, hipStream_t stream) {
-    const dim3 block(256);
     const int64_t bnh = p.B * p.N * p.H;
     const int64_t gk = bnh * ((p.K + 127) / 128), gq = bnh * ((p.Q + 127) / 128);
     if (gk > 0x7fffffff || gq > 0x7fffffff) return hipErrorInvalidConfiguration;
     // head dimensions between the tile widths take the padded instantiations
     const dim3 gdk(static_cast<unsigned>(gk)), gdq(static_cast<unsigned>(gq));
     const bool pad = p.D != D;
-    if (exact && !pad) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, true, false>), gdk, block, 0, stream, p, g, rows, tdead);
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, true, false>), gdq, block, 0, stream, p, g);
-    } else if (!pad) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, false, false>), gdk, block, 0, stream, p, g, rows, tdead);
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, false, false>), gdq, block, 0, stream, p, g);
-    } else if (exact) {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, true, true>), gdk, block, 0, stream, p, g, rows, tdead);
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, true, true>), gdq, block, 0, stream, p, g);
-    } else {
-        hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, KIND, BIAS, false, true>), gdk, block, 0, stream, p, g, rows, tdead);
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D, KIND, BIAS, false, true>), gdq, block, 0, stream, p, g);
-    }
+    if (exact && !pad)
+        launch_bwd_pair<T, D, KIND, BIAS, true, false>(p, g, rows, tdead, gdk, gdq, stream);
+    else if (!pad)
+        launch_bwd_pair<T, D, KIND, BIAS, false, false>(p, g, rows, tdead, gdk, gdq, stream);
+    else if (exact)
+        launch_bwd_pair<T, D, KIND, BIAS, true, true>(p, g, rows, tdead, gdk, gdq, stream);
+    else
+        launch_bwd_pair<T, D, KIND, BIAS, false, true>(p, g, rows, tdead, gdk, gdq, stream);
     return hipGetLastError();
 }
 

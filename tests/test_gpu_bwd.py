@@ -81,8 +81,14 @@ CASES = [
     # D = 32, K not a multiple of 4 (scalar dz and dBias paths), about half
     # the rows fully masked
     (1, 3, 2, 40, 130, 32, "f16", "dense", {"p_valid": 0.005}),
-    # non-causal block mask at D = 64 with 32-row blocks: the general kernels
+    # 32- and 64-row query blocks on the MFMA kernels (dQ: 4 or 2 block rows
+    # per workgroup): non-causal, causal with full lists and a ragged last
+    # block row, sparse lists (rows with no listed block), D = 32 / 64 / 128
     (1, 2, 2, 96, 96, 64, "bf16", "block", {"q_block": 32, "kv_block": 32}),
+    (1, 2, 2, 200, 230, 128, "bf16", "block", {"q_block": 64, "kv_block": 32, "mask_mod": "causal"}),
+    (1, 2, 2, 160, 128, 32, "f16", "block", {"q_block": 32, "kv_block": 64, "block_density": 0.3}),
+    (2, 1, 2, 256, 256, 64, "bf16", "block", {"q_block": 32, "kv_block": 32, "mask_mod": "causal",
+                                               "block_broadcast": True, "bias": False}),
     # MFMA kernels: causal block lists (partial diagonal blocks, unlisted and
     # full blocks) with a bias
     (1, 2, 2, 256, 256, 64, "bf16", "block", {"q_block": 128, "kv_block": 64, "mask_mod": "causal"}),
