@@ -31,7 +31,7 @@ def _specs(n, seed, max_d_half, max_qk):
         Q, K = r.randint(1, max_qk), r.randint(1, max_qk)
         extra = {}
         if kind == "block":
-            extra.update(q_block=r.choice([128, 128, 64, 16]), kv_block=r.choice([32, 64, 128, 16]),
+            extra.update(q_block=r.choice([128, 128, 64, 32, 16]), kv_block=r.choice([32, 64, 128, 16]),
                          mask_mod=r.choice(["none", "causal"]))
         elif kind == "dense":
             extra["p_valid"] = r.choice([0.02, 0.5, 0.9])
