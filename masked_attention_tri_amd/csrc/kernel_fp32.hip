@@ -1,10 +1,10 @@
 // fp32 forward on the matrix core (v_mfma_f32_32x32x2_f32), for fp32 inputs
 // (head dimension D <= 32, a multiple of 4: the triangle_attention page's
 // envelope for fp32, Notes item 3) with no mask, kv_lengths, a dense key
-// mask, a BlockMask whose query blocks are whole 128-row tiles and whose
-// key blocks are whole 32-key tiles, or packed sequences (the Transformer
-// Engine page's layouts, no mask or causal); other block sizes stay on the
-// generic kernel.
+// mask, a BlockMask whose query blocks are 32 or 64 rows or whole 128-row
+// tiles and whose key blocks are whole 32-key tiles, or packed sequences
+// (the Transformer Engine page's layouts, no mask or causal); other block
+// sizes stay on the generic kernel.
 //
 // A workgroup of 4 waves takes 128 query rows of one (b, n, h), wave w rows
 // 32w .. 32w+31, lane l the row 32w + l%32.  Keys go in tiles of 32, staged
@@ -23,12 +23,16 @@
 // row with no valid key gets the uniform-weight result over all K keys
 // (mean of V, max -1e9, lse -1e9 + ln K), as in the other kernels.
 //
-// Block masks (the tensorplay BlockMask page): the workgroup's 128 rows lie
-// in one block row, whose listed and full blocks (kv_indices and
-// full_kv_indices, read as a union, ids out of range ignored) are marked as
-// bits in LDS; key tiles of unlisted blocks are skipped, and the causal
-// mask_mod (query >= key) applies per element only on listed blocks that are
-// not full.
+// Block masks (the tensorplay BlockMask page): the listed and full blocks of
+// the workgroup's block row (kv_indices and full_kv_indices, read as a
+// union, ids out of range ignored) are marked as bits in LDS; key tiles of
+// unlisted blocks are skipped, and the causal mask_mod (query >= key)
+// applies per element only on listed blocks that are not full.  Query
+// blocks of 32 or 64 rows put 4 or 2 block rows in the 128 rows (each
+// wave's 32 rows in one): the workgroup visits the union of their listed
+// blocks, and a wave masks whole the tiles its own row does not list.  Their
+// bitmaps share the LDS of the one-row ones: the union, then each row's
+// listed and full bits, kMultiWords words apiece.
 #include <math.h>
 
 #include "triattn_internal.h"
@@ -44,6 +48,11 @@ constexpr int kQT = 32 * kW;  // query rows per workgroup
 constexpr int kKT = 32;       // keys per tile
 constexpr int kDT = 32;       // head dimension of the tiles (zero columns past D)
 constexpr int kRow = kDT + 1;  // LDS row stride in floats (odd)
+constexpr int kWords = static_cast<int>(kMaxKvBlocks / 32);  // one bitmap of kv blocks
+// 32- or 64-row query blocks: up to kRows block rows per workgroup, whose
+// union and per-row bitmaps share the LDS of two one-row bitmaps
+constexpr int kRows = kQT / 32;
+constexpr int kMultiWords = 2 * kWords / (1 + 2 * kRows);
 
 __device__ __forceinline__ f32x16 mma(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -57,8 +66,9 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
     __shared__ float k_lds[kKT * kRow];
     __shared__ float v_lds[kKT * kRow];
     __shared__ uint32_t valid_word;  // bit i: key k0 + i of the tile valid
-    __shared__ uint32_t listed_bits[kMaxKvBlocks / 32];
-    __shared__ uint32_t full_bits[kMaxKvBlocks / 32];
+    __shared__ uint32_t block_bits[2 * kWords];
+    uint32_t* const listed_bits = block_bits;
+    uint32_t* const full_bits = block_bits + kWords;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 31, half = lane >> 5;
@@ -104,17 +114,23 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
     if (seq_causal) limit = limit < q0 + kQT ? limit : q0 + kQT;
     const int64_t n_tiles = (limit + kKT - 1) / kKT;
 
-    // the block row of the workgroup: listed and full blocks as bits
+    // the block row(s) of the workgroup: listed and full blocks as bits
     const bool block_kind = p.mask_kind == TRIATTN_MASK_BLOCK;
+    const bool multi = block_kind && p.q_block < kQT;  // 32- or 64-row query blocks
+    const int wrow = multi ? static_cast<int>(32 * wave / p.q_block) : 0;
+    uint32_t* const my_listed = multi ? block_bits + kMultiWords * (1 + wrow) : listed_bits;
+    uint32_t* const my_full = multi ? block_bits + kMultiWords * (1 + kRows + wrow) : full_bits;
     if (block_kind) {  // uniform over the workgroup
         const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
-        for (int i = tid; i < words; i += 64 * kW) {
-            listed_bits[i] = 0u;
-            full_bits[i] = 0u;
+        const int clear = multi ? (1 + 2 * kRows) * kMultiWords : 2 * kWords;
+        for (int i = tid; i < clear; i += 64 * kW) {
+            // (one-row bitmaps: only the words of n_kv_blocks)
+            if (multi || i % kWords < words) block_bits[i] = 0u;
         }
         __syncthreads();
-        const int64_t list_row = (b * p.stride_b + n * p.stride_n + h * p.stride_h) * p.n_q_rows + q0 / p.q_block;
-        auto mark = [&](uint32_t* bits, const int32_t* counts, const int32_t* ids, int64_t width) {
+        const int64_t inst = b * p.stride_b + n * p.stride_n + h * p.stride_h;
+        auto mark = [&](uint32_t* bits, const int32_t* counts, const int32_t* ids, int64_t width,
+                        int64_t list_row) {
             int64_t cnt = counts[list_row];
             cnt = cnt < 0 ? 0 : (cnt > width ? width : cnt);
             for (int64_t j = tid; j < cnt; j += 64 * kW) {
@@ -122,10 +138,23 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
                 if (id >= 0 && id < p.n_kv_blocks) atomicOr(&bits[id >> 5], 1u << (id & 31));
             }
         };
-        mark(listed_bits, p.kv_num_blocks, p.kv_indices, p.max_blocks);
-        if (p.full_kv_num_blocks) {
-            mark(full_bits, p.full_kv_num_blocks, p.full_kv_indices, p.full_max_blocks);
-            mark(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, p.full_max_blocks);
+        const int rows = multi ? static_cast<int>(kQT / p.q_block) : 1;
+        for (int r = 0; r < rows; ++r) {
+            const int64_t qrow_blk = q0 / p.q_block + r;
+            if (qrow_blk >= p.n_q_rows) break;  // rows past Q
+            const int64_t list_row = inst * p.n_q_rows + qrow_blk;
+            uint32_t* const rl = multi ? block_bits + kMultiWords * (1 + r) : listed_bits;
+            uint32_t* const rf = multi ? block_bits + kMultiWords * (1 + kRows + r) : full_bits;
+            // (with several rows, listed_bits is their union)
+            mark(rl, p.kv_num_blocks, p.kv_indices, p.max_blocks, list_row);
+            if (multi) mark(listed_bits, p.kv_num_blocks, p.kv_indices, p.max_blocks, list_row);
+            if (p.full_kv_num_blocks) {
+                mark(rf, p.full_kv_num_blocks, p.full_kv_indices, p.full_max_blocks, list_row);
+                mark(rl, p.full_kv_num_blocks, p.full_kv_indices, p.full_max_blocks, list_row);
+                if (multi)
+                    mark(listed_bits, p.full_kv_num_blocks, p.full_kv_indices, p.full_max_blocks,
+                         list_row);
+            }
         }
         __syncthreads();
     }
@@ -151,10 +180,12 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
     for (int64_t t = 0; t < n_tiles; ++t) {
         const int64_t k0 = t * kKT;
         bool causal = false;  // element mask q >= key on this tile
+        bool mine = true;     // listed for this wave's block row
         if (block_kind) {
             const int64_t blk = t / tiles_per_block;
             if (!bit(listed_bits, blk)) continue;  // (uniform: no barrier skipped unevenly)
-            causal = p.mask_mod == TRIATTN_MOD_CAUSAL && !bit(full_bits, blk);
+            mine = bit(my_listed, blk);
+            causal = p.mask_mod == TRIATTN_MOD_CAUSAL && !bit(my_full, blk);
         }
         __syncthreads();  // the previous tile is no longer read
         {
@@ -191,7 +222,7 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int kr = 8 * (r / 4) + 4 * half + (r % 4);
-            const bool ok = ((vw >> kr) & 1u) && (!(causal || seq_causal) || row >= k0 + kr);
+            const bool ok = mine && ((vw >> kr) & 1u) && (!(causal || seq_causal) || row >= k0 + kr);
             const float bias = brow && ok ? brow[k0 + kr] : 0.f;
             z[r] = ok ? fmaf(s[r], p.scale, bias) : -INFINITY;
             tmax = fmaxf(tmax, z[r]);
@@ -269,10 +300,15 @@ bool fp32_mfma_supports(const Params& p) {
         p.mask_kind != TRIATTN_MASK_DENSE && p.mask_kind != TRIATTN_MASK_BLOCK &&
         p.mask_kind != kMaskVarlen)
         return false;
-    // a workgroup's 128 rows in one block row, whole 32-key tiles per block
-    if (p.mask_kind == TRIATTN_MASK_BLOCK &&
-        (p.q_block % kQT != 0 || p.kv_block % kKT != 0 || p.n_kv_blocks > kMaxKvBlocks))
-        return false;
+    // a workgroup's 128 rows in one block row, or 2 or 4 rows of 64 / 32
+    // (their bitmaps hold kMultiWords x 32 kv blocks); whole 32-key tiles
+    // per block
+    if (p.mask_kind == TRIATTN_MASK_BLOCK) {
+        if (p.kv_block % kKT != 0 || p.n_kv_blocks > kMaxKvBlocks) return false;
+        if (p.q_block % kQT != 0 &&
+            ((p.q_block != 32 && p.q_block != 64) || p.n_kv_blocks > kMultiWords * 32))
+            return false;
+    }
     if (p.D < 4 || p.D > kDT || p.D % 4 != 0 || p.bias16) return false;
     // 16-byte loads of Q, K and V rows and stores of O rows
     const uintptr_t al = reinterpret_cast<uintptr_t>(p.q) | reinterpret_cast<uintptr_t>(p.k) |
