@@ -3,9 +3,10 @@
 // Serves every (dtype, D) in the envelope of the triangle_attention page
 // (Notes item 3: D <= 32 for fp32, D <= 256 for the half types, the wider
 // bound being the one that page gives its newest forward kernels) and every
-// mask form; it is the path for shapes the MFMA kernels do not take (fp32
-// inputs with a block mask or packed sequences, and the half-type cases
-// outside the MFMA kernel's envelope).  Lanes split the keys
+// mask form; it is the path for what the MFMA kernels do not take (block
+// masks with query blocks other than 32, 64 or a multiple of 128 rows, or
+// key blocks that are not whole 32-key tiles; unaligned fp32 tensors; and
+// the other half-type cases outside the MFMA kernel's envelope).  Lanes split the keys
 // for the logits and the d coordinates for P.V; the softmax runs online over
 // chunks of 64 keys with a running max and sum (the max-shifted evaluation of
 // the page's softmax), so a row of any length needs O(D) state.
