@@ -14,8 +14,8 @@
 // every key and it passes nothing to Q, K or the bias.  The bias is shared by
 // every n, so dB sums over n.
 //
-// These are the general kernels: fp32 inputs, head dimensions without an MFMA
-// backward (mfma_bwd.h), and the dBias of block-sparse masks.  Three
+// These are the general kernels: fp32 inputs, and the head dimensions and
+// block sizes without an MFMA backward (mfma_bwd.h).  Three
 // launches, no atomics, every sum in a fixed order:
 //   dQ    dq_kernel: 32 query rows per workgroup, fp32 tiles staged in LDS
 //         (see Tiles below), looping over key tiles.  dQ = s dz K.
@@ -264,8 +264,10 @@ __device__ __forceinline__ int mfma_row(int r, int lane) {
 // pairs), and from fp32 FMAs for fp32 inputs.  Every thread of the
 // workgroup must call it (it holds a barrier for the half types).
 template <typename T>
+// blk_state: -1, or (block lists whose kv block holds the whole 32-key tile)
+// this row's state of that block, bit 0 listed and bit 1 full (row_block_state)
 __device__ __forceinline__ void pair_tile(const Params& p, Tiles t, int64_t b, int64_t n,
-                                          int64_t h, int64_t q0, int64_t k0) {
+                                          int64_t h, int64_t q0, int64_t k0, int blk_state = -1) {
     const int64_t D = p.D, ld = D + 1;
     const int ql = threadIdx.x >> 3, kb = threadIdx.x & 7;
     float z[4] = {0.f, 0.f, 0.f, 0.f}, dp[4] = {0.f, 0.f, 0.f, 0.f};
@@ -303,7 +305,10 @@ __device__ __forceinline__ void pair_tile(const Params& p, Tiles t, int64_t b, i
         if (qi < p.Q && kk < p.K) {
             if (dead) {
                 pr = inv_k;
-            } else if (key_valid(p, b, n, h, qi, kk)) {
+            } else if (blk_state >= 0
+                           ? ((blk_state & 2) != 0 ||
+                              ((blk_state & 1) != 0 && (p.mask_mod != TRIATTN_MOD_CAUSAL || qi >= kk)))
+                           : key_valid(p, b, n, h, qi, kk)) {
                 const float bias = p.bias ? p.bias[((b * p.H + h) * p.Q + qi) * p.K + kk] : 0.f;
                 pr = softmax_p(z[j], p.scale * kLog2e, bias, t.lse[ql] * kLog2e);
                 dz = pr * (dp[j] - t.delta[ql]);
@@ -312,6 +317,32 @@ __device__ __forceinline__ void pair_tile(const Params& p, Tiles t, int64_t b, i
         t.ps[ql * (kT + 1) + kl] = pr;
         t.dzs[ql * (kT + 1) + kl] = dz;
     }
+}
+
+// Block lists whose kv blocks are whole 32-key tiles: the state of kv block
+// `blk` in the list rows of query row qi (bit 0 listed in the kv or full
+// list, bit 1 in the full list), the same as key_valid's tests for every key
+// of the block.  The 8 threads of a row (consecutive lanes, threadIdx.x % 8
+// = kb) scan every 8th entry and combine their findings, so every thread
+// must call it.
+__device__ int row_block_state(const Params& p, int64_t b, int64_t n, int64_t h, int64_t qi,
+                               int64_t blk, int kb) {
+    const int64_t inst = b * p.stride_b + n * p.stride_n + h * p.stride_h;
+    const int64_t qc = qi < p.Q ? qi : p.Q - 1;
+    const int64_t row = inst * p.n_q_rows + qc / p.q_block;
+    int st = 0;
+    auto scan = [&](const int32_t* counts, const int32_t* ids, int64_t width, int bits) {
+        int64_t count = counts[row];
+        count = count < 0 ? 0 : (count > width ? width : count);
+        for (int64_t j = kb; j < count; j += 8)
+            if (ids[row * width + j] == blk) st |= bits;
+    };
+    scan(p.kv_num_blocks, p.kv_indices, p.max_blocks, 1);
+    if (p.full_kv_num_blocks) scan(p.full_kv_num_blocks, p.full_kv_indices, p.full_max_blocks, 3);
+    st |= __shfl_xor(st, 1);
+    st |= __shfl_xor(st, 2);
+    st |= __shfl_xor(st, 4);
+    return st;
 }
 
 // dQ: one workgroup per (b, n, h, 32 query rows); loops over key tiles.
@@ -509,6 +540,8 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
     const int ql = threadIdx.x >> 3, kb = threadIdx.x & 7;
     const int64_t qi = q0 + ql;
     float* dbr = g.dbias + (bh * p.Q + qi) * p.K;  // this thread's row (when qi < Q)
+    // block lists of whole 32-key tiles: one list scan per row and tile
+    const bool by_block = p.mask_kind == TRIATTN_MASK_BLOCK && p.kv_block % kT == 0;
     if (qi < p.Q)
         for (int64_t kk = kc0 + kb; kk < kc1; kk += 8) dbr[kk] = 0.f;
     for (int64_t n = 0; n < p.N; ++n) {
@@ -525,7 +558,8 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
             stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
             stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
             __syncthreads();
-            pair_tile<T>(p, t, b, n, h, q0, k0);
+            const int st = by_block ? row_block_state(p, b, n, h, qi, k0 / p.kv_block, kb) : -1;
+            pair_tile<T>(p, t, b, n, h, q0, k0, st);
             if (qi < p.Q) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -537,10 +571,9 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
     }
 }
 
-// The general kernels; with dbias_only, just dBias (the MFMA backward's
-// block-sparse case).
+// The general kernels.
 template <typename T, int NC>
-hipError_t launch_nc(const Params& p, const BwdParams& g, bool dbias_only, hipStream_t stream) {
+hipError_t launch_nc(const Params& p, const BwdParams& g, hipStream_t stream) {
     const int64_t n_qt = (p.Q + kT - 1) / kT, n_kt = (p.K + kT - 1) / kT;
     const int64_t n_kc = (p.K + kT * kChunk - 1) / (kT * kChunk);
     const int64_t gq = p.B * p.N * p.H * n_qt, gk = p.B * p.N * p.H * n_kt,
@@ -562,9 +595,9 @@ hipError_t launch_nc(const Params& p, const BwdParams& g, bool dbias_only, hipSt
                                     hipFuncAttributeMaxDynamicSharedMemorySize, b);
         if (e != hipSuccess) return e;
     }
-    if (!dbias_only && gq > 0)
+    if (gq > 0)
         hipLaunchKernelGGL((dq_kernel<T, NC>), dim3(static_cast<unsigned>(gq)), block, shm, stream, p, g);
-    if (!dbias_only && gk > 0)
+    if (gk > 0)
         hipLaunchKernelGGL((dkdv_kernel<T, NC>), dim3(static_cast<unsigned>(gk)), block, shm, stream, p, g);
     if (g.dbias && gb > 0)
         hipLaunchKernelGGL((dbias_kernel<T, NC>), dim3(static_cast<unsigned>(gb)), block, shm, stream, p, g);
@@ -572,35 +605,28 @@ hipError_t launch_nc(const Params& p, const BwdParams& g, bool dbias_only, hipSt
 }
 
 template <typename T>
-hipError_t launch_t(const Params& p, const BwdParams& g, bool dbias_only, hipStream_t stream) {
-    if (p.D <= 32) return launch_nc<T, 4>(p, g, dbias_only, stream);
-    if (p.D <= 64) return launch_nc<T, 8>(p, g, dbias_only, stream);
-    if (p.D <= 128) return launch_nc<T, 16>(p, g, dbias_only, stream);
-    return launch_nc<T, 32>(p, g, dbias_only, stream);
+hipError_t launch_t(const Params& p, const BwdParams& g, hipStream_t stream) {
+    if (p.D <= 32) return launch_nc<T, 4>(p, g, stream);
+    if (p.D <= 64) return launch_nc<T, 8>(p, g, stream);
+    if (p.D <= 128) return launch_nc<T, 16>(p, g, stream);
+    return launch_nc<T, 32>(p, g, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd(const Params& p, const BwdParams& g, int32_t dtype, float* ws,
                       size_t ws_bytes, hipStream_t stream) {
-    if (bwd_mfma_supports(p, dtype)) {
-        hipError_t e = p.D <= 32   ? launch_bwd_mfma_d32(p, g, dtype, ws, ws_bytes, stream)
-                       : p.D <= 64 ? launch_bwd_mfma_d64(p, g, dtype, ws, ws_bytes, stream)
-                                   : launch_bwd_mfma_d128(p, g, dtype, ws, ws_bytes, stream);
-        if (e != hipSuccess) return e;
-        // dBias of a block-sparse mask: the general walk over n
-        if (p.mask_kind == TRIATTN_MASK_BLOCK && g.dbias && p.bias)
-            return dtype == TRIATTN_BF16 ? launch_t<__bf16>(p, g, true, stream)
-                                         : launch_t<_Float16>(p, g, true, stream);
-        return hipSuccess;
-    }
+    if (bwd_mfma_supports(p, dtype))
+        return p.D <= 32   ? launch_bwd_mfma_d32(p, g, dtype, ws, ws_bytes, stream)
+               : p.D <= 64 ? launch_bwd_mfma_d64(p, g, dtype, ws, ws_bytes, stream)
+                           : launch_bwd_mfma_d128(p, g, dtype, ws, ws_bytes, stream);
     switch (dtype) {
     case TRIATTN_F32:
-        return launch_t<float>(p, g, false, stream);
+        return launch_t<float>(p, g, stream);
     case TRIATTN_F16:
-        return launch_t<_Float16>(p, g, false, stream);
+        return launch_t<_Float16>(p, g, stream);
     case TRIATTN_BF16:
-        return launch_t<__bf16>(p, g, false, stream);
+        return launch_t<__bf16>(p, g, stream);
     }
     return hipErrorInvalidValue;
 }

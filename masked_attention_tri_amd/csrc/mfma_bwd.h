@@ -1065,6 +1065,7 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
     using G = DbGeo<D>;
     constexpr bool kDense = KIND == TRIATTN_MASK_DENSE;
     constexpr bool kLens = KIND == TRIATTN_MASK_KV_LENGTHS;
+    constexpr bool kBlockM = KIND == TRIATTN_MASK_BLOCK;
     constexpr int R = G::slots;
     static_assert(R == 2, "every position waits for all DMAs (counts differ between waves)");
     __shared__ __attribute__((aligned(1024))) char t_lds[R][G::slotBytes];
@@ -1076,6 +1077,12 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
     // for the DMAs issued before it).
     constexpr int kChunkN = 512;
     __shared__ uint64_t valid_w[kChunkN * G::keyWords];
+    // Block lists (query blocks of 32, 64 or a multiple of 128 rows, kv
+    // blocks of whole 32-key tiles: each wave's 32 x 32 block lies in one
+    // block row and one kv block): per n of the chunk, bits 2w and 2w + 1 of
+    // blk_w say whether wave w's kv block is listed (kv or full list) and full.
+    static_assert(G::waves <= 16, "two bits per wave in a word");
+    __shared__ uint32_t blk_w[kBlockM ? kChunkN : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1135,6 +1142,39 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
                     if (drow[kb + j] != 0) word |= 1ull << j;
             }
             valid_w[i] = word;
+        }
+        if constexpr (kBlockM) {
+            for (int i = tid; i < c1 - c0; i += 64 * G::waves) blk_w[i] = 0u;
+            __syncthreads();
+            // one thread per (n, query sub-tile, list entry)
+            const int64_t inst0 = b * p.stride_b + h * p.stride_h;
+            const int64_t wl = p.max_blocks, wf = p.full_kv_num_blocks ? p.full_max_blocks : 0;
+            const int64_t per = G::QW * (wl + wf);
+            const int64_t total = static_cast<int64_t>(c1 - c0) * per;
+            for (int64_t e = tid; e < total; e += 64 * G::waves) {
+                const int m = c0 + static_cast<int>(e / per);
+                const int64_t r = e % per;
+                const int qgi = static_cast<int>(r / (wl + wf));
+                const int64_t j = r % (wl + wf);
+                const int qs = q0 + 32 * qgi;  // the sub-tile's first query
+                if (qs >= Q) continue;
+                const int64_t row = (inst0 + m * p.stride_n) * p.n_q_rows + qs / p.q_block;
+                const bool full = j >= wl;
+                const int32_t* counts = full ? p.full_kv_num_blocks : p.kv_num_blocks;
+                const int32_t* ids = full ? p.full_kv_indices : p.kv_indices;
+                const int64_t width = full ? wf : wl, jj = full ? j - wl : j;
+                int64_t cnt = counts[row];
+                cnt = cnt < 0 ? 0 : (cnt > width ? width : cnt);
+                if (jj >= cnt) continue;
+                const int64_t id = ids[row * width + jj];
+                uint32_t bits = 0u;
+#pragma unroll
+                for (int kgi = 0; kgi < G::KW; ++kgi) {
+                    const int ks = k0 + 32 * kgi;  // the sub-tile's first key
+                    if (ks < K && id == ks / p.kv_block) bits |= (full ? 3u : 1u) << (2 * (qgi + G::QW * kgi));
+                }
+                if (bits) atomicOr(&blk_w[m - c0], bits);
+            }
         }
     };
     auto any_valid = [&](int m) {
@@ -1225,14 +1265,23 @@ __global__ __launch_bounds__(64 * DbGeo<D>::waves) void bwd_dbias_kernel(Params 
         for (int st = 0; st < D / 16; ++st)
             dp = M::run(row_operand<v8>(t + v_tile, rrd, st), row_operand<v8>(t + g_tile, rrd, st), dp);
         // keys valid for this n (the ragged tile of a length, the dense mask)
-        const uint32_t w = static_cast<uint32_t>(valid_w[(m - c0) * G::keyWords + kg / 2] >> (32 * (kg % 2)));
-        if (w != ~0u) {
+        uint32_t w = static_cast<uint32_t>(valid_w[(m - c0) * G::keyWords + kg / 2] >> (32 * (kg % 2)));
+        bool causal = false;  // block lists: the causal mask_mod on a listed, not full block
+        if constexpr (kBlockM) {
+            const uint32_t st = (blk_w[m - c0] >> (2 * wave)) & 3u;
+            if (st == 0u)
+                w = 0u;
+            else if (st == 1u && p.mask_mod == TRIATTN_MOD_CAUSAL && kw + 31 > q0 + 32 * qg)
+                causal = true;
+        }
+        if (w != ~0u || causal) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ka = 8 * (r / 4) + (r % 4);
                 const uint32_t lo = static_cast<uint32_t>(static_cast<int32_t>(w << (31 - ka)) >> 31);
                 const uint32_t hi = static_cast<uint32_t>(static_cast<int32_t>(w << (27 - ka)) >> 31);
-                const bool ok = __builtin_amdgcn_inverse_ballot_w64(lo | (static_cast<uint64_t>(hi) << 32));
+                bool ok = __builtin_amdgcn_inverse_ballot_w64(lo | (static_cast<uint64_t>(hi) << 32));
+                if constexpr (kBlockM) ok = ok && (!causal || qrow >= kw + ka + 4 * half);
                 z[r] = ok ? z[r] : -INFINITY;
             }
         }
@@ -1363,7 +1412,7 @@ hipError_t launch_bwd_kind(const Params& p, const BwdParams& g, bool exact, floa
     else
         e = launch_bwd_bias<T, D, KIND, kBScalar>(p, g, exact, rows, tdead, stream);
     if (e != hipSuccess) return e;
-    if constexpr (KIND != TRIATTN_MASK_BLOCK) {
+    {
         if (g.dbias && p.bias) {
             using G = DbGeo<D>;
             // splits beyond the first need a plane of partial sums each, after

@@ -89,6 +89,11 @@ CASES = [
     (1, 2, 2, 160, 128, 32, "f16", "block", {"q_block": 32, "kv_block": 64, "block_density": 0.3}),
     (2, 1, 2, 256, 256, 64, "bf16", "block", {"q_block": 32, "kv_block": 32, "mask_mod": "causal",
                                                "block_broadcast": True, "bias": False}),
+    # dBias of block lists on the MFMA kernel: lists per n, several n ranges
+    # summed by the combine kernel
+    (1, 8, 2, 256, 200, 64, "bf16", "block", {"q_block": 64, "kv_block": 64, "mask_mod": "causal"}),
+    (1, 6, 1, 130, 260, 128, "f16", "block", {"q_block": 128, "kv_block": 32,
+                                              "block_density": 0.4}),
     # MFMA kernels: causal block lists (partial diagonal blocks, unlisted and
     # full blocks) with a bias
     (1, 2, 2, 256, 256, 64, "bf16", "block", {"q_block": 128, "kv_block": 64, "mask_mod": "causal"}),
