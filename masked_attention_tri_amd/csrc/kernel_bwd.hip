@@ -345,6 +345,16 @@ __device__ int row_block_state(const Params& p, int64_t b, int64_t n, int64_t h,
     return st;
 }
 
+// pair_tile's blk_state for this thread's row of the tile at (q0, k0):
+// the row's block state for block lists whose kv blocks are whole 32-key
+// tiles, else -1 (key_valid per element).  Called by every thread.
+__device__ int tile_block_state(const Params& p, int64_t b, int64_t n, int64_t h, int64_t q0,
+                                int64_t k0) {
+    if (p.mask_kind != TRIATTN_MASK_BLOCK || p.kv_block % kT != 0) return -1;
+    const int ql = threadIdx.x >> 3, kb = threadIdx.x & 7;
+    return row_block_state(p, b, n, h, q0 + ql, k0 / p.kv_block, kb);
+}
+
 // dQ: one workgroup per (b, n, h, 32 query rows); loops over key tiles.
 // Thread t owns row t / 8 and columns d = t % 8 + 8 i.
 template <typename T, int NC>
@@ -376,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void dq_kernel(Params p, BwdParams g) {
         stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
         stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
         __syncthreads();
-        pair_tile<T>(p, t, b, n, h, q0, k0);
+        pair_tile<T>(p, t, b, n, h, q0, k0, tile_block_state(p, b, n, h, q0, k0));
         __syncthreads();
         if constexpr (kMfma) {
             // dQ(q, d) += sum_k dz(q, k) K(k, d)
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void dkdv_kernel(Params p, BwdParams g) {
         stage(t.gos, static_cast<const T*>(g.dout) + bnh * p.Q * D, q0, p.Q, D);
         stage_rows<T>(p, g, t, bnh, q0);
         __syncthreads();
-        pair_tile<T>(p, t, b, n, h, q0, k0);
+        pair_tile<T>(p, t, b, n, h, q0, k0, tile_block_state(p, b, n, h, q0, k0));
         __syncthreads();
         if constexpr (kMfma) {
             // dV(k, d) += sum_q P(q, k) dO(q, d);  dK(k, d) += sum_q dz(q, k) Q(q, d)
@@ -540,8 +550,6 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
     const int ql = threadIdx.x >> 3, kb = threadIdx.x & 7;
     const int64_t qi = q0 + ql;
     float* dbr = g.dbias + (bh * p.Q + qi) * p.K;  // this thread's row (when qi < Q)
-    // block lists of whole 32-key tiles: one list scan per row and tile
-    const bool by_block = p.mask_kind == TRIATTN_MASK_BLOCK && p.kv_block % kT == 0;
     if (qi < p.Q)
         for (int64_t kk = kc0 + kb; kk < kc1; kk += 8) dbr[kk] = 0.f;
     for (int64_t n = 0; n < p.N; ++n) {
@@ -558,8 +566,7 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(Params p, BwdParams g) 
             stage(t.ks, static_cast<const T*>(p.k) + bnh * p.K * D, k0, p.K, D);
             stage(t.vs, static_cast<const T*>(p.v) + bnh * p.K * D, k0, p.K, D);
             __syncthreads();
-            const int st = by_block ? row_block_state(p, b, n, h, qi, k0 / p.kv_block, kb) : -1;
-            pair_tile<T>(p, t, b, n, h, q0, k0, st);
+            pair_tile<T>(p, t, b, n, h, q0, k0, tile_block_state(p, b, n, h, q0, k0));
             if (qi < p.Q) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
