@@ -21,12 +21,13 @@ bool mfma_supports(const Params& p, int32_t dtype) {
         return false;
     if (p.mask_kind == TRIATTN_MASK_BLOCK) {
         // whole 128-row tiles per block, or 2 or 4 blocks of 64 / 32 rows
-        // per tile (each wave's 32 rows in one block; their bitmaps hold
-        // kMultiWords x 32 kv blocks)
-        if (p.kv_block % kKTile != 0) return false;
-        if (p.q_block % kQTileBlock != 0 &&
-            ((p.q_block != 64 && p.q_block != 32) || p.n_kv_blocks > tile::kMultiWords * 32))
-            return false;
+        // per tile (each wave's 32 rows in one block); kv blocks of whole
+        // 32-key tiles, or of 16 keys (two per tile).  Both exceptions take
+        // bitmaps of kMultiWords x 32 kv blocks.
+        const bool q_split = p.q_block % kQTileBlock != 0, kv16 = p.kv_block == 16;
+        if (p.kv_block % kKTile != 0 && !kv16) return false;
+        if (q_split && p.q_block != 64 && p.q_block != 32) return false;
+        if ((q_split || kv16) && p.n_kv_blocks > tile::kMultiWords * 32) return false;
     }
     // Byte offsets within one (b, n, h) or (b, h) slice, including the
     // overhang of a ragged last tile and of the last query tile, must fit

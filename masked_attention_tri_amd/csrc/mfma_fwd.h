@@ -118,7 +118,8 @@ __device__ __forceinline__ uint32_t* row_full_bits(uint32_t* bits, int r) {
 // D = 64 a bias with a block-sparse mask, with a dense mask, or with a scale
 // that is not a power of two needs more than 128 VGPRs (the block
 // bookkeeping, the mask words, the bias / s products), and so does a dense
-// mask with such a scale (the mask operands of the logits' MFMAs): those
+// mask with such a scale (the mask operands of the logits' MFMAs), and so
+// does the variant for 32- / 64-row query blocks and 16-key blocks: those
 // kernels run three waves instead of spilling.
 template <int D, int KIND, int BIAS, bool EXACT>
 constexpr int min_waves_per_simd() {
@@ -127,6 +128,7 @@ constexpr int min_waves_per_simd() {
          !EXACT))
         return 3;
     if (D == 64 && KIND == TRIATTN_MASK_DENSE && !EXACT) return 3;
+    if (D == 64 && KIND == kMaskBlockRows) return 3;  // the per-wave block-row and 16-key state
     return D <= 64 ? 4 : D <= 128 ? 2 : 1;
 }
 
@@ -255,11 +257,13 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
     const int n_tiles = (limit + kKTile - 1) / kKTile;
     const int n_tiles_all = (K + kKTile - 1) / kKTile;
     int tiles_per_block = 1;
-    constexpr bool multi_row = KIND == kMaskBlockRows;  // 32- or 64-row query blocks
+    constexpr bool multi_row = KIND == kMaskBlockRows;  // 32- or 64-row query blocks, 16-key blocks
+    // 16-key kv blocks (only in that variant): tile t holds blocks 2t, 2t + 1
+    const bool kv16 = multi_row && p.kv_block == 16;
     int wrow = 0;  // with multi_row: this wave's block row within the workgroup
     // (if constexpr keeps the block bitmaps out of the other kinds' LDS)
     if constexpr (kBlock) {
-        tiles_per_block = static_cast<int>(p.kv_block / kKTile);
+        tiles_per_block = kv16 ? 1 : static_cast<int>(p.kv_block / kKTile);
         const int words = static_cast<int>((p.n_kv_blocks + 31) / 32);
         const int64_t inst = b * p.stride_b + n * p.stride_n + h * p.stride_h;
         if constexpr (!multi_row) {
@@ -279,8 +283,9 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
             }
         } else {
             const int qb = static_cast<int>(p.q_block);
-            const int rows = kQTileBlock / qb;  // 2 or 4
-            wrow = (32 * wave) / qb;
+            const bool split = qb < kQTileBlock;
+            const int rows = split ? kQTileBlock / qb : 1;  // 2 or 4 block rows, or one
+            wrow = split ? (32 * wave) / qb : 0;
             for (int i = tid; i < (1 + 2 * kRowsMulti) * kMultiWords; i += kThreads)
                 block_bits[i] = 0u;
             __syncthreads();
@@ -312,6 +317,7 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
             return n_tiles > 0 ? 0 : -1;
         } else {
             const int64_t blk = next_set(listed_bits, 0, p.n_kv_blocks);
+            if (kv16) return blk < 0 ? -1 : static_cast<int>(blk >> 1);
             return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
         }
     };
@@ -320,6 +326,10 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         if constexpr (!kBlock) {
             return t + 1 < n_tiles ? t + 1 : -1;
         } else {
+            if (kv16) {  // tile t holds blocks 2t and 2t + 1
+                const int64_t blk = next_set(listed_bits, 2 * static_cast<int64_t>(t) + 2, p.n_kv_blocks);
+                return blk < 0 ? -1 : static_cast<int>(blk >> 1);
+            }
             if ((t + 1) % tiles_per_block != 0 && t + 1 < n_tiles_all) return t + 1;
             const int64_t blk = next_set(listed_bits, t / tiles_per_block + 1, p.n_kv_blocks);
             return blk < 0 ? -1 : static_cast<int>(blk) * tiles_per_block;
@@ -609,9 +619,31 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
         bool causal = false;
         if constexpr (kDense) need_mask = false;  // (masked in the logits' MFMAs)
         bool unlisted = false;  // a tile visited for another block row of the workgroup
+        uint32_t half_w = ~0u;  // 16-key blocks: the keys of the tile's listed blocks
+        uint32_t causal_w = ~0u;  // 16-key blocks: the keys under the causal mask_mod
+        if constexpr (multi_row) {
+            if (kv16) {
+                const uint32_t* rl = row_listed_bits(block_bits, wrow);
+                const uint32_t* rf = row_full_bits(block_bits, wrow);
+                const int b0 = 2 * t;
+                const bool l0 = bit_set(rl, b0), l1 = bit_set(rl, b0 + 1);
+                half_w = (l0 ? 0x0000ffffu : 0u) | (l1 ? 0xffff0000u : 0u);
+                if (half_w != ~0u) need_mask = true;
+                if (p.mask_mod == TRIATTN_MOD_CAUSAL && k0 + kKTile - 1 > q0w) {
+                    causal_w = (l0 && !bit_set(rf, b0) ? 0x0000ffffu : 0u) |
+                               (l1 && !bit_set(rf, b0 + 1) ? 0xffff0000u : 0u);
+                    if (causal_w != 0u) {
+                        causal = true;
+                        need_mask = true;
+                    }
+                }
+            }
+        }
         if constexpr (kBlock) {
             const int blk = t / tiles_per_block;
-            if (multi_row && !bit_set(row_listed_bits(block_bits, wrow), blk)) {
+            if (multi_row && kv16) {
+                // (the 16-key halves above)
+            } else if (multi_row && !bit_set(row_listed_bits(block_bits, wrow), blk)) {
                 unlisted = true;
                 need_mask = true;
             } else if (p.mask_mod == TRIATTN_MOD_CAUSAL &&
@@ -633,7 +665,11 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
             uint32_t w = room >= kKTile ? ~0u : room <= 0 ? 0u : (1u << room) - 1u;
             if constexpr (multi_row) {
                 if (unlisted) w = 0u;
+                w &= half_w;
             }
+            // 16-key blocks: the causal test only on the keys of partial blocks
+            const bool causal_all = causal && causal_w == ~0u;
+            const bool causal_some = causal && causal_w != ~0u;  // (16-key blocks only)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int ka = 8 * (r / 4) + (r % 4);  // key offset in lanes 0-31
@@ -642,7 +678,16 @@ __attribute__((amdgpu_waves_per_eu(min_waves_per_simd<D, KIND, BIAS, EXACT>())))
                 const uint32_t lo = static_cast<uint32_t>(static_cast<int32_t>(w << (31 - ka)) >> 31);
                 const uint32_t hi = static_cast<uint32_t>(static_cast<int32_t>(w << (27 - ka)) >> 31);
                 bool ok = __builtin_amdgcn_inverse_ballot_w64(lo | (static_cast<uint64_t>(hi) << 32));
-                if (causal) ok = ok && qrow >= k0 + ka + 4 * half;
+                if (causal_all) ok = ok && qrow >= k0 + ka + 4 * half;
+                if constexpr (multi_row) {
+                    if (causal_some) {
+                        // the field of key ka (lanes 0-31) or ka + 4 (lanes 32-63)
+                        const uint32_t clo = static_cast<uint32_t>(static_cast<int32_t>(causal_w << (31 - ka)) >> 31);
+                        const uint32_t chi = static_cast<uint32_t>(static_cast<int32_t>(causal_w << (27 - ka)) >> 31);
+                        const bool c = __builtin_amdgcn_inverse_ballot_w64(clo | (static_cast<uint64_t>(chi) << 32));
+                        ok = ok && (!c || qrow >= k0 + ka + 4 * half);
+                    }
+                }
                 s[r] = ok ? s[r] : -INFINITY;
             }
         }
@@ -938,7 +983,8 @@ hipError_t launch_d(const Params& p, bool exact, hipStream_t stream) {
     case TRIATTN_MASK_DENSE:
         return launch_kind<T, D, TRIATTN_MASK_DENSE>(p, exact, stream);
     case TRIATTN_MASK_BLOCK:
-        if (p.q_block < kQTileBlock) return launch_kind<T, D, kMaskBlockRows>(p, exact, stream);
+        if (p.q_block < kQTileBlock || p.kv_block < kKTile)
+            return launch_kind<T, D, kMaskBlockRows>(p, exact, stream);
         return launch_kind<T, D, TRIATTN_MASK_BLOCK>(p, exact, stream);
     case kMaskVarlen:
         return launch_kind<T, D, kMaskVarlen>(p, exact, stream);

@@ -163,8 +163,9 @@ FP32_MFMA_CASES = [
     (1, 2, 2, 9, 1, 32, "f32", "none", {}),
 ]
 
-# half types with 32- or 64-row query blocks on the MFMA kernel (2 or 4
-# block rows per 128-row workgroup, each with its own kv lists): ragged Q
+# half types with 32- or 64-row query blocks or 16-key kv blocks on the MFMA
+# kernel (2 or 4 block rows per 128-row workgroup, each with its own kv
+# lists; two kv blocks per key tile): ragged Q
 # (a last block row partly or wholly past Q), rows with no listed block,
 # causal with full lists, broadcast lists, every width class, an inexact
 # scale, no bias
@@ -182,10 +183,19 @@ MULTI_ROW_BLOCK_CASES = [
     (1, 1, 2, 160, 128, 64, "bf16", "block", {"q_block": 32, "kv_block": 32, "bias": False,
                                                "mask_mod": "causal"}),
     (1, 2, 2, 64, 64, 64, "bf16", "block", {"q_block": 32, "kv_block": 32}),
+    # 16-key kv blocks (two per 32-key tile, each listed, full or causal on
+    # its own), with every query block size of the variant
+    (1, 2, 2, 200, 150, 64, "bf16", "block", {"q_block": 128, "kv_block": 16, "mask_mod": "causal"}),
+    (1, 2, 2, 130, 97, 128, "f16", "block", {"q_block": 64, "kv_block": 16, "block_density": 0.4}),
+    (2, 1, 2, 96, 120, 32, "bf16", "block", {"q_block": 32, "kv_block": 16, "mask_mod": "causal",
+                                              "block_broadcast": True}),
+    (1, 2, 2, 256, 64, 256, "bf16", "block", {"q_block": 256, "kv_block": 16, "mask_mod": "causal",
+                                               "bias": False}),
 ]
 
-# the generic kernel: fp32 block masks, and block masks whose query blocks
-# are not whole 128-row tiles or 32 / 64 rows
+# the generic kernel: block masks whose query blocks are not whole 128-row
+# tiles or 32 / 64 rows, or whose kv blocks are neither 16 keys nor whole
+# 32-key tiles
 GENERIC_CASES = [
     (2, 2, 2, 40, 37, 16, "bf16", "block", {"q_block": 16, "kv_block": 8, "mask_mod": "causal"}),
     (1, 2, 2, 64, 64, 64, "bf16", "block", {"q_block": 96, "kv_block": 32}),
