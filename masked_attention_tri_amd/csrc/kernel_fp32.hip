@@ -2,9 +2,9 @@
 // (head dimension D <= 32, a multiple of 4: the triangle_attention page's
 // envelope for fp32, Notes item 3) with no mask, kv_lengths, a dense key
 // mask, a BlockMask whose query blocks are 32 or 64 rows or whole 128-row
-// tiles and whose key blocks are whole 32-key tiles, or packed sequences
-// (the Transformer Engine page's layouts, no mask or causal); other block
-// sizes stay on the generic kernel.
+// tiles and whose key blocks are 16 keys or whole 32-key tiles, or packed
+// sequences (the Transformer Engine page's layouts, no mask or causal);
+// other block sizes stay on the generic kernel.
 //
 // A workgroup of 4 waves takes 128 query rows of one (b, n, h), wave w rows
 // 32w .. 32w+31, lane l the row 32w + l%32.  Keys go in tiles of 32, staged
@@ -27,7 +27,8 @@
 // the workgroup's block row (kv_indices and full_kv_indices, read as a
 // union, ids out of range ignored) are marked as bits in LDS; key tiles of
 // unlisted blocks are skipped, and the causal mask_mod (query >= key)
-// applies per element only on listed blocks that are not full.  Query
+// applies per element only on listed blocks that are not full (with 16-key
+// blocks, a tile holds two, each listed, full or causal on its own).  Query
 // blocks of 32 or 64 rows put 4 or 2 block rows in the 128 rows (each
 // wave's 32 rows in one): the workgroup visits the union of their listed
 // blocks, and a wave masks whole the tiles its own row does not list.  Their
@@ -158,7 +159,9 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
         }
         __syncthreads();
     }
-    const int64_t tiles_per_block = block_kind ? p.kv_block / kKT : 1;
+    // 16-key blocks: tile t holds blocks 2t and 2t + 1
+    const bool kv16 = block_kind && p.kv_block == 16;
+    const int64_t tiles_per_block = block_kind && !kv16 ? p.kv_block / kKT : 1;
     auto bit = [](const uint32_t* bits, int64_t i) { return ((bits[i >> 5] >> (i & 31)) & 1u) != 0; };
 
     // Q^T operand: dims 16 half .. 16 half + 15 of the row (0 past D)
@@ -179,14 +182,28 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
     const int st_key = tid >> 3, st_c = tid & 7;
     for (int64_t t = 0; t < n_tiles; ++t) {
         const int64_t k0 = t * kKT;
-        bool causal = false;  // element mask q >= key on this tile
-        bool mine = true;     // listed for this wave's block row
+        // keys of the tile listed for this wave's block row, and keys under
+        // the causal mask_mod (listed, not full)
+        uint32_t mine_w = ~0u, causal_w = 0u;
         if (block_kind) {
-            const int64_t blk = t / tiles_per_block;
-            if (!bit(listed_bits, blk)) continue;  // (uniform: no barrier skipped unevenly)
-            mine = bit(my_listed, blk);
-            causal = p.mask_mod == TRIATTN_MOD_CAUSAL && !bit(my_full, blk);
+            const bool causal_mod = p.mask_mod == TRIATTN_MOD_CAUSAL;
+            if (kv16) {
+                const int64_t b0 = 2 * t;
+                // (uniform: no barrier skipped unevenly)
+                if (!bit(listed_bits, b0) && !bit(listed_bits, b0 + 1)) continue;
+                const bool l0 = bit(my_listed, b0), l1 = bit(my_listed, b0 + 1);
+                mine_w = (l0 ? 0x0000ffffu : 0u) | (l1 ? 0xffff0000u : 0u);
+                if (causal_mod)
+                    causal_w = (l0 && !bit(my_full, b0) ? 0x0000ffffu : 0u) |
+                               (l1 && !bit(my_full, b0 + 1) ? 0xffff0000u : 0u);
+            } else {
+                const int64_t blk = t / tiles_per_block;
+                if (!bit(listed_bits, blk)) continue;  // (uniform: no barrier skipped unevenly)
+                mine_w = bit(my_listed, blk) ? ~0u : 0u;
+                causal_w = causal_mod && !bit(my_full, blk) ? ~0u : 0u;
+            }
         }
+        if (seq_causal) causal_w = ~0u;
         __syncthreads();  // the previous tile is no longer read
         {
             const int64_t key = k0 + st_key;
@@ -222,7 +239,7 @@ __global__ __launch_bounds__(64 * kW) void fp32_fwd_kernel(Params p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int kr = 8 * (r / 4) + 4 * half + (r % 4);
-            const bool ok = mine && ((vw >> kr) & 1u) && (!(causal || seq_causal) || row >= k0 + kr);
+            const bool ok = (((vw & mine_w) >> kr) & 1u) && (((causal_w >> kr) & 1u) == 0u || row >= k0 + kr);
             const float bias = brow && ok ? brow[k0 + kr] : 0.f;
             z[r] = ok ? fmaf(s[r], p.scale, bias) : -INFINITY;
             tmax = fmaxf(tmax, z[r]);
@@ -304,7 +321,7 @@ bool fp32_mfma_supports(const Params& p) {
     // (their bitmaps hold kMultiWords x 32 kv blocks); whole 32-key tiles
     // per block
     if (p.mask_kind == TRIATTN_MASK_BLOCK) {
-        if (p.kv_block % kKT != 0 || p.n_kv_blocks > kMaxKvBlocks) return false;
+        if ((p.kv_block % kKT != 0 && p.kv_block != 16) || p.n_kv_blocks > kMaxKvBlocks) return false;
         if (p.q_block % kQT != 0 &&
             ((p.q_block != 32 && p.q_block != 64) || p.n_kv_blocks > kMultiWords * 32))
             return false;

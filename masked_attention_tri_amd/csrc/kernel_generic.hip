@@ -5,7 +5,7 @@
 // bound being the one that page gives its newest forward kernels) and every
 // mask form; it is the path for what the MFMA kernels do not take (block
 // masks with query blocks other than 32, 64 or a multiple of 128 rows, or
-// key blocks that are neither 16 keys (half types) nor whole 32-key tiles;
+// key blocks that are neither 16 keys nor whole 32-key tiles;
 // unaligned fp32 tensors; and
 // the other half-type cases outside the MFMA kernel's envelope).  Lanes split the keys
 // for the logits and the d coordinates for P.V; the softmax runs online over

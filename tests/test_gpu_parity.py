@@ -140,7 +140,8 @@ BLOCK_D128_CASES = [
 ]
 
 # fp32 inputs on the fp32 MFMA kernel (no mask, lengths, dense masks, block
-# masks of 32-, 64- or whole 128-row query blocks and whole 32-key tiles):
+# masks of 32-, 64- or whole 128-row query blocks and 16-key or whole
+# 32-key blocks):
 # several 128-row query tiles and 32-key tiles with ragged tails, rows with no valid key (length 0, a 2%
 # dense mask, sparse block lists), an inexact scale, no bias, widths below 32
 FP32_MFMA_CASES = [
@@ -153,6 +154,9 @@ FP32_MFMA_CASES = [
     (1, 2, 2, 130, 200, 16, "f32", "block", {"q_block": 32, "kv_block": 64, "block_density": 0.3}),
     (2, 1, 2, 96, 96, 8, "f32", "block", {"q_block": 32, "kv_block": 32, "mask_mod": "causal",
                                            "block_broadcast": True, "bias": False}),
+    # 16-key blocks (two per key tile)
+    (1, 2, 2, 150, 97, 32, "f32", "block", {"q_block": 128, "kv_block": 16, "mask_mod": "causal"}),
+    (1, 2, 2, 100, 130, 16, "f32", "block", {"q_block": 64, "kv_block": 16, "block_density": 0.4}),
     (1, 2, 2, 300, 250, 28, "f32", "kv_lengths", {"len_range": (0, 250)}),
     (1, 3, 2, 150, 131, 32, "f32", "dense", {}),
     (1, 2, 2, 140, 70, 16, "f32", "dense", {"p_valid": 0.02}),
